@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the scan workloads.
+
+This module holds no recurrence arithmetic.  It draws the inputs that both the
+GPU library and the CPU reference consume, so the two sides always see exactly
+the same values.  Every generator returns host (CPU) torch tensors.
+
+Recipe (all draws from ``numpy.random.default_rng(seed)``; transcendentals in
+float64; rounding to float32 by round-to-nearest-even; bfloat16 values are
+float64 -> float32 -> bfloat16, each step round-to-nearest-even):
+
+* elementwise, small:  a ~ U(0.5, 1), b ~ N(0, 1), u ~ N(0, 1), s0 = none, [B,T,N]
+* elementwise, gated:  a = sigmoid(z), z ~ N(2, 1); u ~ N(0, 1); s0 ~ N(0, 1)
+* Mamba-2 shaped:      dt = softplus(N(0,1)) [B,T,H]; A_h = -exp(U(0,2)) [H];
+                       g = dt * A_h (one log-decay per head and step);
+                       B, C ~ N(0,1) bf16 [B,T,1,K]; x ~ N(0,1) bf16 [B,T,H,V]
+* GLA shaped:          q, k, v ~ N(0,1) bf16 [B,T,H,D]; gk = logsigmoid(N(0,1))/16
+                       fp32 [B,T,H,K]; readout scale K**-0.5
+* DeltaNet shaped:     q, k = row-L2-normalised N(0,1), bf16 [B,T,H,K];
+                       v ~ N(0,1) bf16 [B,T,H,V]; beta = sigmoid(N(0,1)) fp32 [B,T,H]
+
+Model shapes follow the models named on the pages: Mamba-2 130m (24 heads x 64,
+state 128) [SunnyNet log §4.1]; GLA 340M (4 heads x 128) [SunnyNet log §4.3];
+DeltaNet 340M (8 heads x 128) [SunnyNet log §4.2].  SunnyNet log =
+"SunnyNet 工程化实录：一个 O(N) 架构如何长出自己的 C 推理运行时" (developer.aliyun.com/article/1773847).
+"""
+from __future__ import annotations
+
+import hashlib
+
+import numpy as np
+import torch
+
+SEED_BASE = 1000  # config i uses SEED_BASE + i
+
+# Full workload sizes (one GPU).
+ELEM_SMALL = dict(B=2, T=128, N=128)
+GATED_LARGE = dict(B=16, T=8192, N=2048)
+MAMBA2 = dict(B=8, T=4096, H=24, Hg=1, K=128, V=64)
+GLA = dict(B=4, T=4096, H=4, K=128, V=128)
+DELTANET = dict(B=4, T=4096, H=8, K=128, V=128)
+DELTANET_K64 = dict(B=4, T=4096, H=8, K=64, V=128)
+
+
+def _f32(x64: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x64, dtype=np.float32))
+
+
+def _bf16(x64: np.ndarray) -> torch.Tensor:
+    return _f32(x64).to(torch.bfloat16)
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _softplus(z):
+    return np.logaddexp(0.0, z)
+
+
+def _logsigmoid(z):
+    return -np.logaddexp(0.0, -z)
+
+
+def digest(t: torch.Tensor) -> str:
+    """sha256 (first 16 hex digits) of a tensor's bytes, for logging inputs."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    return hashlib.sha256(t.numpy().tobytes()).hexdigest()[:16]
+
+
+def elementwise_small(B=2, T=128, N=128, seed=SEED_BASE + 1):
+    """a ~ U(0.5,1), b ~ N(0,1), u ~ N(0,1), fp32 [B,T,N]; no initial state."""
+    rng = np.random.default_rng(seed)
+    a = rng.uniform(0.5, 1.0, size=(B, T, N))
+    b = rng.standard_normal((B, T, N))
+    u = rng.standard_normal((B, T, N))
+    return dict(a=_f32(a), b=_f32(b), u=_f32(u), s0=None)
+
+
+def gated_large(B=16, T=8192, N=2048, seed=SEED_BASE + 2, with_s0=True):
+    """a = sigmoid(z), z ~ N(2,1); u ~ N(0,1); s0 ~ N(0,1); fp32 [B,T,N].
+
+    Drawn one batch row at a time so the float64 temporaries stay small.
+    """
+    rng = np.random.default_rng(seed)
+    a = torch.empty((B, T, N), dtype=torch.float32)
+    u = torch.empty((B, T, N), dtype=torch.float32)
+    for b in range(B):
+        z = rng.standard_normal((T, N)) + 2.0
+        a[b] = _f32(_sigmoid(z))
+        del z
+        u[b] = _f32(rng.standard_normal((T, N)))
+    s0 = _f32(rng.standard_normal((B, N))) if with_s0 else None
+    return dict(a=a, u=u, s0=s0)
+
+
+def mamba2(B=8, T=4096, H=24, K=128, V=64, seed=SEED_BASE + 3):
+    """Mamba-2 shaped decay-separable scan, one B/C group (Hg = 1).
+
+    Mapping onto the scan: q = C, k = B, v = x, g = dt*A (one value per head and
+    step, decay mode 0), k_scale = dt, readout scale 1.
+    """
+    rng = np.random.default_rng(seed)
+    dt = _softplus(rng.standard_normal((B, T, H)))
+    A = -np.exp(rng.uniform(0.0, 2.0, size=(H,)))
+    dt32 = np.asarray(dt, dtype=np.float32)
+    A32 = np.asarray(A, dtype=np.float32)
+    g = dt32.astype(np.float64) * A32.astype(np.float64)[None, None, :]
+    Bm = rng.standard_normal((B, T, 1, K))
+    Cm = rng.standard_normal((B, T, 1, K))
+    x = rng.standard_normal((B, T, H, V))
+    return dict(q=_bf16(Cm), k=_bf16(Bm), v=_bf16(x), g=_f32(g), decay_mode=0,
+                k_scale=_f32(dt32), scale=1.0, s0=None, A=_f32(A32))
+
+
+def gla(B=4, T=4096, H=4, K=128, V=128, seed=SEED_BASE + 4):
+    """GLA shaped scan: per-key decay gk = logsigmoid(N(0,1))/16 (decay mode 1)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, K))
+    k = rng.standard_normal((B, T, H, K))
+    v = rng.standard_normal((B, T, H, V))
+    gk = _logsigmoid(rng.standard_normal((B, T, H, K))) / 16.0
+    return dict(q=_bf16(q), k=_bf16(k), v=_bf16(v), g=_f32(gk), decay_mode=1,
+                k_scale=None, scale=float(K) ** -0.5, s0=None)
+
+
+def deltanet(B=4, T=4096, H=8, K=128, V=128, seed=SEED_BASE + 5):
+    """DeltaNet shaped delta-rule scan: L2-normalised q, k; beta = sigmoid(N(0,1))."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, K))
+    k = rng.standard_normal((B, T, H, K))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, V))
+    beta = _sigmoid(rng.standard_normal((B, T, H)))
+    return dict(q=_bf16(q), k=_bf16(k), v=_bf16(v), beta=_f32(beta), scale=1.0, s0=None)
+
+
+def random_state(shape, seed, std=1.0):
+    """An fp32 initial state ~ N(0, std^2) for continuation and unit tests."""
+    rng = np.random.default_rng(seed)
+    return _f32(rng.standard_normal(shape) * std)

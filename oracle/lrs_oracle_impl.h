@@ -1,0 +1,226 @@
+/*
+ * Body of the sequential reference recurrences.  Included twice by
+ * lrs_oracle.c, once with REAL=double (suffix _f64) and once with REAL=float
+ * (suffix _f32).  Every loop below is the plain definition of the recurrence,
+ * one time step after another, with no blocking, fusion or reordering.
+ *
+ * TEST INFRASTRUCTURE: see the header comment of lrs_oracle.c.
+ */
+
+#define ORC_CAT2(a, b) a##b
+#define ORC_CAT(a, b) ORC_CAT2(a, b)
+#define ORC_FN(name) ORC_CAT(name, SFX)
+
+/*
+ * First-order FMA recurrence, per channel (b, n):
+ *     s_t = a_t * s_{t-1} + b_t,   t = 1..T,   s_0 = s0[b,n] (0 when s0 is NULL)
+ * [SunnyNet log §2.1, the "FMA" form of the unified update].
+ * Layout: a, bb, s are [B,T,N] row-major; s0, s_final are [B,N].
+ * Memory row t-1 of s holds s_t; s_final = s_T.
+ * The channels of one batch row are advanced together (loop over n inside the
+ * loop over t) only so that memory is read in order; each channel's own
+ * arithmetic is the definition, step by step.
+ */
+void ORC_FN(orc_scan_fma)(const REAL* a, const REAL* bb, const REAL* s0, REAL* s,
+                          REAL* s_final, int64_t B, int64_t T, int64_t N, int nthreads) {
+    int64_t nblk = (N + ORC_NBLK - 1) / ORC_NBLK;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t w = 0; w < B * nblk; ++w) {
+        int64_t b = w / nblk, n_lo = (w % nblk) * ORC_NBLK;
+        int64_t n_hi = n_lo + ORC_NBLK < N ? n_lo + ORC_NBLK : N;
+        REAL st[ORC_NBLK];
+        for (int64_t n = n_lo; n < n_hi; ++n) st[n - n_lo] = s0 ? s0[b * N + n] : (REAL)0;
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t row = (b * T + t) * N;
+            for (int64_t n = n_lo; n < n_hi; ++n) {
+                REAL prod = a[row + n] * st[n - n_lo];
+                REAL next = prod + bb[row + n];
+                st[n - n_lo] = next;
+                s[row + n] = next;
+            }
+        }
+        for (int64_t n = n_lo; n < n_hi; ++n) s_final[b * N + n] = st[n - n_lo];
+    }
+}
+
+/*
+ * Gated (convex) first-order recurrence, per channel (b, n):
+ *     s_t = a_t * s_{t-1} + (1 - a_t) * u_t
+ * [SunnyNet log §2.1, the gated form of the unified update], evaluated in the
+ * literal order written there.  Layout and s0 / s_final as orc_scan_fma.
+ */
+void ORC_FN(orc_scan_gated)(const REAL* a, const REAL* u, const REAL* s0, REAL* s,
+                            REAL* s_final, int64_t B, int64_t T, int64_t N, int nthreads) {
+    int64_t nblk = (N + ORC_NBLK - 1) / ORC_NBLK;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t w = 0; w < B * nblk; ++w) {
+        int64_t b = w / nblk, n_lo = (w % nblk) * ORC_NBLK;
+        int64_t n_hi = n_lo + ORC_NBLK < N ? n_lo + ORC_NBLK : N;
+        REAL st[ORC_NBLK];
+        for (int64_t n = n_lo; n < n_hi; ++n) st[n - n_lo] = s0 ? s0[b * N + n] : (REAL)0;
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t row = (b * T + t) * N;
+            for (int64_t n = n_lo; n < n_hi; ++n) {
+                REAL at = a[row + n];
+                REAL keep = at * st[n - n_lo];
+                REAL inject = ((REAL)1 - at) * u[row + n];
+                REAL next = keep + inject;
+                st[n - n_lo] = next;
+                s[row + n] = next;
+            }
+        }
+        for (int64_t n = n_lo; n < n_hi; ++n) s_final[b * N + n] = st[n - n_lo];
+    }
+}
+
+/*
+ * Decay-separable outer-product state recurrence with readout, per (b, h):
+ *     alpha_t[i] = exp(g[b,t,h])        (decay_mode 0: one decay per head and step)
+ *     alpha_t[i] = exp(g[b,t,h,i])      (decay_mode 1: one decay per key row)
+ *     S_t[i][j]  = alpha_t[i] * S_{t-1}[i][j] + (kappa_t * k_t[i]) * v_t[j]
+ *     o_t[j]     = scale * sum_i S_t[i][j] * q_t[i]      (read after the update)
+ * Mamba-2: decay exp(dt*A) shared by the whole state, injection (dt*B) outer x
+ * [SunnyNet log §4.1]; GLA: decay diag(exp(gk)) on the key axis, readout
+ * scale * S^T q [SunnyNet log §4.3]; both restated in [vs llama.cpp §3].
+ * kappa_t = k_scale[b,t,h] (1 when k_scale is NULL).
+ * Layouts: q, k [B,T,Hg,K]; v, o [B,T,H,V]; g [B,T,H] or [B,T,H,K];
+ * k_scale [B,T,H]; s0, s_final [B,H,K,V].  Head h reads q/k group h/(H/Hg).
+ */
+void ORC_FN(orc_scan_diag_outer)(const REAL* q, const REAL* k, const REAL* v, const REAL* g,
+                                 int decay_mode, const REAL* k_scale, REAL scale,
+                                 const REAL* s0, REAL* o, REAL* s_final, int64_t B, int64_t T,
+                                 int64_t H, int64_t Hg, int64_t K, int64_t V, int nthreads) {
+    int64_t heads_per_group = H / Hg;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int64_t b = bh / H, h = bh % H, grp = h / heads_per_group;
+        REAL* S = (REAL*)malloc(sizeof(REAL) * (size_t)(K * V));
+        REAL* alpha = (REAL*)malloc(sizeof(REAL) * (size_t)K);
+        for (int64_t e = 0; e < K * V; ++e) S[e] = s0 ? s0[bh * K * V + e] : (REAL)0;
+        for (int64_t t = 0; t < T; ++t) {
+            const REAL* qt = q + ((b * T + t) * Hg + grp) * K;
+            const REAL* kt = k + ((b * T + t) * Hg + grp) * K;
+            const REAL* vt = v + ((b * T + t) * H + h) * V;
+            REAL kap = k_scale ? k_scale[(b * T + t) * H + h] : (REAL)1;
+            for (int64_t i = 0; i < K; ++i) {
+                REAL gi = decay_mode == 0 ? g[(b * T + t) * H + h] : g[((b * T + t) * H + h) * K + i];
+                alpha[i] = ORC_EXP(gi);
+            }
+            for (int64_t i = 0; i < K; ++i) {
+                REAL kk = kap * kt[i];
+                for (int64_t j = 0; j < V; ++j) {
+                    REAL keep = alpha[i] * S[i * V + j];
+                    REAL inject = kk * vt[j];
+                    S[i * V + j] = keep + inject;
+                }
+            }
+            REAL* ot = o + ((b * T + t) * H + h) * V;
+            for (int64_t j = 0; j < V; ++j) {
+                REAL acc = 0;
+                for (int64_t i = 0; i < K; ++i) acc += S[i * V + j] * qt[i];
+                ot[j] = scale * acc;
+            }
+        }
+        for (int64_t e = 0; e < K * V; ++e) s_final[bh * K * V + e] = S[e];
+        free(S);
+        free(alpha);
+    }
+}
+
+/*
+ * Delta rule with readout, rank-1 form, per (b, h):
+ *     p_j      = sum_i S_{t-1}[i][j] * k_t[i]          (p = S^T k)
+ *     delta_j  = beta_t * (v_t[j] - p_j)
+ *     S_t[i][j]= S_{t-1}[i][j] + k_t[i] * delta_j       (S += k outer delta)
+ *     o_t[j]   = scale * sum_i S_t[i][j] * q_t[i]       (o = scale * S^T q)
+ * [SunnyNet log §4.2]; restated in [vs llama.cpp §3].  The pages read out
+ * with no scale, i.e. scale = 1.
+ * Layouts: q, k [B,T,H,K]; v, o [B,T,H,V]; beta [B,T,H]; s0, s_final [B,H,K,V].
+ */
+void ORC_FN(orc_scan_delta)(const REAL* q, const REAL* k, const REAL* v, const REAL* beta,
+                            REAL scale, const REAL* s0, REAL* o, REAL* s_final, int64_t B,
+                            int64_t T, int64_t H, int64_t K, int64_t V, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int64_t b = bh / H, h = bh % H;
+        REAL* S = (REAL*)malloc(sizeof(REAL) * (size_t)(K * V));
+        REAL* dl = (REAL*)malloc(sizeof(REAL) * (size_t)V);
+        for (int64_t e = 0; e < K * V; ++e) S[e] = s0 ? s0[bh * K * V + e] : (REAL)0;
+        for (int64_t t = 0; t < T; ++t) {
+            const REAL* qt = q + ((b * T + t) * H + h) * K;
+            const REAL* kt = k + ((b * T + t) * H + h) * K;
+            const REAL* vt = v + ((b * T + t) * H + h) * V;
+            REAL bt = beta[(b * T + t) * H + h];
+            for (int64_t j = 0; j < V; ++j) {
+                REAL p = 0;
+                for (int64_t i = 0; i < K; ++i) p += S[i * V + j] * kt[i];
+                dl[j] = bt * (vt[j] - p);
+            }
+            for (int64_t i = 0; i < K; ++i)
+                for (int64_t j = 0; j < V; ++j) S[i * V + j] += kt[i] * dl[j];
+            REAL* ot = o + ((b * T + t) * H + h) * V;
+            for (int64_t j = 0; j < V; ++j) {
+                REAL acc = 0;
+                for (int64_t i = 0; i < K; ++i) acc += S[i * V + j] * qt[i];
+                ot[j] = scale * acc;
+            }
+        }
+        for (int64_t e = 0; e < K * V; ++e) s_final[bh * K * V + e] = S[e];
+        free(S);
+        free(dl);
+    }
+}
+
+/*
+ * Delta rule, explicit form, per (b, h): a second, independent implementation
+ * of the same update, written as a dense K x K transition
+ *     M_t = I - beta_t * k_t k_t^T,      S_t = M_t S_{t-1} + beta_t * k_t v_t^T
+ * [SunnyNet log §4.2, the explicit (I - beta k k^T) S + beta k v^T form that
+ * the page says must be implemented and checked separately from the rank-1
+ * form].  Readout and layouts as orc_scan_delta.
+ */
+void ORC_FN(orc_scan_delta_explicit)(const REAL* q, const REAL* k, const REAL* v,
+                                     const REAL* beta, REAL scale, const REAL* s0, REAL* o,
+                                     REAL* s_final, int64_t B, int64_t T, int64_t H, int64_t K,
+                                     int64_t V, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int64_t b = bh / H, h = bh % H;
+        REAL* S = (REAL*)malloc(sizeof(REAL) * (size_t)(K * V));
+        REAL* Sn = (REAL*)malloc(sizeof(REAL) * (size_t)(K * V));
+        REAL* M = (REAL*)malloc(sizeof(REAL) * (size_t)(K * K));
+        for (int64_t e = 0; e < K * V; ++e) S[e] = s0 ? s0[bh * K * V + e] : (REAL)0;
+        for (int64_t t = 0; t < T; ++t) {
+            const REAL* qt = q + ((b * T + t) * H + h) * K;
+            const REAL* kt = k + ((b * T + t) * H + h) * K;
+            const REAL* vt = v + ((b * T + t) * H + h) * V;
+            REAL bt = beta[(b * T + t) * H + h];
+            for (int64_t r = 0; r < K; ++r)
+                for (int64_t c = 0; c < K; ++c)
+                    M[r * K + c] = (r == c ? (REAL)1 : (REAL)0) - bt * kt[r] * kt[c];
+            for (int64_t r = 0; r < K; ++r)
+                for (int64_t j = 0; j < V; ++j) {
+                    REAL acc = 0;
+                    for (int64_t c = 0; c < K; ++c) acc += M[r * K + c] * S[c * V + j];
+                    Sn[r * V + j] = acc + bt * kt[r] * vt[j];
+                }
+            REAL* tmp = S;
+            S = Sn;
+            Sn = tmp;
+            REAL* ot = o + ((b * T + t) * H + h) * V;
+            for (int64_t j = 0; j < V; ++j) {
+                REAL acc = 0;
+                for (int64_t i = 0; i < K; ++i) acc += S[i * V + j] * qt[i];
+                ot[j] = scale * acc;
+            }
+        }
+        for (int64_t e = 0; e < K * V; ++e) s_final[bh * K * V + e] = S[e];
+        free(S);
+        free(Sn);
+        free(M);
+    }
+}
+
+#undef ORC_FN
+#undef ORC_CAT
+#undef ORC_CAT2

@@ -1,0 +1,477 @@
+"""Pins of the CPU oracle against facts it does not compute itself.
+
+Each test fixes the oracle to something independent of its own loops: values
+worked by hand from the pages' update equations (tests/golden/), closed forms
+(cumulative products and sums, geometric series, quadratic "attention" forms),
+exact rational arithmetic on a different formula, special cases that reduce to
+a textbook routine (a causal masked matmul), invariants, a second algorithm
+(the chunked UT form of the delta rule, solved with numpy.linalg), and the
+structural facts the pages assert (decay decomposability, segment
+continuation).  Citations use the page titles:
+  SunnyNet log  = "SunnyNet 工程化实录：一个 O(N) 架构如何长出自己的 C 推理运行时"
+  vs llama.cpp  = "我拿同一份权重和 llama.cpp 正面比了一场：我手写的 C 内核，慢了 1.1–1.7 倍"
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rel(x, y):
+    """Normwise relative difference max|x-y| / max|y|."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    d = np.max(np.abs(x - y)) if x.size else 0.0
+    m = np.max(np.abs(y)) if y.size else 0.0
+    return d / m if m > 0 else d
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ----------------------------------------------------------------------------
+# Hand-worked examples (tests/golden/*.json, each citing its equation)
+# ----------------------------------------------------------------------------
+
+def test_golden_fma_hand():
+    d = _load("fma_hand.json")
+    s, fin = oracle.scan_fma(np.array(d["a"]), np.array(d["b"]), np.array(d["s0"]))
+    assert np.array_equal(s, np.array(d["s"]))
+    assert np.array_equal(fin, np.array(d["s_final"]))
+
+
+def test_golden_gated_hand():
+    d = _load("gated_hand.json")
+    s, fin = oracle.scan_gated(np.array(d["a"]), np.array(d["u"]), np.array(d["s0"]))
+    assert np.array_equal(s, np.array(d["s"]))
+    assert np.array_equal(fin, np.array(d["s_final"]))
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_golden_diag_outer_hand(case):
+    d = _load("diag_outer_hand.json")["cases"][case]
+    g = np.log(np.array(d["alpha"]))
+    ks = None if d["k_scale"] is None else np.array(d["k_scale"])
+    s0 = None if d["s0"] is None else np.array(d["s0"])
+    o, fin = oracle.scan_diag_outer(np.array(d["q"]), np.array(d["k"]), np.array(d["v"]), g,
+                                    d["decay_mode"], ks, d["scale"], s0)
+    assert rel(o, d["o"]) < 1e-15
+    assert rel(fin, d["s_final"]) < 1e-15
+
+
+@pytest.mark.parametrize("case", [0, 1])
+@pytest.mark.parametrize("form", ["rank1", "explicit"])
+def test_golden_delta_hand(case, form):
+    d = _load("delta_hand.json")["cases"][case]
+    fn = oracle.scan_delta if form == "rank1" else oracle.scan_delta_explicit
+    s0 = None if d["s0"] is None else np.array(d["s0"])
+    o, fin = fn(np.array(d["q"]), np.array(d["k"]), np.array(d["v"]), np.array(d["beta"]),
+                d["scale"], s0)
+    assert np.array_equal(o, np.array(d["o"]))
+    assert np.array_equal(fin, np.array(d["s_final"]))
+
+
+# ----------------------------------------------------------------------------
+# Elementwise scans: closed forms [SunnyNet log §2.1; the pages' torch baseline
+# is the cumsum closed form, §2.3]
+# ----------------------------------------------------------------------------
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def test_fma_cumprod_cumsum_closed_form():
+    # s_t = P_t * (s0 + sum_{i<=t} b_i / P_i),  P_t = prod_{j<=t} a_j
+    r = _rng(1)
+    B, T, N = 3, 16, 5
+    a = r.uniform(0.5, 1.0, (B, T, N))
+    b = r.standard_normal((B, T, N))
+    s0 = r.standard_normal((B, N))
+    P = np.cumprod(a, axis=1)
+    ref = P * (s0[:, None, :] + np.cumsum(b / P, axis=1))
+    s, fin = oracle.scan_fma(a, b, s0)
+    assert rel(s, ref) < 1e-12
+    assert np.array_equal(fin, s[:, -1])
+
+
+def test_fma_double_sum_exact_rational():
+    # s_t = (prod_{j<=t} a_j) s0 + sum_{i<=t} (prod_{i<j<=t} a_j) b_i, in exact
+    # rationals, with signed a (where the cumprod form would divide by ~0).
+    r = _rng(2)
+    B, T, N = 2, 9, 3
+    a = r.integers(-6, 7, (B, T, N)) / 4.0
+    b = r.integers(-8, 9, (B, T, N)) / 8.0
+    s0 = r.integers(-4, 5, (B, N)) / 2.0
+    s, fin = oracle.scan_fma(a, b, s0)
+    for bi in range(B):
+        for n in range(N):
+            A = [Fraction(x) for x in a[bi, :, n]]
+            Bv = [Fraction(x) for x in b[bi, :, n]]
+            for t in range(T):
+                val = Fraction(s0[bi, n])
+                for j in range(t + 1):
+                    val *= A[j]
+                for i in range(t + 1):
+                    term = Bv[i]
+                    for j in range(i + 1, t + 1):
+                        term *= A[j]
+                    val += term
+                # dyadic inputs with few bits: fp64 holds every partial result exactly
+                assert s[bi, t, n] == float(val)
+    assert np.array_equal(fin, s[:, -1])
+
+
+def test_fma_special_cases():
+    r = _rng(3)
+    B, T, N = 2, 20, 4
+    b = r.standard_normal((B, T, N))
+    s0 = r.standard_normal((B, N))
+    s, _ = oracle.scan_fma(np.ones((B, T, N)), b, s0)          # a = 1: running sum
+    assert rel(s, s0[:, None, :] + np.cumsum(b, axis=1)) < 1e-14
+    a = r.uniform(0.5, 1.0, (B, T, N))
+    s, _ = oracle.scan_fma(a, np.zeros((B, T, N)), s0)         # b = 0: running product
+    assert rel(s, s0[:, None, :] * np.cumprod(a, axis=1)) < 1e-14
+    alpha, beta = 0.9, 0.3                                     # constants: geometric series
+    s, _ = oracle.scan_fma(np.full((B, T, N), alpha), np.full((B, T, N), beta), s0)
+    t = np.arange(1, T + 1)[None, :, None]
+    ref = alpha ** t * s0[:, None, :] + beta * (1 - alpha ** t) / (1 - alpha)
+    assert rel(s, ref) < 1e-13
+    s, fin = oracle.scan_fma(np.ones((B, T, N)), b, None)      # NULL s0 means zeros
+    assert rel(s, np.cumsum(b, axis=1)) < 1e-14
+
+
+def test_gated_closed_forms():
+    r = _rng(4)
+    B, T, N = 2, 24, 3
+    s0 = r.standard_normal((B, N))
+    u = r.standard_normal((B, T, N))
+    # a = 0 copies the input, a = 1 holds the state
+    s, _ = oracle.scan_gated(np.zeros((B, T, N)), u, s0)
+    assert np.array_equal(s, u)
+    s, _ = oracle.scan_gated(np.ones((B, T, N)), u, s0)
+    assert np.array_equal(s, np.broadcast_to(s0[:, None, :], (B, T, N)))
+    # constant a = alpha, u = c: s_t = c + alpha^t (s0 - c)
+    alpha, c = 0.75, 2.5
+    s, _ = oracle.scan_gated(np.full((B, T, N), alpha), np.full((B, T, N), c), s0)
+    t = np.arange(1, T + 1)[None, :, None]
+    assert rel(s, c + alpha ** t * (s0[:, None, :] - c)) < 1e-13
+    # fixed point: u = s0 = c everywhere stays c for any a in [0, 1]
+    a = r.uniform(0.0, 1.0, (B, T, N))
+    s, _ = oracle.scan_gated(a, np.full((B, T, N), 0.5), np.full((B, N), 0.5))
+    assert np.all(np.abs(s - 0.5) <= 1e-15)
+
+
+def test_gated_double_sum_exact_rational_and_convexity():
+    # s_t = (prod_{j<=t} a_j) s0 + sum_{i<=t} (prod_{i<j<=t} a_j) (1 - a_i) u_i
+    r = _rng(5)
+    B, T, N = 2, 8, 2
+    a = r.integers(0, 9, (B, T, N)) / 8.0
+    u = r.integers(-8, 9, (B, T, N)) / 4.0
+    s0 = r.integers(-4, 5, (B, N)) / 2.0
+    s, _ = oracle.scan_gated(a, u, s0)
+    for bi in range(B):
+        for n in range(N):
+            for t in range(T):
+                val = Fraction(s0[bi, n])
+                for j in range(t + 1):
+                    val *= Fraction(a[bi, j, n])
+                for i in range(t + 1):
+                    term = (1 - Fraction(a[bi, i, n])) * Fraction(u[bi, i, n])
+                    for j in range(i + 1, t + 1):
+                        term *= Fraction(a[bi, j, n])
+                    val += term
+                assert s[bi, t, n] == float(val)
+    # convex combination: the state stays inside [min, max] of s0 and the inputs so far
+    a = r.uniform(0.0, 1.0, (3, 50, 4))
+    u = r.standard_normal((3, 50, 4))
+    s0 = r.standard_normal((3, 4))
+    s, _ = oracle.scan_gated(a, u, s0)
+    lo = np.minimum(s0[:, None, :], np.minimum.accumulate(u, axis=1))
+    hi = np.maximum(s0[:, None, :], np.maximum.accumulate(u, axis=1))
+    assert np.all(s >= lo - 1e-12) and np.all(s <= hi + 1e-12)
+
+
+# ----------------------------------------------------------------------------
+# Decay-separable state scan [SunnyNet log §4.1, §4.3]
+# ----------------------------------------------------------------------------
+
+def _diag_inputs(r, B, T, H, Hg, K, V, mode, with_kscale, with_s0, gscale=0.3):
+    q = r.standard_normal((B, T, Hg, K))
+    k = r.standard_normal((B, T, Hg, K))
+    v = r.standard_normal((B, T, H, V))
+    gshape = (B, T, H) if mode == 0 else (B, T, H, K)
+    g = -gscale * r.uniform(0.0, 1.0, gshape)
+    ks = r.uniform(0.2, 2.0, (B, T, H)) if with_kscale else None
+    s0 = r.standard_normal((B, H, K, V)) if with_s0 else None
+    return q, k, v, g, ks, s0
+
+
+def _diag_quadratic(q, k, v, g, mode, ks, scale, s0, H):
+    """O(T^2) closed form: o_t = scale sum_{i<=t} sum_d q_td k_id kappa_i e^{G_td - G_id} v_i
+    + scale sum_d q_td e^{G_td} S0_d,  S_T = e^{G_T} S0 + sum_i e^{G_T - G_i} kappa_i k_i v_i^T,
+    with G_t = sum_{j<=t} g_j."""
+    B, T, Hg, K = q.shape
+    V = v.shape[-1]
+    hpg = H // Hg
+    o = np.zeros((B, T, H, V))
+    fin = np.zeros((B, H, K, V))
+    for b in range(B):
+        for h in range(H):
+            grp = h // hpg
+            gg = g[b, :, h] if mode == 1 else np.repeat(g[b, :, h][:, None], K, axis=1)
+            G = np.cumsum(gg, axis=0)                                   # [T, K]
+            kap = ks[b, :, h] if ks is not None else np.ones(T)
+            Q = q[b, :, grp]                                            # [T, K]
+            Km = k[b, :, grp]
+            W = np.exp(G[:, None, :] - G[None, :, :])                   # [t, i, d]
+            Pm = np.einsum("td,id,tid->ti", Q, Km, W) * kap[None, :]
+            Pm = np.tril(Pm)
+            o[b, :, h] = Pm @ v[b, :, h]
+            S0 = s0[b, h] if s0 is not None else np.zeros((K, V))
+            o[b, :, h] += (Q * np.exp(G)) @ S0
+            o[b, :, h] *= scale
+            fin[b, h] = np.exp(G[-1])[:, None] * S0 + (
+                (Km * np.exp(G[-1][None, :] - G) * kap[:, None]).T @ v[b, :, h])
+    return o, fin
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_diag_outer_quadratic_form(mode, with_s0):
+    r = _rng(10 + mode + 2 * with_s0)
+    B, T, H, Hg, K, V = 2, 23, 4, 2, 5, 7   # K != V and Hg < H: a wrong offset cannot hide
+    q, k, v, g, ks, s0 = _diag_inputs(r, B, T, H, Hg, K, V, mode, True, with_s0)
+    scale = 0.37
+    o, fin = oracle.scan_diag_outer(q, k, v, g, mode, ks, scale, s0)
+    ro, rf = _diag_quadratic(q, k, v, g, mode, ks, scale, s0, H)
+    assert rel(o, ro) < 1e-12
+    assert rel(fin, rf) < 1e-12
+
+
+def test_diag_outer_zero_decay_is_causal_linear_attention():
+    # g = 0, kappa = 1: O = scale (tril(Q K^T) V + Q S0) per head (a masked matmul)
+    r = _rng(20)
+    B, T, H, Hg, K, V = 2, 17, 3, 3, 6, 4
+    q, k, v, _, _, s0 = _diag_inputs(r, B, T, H, Hg, K, V, 1, False, True)
+    g = np.zeros((B, T, H, K))
+    o, fin = oracle.scan_diag_outer(q, k, v, g, 1, None, 0.5, s0)
+    for b in range(B):
+        for h in range(H):
+            Q, Km, Vm = q[b, :, h], k[b, :, h], v[b, :, h]
+            ref = 0.5 * (np.tril(Q @ Km.T) @ Vm + Q @ s0[b, h])
+            assert rel(o[b, :, h], ref) < 1e-13
+            assert rel(fin[b, h], s0[b, h] + Km.T @ Vm) < 1e-13
+
+
+def test_diag_outer_k1_reduces_to_fma_scan():
+    # K = V = 1: S_t = e^{g_t} S_{t-1} + kappa k v, o = scale S q, i.e. an FMA scan
+    r = _rng(21)
+    B, T, H = 2, 30, 3
+    q, k, v, g, ks, s0 = _diag_inputs(r, B, T, H, H, 1, 1, 0, True, True)
+    o, fin = oracle.scan_diag_outer(q, k, v, g, 0, ks, 1.0, s0)
+    a = np.exp(g)                                           # [B,T,H]
+    bb = ks * k[..., 0] * v[..., 0]
+    s, sf = oracle.scan_fma(a, bb, s0[..., 0, 0])
+    assert rel(o[..., 0], s * q[..., 0]) < 1e-14
+    assert rel(fin[..., 0, 0], sf) < 1e-14
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_diag_outer_is_elementwise_decomposable(mode):
+    # [SunnyNet log §4.3] asserts GLA decay is elementwise decomposable (and §4.1
+    # says the same of Mamba-2).  Run the elementwise FMA scan on K*V channels with
+    # a = exp(g_i) and b = (kappa k_i) v_j: its states equal S bit for bit.
+    r = _rng(30 + mode)
+    B, T, H, K, V = 2, 19, 2, 4, 3
+    q, k, v, g, ks, s0 = _diag_inputs(r, B, T, H, H, K, V, mode, True, True)
+    for t_end in (1, 7, T):
+        _, fin = oracle.scan_diag_outer(q[:, :t_end], k[:, :t_end], v[:, :t_end],
+                                        g[:, :t_end], mode, ks[:, :t_end], 1.0, s0)
+        gi = g[:, :t_end] if mode == 1 else np.repeat(g[:, :t_end, :, None], K, axis=3)
+        alpha = np.vectorize(math.exp)(gi)                   # libm exp, as the C oracle
+        a = np.repeat(alpha[..., :, None], V, axis=4)        # [B,t,H,K,V]
+        kk = ks[:, :t_end, :, None] * k[:, :t_end]           # [B,t,H,K]
+        bb = kk[..., :, None] * v[:, :t_end, :, None, :]
+        s, sf = oracle.scan_fma(a.reshape(B, t_end, -1), bb.reshape(B, t_end, -1),
+                                s0.reshape(B, -1))
+        assert np.array_equal(sf.reshape(B, H, K, V), fin)
+
+
+def test_delta_rule_is_not_elementwise():
+    # The converse [SunnyNet log §4.4]: the rank-1 term cannot be written as a
+    # per-channel a*s + b, so the same mapping does not reproduce the delta rule.
+    r = _rng(33)
+    B, T, H, K, V = 1, 6, 1, 4, 3
+    q = r.standard_normal((B, T, H, K))
+    k = r.standard_normal((B, T, H, K))
+    v = r.standard_normal((B, T, H, V))
+    beta = np.full((B, T, H), 0.5)
+    _, fin = oracle.scan_delta(q, k, v, beta)
+    bb = (beta[..., None] * k)[..., :, None] * v[..., None, :]
+    _, sf = oracle.scan_fma(np.ones((B, T, H * K * V)), bb.reshape(B, T, -1))
+    assert rel(sf.reshape(B, H, K, V), fin) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# Delta rule [SunnyNet log §4.2; vs llama.cpp §3]
+# ----------------------------------------------------------------------------
+
+def _delta_inputs(r, B, T, H, K, V, with_s0=True, normalise=True):
+    q = r.standard_normal((B, T, H, K))
+    k = r.standard_normal((B, T, H, K))
+    if normalise:
+        q /= np.linalg.norm(q, axis=-1, keepdims=True)
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = r.standard_normal((B, T, H, V))
+    beta = r.uniform(0.0, 1.0, (B, T, H))
+    s0 = r.standard_normal((B, H, K, V)) if with_s0 else None
+    return q, k, v, beta, s0
+
+
+@pytest.mark.parametrize("K,V", [(6, 10), (10, 6), (8, 8)])
+def test_delta_rank1_matches_explicit(K, V):
+    # The page requires the two forms to be built and checked separately, with
+    # K != V so that a wrong-side product cannot pass silently.
+    r = _rng(40 + K)
+    q, k, v, beta, s0 = _delta_inputs(r, 2, 40, 3, K, V)
+    o1, f1 = oracle.scan_delta(q, k, v, beta, 0.7, s0)
+    o2, f2 = oracle.scan_delta_explicit(q, k, v, beta, 0.7, s0)
+    assert rel(o1, o2) < 1e-12
+    assert rel(f1, f2) < 1e-12
+
+
+def test_delta_key_readback_invariant():
+    # S_t^T k_t = (1 - beta ||k||^2) S_{t-1}^T k_t + beta ||k||^2 v_t, for any K, V;
+    # a product taken on the wrong side of S breaks it.
+    r = _rng(50)
+    B, T, H, K, V = 1, 12, 2, 5, 9
+    q, k, v, beta, s0 = _delta_inputs(r, B, T, H, K, V, normalise=False)
+    prev = s0
+    for t in range(T):
+        _, cur = oracle.scan_delta(q[:, :t + 1], k[:, :t + 1], v[:, :t + 1], beta[:, :t + 1],
+                                   1.0, s0)
+        for h in range(H):
+            kt, vt, bt = k[0, t, h], v[0, t, h], beta[0, t, h]
+            nk = kt @ kt
+            lhs = cur[0, h].T @ kt
+            rhs = (1 - bt * nk) * (prev[0, h].T @ kt) + bt * nk * vt
+            assert rel(lhs, rhs) < 1e-12
+        prev = cur
+
+
+def test_delta_beta_zero_and_one_hot_overwrite():
+    r = _rng(51)
+    B, T, H, K, V = 2, 9, 2, 4, 6
+    q, k, v, _, s0 = _delta_inputs(r, B, T, H, K, V)
+    o, fin = oracle.scan_delta(q, k, v, np.zeros((B, T, H)), 1.5, s0)
+    assert np.array_equal(fin, s0)                     # beta = 0 leaves S unchanged
+    assert rel(o, 1.5 * np.einsum("bhkv,bthk->bthv", s0, q)) < 1e-14
+    # one-hot keys with beta = 1 overwrite row i_t of S with v_t
+    idx = r.integers(0, K, (B, T, H))
+    k1 = np.zeros((B, T, H, K))
+    np.put_along_axis(k1, idx[..., None], 1.0, axis=-1)
+    o, fin = oracle.scan_delta(q, k1, v, np.ones((B, T, H)), 1.0, s0)
+    S = s0.copy()
+    for t in range(T):
+        for b in range(B):
+            for h in range(H):
+                S[b, h, idx[b, t, h]] = v[b, t, h]
+        assert rel(o[:, t], np.einsum("bhkv,bhk->bhv", S, q[:, t])) < 1e-14
+    # S + (v - S) equals v up to one rounding of the subtraction and the add
+    assert rel(fin, S) < 1e-15
+
+
+def test_delta_chunked_ut_form():
+    # A second algorithm for the same map over one chunk (WY/UT form):
+    #   A = strict_lower(diag(beta) K K^T),  Delta = (I + A)^{-1} diag(beta) (V - K S0),
+    #   O = scale (Q S0 + tril(Q K^T) Delta),  S_L = S0 + K^T Delta.
+    r = _rng(52)
+    B, T, H, K, V = 1, 32, 2, 7, 5
+    q, k, v, beta, s0 = _delta_inputs(r, B, T, H, K, V)
+    o, fin = oracle.scan_delta(q, k, v, beta, 0.9, s0)
+    for h in range(H):
+        Q, Km, Vm, bt, S0 = q[0, :, h], k[0, :, h], v[0, :, h], beta[0, :, h], s0[0, h]
+        A = np.tril(bt[:, None] * (Km @ Km.T), -1)
+        Dl = np.linalg.solve(np.eye(T) + A, bt[:, None] * (Vm - Km @ S0))
+        assert rel(o[0, :, h], 0.9 * (Q @ S0 + np.tril(Q @ Km.T) @ Dl)) < 1e-11
+        assert rel(fin[0, h], S0 + Km.T @ Dl) < 1e-11
+
+
+# ----------------------------------------------------------------------------
+# Segment continuation [SunnyNet log §4: two segments with the state carried
+# across reproduce the full run exactly] and thread-count invariance
+# ----------------------------------------------------------------------------
+
+def _split_runs(run, T, splits):
+    full = run(0, T, None)
+    for t1 in splits:
+        first = run(0, t1, None)
+        second = run(t1, T, first[-1])
+        yield full, first, second, t1
+
+
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_continuation_bit_exact(dtype):
+    r = _rng(60)
+    B, T, N = 2, 80, 6
+    a = r.uniform(0.5, 1.0, (B, T, N)).astype(dtype)
+    x = r.standard_normal((B, T, N)).astype(dtype)
+    s0 = r.standard_normal((B, N)).astype(dtype)
+    splits = (1, 37, T // 2, T - 1)
+    for fn in (oracle.scan_fma, oracle.scan_gated):
+        def run(lo, hi, init):
+            return fn(a[:, lo:hi], x[:, lo:hi], s0 if init is None and lo == 0 else init,
+                      dtype=dtype)
+        for full, first, second, t1 in _split_runs(run, T, splits):
+            assert np.array_equal(np.concatenate([first[0], second[0]], axis=1), full[0])
+            assert np.array_equal(second[1], full[1])
+    # matrix scans
+    H, Hg, K, V = 2, 1, 5, 3
+    q, k, v, g, ks, S0 = _diag_inputs(r, B, T, H, Hg, K, V, 1, True, True)
+    q, k, v, g, ks, S0 = (z.astype(dtype) for z in (q, k, v, g, ks, S0))
+    def run_d(lo, hi, init):
+        return oracle.scan_diag_outer(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], g[:, lo:hi], 1,
+                                      ks[:, lo:hi], 0.5, S0 if lo == 0 else init, dtype=dtype)
+    for full, first, second, t1 in _split_runs(run_d, T, splits):
+        assert np.array_equal(np.concatenate([first[0], second[0]], axis=1), full[0])
+        assert np.array_equal(second[1], full[1])
+    qd, kd, vd, bd, Sd = (z.astype(dtype) for z in _delta_inputs(r, B, T, H, K, V))
+    def run_l(lo, hi, init):
+        return oracle.scan_delta(qd[:, lo:hi], kd[:, lo:hi], vd[:, lo:hi], bd[:, lo:hi], 1.0,
+                                 Sd if lo == 0 else init, dtype=dtype)
+    for full, first, second, t1 in _split_runs(run_l, T, splits):
+        assert np.array_equal(np.concatenate([first[0], second[0]], axis=1), full[0])
+        assert np.array_equal(second[1], full[1])
+
+
+def test_thread_count_does_not_change_bits():
+    r = _rng(70)
+    a = r.uniform(0.5, 1.0, (3, 50, 700))
+    x = r.standard_normal((3, 50, 700))
+    s1 = oracle.scan_gated(a, x, nthreads=1)
+    s4 = oracle.scan_gated(a, x, nthreads=4)
+    assert np.array_equal(s1[0], s4[0]) and np.array_equal(s1[1], s4[1])
+    q, k, v, beta, s0 = _delta_inputs(r, 2, 20, 3, 4, 6)
+    d1 = oracle.scan_delta(q, k, v, beta, 1.0, s0, nthreads=1)
+    d4 = oracle.scan_delta(q, k, v, beta, 1.0, s0, nthreads=4)
+    assert np.array_equal(d1[0], d4[0]) and np.array_equal(d1[1], d4[1])
+
+
+def test_float32_mode_tracks_float64():
+    # The pages report fp32 scan accumulation error near 5e-7 relative
+    # [SunnyNet log §9.3]; the single-precision mode must stay in that class.
+    r = _rng(71)
+    a = r.uniform(0.5, 1.0, (2, 2048, 16)).astype(np.float32)
+    x = r.standard_normal((2, 2048, 16)).astype(np.float32)
+    s64, _ = oracle.scan_gated(a, x)
+    s32, _ = oracle.scan_gated(a, x, dtype=np.float32)
+    assert rel(s32, s64) < 5e-6

@@ -1,0 +1,311 @@
+// C-ABI layer: argument validation, the opaque context and its workspace,
+// and kernel launches.  Declarations and the contract live in include/lrs_abi.h.
+//
+// ABI style after [SunnyNet log §6] ("SunnyNet 工程化实录：一个 O(N) 架构如何长出自己的
+// C 推理运行时", developer.aliyun.com/article/1773847): prefixed symbols, opaque
+// handles, packed version, capability bits, int32 status codes and dims.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "lrs_abi.h"
+#include "lrs_internal.h"
+
+#define LRS_API extern "C" __attribute__((visibility("default")))
+
+struct LrsContext {
+    int device = 0;
+    int num_cus = 256;
+    int elem_schedule = LRS_ELEM_SCHEDULE_AUTO;
+    // small fixed block: [0] tile counter (u64), [1] error flag (u32 in a u64 slot)
+    unsigned long long* fixed = nullptr;
+    // look-back status words, grown on demand
+    unsigned long long* words = nullptr;
+    size_t words_cap = 0;
+    unsigned int epoch = 0;                 // last epoch used; status words hold 0 initially
+    unsigned long long counter_base = 0;    // tiles taken from the counter so far
+    hipStream_t last_stream = nullptr;
+    bool used = false;
+};
+
+namespace {
+
+// Keeps the caller's current device unchanged across a call.
+class DeviceGuard {
+   public:
+    explicit DeviceGuard(int dev) {
+        ok_ = hipGetDevice(&prev_) == hipSuccess;
+        if (ok_ && prev_ != dev) ok_ = hipSetDevice(dev) == hipSuccess;
+        else if (ok_) prev_ = -1;
+    }
+    ~DeviceGuard() {
+        if (prev_ >= 0) (void)hipSetDevice(prev_);
+    }
+    bool ok() const { return ok_; }
+
+   private:
+    int prev_ = -1;
+    bool ok_ = false;
+};
+
+struct Span {
+    const void* p;
+    size_t bytes;
+};
+
+bool overlaps(const Span& x, const Span& y) {
+    if (!x.p || !y.p || x.bytes == 0 || y.bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(x.p), a1 = a0 + x.bytes;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(y.p), b1 = b0 + y.bytes;
+    return a0 < b1 && b0 < a1;
+}
+
+// Every output must be disjoint from every other buffer.
+bool outputs_disjoint(const Span* outs, int nout, const Span* ins, int nin) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlaps(outs[i], ins[j])) return false;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlaps(outs[i], outs[j])) return false;
+    }
+    return true;
+}
+
+bool aligned(const void* p, size_t a) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool mul_ok(int64_t& acc, int64_t v) {
+    if (v <= 0) return false;
+    if (acc > INT64_MAX / v) return false;
+    acc *= v;
+    return true;
+}
+
+lrs_status grow_words(LrsContext* ctx, size_t need, hipStream_t stream) {
+    if (need <= ctx->words_cap) return LRS_OK;
+    size_t cap = ctx->words_cap ? ctx->words_cap : 4096;
+    while (cap < need) cap *= 2;
+    if (ctx->words) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return LRS_E_DEVICE;
+        (void)hipFree(ctx->words);
+        ctx->words = nullptr;
+        ctx->words_cap = 0;
+    }
+    void* p = nullptr;
+    if (hipMalloc(&p, cap * sizeof(unsigned long long)) != hipSuccess) {
+        (void)hipGetLastError();
+        return LRS_E_NOMEM;
+    }
+    ctx->words = static_cast<unsigned long long*>(p);
+    ctx->words_cap = cap;
+    if (lrs::launch_fill_zero_u64(ctx->words, cap, stream) != hipSuccess) return LRS_E_DEVICE;
+    ctx->epoch = 0;  // fresh words hold tag 0; the next epoch is 1
+    return LRS_OK;
+}
+
+// Next epoch tag for look-back status words; tags are never 0 and never reused
+// without clearing the words first.
+lrs_status next_epoch(LrsContext* ctx, hipStream_t stream, unsigned int* out) {
+    if (ctx->epoch == 0xffffffffu) {
+        if (lrs::launch_fill_zero_u64(ctx->words, ctx->words_cap, stream) != hipSuccess)
+            return LRS_E_DEVICE;
+        ctx->epoch = 0;
+    }
+    *out = ++ctx->epoch;
+    return LRS_OK;
+}
+
+lrs_status scan_elem(LrsContext* ctx, bool gated, const float* a, const float* x,
+                     const float* s0, float* s, float* s_final, int32_t B, int32_t T, int32_t N,
+                     void* stream_ptr) {
+    if (!ctx || !a || !x || !s || !s_final) return LRS_E_INVAL;
+    if (B < 1 || T < 1 || N < 1) return LRS_E_INVAL;
+    if (!aligned(a, 4) || !aligned(x, 4) || !aligned(s0, 4) || !aligned(s, 4) || !aligned(s_final, 4))
+        return LRS_E_INVAL;
+    int64_t seq = B;
+    if (!mul_ok(seq, T) || !mul_ok(seq, N) || seq > INT64_MAX / 8) return LRS_E_INVAL;
+    const size_t seq_bytes = static_cast<size_t>(seq) * sizeof(float);
+    const size_t st_bytes = static_cast<size_t>(B) * N * sizeof(float);
+    const Span ins[] = {{a, seq_bytes}, {x, seq_bytes}, {s0, st_bytes}};
+    const Span outs[] = {{s, seq_bytes}, {s_final, st_bytes}};
+    if (!outputs_disjoint(outs, 2, ins, 3)) return LRS_E_INVAL;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+
+    const bool al16 = aligned(a, 16) && aligned(x, 16) && aligned(s, 16);
+    int schedule = ctx->elem_schedule;
+    if (schedule == LRS_ELEM_SCHEDULE_AUTO)
+        schedule = lrs::elem_auto_schedule(B, T, N, al16, ctx->num_cus);
+    const int ksched = schedule == LRS_ELEM_SCHEDULE_LOOKBACK ? lrs::kElemLookback : lrs::kElemStream;
+    const lrs::ElemPlan plan = lrs::elem_plan(B, T, N, al16, ksched);
+    if (plan.grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
+
+    lrs::ElemParams p{};
+    p.a = a;
+    p.x = x;
+    p.s0 = s0;
+    p.s = s;
+    p.s_final = s_final;
+    p.B = B;
+    p.T = T;
+    p.N = N;
+    p.gated = gated;
+    p.schedule = ksched;
+    if (ksched == lrs::kElemLookback) {
+        lrs_status st = grow_words(ctx, plan.words, stream);
+        if (st != LRS_OK) return st;
+        st = next_epoch(ctx, stream, &p.epoch);
+        if (st != LRS_OK) return st;
+        p.words = ctx->words;
+        p.counter = ctx->fixed;
+        p.counter_base = ctx->counter_base;
+        p.error_flag = reinterpret_cast<unsigned int*>(ctx->fixed + 1);
+    }
+    if (lrs::launch_scan_elem(p, plan, stream) != hipSuccess) return LRS_E_DEVICE;
+    if (ksched == lrs::kElemLookback) ctx->counter_base += static_cast<unsigned long long>(plan.grid);
+    ctx->last_stream = stream;
+    ctx->used = true;
+    return LRS_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// version, capabilities, status strings
+// ---------------------------------------------------------------------------
+LRS_API uint32_t lrs_abi_version(void) { return LRS_ABI_VERSION; }
+
+LRS_API lrs_status lrs_abi_check(int32_t caller_major) {
+    return caller_major == LRS_ABI_VERSION_MAJOR ? LRS_OK : LRS_E_UNSUPPORTED;
+}
+
+LRS_API uint32_t lrs_abi_caps(void) {
+    return LRS_CAP_SCAN_FMA | LRS_CAP_SCAN_GATED | LRS_CAP_SCAN_DIAG_OUTER | LRS_CAP_SCAN_DELTA;
+}
+
+LRS_API const char* lrs_status_string(lrs_status status) {
+    switch (status) {
+        case LRS_OK: return "ok";
+        case LRS_E_INVAL: return "invalid argument";
+        case LRS_E_NOMEM: return "out of device memory";
+        case LRS_E_IO: return "i/o error";
+        case LRS_E_FORMAT: return "bad format";
+        case LRS_E_UNSUPPORTED: return "unsupported";
+        case LRS_E_DEVICE: return "device or runtime error";
+        default: return "unknown status";
+    }
+}
+
+// ---------------------------------------------------------------------------
+// context
+// ---------------------------------------------------------------------------
+LRS_API lrs_status lrs_context_create(int32_t hip_device, LrsContext** out) {
+    if (!out) return LRS_E_INVAL;
+    *out = nullptr;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || hip_device < 0 || hip_device >= count) {
+        (void)hipGetLastError();
+        return LRS_E_UNSUPPORTED;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, hip_device) != hipSuccess) return LRS_E_DEVICE;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return LRS_E_UNSUPPORTED;
+
+    DeviceGuard guard(hip_device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+    LrsContext* ctx = new (std::nothrow) LrsContext();
+    if (!ctx) return LRS_E_NOMEM;
+    ctx->device = hip_device;
+    ctx->num_cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
+    void* p = nullptr;
+    if (hipMalloc(&p, 256) != hipSuccess) {
+        (void)hipGetLastError();
+        delete ctx;
+        return LRS_E_NOMEM;
+    }
+    ctx->fixed = static_cast<unsigned long long*>(p);
+    if (hipMemset(ctx->fixed, 0, 256) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(ctx->fixed);
+        delete ctx;
+        return LRS_E_DEVICE;
+    }
+    *out = ctx;
+    return LRS_OK;
+}
+
+LRS_API void lrs_context_destroy(LrsContext* ctx) {
+    if (!ctx) return;
+    {
+        DeviceGuard guard(ctx->device);
+        (void)hipDeviceSynchronize();
+        if (ctx->words) (void)hipFree(ctx->words);
+        if (ctx->fixed) (void)hipFree(ctx->fixed);
+    }
+    delete ctx;
+}
+
+LRS_API lrs_status lrs_context_set_param(LrsContext* ctx, int32_t param, int32_t value) {
+    if (!ctx) return LRS_E_INVAL;
+    if (param == LRS_PARAM_ELEM_SCHEDULE) {
+        if (value != LRS_ELEM_SCHEDULE_AUTO && value != LRS_ELEM_SCHEDULE_STREAM &&
+            value != LRS_ELEM_SCHEDULE_LOOKBACK)
+            return LRS_E_INVAL;
+        ctx->elem_schedule = value;
+        return LRS_OK;
+    }
+    return LRS_E_INVAL;
+}
+
+LRS_API lrs_status lrs_context_check(LrsContext* ctx) {
+    if (!ctx) return LRS_E_INVAL;
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+    if (hipDeviceSynchronize() != hipSuccess) return LRS_E_DEVICE;
+    unsigned int flag = 0;
+    if (hipMemcpy(&flag, ctx->fixed + 1, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess)
+        return LRS_E_DEVICE;
+    if (flag) {
+        const unsigned int zero = 0;
+        (void)hipMemcpy(ctx->fixed + 1, &zero, sizeof(zero), hipMemcpyHostToDevice);
+        return LRS_E_DEVICE;
+    }
+    return LRS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// scans
+// ---------------------------------------------------------------------------
+LRS_API lrs_status lrs_scan_fma(LrsContext* ctx, const float* a, const float* b, const float* s0,
+                                float* s, float* s_final, int32_t B, int32_t T, int32_t N,
+                                void* stream) {
+    return scan_elem(ctx, false, a, b, s0, s, s_final, B, T, N, stream);
+}
+
+LRS_API lrs_status lrs_scan_gated(LrsContext* ctx, const float* a, const float* u,
+                                  const float* s0, float* s, float* s_final, int32_t B,
+                                  int32_t T, int32_t N, void* stream) {
+    return scan_elem(ctx, true, a, u, s0, s, s_final, B, T, N, stream);
+}
+
+LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                       const lrs_bf16* v, const float* g, int32_t decay_mode,
+                                       const float* k_scale, float scale, const float* s0,
+                                       float* o, float* s_final, int32_t B, int32_t T, int32_t H,
+                                       int32_t Hg, int32_t K, int32_t V, void* stream) {
+    (void)ctx; (void)q; (void)k; (void)v; (void)g; (void)decay_mode; (void)k_scale; (void)scale;
+    (void)s0; (void)o; (void)s_final; (void)B; (void)T; (void)H; (void)Hg; (void)K; (void)V;
+    (void)stream;
+    return LRS_E_UNSUPPORTED;
+}
+
+LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                  const lrs_bf16* v, const float* beta, float scale,
+                                  const float* s0, float* o, float* s_final, int32_t B, int32_t T,
+                                  int32_t H, int32_t K, int32_t V, void* stream) {
+    (void)ctx; (void)q; (void)k; (void)v; (void)beta; (void)scale; (void)s0; (void)o;
+    (void)s_final; (void)B; (void)T; (void)H; (void)K; (void)V; (void)stream;
+    return LRS_E_UNSUPPORTED;
+}

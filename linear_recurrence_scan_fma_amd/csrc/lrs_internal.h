@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the HIP kernels.
+// Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace lrs {
+
+// ---------------------------------------------------------------------------
+// Elementwise first-order scans (FMA and gated forms).
+// ---------------------------------------------------------------------------
+enum ElemSchedule : int { kElemStream = 1, kElemLookback = 2 };
+
+struct ElemParams {
+    const float* a;
+    const float* x;      // b (FMA form) or u (gated form)
+    const float* s0;     // nullable
+    float* s;
+    float* s_final;
+    int64_t B, T, N;
+    bool gated;
+    int schedule;        // kElemStream or kElemLookback (already resolved)
+    // look-back workspace (schedule == kElemLookback only)
+    unsigned long long* words;    // status words, elem_lookback_words() of them
+    unsigned long long* counter;  // monotonically increasing tile counter
+    unsigned long long counter_base;
+    unsigned int epoch;           // tag of this call's status words, never 0
+    unsigned int* error_flag;     // set to 1 when a bounded wait expires
+};
+
+struct ElemPlan {
+    int vec;            // channels per lane (4 or 1)
+    int rows;           // rows per lane per chunk
+    int64_t chan_tiles; // channel tiles per batch row
+    int64_t chunks;     // time chunks
+    int64_t grid;       // workgroups launched
+    size_t words;       // status words needed (look-back only)
+};
+
+// Resolves vector width, chunk shape and grid for a schedule.
+ElemPlan elem_plan(int64_t B, int64_t T, int64_t N, bool aligned16, int schedule);
+// Picks a schedule for a shape when the caller asked for "auto".
+int elem_auto_schedule(int64_t B, int64_t T, int64_t N, bool aligned16, int num_cus);
+hipError_t launch_scan_elem(const ElemParams& p, const ElemPlan& plan, hipStream_t stream);
+
+// Fills `n` 64-bit words with zero (used to reset look-back status words).
+hipError_t launch_fill_zero_u64(unsigned long long* p, size_t n, hipStream_t stream);
+
+}  // namespace lrs

@@ -1,0 +1,430 @@
+// Elementwise first-order scans on gfx950:
+//   FMA form    s_t = a_t s_{t-1} + b_t
+//   gated form  s_t = a_t s_{t-1} + (1 - a_t) u_t   (evaluated as fma(a, s - u, u))
+// [SunnyNet log §2.1: "SunnyNet 工程化实录：一个 O(N) 架构如何长出自己的 C 推理运行时",
+//  developer.aliyun.com/article/1773847 -- the unified kernel's two forms].
+//
+// Both forms are affine maps s -> A s + B, and composing two steps gives
+// (A2 A1, A2 B1 + B2).  The scan is computed on (A, B) pairs:
+//
+//  * Layout: [B,T,N] fp32, channels contiguous.  A workgroup (4 waves) owns a
+//    tile of NC = 16*VEC channels.  Inside a wave, 16 lanes run along the
+//    channels (VEC channels each, one float4 per lane per row when VEC = 4)
+//    and 4 lanes along time; the 4 waves stack further along time.  So a
+//    chunk is 16 time-lanes x R rows, and each lane owns R consecutive rows.
+//  * Per chunk: every lane folds its R rows into one (A, B) pair per channel,
+//    the 4 time-lanes of a wave combine by cross-lane shuffles (an inclusive
+//    Hillis-Steele scan over lanes 16 apart), the 4 waves combine through LDS,
+//    and each lane then replays its rows from its exact carry-in and streams
+//    the states out.  Inputs are held in registers between the load and the
+//    replay, so every input byte crosses HBM once and every output byte once.
+//  * Across chunks, two schedules:
+//      stream:   a workgroup walks the whole time axis of its channel tile,
+//                prefetching chunk c+1 while it scans chunk c; the carry stays
+//                in registers.  No inter-workgroup traffic at all.
+//      lookback: a workgroup owns a single chunk of a channel tile.  It
+//                publishes its chunk aggregate, then walks back over
+//                predecessors' status words until it finds an inclusive
+//                prefix (decoupled look-back), then publishes its own
+//                inclusive prefix.  Used when there are too few channel tiles
+//                to fill the GPU.  Status words pack (epoch, fp32 value) into
+//                one 64-bit word written and read with agent-scope atomics,
+//                so a word is valid exactly when its tag equals this call's
+//                epoch: no fences, no reset between calls.  Tiles are taken
+//                in order from an atomic counter, so every predecessor of a
+//                running tile has already been taken by a running or finished
+//                workgroup, and aggregates never wait on anything: the walk
+//                always terminates.  It is additionally bounded in wall time.
+#include "lrs_internal.h"
+
+namespace lrs {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kChanLanes = 16;                     // lanes along channels per wave
+constexpr int kTimeLanesPerWave = 64 / kChanLanes; // 4
+constexpr int kTimeLanes = kWaves * kTimeLanesPerWave;  // 16
+constexpr unsigned long long kSpinTicks = 1ull << 29;   // ~5 s of the 100 MHz real-time counter
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct ElemArgs {
+    const float* a;
+    const float* x;
+    const float* s0;
+    float* s;
+    float* s_final;
+    int64_t T, N;
+    int64_t chan_tiles;   // channel tiles per batch row
+    int64_t ncols;        // B * chan_tiles
+    int64_t nchunks;
+    unsigned long long* words;
+    unsigned long long* counter;
+    unsigned long long counter_base;
+    unsigned int epoch;
+    unsigned int* error_flag;
+};
+
+template <bool GATED>
+__device__ __forceinline__ float step(float a, float x, float s) {
+    if constexpr (GATED) {
+        return __builtin_fmaf(a, s - x, x);
+    } else {
+        return __builtin_fmaf(a, s, x);
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_vec(const float* p, float (&v)[VEC]) {
+    if constexpr (VEC == 4) {
+        f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+        v[0] = __builtin_nontemporal_load(p);
+    }
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_vec(float* p, const float (&v)[VEC]) {
+    if constexpr (VEC == 4) {
+        f32x4 t = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(t, reinterpret_cast<f32x4*>(p));
+    } else {
+        __builtin_nontemporal_store(v[0], p);
+    }
+}
+
+__device__ __forceinline__ unsigned long long pack_word(unsigned int epoch, float v) {
+    return (static_cast<unsigned long long>(epoch) << 32) | __float_as_uint(v);
+}
+
+__device__ __forceinline__ void publish(unsigned long long* w, unsigned int epoch, float v) {
+    __hip_atomic_store(w, pack_word(epoch, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ unsigned long long poll(const unsigned long long* w) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(w), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Walks back from tile `pred` (same channel column, earlier chunk) composing
+// aggregates until an inclusive prefix is found; returns the carry-in.
+__device__ float look_back(const ElemArgs& p, int64_t pred, int c, int nc) {
+    float accA = 1.0f, accB = 0.0f;  // maps of the tiles between pred and the caller
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    while (true) {
+        const unsigned long long wi = poll(p.words + (pred * 3 + 2) * nc + c);
+        if (static_cast<unsigned int>(wi >> 32) == p.epoch) {
+            return __builtin_fmaf(accA, __uint_as_float(static_cast<unsigned int>(wi)), accB);
+        }
+        if (pred >= p.ncols) {  // chunk 0 tiles publish only inclusive prefixes
+            const unsigned long long wa = poll(p.words + (pred * 3 + 0) * nc + c);
+            const unsigned long long wb = poll(p.words + (pred * 3 + 1) * nc + c);
+            if (static_cast<unsigned int>(wa >> 32) == p.epoch &&
+                static_cast<unsigned int>(wb >> 32) == p.epoch) {
+                const float pa = __uint_as_float(static_cast<unsigned int>(wa));
+                const float pb = __uint_as_float(static_cast<unsigned int>(wb));
+                accB = __builtin_fmaf(accA, pb, accB);  // pred's map first, then acc
+                accA = accA * pa;
+                pred -= p.ncols;
+                continue;
+            }
+        }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+            __hip_atomic_store(p.error_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return __builtin_nanf("");
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
+template <bool GATED, int VEC, int R, bool LOOKBACK>
+__global__ __launch_bounds__(kThreads) void scan_elem_kernel(ElemArgs p) {
+    constexpr int NC = kChanLanes * VEC;   // channels per tile
+    constexpr int CH = kTimeLanes * R;     // rows per chunk
+
+    __shared__ float sh_tot[2][kWaves][2][NC];
+    __shared__ float sh_carry[NC];
+    __shared__ long long sh_tile;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cl = lane & (kChanLanes - 1);
+    const int tlw = lane / kChanLanes;
+    const int tl = wave * kTimeLanesPerWave + tlw;
+
+    int64_t col, chunk_lo, chunk_hi, tile = 0;
+    if constexpr (LOOKBACK) {
+        if (tid == 0) {
+            sh_tile = static_cast<long long>(
+                __hip_atomic_fetch_add(p.counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                p.counter_base);
+        }
+        __syncthreads();
+        tile = sh_tile;
+        chunk_lo = tile / p.ncols;
+        chunk_hi = chunk_lo + 1;
+        col = tile - chunk_lo * p.ncols;
+    } else {
+        col = blockIdx.x;
+        chunk_lo = 0;
+        chunk_hi = p.nchunks;
+    }
+    const int64_t b = col / p.chan_tiles;
+    const int64_t jt = col - b * p.chan_tiles;
+    const int64_t ch0 = jt * NC + cl * VEC;
+    const bool chan_ok = ch0 < p.N;   // VEC = 4 only when N % 4 == 0
+    const int64_t base = b * p.T * p.N + ch0;
+
+    float carry[VEC];
+    if constexpr (!LOOKBACK) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) carry[v] = (p.s0 && chan_ok) ? p.s0[b * p.N + ch0 + v] : 0.0f;
+    }
+
+    float ca[R][VEC], cx[R][VEC];
+    auto load_chunk = [&](int64_t chunk, float (&A)[R][VEC], float (&X)[R][VEC]) {
+        const int64_t row0 = chunk * CH + static_cast<int64_t>(tl) * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int64_t row = row0 + r;
+            if (chan_ok && row < p.T) {
+                load_vec<VEC>(p.a + base + row * p.N, A[r]);
+                load_vec<VEC>(p.x + base + row * p.N, X[r]);
+            } else {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) { A[r][v] = 1.0f; X[r][v] = 0.0f; }
+            }
+        }
+    };
+    load_chunk(chunk_lo, ca, cx);
+
+    for (int64_t chunk = chunk_lo; chunk < chunk_hi; ++chunk) {
+        float na[R][VEC], nx[R][VEC];
+        const bool has_next = chunk + 1 < chunk_hi;
+        if (has_next) load_chunk(chunk + 1, na, nx);
+
+        const int64_t row0 = chunk * CH + static_cast<int64_t>(tl) * R;
+        const int64_t rem = chan_ok ? p.T - row0 : 0;   // lanes past N store nothing
+        const int nvalid = rem <= 0 ? 0 : (rem >= R ? R : static_cast<int>(rem));
+
+        // 1. fold this lane's rows into one affine pair per channel
+        float A[VEC], Bv[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { A[v] = 1.0f; Bv[v] = 0.0f; }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r < nvalid) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) {
+                    A[v] *= ca[r][v];
+                    Bv[v] = step<GATED>(ca[r][v], cx[r][v], Bv[v]);
+                }
+            }
+        }
+        // 2. inclusive scan over the 4 time-lanes of the wave (lanes 16 apart)
+#pragma unroll
+        for (int off = kChanLanes; off < 64; off <<= 1) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const float pA = __shfl_up(A[v], off);
+                const float pB = __shfl_up(Bv[v], off);
+                if (lane >= off) {
+                    Bv[v] = __builtin_fmaf(A[v], pB, Bv[v]);
+                    A[v] = A[v] * pA;
+                }
+            }
+        }
+        // exclusive prefix inside the wave
+        float eA[VEC], eB[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const float pA = __shfl_up(A[v], kChanLanes);
+            const float pB = __shfl_up(Bv[v], kChanLanes);
+            eA[v] = tlw == 0 ? 1.0f : pA;
+            eB[v] = tlw == 0 ? 0.0f : pB;
+        }
+        // 3. wave totals through LDS (double-buffered: one barrier per chunk)
+        const int buf = static_cast<int>(chunk & 1);
+        if (tlw == kTimeLanesPerWave - 1) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                sh_tot[buf][wave][0][cl * VEC + v] = A[v];
+                sh_tot[buf][wave][1][cl * VEC + v] = Bv[v];
+            }
+        }
+        __syncthreads();
+
+        if constexpr (LOOKBACK) {
+            if (wave == 0 && lane < NC) {
+                const int c = lane;
+                float TA = 1.0f, TB = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    const float wa = sh_tot[buf][w][0][c];
+                    const float wb = sh_tot[buf][w][1][c];
+                    TB = __builtin_fmaf(wa, TB, wb);
+                    TA = TA * wa;
+                }
+                float cin;
+                if (chunk == 0) {
+                    const int64_t ch = jt * NC + c;
+                    cin = (p.s0 && ch < p.N) ? p.s0[b * p.N + ch] : 0.0f;
+                } else {
+                    publish(p.words + (tile * 3 + 0) * NC + c, p.epoch, TA);
+                    publish(p.words + (tile * 3 + 1) * NC + c, p.epoch, TB);
+                    cin = look_back(p, tile - p.ncols, c, NC);
+                }
+                publish(p.words + (tile * 3 + 2) * NC + c, p.epoch, __builtin_fmaf(TA, cin, TB));
+                sh_carry[c] = cin;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) carry[v] = sh_carry[cl * VEC + v];
+        }
+
+        // 4. this lane's carry-in: waves before it, then lanes before it in its wave
+        float PA[VEC], PB[VEC], TA[VEC], TB[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { PA[v] = 1.0f; PB[v] = 0.0f; TA[v] = 1.0f; TB[v] = 0.0f; }
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const float wa = sh_tot[buf][w][0][cl * VEC + v];
+                const float wb = sh_tot[buf][w][1][cl * VEC + v];
+                if (w < wave) {
+                    PB[v] = __builtin_fmaf(wa, PB[v], wb);
+                    PA[v] = PA[v] * wa;
+                }
+                TB[v] = __builtin_fmaf(wa, TB[v], wb);
+                TA[v] = TA[v] * wa;
+            }
+        }
+        float st[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            const float xa = eA[v] * PA[v];
+            const float xb = __builtin_fmaf(eA[v], PB[v], eB[v]);
+            st[v] = __builtin_fmaf(xa, carry[v], xb);
+        }
+        // 5. replay this lane's rows from the exact carry-in and stream states out
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r < nvalid) {
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) st[v] = step<GATED>(ca[r][v], cx[r][v], st[v]);
+                const int64_t row = row0 + r;
+                store_vec<VEC>(p.s + base + row * p.N, st);
+                if (row == p.T - 1) {
+#pragma unroll
+                    for (int v = 0; v < VEC; ++v) p.s_final[b * p.N + ch0 + v] = st[v];
+                }
+            }
+        }
+        // carry into the next chunk (stream schedule)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) carry[v] = __builtin_fmaf(TA[v], carry[v], TB[v]);
+
+        if (has_next) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int v = 0; v < VEC; ++v) { ca[r][v] = na[r][v]; cx[r][v] = nx[r][v]; }
+        }
+    }
+}
+
+__global__ void fill_zero_u64_kernel(unsigned long long* p, size_t n) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = 0ull;
+}
+
+template <bool GATED, int VEC, int R>
+hipError_t launch_variant(const ElemArgs& a, bool lookback, int64_t grid, hipStream_t stream) {
+    if (lookback) {
+        hipLaunchKernelGGL((scan_elem_kernel<GATED, VEC, R, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kThreads), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((scan_elem_kernel<GATED, VEC, R, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <bool GATED>
+hipError_t launch_gated(const ElemArgs& a, const ElemPlan& plan, bool lookback, hipStream_t s) {
+    if (plan.vec == 4) {
+        return plan.rows == 8 ? launch_variant<GATED, 4, 8>(a, lookback, plan.grid, s)
+                              : launch_variant<GATED, 4, 2>(a, lookback, plan.grid, s);
+    }
+    return plan.rows == 8 ? launch_variant<GATED, 1, 8>(a, lookback, plan.grid, s)
+                          : launch_variant<GATED, 1, 2>(a, lookback, plan.grid, s);
+}
+
+}  // namespace
+
+ElemPlan elem_plan(int64_t B, int64_t T, int64_t N, bool aligned16, int schedule) {
+    ElemPlan pl{};
+    pl.vec = (aligned16 && N % 4 == 0) ? 4 : 1;
+    const int64_t nc = kChanLanes * pl.vec;
+    pl.chan_tiles = (N + nc - 1) / nc;
+    if (schedule == kElemStream) {
+        pl.rows = 8;
+    } else {
+        // short sequences get short chunks so that the look-back has tiles to chain
+        pl.rows = T >= 4 * kTimeLanes * 8 ? 8 : 2;
+    }
+    const int64_t ch = kTimeLanes * pl.rows;
+    pl.chunks = (T + ch - 1) / ch;
+    if (schedule == kElemStream) {
+        pl.grid = B * pl.chan_tiles;
+        pl.words = 0;
+    } else {
+        pl.grid = B * pl.chan_tiles * pl.chunks;
+        pl.words = static_cast<size_t>(pl.grid) * 3 * static_cast<size_t>(nc);
+    }
+    return pl;
+}
+
+int elem_auto_schedule(int64_t B, int64_t T, int64_t N, bool aligned16, int num_cus) {
+    const ElemPlan st = elem_plan(B, T, N, aligned16, kElemStream);
+    if (st.grid >= 2 * static_cast<int64_t>(num_cus) || st.chunks <= 1) return kElemStream;
+    return kElemLookback;
+}
+
+hipError_t launch_scan_elem(const ElemParams& p, const ElemPlan& plan, hipStream_t stream) {
+    ElemArgs a{};
+    a.a = p.a;
+    a.x = p.x;
+    a.s0 = p.s0;
+    a.s = p.s;
+    a.s_final = p.s_final;
+    a.T = p.T;
+    a.N = p.N;
+    a.chan_tiles = plan.chan_tiles;
+    a.ncols = p.B * plan.chan_tiles;
+    a.nchunks = plan.chunks;
+    a.words = p.words;
+    a.counter = p.counter;
+    a.counter_base = p.counter_base;
+    a.epoch = p.epoch;
+    a.error_flag = p.error_flag;
+    const bool lookback = p.schedule == kElemLookback;
+    return p.gated ? launch_gated<true>(a, plan, lookback, stream)
+                   : launch_gated<false>(a, plan, lookback, stream);
+}
+
+hipError_t launch_fill_zero_u64(unsigned long long* p, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_u64_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, p, n);
+    return hipGetLastError();
+}
+
+}  // namespace lrs

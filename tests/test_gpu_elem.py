@@ -1,0 +1,170 @@
+"""GPU parity of the elementwise scans (FMA and gated forms) against the
+sequential fp64 oracle, through the C ABI.
+
+Tolerance: normwise relative error <= 1e-5 per output tensor (fp32 state; the
+pages measured fp32 scan accumulation error near 5e-7 [SunnyNet log §9.3]).
+s_final must equal the last row of s bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrence_scan_fma_amd import binding, inputs
+from _helpers import dev, rel, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = binding.Context(0)
+    yield c
+    c.close()
+
+
+def _run(ctx, kind, a, x, s0, schedule):
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, schedule)
+    s, fin = binding.scan_elementwise(ctx, kind, dev(a), dev(x), dev(s0))
+    torch.cuda.synchronize()
+    assert binding.lrs_context_check(ctx) == binding.LRS_OK
+    return s, fin
+
+
+def _oracle(kind, a, x, s0):
+    fn = oracle.scan_fma if kind == "fma" else oracle.scan_gated
+    return fn(a, x, s0)
+
+
+def _inputs(kind, B, T, N, seed, with_s0):
+    d = inputs.elementwise_small(B, T, N, seed=seed)
+    x = d["b"] if kind == "fma" else d["u"]
+    s0 = inputs.random_state((B, N), seed + 1) if with_s0 else None
+    return d["a"], x, s0
+
+
+SCHEDULES = [binding.LRS_ELEM_SCHEDULE_STREAM, binding.LRS_ELEM_SCHEDULE_LOOKBACK]
+
+# (B, T, N): the small workload, then shapes spanning several tiles and
+# chunks with ragged tails in both T and N, N not a multiple of 4, T = 1, N = 1.
+SHAPES = [
+    (2, 128, 128),     # the small elementwise workload
+    (2, 1000, 300),    # N % 4 != 0 -> one channel per lane; ragged T
+    (3, 777, 260),     # N % 64 != 0 with float4 lanes; ragged T
+    (1, 1, 5),
+    (4, 4096, 64),     # long time axis, few channels
+    (1, 3000, 1),
+    (2, 33, 4096),     # many channels, short time axis
+]
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES, ids=["stream", "lookback"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("kind", ["fma", "gated"])
+def test_elementwise_parity(ctx, kind, shape, schedule):
+    B, T, N = shape
+    for with_s0 in (False, True):
+        say(f"elem {kind} {shape} sched={schedule} s0={with_s0}")
+        a, x, s0 = _inputs(kind, B, T, N, seed=11 + T + N, with_s0=with_s0)
+        s, fin = _run(ctx, kind, a, x, s0, schedule)
+        rs, rf = _oracle(kind, a, x, s0)
+        assert rel(s, rs) <= TOL, (kind, shape, schedule, with_s0, rel(s, rs))
+        assert rel(fin, rf) <= TOL
+        assert torch.equal(fin, s[:, -1])
+
+
+@pytest.mark.parametrize("kind", ["fma", "gated"])
+def test_auto_schedule_small_workload(ctx, kind):
+    a, x, s0 = _inputs(kind, 2, 128, 128, seed=1001, with_s0=False)
+    s, fin = _run(ctx, kind, a, x, None, binding.LRS_ELEM_SCHEDULE_AUTO)
+    rs, rf = _oracle(kind, a, x, None)
+    assert rel(s, rs) <= TOL and rel(fin, rf) <= TOL
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES, ids=["stream", "lookback"])
+def test_continuation(ctx, schedule):
+    # [SunnyNet log §4]: two segments with the state passed across equal one run.
+    B, T, N = 2, 2000, 96
+    a, x, s0 = _inputs("gated", B, T, N, seed=77, with_s0=True)
+    full_s, full_f = _run(ctx, "gated", a, x, s0, schedule)
+    for t1 in (1, 37, 128, T // 2, T - 1):
+        s1, f1 = _run(ctx, "gated", a[:, :t1], x[:, :t1], s0, schedule)
+        s2, f2 = _run(ctx, "gated", a[:, t1:], x[:, t1:], f1.cpu(), schedule)
+        assert rel(torch.cat([s1, s2], dim=1), full_s) <= TOL
+        assert rel(f2, full_f) <= TOL
+
+
+def test_repeated_lookback_calls_reuse_workspace(ctx):
+    # Status words are tagged with a per-call epoch: back-to-back calls on one
+    # context, with growing and shrinking shapes, must each be right.
+    for i, (B, T, N) in enumerate([(1, 5000, 64), (2, 300, 32), (1, 9000, 128), (1, 40, 8)] * 3):
+        a, x, s0 = _inputs("fma", B, T, N, seed=300 + i, with_s0=True)
+        s, fin = _run(ctx, "fma", a, x, s0, binding.LRS_ELEM_SCHEDULE_LOOKBACK)
+        rs, rf = _oracle("fma", a, x, s0)
+        assert rel(s, rs) <= TOL and rel(fin, rf) <= TOL
+
+
+def test_stream_schedule_is_deterministic(ctx):
+    a, x, s0 = _inputs("gated", 2, 3000, 512, seed=5, with_s0=True)
+    s1, _ = _run(ctx, "gated", a, x, s0, binding.LRS_ELEM_SCHEDULE_STREAM)
+    s2, _ = _run(ctx, "gated", a, x, s0, binding.LRS_ELEM_SCHEDULE_STREAM)
+    assert torch.equal(s1, s2)
+
+
+def test_invalid_arguments_enqueue_nothing(ctx):
+    a = torch.zeros((1, 4, 4), device="cuda:0")
+    s = torch.full((1, 4, 4), 7.0, device="cuda:0")
+    f = torch.full((1, 4), 7.0, device="cuda:0")
+    L = binding.lib()
+    P = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    # zero and negative dims
+    assert L.lrs_scan_fma(ctx.handle, P(a), P(a), None, P(s), P(f), 0, 4, 4, None) == binding.LRS_E_INVAL
+    assert L.lrs_scan_gated(ctx.handle, P(a), P(a), None, P(s), P(f), 1, -4, 4, None) == binding.LRS_E_INVAL
+    # output aliasing an input
+    assert L.lrs_scan_fma(ctx.handle, P(a), P(a), None, P(a), P(f), 1, 4, 4, None) == binding.LRS_E_INVAL
+    assert L.lrs_scan_fma(ctx.handle, P(a), P(a), None, P(s), P(s), 1, 4, 4, None) == binding.LRS_E_INVAL
+    # misaligned pointer
+    assert L.lrs_scan_fma(ctx.handle, P(a) + 2, P(a), None, P(s), P(f), 1, 1, 1, None) == binding.LRS_E_INVAL
+    # bad parameter values
+    assert L.lrs_context_set_param(ctx.handle, 1, 9) == binding.LRS_E_INVAL
+    assert L.lrs_context_set_param(ctx.handle, 42, 0) == binding.LRS_E_INVAL
+    torch.cuda.synchronize()
+    assert torch.all(s == 7.0) and torch.all(f == 7.0)
+
+
+def test_gated_full_size_sampled(ctx):
+    """The large gated workload (B=16, T=8192, N=2048) in the launch
+    configuration the benchmark times (auto schedule), checked on sampled
+    channels against the oracle and on every element by invariants."""
+    cfg = inputs.GATED_LARGE
+    say("elem gated full size: generating inputs")
+    d = inputs.gated_large(**cfg)
+    a, u, s0 = d["a"], d["u"], d["s0"]
+    s, fin = _run(ctx, "gated", a, u, s0, binding.LRS_ELEM_SCHEDULE_AUTO)
+    say("elem gated full size: ran")
+    B, T, N = a.shape
+    rng = np.random.default_rng(9)
+    bs = rng.integers(0, B, 48)
+    ns = rng.integers(0, N, 48)
+    ns[:4] = [0, N - 1, N // 2, 63]   # tile edges
+    bs[:4] = [0, B - 1, 7, 3]
+    a_s = torch.stack([a[b, :, n] for b, n in zip(bs, ns)], dim=1)[None]
+    u_s = torch.stack([u[b, :, n] for b, n in zip(bs, ns)], dim=1)[None]
+    s0_s = torch.stack([s0[b, n] for b, n in zip(bs, ns)])[None]
+    rs, rf = oracle.scan_gated(a_s, u_s, s0_s)
+    gs = torch.stack([s[b, :, n] for b, n in zip(bs, ns)], dim=1)[None]
+    gf = torch.stack([fin[b, n] for b, n in zip(bs, ns)])[None]
+    assert rel(gs, rs) <= TOL
+    assert rel(gf, rf) <= TOL
+    # every element: finite, last row equals s_final, and the convex
+    # combination stays within the running [min, max] of s0 and u
+    assert torch.isfinite(s).all()
+    assert torch.equal(fin, s[:, -1])
+    ud = dev(u)
+    lo = torch.minimum(torch.cummin(ud, dim=1).values, dev(s0)[:, None, :])
+    hi = torch.maximum(torch.cummax(ud, dim=1).values, dev(s0)[:, None, :])
+    assert bool((s >= lo - 1e-5).all()) and bool((s <= hi + 1e-5).all())

@@ -164,6 +164,11 @@ __global__ __launch_bounds__(kThreads) void scan_elem_kernel(ElemArgs p) {
         }
         __syncthreads();
         tile = sh_tile;
+        if (tile < 0 || tile >= p.ncols * p.nchunks) {  // counter out of step: refuse the tile
+            if (tid == 0)
+                __hip_atomic_store(p.error_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
         chunk_lo = tile / p.ncols;
         chunk_hi = chunk_lo + 1;
         col = tile - chunk_lo * p.ncols;

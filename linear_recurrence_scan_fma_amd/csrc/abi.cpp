@@ -295,10 +295,55 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
                                        const float* k_scale, float scale, const float* s0,
                                        float* o, float* s_final, int32_t B, int32_t T, int32_t H,
                                        int32_t Hg, int32_t K, int32_t V, void* stream) {
-    (void)ctx; (void)q; (void)k; (void)v; (void)g; (void)decay_mode; (void)k_scale; (void)scale;
-    (void)s0; (void)o; (void)s_final; (void)B; (void)T; (void)H; (void)Hg; (void)K; (void)V;
-    (void)stream;
-    return LRS_E_UNSUPPORTED;
+    if (!ctx || !q || !k || !v || !g || !o || !s_final) return LRS_E_INVAL;
+    if (B < 1 || T < 1 || H < 1 || Hg < 1 || K < 1 || V < 1) return LRS_E_INVAL;
+    if (H % Hg != 0 || (decay_mode != 0 && decay_mode != 1)) return LRS_E_INVAL;
+    if (K > 128) return LRS_E_UNSUPPORTED;
+    if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(g, 4) || !aligned(k_scale, 4) ||
+        !aligned(s0, 4) || !aligned(o, 4) || !aligned(s_final, 4))
+        return LRS_E_INVAL;
+    int64_t bt = B;
+    if (!mul_ok(bt, T)) return LRS_E_INVAL;
+    int64_t nqk = bt, nv = bt, ng = bt, nst = B;
+    if (!mul_ok(nqk, Hg) || !mul_ok(nqk, K) || !mul_ok(nv, H) || !mul_ok(nv, V) || !mul_ok(ng, H) ||
+        (decay_mode == 1 && !mul_ok(ng, K)) || !mul_ok(nst, H) || !mul_ok(nst, K) || !mul_ok(nst, V))
+        return LRS_E_INVAL;
+    const size_t bqk = static_cast<size_t>(nqk) * 2, bv = static_cast<size_t>(nv) * 2;
+    const size_t bg = static_cast<size_t>(ng) * 4, bks = static_cast<size_t>(bt) * H * 4;
+    const size_t bo = static_cast<size_t>(nv) * 4, bst = static_cast<size_t>(nst) * 4;
+    const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {g, bg}, {k_scale, bks}, {s0, bst}};
+    const Span outs[] = {{o, bo}, {s_final, bst}};
+    if (!outputs_disjoint(outs, 2, ins, 6)) return LRS_E_INVAL;
+
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+    lrs::DiagParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.decay_mode = decay_mode;
+    p.k_scale = k_scale;
+    p.scale = scale;
+    p.s0 = s0;
+    p.o = o;
+    p.s_final = s_final;
+    p.B = B;
+    p.T = T;
+    p.H = H;
+    p.Hg = Hg;
+    p.K = K;
+    p.V = V;
+    p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
+             aligned(g, 16)) ? 1 : 0;
+    const int64_t grid = static_cast<int64_t>(B) * H * ((V + lrs::diag_outer_vtile(decay_mode) - 1) /
+                                                         lrs::diag_outer_vtile(decay_mode));
+    if (grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (lrs::launch_scan_diag_outer(p, st) != hipSuccess) return LRS_E_DEVICE;
+    ctx->last_stream = st;
+    ctx->used = true;
+    return LRS_OK;
 }
 
 LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,

@@ -46,6 +46,27 @@ ElemPlan elem_plan(int64_t B, int64_t T, int64_t N, bool aligned16, int schedule
 int elem_auto_schedule(int64_t B, int64_t T, int64_t N, bool aligned16, int num_cus);
 hipError_t launch_scan_elem(const ElemParams& p, const ElemPlan& plan, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Decay-separable outer-product state scan.
+// ---------------------------------------------------------------------------
+struct DiagParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* g;
+    int decay_mode;        // 0: g [B,T,H]; 1: g [B,T,H,K]
+    const float* k_scale;  // nullable
+    float scale;
+    const float* s0;       // nullable
+    float* o;
+    float* s_final;
+    int B, T, H, Hg, K, V;
+    int vec;               // 16-byte vector loads allowed
+};
+
+int diag_outer_vtile(int decay_mode);
+hipError_t launch_scan_diag_outer(const DiagParams& p, hipStream_t stream);
+
 // Fills `n` 64-bit words with zero (used to reset look-back status words).
 hipError_t launch_fill_zero_u64(unsigned long long* p, size_t n, hipStream_t stream);
 

@@ -1,0 +1,78 @@
+// Small helpers for the matrix-state scans: bf16 conversion and splitting,
+// MFMA fragment loads from LDS, and the 16x16x32 bf16 matrix-core op.
+//
+// Lane layout of v_mfma_f32_16x16x32_bf16 (64 lanes, g = lane / 16):
+//   A fragment: row (lane % 16), k = 8g .. 8g+7           (8 bf16 per lane)
+//   B fragment: col (lane % 16), k = 8g .. 8g+7
+//   D fragment: col (lane % 16), rows 4g .. 4g+3           (4 fp32 per lane)
+// Every operand is kept in LDS as a row-major array whose rows are the M (or N)
+// index and whose columns are the contraction index, so both A and B fragments
+// are one aligned 16-byte LDS read per lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace lrs {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u16 f2bf(float x) {
+    __bf16 b = static_cast<__bf16>(x);  // round to nearest even
+    return __builtin_bit_cast(u16, b);
+}
+
+__device__ __forceinline__ float bf2f(u16 h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+// x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, u16& hi, u16& lo) {
+    hi = f2bf(x);
+    lo = f2bf(x - bf2f(hi));
+}
+
+template <int LD>
+__device__ __forceinline__ bf16x8 frag(const u16* base, int r0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(base + (r0 + (lane & 15)) * LD + k0 + 8 * (lane >> 4));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() {
+    f32x4 z = {0.0f, 0.0f, 0.0f, 0.0f};
+    return z;
+}
+
+// 8 consecutive bf16 (16 bytes) of a row of length n starting at column c0;
+// zero beyond n.  `vec` says the row start is 16-byte aligned and n % 8 == 0.
+__device__ __forceinline__ u32x4 load8_bf16(const u16* row, int c0, int n, bool vec) {
+    if (vec) {
+        if (c0 + 8 <= n) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c0));
+        return u32x4{0u, 0u, 0u, 0u};
+    }
+    u16 t[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = (c0 + e < n) ? row[c0 + e] : static_cast<u16>(0);
+    return u32x4{t[0] | (static_cast<uint32_t>(t[1]) << 16), t[2] | (static_cast<uint32_t>(t[3]) << 16),
+                 t[4] | (static_cast<uint32_t>(t[5]) << 16), t[6] | (static_cast<uint32_t>(t[7]) << 16)};
+}
+
+__device__ __forceinline__ u16 piece_elem(const u32x4& v, int e) {
+    const uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
+    return static_cast<u16>((e & 1) ? (w >> 16) : (w & 0xffff));
+}
+
+// XCD-aware workgroup order: the hardware hands consecutive workgroup ids to
+// the 8 XCDs in turn; remap so that consecutive logical ids share an XCD
+// (and its L2) when the grid divides evenly.
+__device__ __forceinline__ int xcd_logical_id(int bid, int grid) {
+    if (grid % 8 != 0) return bid;
+    return (bid % 8) * (grid / 8) + bid / 8;
+}
+
+}  // namespace lrs

@@ -1,0 +1,186 @@
+"""GPU parity of the decay-separable state scan (Mamba-2 and GLA shapes)
+against the sequential fp64 oracle, through the C ABI.
+
+Tolerance: normwise relative error <= 2e-3 per (batch, head) slice of o and of
+s_final (bf16 inputs, fp32 state).  The kernel keeps fp32 operands of its
+matrix-core products as two bf16 terms, so the observed error is far smaller.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrence_scan_fma_amd import binding, inputs
+from _helpers import dev, rel_heads, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = binding.Context(0)
+    yield c
+    c.close()
+
+
+def _gpu(ctx, d, s0=None):
+    o, fin = binding.scan_diag_outer(ctx, dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["g"]),
+                                     d["decay_mode"], dev(d["k_scale"]), d["scale"], dev(s0))
+    torch.cuda.synchronize()
+    return o, fin
+
+
+def _ref(d, s0=None):
+    return oracle.scan_diag_outer(d["q"], d["k"], d["v"], d["g"], d["decay_mode"], d["k_scale"],
+                                  d["scale"], s0)
+
+
+def _check(ctx, d, s0=None, tol=TOL):
+    o, fin = _gpu(ctx, d, s0)
+    ro, rf = _ref(d, s0)
+    eo, ef = rel_heads(o, ro, "bthv"), rel_heads(fin, rf, "bhkv")
+    say(f"   rel err o={eo:.2e} s_final={ef:.2e}")
+    assert eo <= tol and ef <= tol, (eo, ef)
+    return eo, ef
+
+
+def _mamba(B, T, H, K, V, seed, Hg=1):
+    d = inputs.mamba2(B=B, T=T, H=H, K=K, V=V, seed=seed)
+    if Hg > 1:   # give each group its own B/C rows
+        rng = np.random.default_rng(seed + 7)
+        d["q"] = torch.from_numpy(rng.standard_normal((B, T, Hg, K)).astype(np.float32)).to(torch.bfloat16)
+        d["k"] = torch.from_numpy(rng.standard_normal((B, T, Hg, K)).astype(np.float32)).to(torch.bfloat16)
+    return d
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 200, 4, 1, 128, 64),    # Mamba-2 head shape, ragged T
+    (1, 64, 2, 1, 128, 64),     # exactly one chunk
+    (2, 150, 4, 2, 64, 40),     # two groups, K = 64, ragged V tile
+    (1, 130, 3, 3, 100, 37),    # K, V not multiples of 8 (scalar loads)
+    (1, 1, 2, 1, 128, 64),      # T = 1
+    (2, 70, 2, 2, 1, 1),        # K = V = 1
+], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_scalar_decay_parity(ctx, shape, with_s0):
+    B, T, H, Hg, K, V = shape
+    say(f"diag mode0 {shape} s0={with_s0}")
+    d = _mamba(B, T, H, K, V, seed=100 + T + K, Hg=Hg)
+    s0 = inputs.random_state((B, H, K, V), 5) if with_s0 else None
+    _check(ctx, d, s0)
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 300, 3, 128, 128),      # GLA head shape, ragged T
+    (1, 64, 2, 128, 128),
+    (2, 100, 2, 64, 128),       # K != V
+    (1, 90, 2, 128, 48),        # V tile ragged
+    (1, 77, 2, 36, 20),         # K, V multiples of 4 but not 8
+    (1, 1, 1, 128, 128),
+], ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_key_decay_parity(ctx, shape, with_s0):
+    B, T, H, K, V = shape
+    say(f"diag mode1 {shape} s0={with_s0}")
+    d = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=200 + T + K)
+    s0 = inputs.random_state((B, H, K, V), 6) if with_s0 else None
+    _check(ctx, d, s0)
+
+
+def test_key_decay_with_k_scale_and_groups(ctx):
+    B, T, H, Hg, K, V = 2, 140, 4, 2, 64, 64
+    rng = np.random.default_rng(9)
+    d = dict(
+        q=torch.from_numpy(rng.standard_normal((B, T, Hg, K)).astype(np.float32)).to(torch.bfloat16),
+        k=torch.from_numpy(rng.standard_normal((B, T, Hg, K)).astype(np.float32)).to(torch.bfloat16),
+        v=torch.from_numpy(rng.standard_normal((B, T, H, V)).astype(np.float32)).to(torch.bfloat16),
+        g=torch.from_numpy((-0.1 * rng.uniform(0, 1, (B, T, H, K))).astype(np.float32)),
+        decay_mode=1,
+        k_scale=torch.from_numpy(rng.uniform(0.1, 2.0, (B, T, H)).astype(np.float32)),
+        scale=0.3)
+    _check(ctx, d, inputs.random_state((B, H, K, V), 3))
+
+
+@pytest.mark.parametrize("gval", [-1.5, -4.0])
+def test_key_decay_strong_gates_exact_fallback(ctx, gval):
+    # chunk decay of 64 * |g| nats exceeds the factorised path's range: the
+    # kernel must switch to per-pair exponentials and stay accurate
+    B, T, H, K, V = 1, 200, 2, 128, 64
+    d = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=31)
+    rng = np.random.default_rng(32)
+    d["g"] = torch.from_numpy((gval * rng.uniform(0.5, 1.0, (B, T, H, K))).astype(np.float32))
+    say(f"diag strong gates g~{gval}")
+    _check(ctx, d, inputs.random_state((B, H, K, V), 4))
+
+
+def test_scalar_decay_strong_gates(ctx):
+    B, T, H, K, V = 1, 192, 2, 128, 64
+    d = _mamba(B, T, H, K, V, seed=41)
+    d["g"] = d["g"] * 10.0     # decays of tens of nats per step
+    _check(ctx, d, inputs.random_state((B, H, K, V), 4))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_continuation(ctx, mode):
+    B, T, H, K, V = 1, 260, 2, 128, 64
+    d = _mamba(B, T, H, K, V, seed=51) if mode == 0 else inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=52)
+    s0 = inputs.random_state((B, H, K, V), 7)
+    o_full, f_full = _gpu(ctx, d, s0)
+    for t1 in (1, 37, 64, 130):
+        seq = ("q", "k", "v", "g", "k_scale")
+        first = {n: (x[:, :t1] if n in seq and x is not None else x) for n, x in d.items()}
+        second = {n: (x[:, t1:] if n in seq and x is not None else x) for n, x in d.items()}
+        o1, f1 = _gpu(ctx, first, s0)
+        o2, f2 = _gpu(ctx, second, f1.cpu())
+        assert rel_heads(torch.cat([o1, o2], 1), o_full, "bthv") <= 1e-4
+        assert rel_heads(f2, f_full, "bhkv") <= 1e-4
+
+
+def test_rejects_bad_arguments(ctx):
+    d = inputs.gla(B=1, T=8, H=2, K=16, V=16, seed=1)
+    q, k, v, g = (dev(d[n]) for n in ("q", "k", "v", "g"))
+    o = torch.empty((1, 8, 2, 16), device="cuda:0")
+    f = torch.empty((1, 2, 16, 16), device="cuda:0")
+    L = binding.lib()
+    P = lambda t: t.data_ptr()  # noqa: E731
+    args = lambda mode, H, Hg, K: (ctx.handle, P(q), P(k), P(v), P(g), mode, None, 1.0, None,  # noqa: E731
+                                   P(o), P(f), 1, 8, H, Hg, K, 16, None)
+    assert L.lrs_scan_diag_outer(*args(2, 2, 2, 16)) == binding.LRS_E_INVAL      # decay mode
+    assert L.lrs_scan_diag_outer(*args(1, 3, 2, 16)) == binding.LRS_E_INVAL      # H % Hg
+    assert L.lrs_scan_diag_outer(*args(1, 2, 2, 200)) == binding.LRS_E_UNSUPPORTED  # K > 128
+    bad = list(args(1, 2, 2, 16))
+    bad[9] = P(v)   # o aliases an input
+    assert L.lrs_scan_diag_outer(*bad) == binding.LRS_E_INVAL
+
+
+def _sampled_heads(ctx, d, heads, hg_one):
+    o, fin = _gpu(ctx, d)
+    for b, h in heads:
+        grp = 0 if hg_one else h
+        sub = dict(q=d["q"][b:b + 1, :, grp:grp + 1], k=d["k"][b:b + 1, :, grp:grp + 1],
+                   v=d["v"][b:b + 1, :, h:h + 1],
+                   g=d["g"][b:b + 1, :, h:h + 1], decay_mode=d["decay_mode"],
+                   k_scale=None if d["k_scale"] is None else d["k_scale"][b:b + 1, :, h:h + 1],
+                   scale=d["scale"])
+        ro, rf = _ref(sub)
+        eo = rel_heads(o[b:b + 1, :, h:h + 1], ro, "bthv")
+        ef = rel_heads(fin[b:b + 1, h:h + 1], rf, "bhkv")
+        say(f"   head ({b},{h}): rel err o={eo:.2e} s_final={ef:.2e}")
+        assert eo <= TOL and ef <= TOL
+    assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+
+
+def test_mamba2_full_size_sampled(ctx):
+    say("diag mamba2 full size")
+    d = inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"})
+    _sampled_heads(ctx, d, [(0, 0), (7, 23), (3, 11)], hg_one=True)
+
+
+def test_gla_full_size_sampled(ctx):
+    say("diag gla full size")
+    d = inputs.gla(**inputs.GLA)
+    _sampled_heads(ctx, d, [(0, 0), (3, 3), (1, 2)], hg_one=False)

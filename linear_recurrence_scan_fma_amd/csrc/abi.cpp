@@ -26,6 +26,9 @@ struct LrsContext {
     size_t words_cap = 0;
     unsigned int epoch = 0;                 // last epoch used; status words hold 0 initially
     unsigned long long counter_base = 0;    // tiles taken from the counter so far
+    // delta-rule scratch (per-chunk UT-transform planes), grown on demand
+    void* delta_ws = nullptr;
+    size_t delta_ws_bytes = 0;
     hipStream_t last_stream = nullptr;
     bool used = false;
 };
@@ -242,6 +245,7 @@ LRS_API void lrs_context_destroy(LrsContext* ctx) {
         DeviceGuard guard(ctx->device);
         (void)hipDeviceSynchronize();
         if (ctx->words) (void)hipFree(ctx->words);
+        if (ctx->delta_ws) (void)hipFree(ctx->delta_ws);
         if (ctx->fixed) (void)hipFree(ctx->fixed);
     }
     delete ctx;
@@ -350,7 +354,65 @@ LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_
                                   const lrs_bf16* v, const float* beta, float scale,
                                   const float* s0, float* o, float* s_final, int32_t B, int32_t T,
                                   int32_t H, int32_t K, int32_t V, void* stream) {
-    (void)ctx; (void)q; (void)k; (void)v; (void)beta; (void)scale; (void)s0; (void)o;
-    (void)s_final; (void)B; (void)T; (void)H; (void)K; (void)V; (void)stream;
-    return LRS_E_UNSUPPORTED;
+    if (!ctx || !q || !k || !v || !beta || !o || !s_final) return LRS_E_INVAL;
+    if (B < 1 || T < 1 || H < 1 || K < 1 || V < 1) return LRS_E_INVAL;
+    if (K > 128) return LRS_E_UNSUPPORTED;
+    if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(beta, 4) || !aligned(s0, 4) ||
+        !aligned(o, 4) || !aligned(s_final, 4))
+        return LRS_E_INVAL;
+    int64_t bth = B;
+    if (!mul_ok(bth, T) || !mul_ok(bth, H)) return LRS_E_INVAL;
+    int64_t nqk = bth, nv = bth, nst = B;
+    if (!mul_ok(nqk, K) || !mul_ok(nv, V) || !mul_ok(nst, H) || !mul_ok(nst, K) || !mul_ok(nst, V))
+        return LRS_E_INVAL;
+    const size_t bqk = static_cast<size_t>(nqk) * 2, bv = static_cast<size_t>(nv) * 2;
+    const size_t bb = static_cast<size_t>(bth) * 4, bo = static_cast<size_t>(nv) * 4;
+    const size_t bst = static_cast<size_t>(nst) * 4;
+    const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {beta, bb}, {s0, bst}};
+    const Span outs[] = {{o, bo}, {s_final, bst}};
+    if (!outputs_disjoint(outs, 2, ins, 5)) return LRS_E_INVAL;
+
+    const int64_t nchunks = (static_cast<int64_t>(T) + 63) / 64;
+    const int64_t vtiles = (V + lrs::delta_vtile() - 1) / lrs::delta_vtile();
+    if (static_cast<int64_t>(B) * H * nchunks > 0x7fffffff || static_cast<int64_t>(B) * H * vtiles > 0x7fffffff)
+        return LRS_E_UNSUPPORTED;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+    const size_t need = lrs::delta_workspace_bytes(B, T, H);
+    if (need > ctx->delta_ws_bytes) {
+        if (ctx->delta_ws) {
+            if (hipStreamSynchronize(st) != hipSuccess) return LRS_E_DEVICE;
+            (void)hipFree(ctx->delta_ws);
+            ctx->delta_ws = nullptr;
+            ctx->delta_ws_bytes = 0;
+        }
+        void* pws = nullptr;
+        if (hipMalloc(&pws, need) != hipSuccess) {
+            (void)hipGetLastError();
+            return LRS_E_NOMEM;
+        }
+        ctx->delta_ws = pws;
+        ctx->delta_ws_bytes = need;
+    }
+    lrs::DeltaParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.scale = scale;
+    p.s0 = s0;
+    p.o = o;
+    p.s_final = s_final;
+    p.B = B;
+    p.T = T;
+    p.H = H;
+    p.K = K;
+    p.V = V;
+    p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16)) ? 1 : 0;
+    if (lrs::launch_scan_delta(p, ctx->delta_ws, st) != hipSuccess) return LRS_E_DEVICE;
+    ctx->last_stream = st;
+    ctx->used = true;
+    return LRS_OK;
 }

@@ -67,6 +67,27 @@ struct DiagParams {
 int diag_outer_vtile(int decay_mode);
 hipError_t launch_scan_diag_outer(const DiagParams& p, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Delta-rule state scan.
+// ---------------------------------------------------------------------------
+struct DeltaParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* beta;
+    float scale;
+    const float* s0;       // nullable
+    float* o;
+    float* s_final;
+    int B, T, H, K, V;
+    int vec;               // 16-byte vector loads allowed
+};
+
+int delta_vtile();
+// Device workspace the delta scan needs (per-chunk UT-transform planes).
+size_t delta_workspace_bytes(int B, int T, int H);
+hipError_t launch_scan_delta(const DeltaParams& p, void* workspace, hipStream_t stream);
+
 // Fills `n` 64-bit words with zero (used to reset look-back status words).
 hipError_t launch_fill_zero_u64(unsigned long long* p, size_t n, hipStream_t stream);
 

@@ -69,7 +69,7 @@ __device__ __forceinline__ void store8(u16* dst, const u16 (&x)[8]) {
     *reinterpret_cast<u32x4*>(dst) = w;
 }
 
-template <int MODE, int KP, int VT>
+template <int MODE, int KP, int VT, bool VEC>
 __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
     constexpr int LDK = KP + 8;   // padded row length for [*][KP] bf16 arrays
     constexpr int LDL = L + 8;    // padded row length for [*][L] bf16 arrays
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
     const int h = bh - b * p.H;
     const int grp = h / (p.H / p.Hg);
     const int v0 = vt * VT;
-    const bool vec = p.vec != 0;
+    constexpr bool vec = VEC;   // compile-time, so the vector path never waits on a scalar one
     const int64_t T = p.T;
     const int K = p.K, V = p.V, H = p.H, Hg = p.Hg;
     const int nchunks = static_cast<int>((T + L - 1) / L);
@@ -158,9 +158,12 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
                 for (int e = 0; e < 4; ++e) Gx[r][e] = 0.0f;
                 if (t < T) {
                     const float* grow = p.g + ((b * T + t) * H + h) * static_cast<int64_t>(K);
-                    if (vec && d0 + 4 <= K) {
-                        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grow + d0));
-                        Gx[r][0] = x.x; Gx[r][1] = x.y; Gx[r][2] = x.z; Gx[r][3] = x.w;
+                    if constexpr (VEC) {   // K % 8 == 0: a group of 4 keys is all in or all out
+                        if (d0 < K) {
+                            const f32x4 x =
+                                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grow + d0));
+                            Gx[r][0] = x.x; Gx[r][1] = x.y; Gx[r][2] = x.z; Gx[r][3] = x.w;
+                        }
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) Gx[r][e] = d0 + e < K ? grow[d0 + e] : 0.0f;
@@ -478,8 +481,13 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
 template <int MODE, int KP, int VT>
 hipError_t launch_t(const DiagArgs& a, hipStream_t stream) {
     const int64_t grid = static_cast<int64_t>(a.B) * a.H * a.vtiles;
-    hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, VT>), dim3(static_cast<unsigned>(grid)), dim3(NT), 0,
-                       stream, a);
+    if (a.vec) {
+        hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, VT, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(NT), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, VT, false>), dim3(static_cast<unsigned>(grid)),
+                           dim3(NT), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

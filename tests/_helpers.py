@@ -21,9 +21,14 @@ def rel(x, y):
 def rel_heads(x, y, layout):
     """Max over (b, h) slices of the normwise relative error, so one bad head
     cannot hide behind the others.  layout: "bthv" ([B,T,H,V] outputs) or
-    "bhkv" ([B,H,K,V] states)."""
+    "bhkv" ([B,H,K,V] states).  A slice with fewer than 16 elements (a K = V = 1
+    state is a single number, possibly ~0) is not a matrix and has no useful
+    normwise error of its own; such tensors are compared normwise as a whole."""
     x = x.detach().cpu().double().numpy() if isinstance(x, torch.Tensor) else np.asarray(x, np.float64)
     y = y.detach().cpu().double().numpy() if isinstance(y, torch.Tensor) else np.asarray(y, np.float64)
+    per_slice = x[0, :, 0].size if layout == "bthv" else x[0, 0].size
+    if per_slice < 16:
+        return rel(x, y)
     B = x.shape[0]
     H = x.shape[2] if layout == "bthv" else x.shape[1]
     worst = 0.0

@@ -338,8 +338,10 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
     p.Hg = Hg;
     p.K = K;
     p.V = V;
+    // the vector path addresses one batch row of each tensor with 32-bit buffer offsets
+    const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
-             aligned(g, 16)) ? 1 : 0;
+             aligned(g, 16) && row_bytes < (int64_t{1} << 31)) ? 1 : 0;
     const int64_t grid = static_cast<int64_t>(B) * H * ((V + lrs::diag_outer_vtile(decay_mode) - 1) /
                                                          lrs::diag_outer_vtile(decay_mode));
     if (grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
@@ -410,7 +412,10 @@ LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_
     p.H = H;
     p.K = K;
     p.V = V;
-    p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16)) ? 1 : 0;
+    // the vector path addresses one batch row of each tensor with 32-bit buffer offsets
+    const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
+    p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
+             row_bytes < (int64_t{1} << 31)) ? 1 : 0;
     if (lrs::launch_scan_delta(p, ctx->delta_ws, st) != hipSuccess) return LRS_E_DEVICE;
     ctx->last_stream = st;
     ctx->used = true;

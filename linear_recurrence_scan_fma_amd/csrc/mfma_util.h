@@ -52,8 +52,11 @@ __device__ __forceinline__ f32x4 zero4() {
 // zero beyond n.  `vec` says the row start is 16-byte aligned and n % 8 == 0.
 __device__ __forceinline__ u32x4 load8_bf16(const u16* row, int c0, int n, bool vec) {
     if (vec) {
-        if (c0 + 8 <= n) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c0));
-        return u32x4{0u, 0u, 0u, 0u};
+        // zero first, then the guarded load: a zero written after a masked load
+        // to the same registers would force the load to drain first
+        u32x4 r = {0u, 0u, 0u, 0u};
+        if (c0 + 8 <= n) r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + c0));
+        return r;
     }
     u16 t[8];
 #pragma unroll
@@ -65,6 +68,27 @@ __device__ __forceinline__ u32x4 load8_bf16(const u16* row, int c0, int n, bool 
 __device__ __forceinline__ u16 piece_elem(const u32x4& v, int e) {
     const uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
     return static_cast<u16>((e & 1) ? (w >> 16) : (w & 0xffff));
+}
+
+// Raw buffer access.  A buffer resource covers [base, base + bytes); a load
+// whose offset falls outside returns zero without touching memory.  The kernels
+// give each (batch) row of a tensor its own resource, so time steps past T and
+// columns past K or V read as zero with no branch, and the prefetch of the next
+// chunk stays a straight run of loads.
+typedef __amdgpu_buffer_rsrc_t BufRes;
+constexpr int kBufOOB = 0x7fffffff;   // an offset past every resource
+
+__device__ __forceinline__ BufRes make_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(BufRes r, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ float buf_load_f32(BufRes r, int off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
 // XCD-aware workgroup order: the hardware hands consecutive workgroup ids to

@@ -89,11 +89,16 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     const int64_t T = p.T, t0 = static_cast<int64_t>(c) * L;
     const int K = p.K;
 
+    const BufRes rk = make_rsrc(p.k + b * T * p.H * static_cast<int64_t>(K), T * p.H * static_cast<int64_t>(K) * 2);
     for (int pi = tid; pi < L * KP / 8; pi += NT) {
         const int row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
         const int64_t t = t0 + row;
         u32x4 x = {0u, 0u, 0u, 0u};
-        if (t < T) x = load8_bf16(p.k + ((b * T + t) * p.H + h) * static_cast<int64_t>(K), c8, K, VEC);
+        if constexpr (VEC) {
+            x = buf_load16(rk, c8 < K ? ((static_cast<int>(t) * p.H + h) * K + c8) * 2 : kBufOOB);
+        } else {
+            if (t < T) x = load8_bf16(p.k + ((b * T + t) * p.H + h) * static_cast<int64_t>(K), c8, K, false);
+        }
         *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = x;
     }
     if (tid < L) sBeta[tid] = (t0 + tid < T) ? p.beta[(b * T + t0 + tid) * p.H + h] : 0.0f;
@@ -232,41 +237,66 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     const int nchunks = p.nchunks;
     const u16* tbase = p.tb + static_cast<int64_t>(bh) * nchunks * 2 * L * L;
 
-    // q/k pieces: row = pi % 64 (lanes along time), columns c8 = 8 * (pi / 64)
+    // q/k pieces: row = pi % 64 (lanes along time), columns c8 = 8 * (pi / 64).
+    // Vector path: per-batch-row buffer resources; rows past T and columns past
+    // K / V read as zero in hardware, so the prefetch is a straight run of loads.
+    const int64_t qk_row = static_cast<int64_t>(H) * K, v_row = static_cast<int64_t>(H) * V;
+    const BufRes rq = make_rsrc(p.q + b * T * qk_row, T * qk_row * 2);
+    const BufRes rk = make_rsrc(p.k + b * T * qk_row, T * qk_row * 2);
+    const BufRes rv = make_rsrc(p.v + b * T * v_row, T * v_row * 2);
+    const BufRes rt = make_rsrc(tbase, static_cast<int64_t>(nchunks) * 2 * L * L * 2);
     u32x4 cq[PQ], ck[PQ], nq[PQ], nk[PQ], cv[PVT], nv[PVT], ct[PT], nt[PT];
     auto load_chunk = [&](int c, u32x4 (&Q)[PQ], u32x4 (&Kx)[PQ], u32x4 (&Vx)[PVT], u32x4 (&Tx)[PT]) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
+        if constexpr (VEC) {
 #pragma unroll
-        for (int i = 0; i < PQ; ++i) {
-            const int pi = tid + NT * i;
-            const int row = pi % L, c8 = (pi / L) * 8;
-            const int64_t t = t0 + row;
-            if (t < T) {
-                const int64_t off = ((b * T + t) * H + h) * static_cast<int64_t>(K);
-                Q[i] = load8_bf16(p.q + off, c8, K, VEC);
-                Kx[i] = load8_bf16(p.k + off, c8, K, VEC);
-            } else {
-                Q[i] = u32x4{0u, 0u, 0u, 0u};
-                Kx[i] = u32x4{0u, 0u, 0u, 0u};
+            for (int i = 0; i < PQ; ++i) {
+                const int pi = tid + NT * i;
+                const int row = pi % L, c8 = (pi / L) * 8;
+                const int t = static_cast<int>(t0) + row;
+                const int off = c8 < K ? ((t * H + h) * K + c8) * 2 : kBufOOB;
+                Q[i] = buf_load16(rq, off);
+                Kx[i] = buf_load16(rk, off);
             }
-        }
 #pragma unroll
-        for (int i = 0; i < PVT; ++i) {
-            const int pi = tid + NT * i;
-            Vx[i] = u32x4{0u, 0u, 0u, 0u};
-            if (pi < NVP) {
+            for (int i = 0; i < PVT; ++i) {
+                const int pi = tid + NT * i;
+                const int row = pi % L, c8 = (pi / L) * 8;
+                const int t = static_cast<int>(t0) + row;
+                const int off = (pi < NVP && v0 + c8 < V) ? ((t * H + h) * V + v0 + c8) * 2 : kBufOOB;
+                Vx[i] = buf_load16(rv, off);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PQ; ++i) {
+                const int pi = tid + NT * i;
                 const int row = pi % L, c8 = (pi / L) * 8;
                 const int64_t t = t0 + row;
-                if (t < T)
-                    Vx[i] = load8_bf16(p.v + ((b * T + t) * H + h) * static_cast<int64_t>(V) + v0, c8, V - v0,
-                                       VEC);
+                Q[i] = u32x4{0u, 0u, 0u, 0u};
+                Kx[i] = u32x4{0u, 0u, 0u, 0u};
+                if (t < T) {
+                    const int64_t off = ((b * T + t) * H + h) * static_cast<int64_t>(K);
+                    Q[i] = load8_bf16(p.q + off, c8, K, false);
+                    Kx[i] = load8_bf16(p.k + off, c8, K, false);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < PVT; ++i) {
+                const int pi = tid + NT * i;
+                Vx[i] = u32x4{0u, 0u, 0u, 0u};
+                if (pi < NVP) {
+                    const int row = pi % L, c8 = (pi / L) * 8;
+                    const int64_t t = t0 + row;
+                    if (t < T)
+                        Vx[i] = load8_bf16(p.v + ((b * T + t) * H + h) * static_cast<int64_t>(V) + v0, c8,
+                                           V - v0, false);
+                }
             }
         }
-        const u16* tb = tbase + static_cast<int64_t>(c) * 2 * L * L;
 #pragma unroll
         for (int i = 0; i < PT; ++i) {
             const int pi = tid + NT * i;   // hi plane pieces 0..511, lo plane 512..1023
-            Tx[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + 8 * pi));
+            Tx[i] = buf_load16(rt, (c * 2 * L * L + 8 * pi) * 2);
         }
     };
 

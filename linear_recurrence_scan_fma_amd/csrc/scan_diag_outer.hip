@@ -119,67 +119,105 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
     float ng[MODE == 1 ? RPG : 1][4];
     float cgs = 0.0f, ngs = 0.0f, ckap = 0.0f, nkap = 0.0f;
 
+    // Per-batch-row buffer resources (vector path): rows past T and columns
+    // past K / V fall outside and read as zero.
+    const BufRes rq = make_rsrc(p.q + b * T * Hg * static_cast<int64_t>(K), T * Hg * static_cast<int64_t>(K) * 2);
+    const BufRes rk = make_rsrc(p.k + b * T * Hg * static_cast<int64_t>(K), T * Hg * static_cast<int64_t>(K) * 2);
+    const BufRes rv = make_rsrc(p.v + b * T * H * static_cast<int64_t>(V), T * H * static_cast<int64_t>(V) * 2);
+    const int64_t gcols = MODE == 1 ? K : 1;
+    const BufRes rdec = make_rsrc(p.g + b * T * H * gcols, T * H * gcols * 4);
+    const BufRes rks = make_rsrc(p.ks ? p.ks + b * T * H : p.g, p.ks ? T * H * 4 : 0);
+
     auto load_chunk = [&](int64_t t0, u32x4 (&Q)[PQ], u32x4 (&Kx)[PQ], u32x4 (&Vx)[PV],
                           float (&Gx)[MODE == 1 ? RPG : 1][4], float& gs, float& kap) {
+        if constexpr (VEC) {
 #pragma unroll
-        for (int i = 0; i < PQ; ++i) {
-            const int pi = tid + NT * i;
-            const int row = pi / (KP / 8);
-            const int c8 = (pi % (KP / 8)) * 8;
-            const int64_t t = t0 + row;
-            if (t < T) {
-                const int64_t off = ((b * T + t) * Hg + grp) * static_cast<int64_t>(K);
-                Q[i] = load8_bf16(p.q + off, c8, K, vec);
-                Kx[i] = load8_bf16(p.k + off, c8, K, vec);
-            } else {
+            for (int i = 0; i < PQ; ++i) {
+                const int pi = tid + NT * i;
+                const int row = pi / (KP / 8);
+                const int c8 = (pi % (KP / 8)) * 8;
+                const int t = static_cast<int>(t0) + row;
+                const int off = c8 < K ? ((t * Hg + grp) * K + c8) * 2 : kBufOOB;
+                Q[i] = buf_load16(rq, off);
+                Kx[i] = buf_load16(rk, off);
+            }
+#pragma unroll
+            for (int i = 0; i < PV; ++i) {
+                const int pi = tid + NT * i;
+                const int row = pi / (VT / 8);
+                const int c8 = (pi % (VT / 8)) * 8;
+                const int t = static_cast<int>(t0) + row;
+                const int off = v0 + c8 < V ? ((t * H + h) * V + v0 + c8) * 2 : kBufOOB;
+                Vx[i] = buf_load16(rv, off);
+            }
+            if constexpr (MODE == 1) {
+                const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
+#pragma unroll
+                for (int r = 0; r < RPG; ++r) {
+                    const int t = static_cast<int>(t0) + rg * RPG + r;
+                    const int off = d0 < K ? ((t * H + h) * K + d0) * 4 : kBufOOB;
+                    const u32x4 x = buf_load16(rdec, off);
+                    Gx[r][0] = __uint_as_float(x.x);
+                    Gx[r][1] = __uint_as_float(x.y);
+                    Gx[r][2] = __uint_as_float(x.z);
+                    Gx[r][3] = __uint_as_float(x.w);
+                }
+            }
+            if (tid < L) {
+                const int t = static_cast<int>(t0) + tid;
+                if constexpr (MODE == 0) gs = buf_load_f32(rdec, (t * H + h) * 4);
+                kap = buf_load_f32(rks, (t * H + h) * 4);   // raw; NULL k_scale handled in phase 0
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PQ; ++i) {
+                const int pi = tid + NT * i;
+                const int row = pi / (KP / 8);
+                const int c8 = (pi % (KP / 8)) * 8;
+                const int64_t t = t0 + row;
                 Q[i] = u32x4{0u, 0u, 0u, 0u};
                 Kx[i] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < PV; ++i) {
-            const int pi = tid + NT * i;
-            const int row = pi / (VT / 8);
-            const int c8 = (pi % (VT / 8)) * 8;
-            const int64_t t = t0 + row;
-            if (t < T) {
-                const int64_t off = ((b * T + t) * H + h) * static_cast<int64_t>(V) + v0;
-                Vx[i] = load8_bf16(p.v + off, c8, V - v0, vec);
-            } else {
-                Vx[i] = u32x4{0u, 0u, 0u, 0u};
-            }
-        }
-        if constexpr (MODE == 1) {
-            const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
-#pragma unroll
-            for (int r = 0; r < RPG; ++r) {
-                const int64_t t = t0 + rg * RPG + r;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Gx[r][e] = 0.0f;
                 if (t < T) {
-                    const float* grow = p.g + ((b * T + t) * H + h) * static_cast<int64_t>(K);
-                    if constexpr (VEC) {   // K % 8 == 0: a group of 4 keys is all in or all out
-                        if (d0 < K) {
-                            const f32x4 x =
-                                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(grow + d0));
-                            Gx[r][0] = x.x; Gx[r][1] = x.y; Gx[r][2] = x.z; Gx[r][3] = x.w;
-                        }
-                    } else {
+                    const int64_t off = ((b * T + t) * Hg + grp) * static_cast<int64_t>(K);
+                    Q[i] = load8_bf16(p.q + off, c8, K, false);
+                    Kx[i] = load8_bf16(p.k + off, c8, K, false);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < PV; ++i) {
+                const int pi = tid + NT * i;
+                const int row = pi / (VT / 8);
+                const int c8 = (pi % (VT / 8)) * 8;
+                const int64_t t = t0 + row;
+                Vx[i] = u32x4{0u, 0u, 0u, 0u};
+                if (t < T) {
+                    const int64_t off = ((b * T + t) * H + h) * static_cast<int64_t>(V) + v0;
+                    Vx[i] = load8_bf16(p.v + off, c8, V - v0, false);
+                }
+            }
+            if constexpr (MODE == 1) {
+                const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
+#pragma unroll
+                for (int r = 0; r < RPG; ++r) {
+                    const int64_t t = t0 + rg * RPG + r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Gx[r][e] = 0.0f;
+                    if (t < T) {
+                        const float* grow = p.g + ((b * T + t) * H + h) * static_cast<int64_t>(K);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) Gx[r][e] = d0 + e < K ? grow[d0 + e] : 0.0f;
                     }
                 }
             }
-        }
-        if (tid < L) {
-            const int64_t t = t0 + tid;
-            if (t < T) {
-                const int64_t idx = (b * T + t) * H + h;
-                if constexpr (MODE == 0) gs = p.g[idx];
-                kap = p.ks ? p.ks[idx] : 1.0f;
-            } else {
+            if (tid < L) {
+                const int64_t t = t0 + tid;
                 gs = 0.0f;
                 kap = 0.0f;
+                if (t < T) {
+                    const int64_t idx = (b * T + t) * H + h;
+                    if constexpr (MODE == 0) gs = p.g[idx];
+                    kap = p.ks ? p.ks[idx] : 1.0f;
+                }
             }
         }
     };
@@ -232,7 +270,7 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sVT[(c8 + e) * LDL + row] = piece_elem(cv[i], e);
         }
-        if (tid < L) sKap[tid] = ckap;
+        if (tid < L) sKap[tid] = (VEC && !p.ks) ? (t0 + tid < T ? 1.0f : 0.0f) : ckap;
         if constexpr (MODE == 1) {
             const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3 runs: launch each kernel a few times, plus a plain 1 GiB "
+                         "device copy that calibrates the HBM byte counters; prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the scans run on a single MI355X and this "
@@ -101,6 +104,10 @@ def main():
 
     dev = torch.device("cuda:0")
     ctx = binding.Context(0)
+    if args.profile:
+        profile_run(ctx, binding, inputs, dev, args.steps)
+        ctx.close()
+        return
 
     # ---- headline: gated elementwise scan, B=16 T=8192 N=2048 --------------------
     cfg = inputs.GATED_LARGE
@@ -121,7 +128,7 @@ def main():
     nbytes = elem_bytes(B, T, N)
     value = nbytes / (ms_step * 1e-3) / 1e9
     achieved = nbytes / (ms_kernel * 1e-3) / 1e9
-    traffic = measured_traffic("scan_elem_gated_stream_16x8192x2048", "scan_elem.hip")
+    traffic = measured_traffic("scan_elem_gated_B16_T8192_N2048", "scan_elem.hip")
     line = {
         "metric": "gated elementwise scan throughput (algorithmic HBM GB/s)",
         "value": round(value, 2),
@@ -171,9 +178,87 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def run_rows(ctx, args, binding, inputs, dev):
-    """The other scans at their workload shapes."""
+def profile_run(ctx, binding, inputs, dev, steps):
+    """Each kernel at its workload shape, `steps` launches, for rocprofv3
+    (kernel trace or counters).  The copy of a 1 GiB tensor reads and writes
+    exactly 2^30 bytes each way and calibrates FETCH_SIZE / WRITE_SIZE."""
     import torch
+
+    src = torch.ones(1 << 28, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    del src, dst
+    d = inputs.gated_large(**inputs.GATED_LARGE)
+    a, u, s0 = d["a"].to(dev), d["u"].to(dev), d["s0"].to(dev)
+    s = torch.empty_like(a)
+    fin = torch.empty_like(s0)
+    for _ in range(steps):
+        binding.lrs_scan_gated(ctx, a, u, s0, s, fin)
+    torch.cuda.synchronize()
+    del a, u, s, d
+    for gen, kind in ((lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}), "diag"),
+                      (lambda: inputs.gla(**inputs.GLA), "diag"),
+                      (lambda: inputs.deltanet(**inputs.DELTANET), "delta"),
+                      (lambda: inputs.deltanet(**inputs.DELTANET_K64), "delta")):
+        m = gen()
+        q, k, v = (m[n].to(dev) for n in ("q", "k", "v"))
+        for _ in range(steps):
+            if kind == "diag":
+                binding.scan_diag_outer(ctx, q, k, v, m["g"].to(dev), m["decay_mode"],
+                                        None if m["k_scale"] is None else m["k_scale"].to(dev), m["scale"])
+            else:
+                binding.scan_delta(ctx, q, k, v, m["beta"].to(dev), m["scale"])
+        torch.cuda.synchronize()
+    assert binding.lrs_context_check(ctx) == binding.LRS_OK
+    log("[bench] profile run done")
+
+
+def diag_bytes(d):
+    """Algorithmic HBM bytes of one scan_diag_outer call (inputs read once,
+    outputs written once, no initial state)."""
+    q, v, g, ks = d["q"], d["v"], d["g"], d["k_scale"]
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    n = 2 * q.numel() * 2 + v.numel() * 2 + g.numel() * 4 + (ks.numel() * 4 if ks is not None else 0)
+    return n + B * T * H * V * 4 + B * H * K * V * 4
+
+
+def delta_bytes(d):
+    q, v, beta = d["q"], d["v"], d["beta"]
+    B, T, H, K = q.shape
+    V = v.shape[3]
+    return 2 * q.numel() * 2 + v.numel() * 2 + beta.numel() * 4 + B * T * H * V * 4 + B * H * K * V * 4
+
+
+def time_launches(fn, reps, warmup, flush):
+    """Median and min of per-launch HIP-event times on the current stream, with
+    the 256 MB last-level cache flushed (a 512 MB write) before each launch."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    ts = []
+    for i in range(warmup + reps):
+        flush.add_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= warmup:
+            ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return ts[len(ts) // 2], ts[0]
+
+
+def run_rows(ctx, args, binding, inputs, dev):
+    """The other scans at their workload shapes, each with a roofline figure,
+    parity on sampled heads, and the CPU oracle timed on a sample beside it."""
+    import numpy as np
+    import torch
+
+    import oracle
 
     rows = []
     # small elementwise workload (launch-latency bound; no roofline claim)
@@ -185,9 +270,85 @@ def run_rows(ctx, args, binding, inputs, dev):
         fn = binding.lrs_scan_fma if kind == "fma" else binding.lrs_scan_gated
         ms_step, ms_kernel = time_steps(lambda: fn(ctx, a, x, None, s, fin), 200, 10)
         nbytes = elem_bytes(2, 128, 128, with_s0=False)
-        rows.append({"row": f"scan_{kind} B=2 T=128 N=128", "us_per_call": round(ms_kernel * 1e3, 3),
+        rows.append({"row": f"scan_{kind} B=2 T=128 N=128 fp32", "us_per_call": round(ms_kernel * 1e3, 3),
+                     "elements_per_s": round(32768 / (ms_kernel * 1e-3), 1),
                      "GB/s": round(nbytes / (ms_kernel * 1e-3) / 1e9, 2),
-                     "note": "launch-latency bound (394 KB per call)"})
+                     "note": "launch-latency bound (394 KB per call); no roofline claim"})
+
+    flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
+    nth = oracle.default_threads()
+    heads = [(0, 0), (1, 1)]
+    specs = [
+        ("scan_diag_outer Mamba-2 B=8 T=4096 H=24 P=64 N=128 (scalar decay, 1 group)", "diag",
+         lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}),
+         ["diag_outer_mamba2_B8_T4096_H24_P64_N128"]),
+        ("scan_diag_outer GLA B=4 T=4096 H=4 K=128 V=128 (per-key decay)", "diag",
+         lambda: inputs.gla(**inputs.GLA), ["diag_outer_gla_B4_T4096_H4_K128_V128"]),
+        ("scan_delta DeltaNet B=4 T=4096 H=8 K=128 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET),
+         ["delta_prep_deltanet_B4_T4096_H8_K128", "delta_scan_deltanet_B4_T4096_H8_K128_V128"]),
+        ("scan_delta DeltaNet B=4 T=4096 H=8 K=64 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET_K64),
+         ["delta_prep_deltanet_B4_T4096_H8_K64", "delta_scan_deltanet_B4_T4096_H8_K64_V128"]),
+    ]
+    for name, kind, gen, traffic_keys in specs:
+        log(f"[bench] row {name}")
+        d = gen()
+        q, k, v = (d[n].to(dev) for n in ("q", "k", "v"))
+        B, T = q.shape[0], q.shape[1]
+        H, V, K = v.shape[2], v.shape[3], q.shape[3]
+        o = torch.empty((B, T, H, V), device=dev)
+        fin = torch.empty((B, H, K, V), device=dev)
+        if kind == "diag":
+            g = d["g"].to(dev)
+            ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
+            fn = lambda: binding.lrs_scan_diag_outer(ctx, q, k, v, g, d["decay_mode"], ks, d["scale"],  # noqa: E731
+                                                     None, o, fin)
+            nbytes = diag_bytes(d)
+            flops_per_unit = 5 * K * V
+        else:
+            beta = d["beta"].to(dev)
+            fn = lambda: binding.lrs_scan_delta(ctx, q, k, v, beta, d["scale"], None, o, fin)  # noqa: E731
+            nbytes = delta_bytes(d)
+            flops_per_unit = 6 * K * V
+        med, mn = time_launches(fn, 20, 3, flush)
+        units = B * T * H
+        row = {"row": name, "us_median": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+               "tokens_heads_per_s": round(units / (med * 1e-3), 1),
+               "roofline": {"bound": "hbm", "achieved": round(nbytes / (med * 1e-3) / 1e9, 2),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes_per_call": nbytes},
+               "algorithmic_TFLOP/s": round(units * flops_per_unit / (med * 1e-3) / 1e12, 3)}
+        src = "scan_diag_outer.hip" if kind == "diag" else "scan_delta.hip"
+        tr = [measured_traffic(key, src) for key in traffic_keys]
+        row["roofline"]["traffic"] = None if any(t is None for t in tr) else sum(tr)
+        # parity and the CPU oracle on sampled heads (full time axis)
+        errs = []
+        t_cpu = 0.0
+        for (bb, hh) in heads:
+            if kind == "diag":
+                grp = 0 if d["q"].shape[2] == 1 else hh
+                sub = (d["q"][bb:bb + 1, :, grp:grp + 1], d["k"][bb:bb + 1, :, grp:grp + 1],
+                       d["v"][bb:bb + 1, :, hh:hh + 1], d["g"][bb:bb + 1, :, hh:hh + 1], d["decay_mode"],
+                       None if d["k_scale"] is None else d["k_scale"][bb:bb + 1, :, hh:hh + 1], d["scale"])
+                t0 = time.perf_counter()
+                ro, rf = oracle.scan_diag_outer(*sub, nthreads=1)
+            else:
+                sub = tuple(d[n][bb:bb + 1, :, hh:hh + 1] for n in ("q", "k", "v", "beta"))
+                t0 = time.perf_counter()
+                ro, rf = oracle.scan_delta(*sub, d["scale"], nthreads=1)
+            t_cpu += time.perf_counter() - t0
+            go = o[bb:bb + 1, :, hh:hh + 1].cpu().double().numpy()
+            gf = fin[bb:bb + 1, hh:hh + 1].cpu().double().numpy()
+            errs.append(max(float(np.max(np.abs(go - ro)) / np.max(np.abs(ro))),
+                            float(np.max(np.abs(gf - rf)) / np.max(np.abs(rf)))))
+        row["parity_max_rel_err_sampled_heads"] = max(errs)
+        # heads are independent: one oracle thread per head gives nth heads in parallel
+        row["cpu_baseline"] = {"value": round(len(heads) * T / t_cpu * min(nth, B * H), 1),
+                               "unit": "tokens*heads/s", "cores": min(nth, B * H), "kind": "oracle",
+                               "sample": f"{len(heads)} heads x full T timed on one thread (fp64 oracle), "
+                                         f"scaled by the {min(nth, B * H)} threads the oracle spreads heads over"}
+        rows.append(row)
+        del q, k, v, o, fin
     return rows
 
 

@@ -119,7 +119,9 @@ void lrs_context_destroy(LrsContext* ctx);
 
 /* Tuning knobs.  LRS_PARAM_ELEM_SCHEDULE picks how the elementwise scans
  * split the time axis:
- *   LRS_ELEM_SCHEDULE_AUTO      (default) chooses from the shape;
+ *   LRS_ELEM_SCHEDULE_AUTO      (default) look-back when the time axis spans
+ *                               at least two chunks (128 steps) and its status
+ *                               words fit in 256 MB, stream otherwise;
  *   LRS_ELEM_SCHEDULE_STREAM    each workgroup owns a set of channels and
  *                               walks the whole time axis, carrying the state
  *                               on chip (no inter-workgroup traffic);
@@ -152,8 +154,9 @@ lrs_status lrs_context_check(LrsContext* ctx);
  *   s_final       fp32 [B,N]     output: s_T (bit-equal to s[:,T-1,:])
  *
  * The gated form is evaluated as fma(a, s - u, u), algebraically equal to
- * a s + (1 - a) u.  Limits: B*N and B*T*N below 2^31 channel-steps per
- * batch row are not required; any int32 sizes are accepted.
+ * a s + (1 - a) u.  Any int32 sizes are accepted (offsets are 64-bit).  The
+ * look-back schedule keeps 24 bytes of status words per channel and 128 time
+ * steps in the context workspace (about 50 MB for B=16, T=8192, N=2048).
  */
 lrs_status lrs_scan_fma(LrsContext* ctx, const float* a, const float* b, const float* s0,
                         float* s, float* s_final, int32_t B, int32_t T, int32_t N,

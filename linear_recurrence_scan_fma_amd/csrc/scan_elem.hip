@@ -22,7 +22,8 @@
 //      stream:   a workgroup walks the whole time axis of its channel tile,
 //                prefetching chunk c+1 while it scans chunk c; the carry stays
 //                in registers.  No inter-workgroup traffic at all.
-//      lookback: a workgroup owns a single chunk of a channel tile.  It
+//      lookback: a workgroup owns a single chunk of a channel tile (the
+//                default whenever there are several chunks).  It
 //                publishes its chunk aggregate, then walks back over
 //                predecessors' status words until it finds an inclusive
 //                prefix (decoupled look-back), then publishes its own
@@ -360,14 +361,19 @@ hipError_t launch_variant(const ElemArgs& a, bool lookback, int64_t grid, hipStr
     return hipGetLastError();
 }
 
+template <bool GATED, int VEC>
+hipError_t launch_rows(const ElemArgs& a, const ElemPlan& plan, bool lookback, hipStream_t s) {
+    switch (plan.rows) {
+        case 2: return launch_variant<GATED, VEC, 2>(a, lookback, plan.grid, s);
+        case 4: return launch_variant<GATED, VEC, 4>(a, lookback, plan.grid, s);
+        case 16: return launch_variant<GATED, VEC, 16>(a, lookback, plan.grid, s);
+        default: return launch_variant<GATED, VEC, 8>(a, lookback, plan.grid, s);
+    }
+}
+
 template <bool GATED>
 hipError_t launch_gated(const ElemArgs& a, const ElemPlan& plan, bool lookback, hipStream_t s) {
-    if (plan.vec == 4) {
-        return plan.rows == 8 ? launch_variant<GATED, 4, 8>(a, lookback, plan.grid, s)
-                              : launch_variant<GATED, 4, 2>(a, lookback, plan.grid, s);
-    }
-    return plan.rows == 8 ? launch_variant<GATED, 1, 8>(a, lookback, plan.grid, s)
-                          : launch_variant<GATED, 1, 2>(a, lookback, plan.grid, s);
+    return plan.vec == 4 ? launch_rows<GATED, 4>(a, plan, lookback, s) : launch_rows<GATED, 1>(a, plan, lookback, s);
 }
 
 }  // namespace
@@ -395,9 +401,16 @@ ElemPlan elem_plan(int64_t B, int64_t T, int64_t N, bool aligned16, int schedule
     return pl;
 }
 
+// The look-back schedule takes tiles in time-major order, so at any moment the
+// running workgroups cover a compact band of rows of every tensor; measured on
+// the B=16 T=8192 N=2048 gated workload it streams at 5.8 TB/s against 4.9 TB/s
+// for the stream schedule (whose workgroups each sweep their own column strip
+// over the whole time axis).  It is used whenever there are at least two time
+// chunks and its status words stay within 256 MB.
 int elem_auto_schedule(int64_t B, int64_t T, int64_t N, bool aligned16, int num_cus) {
-    const ElemPlan st = elem_plan(B, T, N, aligned16, kElemStream);
-    if (st.grid >= 2 * static_cast<int64_t>(num_cus) || st.chunks <= 1) return kElemStream;
+    (void)num_cus;
+    const ElemPlan lb = elem_plan(B, T, N, aligned16, kElemLookback);
+    if (lb.chunks <= 1 || lb.words * sizeof(unsigned long long) > (size_t{256} << 20)) return kElemStream;
     return kElemLookback;
 }
 

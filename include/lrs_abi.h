@@ -211,7 +211,10 @@ lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf1
  *   o         fp32 [B,T,H,V]     output
  *   s_final   fp32 [B,H,K,V]     output
  *
- * Limits: 1 <= K <= 128 (LRS_E_UNSUPPORTED above).
+ * Limits: 1 <= K <= 128 and T <= 4194304 (LRS_E_UNSUPPORTED beyond).  The
+ * context keeps a workspace of 32 KiB per (batch, head, 64-step chunk),
+ * grown on demand (LRS_E_NOMEM if that allocation fails); growing it waits
+ * for the stream of the call.
  */
 lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                           const lrs_bf16* v, const float* beta, float scale, const float* s0,

@@ -378,6 +378,8 @@ LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_
     const int64_t vtiles = (V + lrs::delta_vtile() - 1) / lrs::delta_vtile();
     if (static_cast<int64_t>(B) * H * nchunks > 0x7fffffff || static_cast<int64_t>(B) * H * vtiles > 0x7fffffff)
         return LRS_E_UNSUPPORTED;
+    // the scan kernel addresses one (batch, head) slice of the workspace with 32-bit offsets
+    if (lrs::delta_workspace_bytes(1, T, 1) >= (size_t{1} << 31)) return LRS_E_UNSUPPORTED;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     DeviceGuard guard(ctx->device);

@@ -10,29 +10,29 @@
 // Chunked (WY / UT) form.  Inside a chunk of L = 64 steps with entering state
 // S0, the deltas Delta (L x V) satisfy (I + A) Delta = diag(beta)(V - K S0)
 // with A = strict_lower(diag(beta) K K^T), because step t subtracts the
-// read-back of the earlier deltas of the same chunk.  So, with
-// Tb = (I + A)^{-1} diag(beta):
-//   Delta = Tb (V - K S0),   O = scale (Q S0 + tril(Q K^T) Delta),
-//   S_L   = S0 + K^T Delta.
+// read-back of the earlier deltas of the same chunk.  With
+// Tb = (I + A)^{-1} diag(beta) and MTb = tril(Q K^T) Tb:
+//   R = V - K S0,   Delta = Tb R,   O = scale (Q S0 + MTb R),   S_L = S0 + K^T Delta.
 // This is the sequential recurrence regrouped exactly (the pages call the
 // rank-1 form token-serial; the regrouping changes only the order of
 // additions).
 //
 // Two kernels:
-//  * delta_prep: one workgroup per (batch, head, chunk), all in parallel.  It
-//    forms A on the matrix cores (bf16 keys enter exactly), inverts I + A by
-//    blocked forward substitution in fp32 (16 x 16 diagonal blocks, then the
-//    off-diagonal blocks in three dependent stages), and stores Tb as a pair of
-//    bf16 planes (hi + lo ~ fp32) in the context workspace.
-//  * delta_scan: one workgroup per (batch, head, V-tile of VT columns) walks the
-//    chunks in order with its K x VT state tile in registers, prefetching the
-//    next chunk (q, k, v tile, Tb) while computing the current one.  Per chunk:
-//    M = tril(Q K^T) and Y = K S0 (matrix cores), R = V - Y, Delta = Tb R,
-//    O = scale (Q S0 + M Delta), S += K^T Delta.  fp32 operands of the matrix
-//    cores are split into hi + lo bf16 terms.
-//  Arrays that must be stored transposed in LDS (K^T for the state update) are
-//  loaded with lanes running along time, so the transposed 2-byte LDS writes of
-//  a wave land in consecutive halfwords (no bank conflicts).
+//  * delta_prep, one workgroup per (batch, head, chunk), all in parallel:
+//    A and tril(Q K^T) on the matrix cores (bf16 inputs enter exactly); the
+//    16x16 diagonal blocks of (I + A)^{-1} by forward substitution; the
+//    off-diagonal blocks column block by column block, each in one wave with
+//    no barrier, on 16x16x16 matrix-core products whose 16x16 result is laid
+//    out exactly as the next product's right operand.  Tb and MTb go to the
+//    context workspace as hi/lo bf16 planes (hi + lo ~ fp32).
+//  * delta_scan, one workgroup per (batch, head, 16-wide V-tile), walks the
+//    chunks in order with its K x 16 state in registers.  q, k, Tb and MTb of
+//    the next chunk are prefetched straight into matrix-core operand
+//    registers (no LDS round trip).  K also goes to LDS row-major once; the
+//    state update reads K^T operands from it with the transposing LDS read
+//    (ds_read_b64_tr_b16).  Per chunk: Y = K S0 and Q S0, R = V - Y,
+//    Delta = Tb R and MTb R, S += K^T Delta.  fp32 operands are split into
+//    hi + lo bf16 terms.
 #include "lrs_internal.h"
 #include "mfma_util.h"
 
@@ -41,6 +41,12 @@ namespace {
 
 constexpr int L = 64;
 constexpr int NT = 256;
+constexpr int PLANE = L * L;   // elements of one 64 x 64 bf16 plane
+constexpr int NPLANES = 4;     // per chunk: Tb hi, Tb lo, MTb hi, MTb lo
+constexpr int VT = 16;         // V-tile width of the scan kernel
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct DeltaArgs {
     const u16* q;
@@ -50,7 +56,7 @@ struct DeltaArgs {
     const float* s0;
     float* o;
     float* s_final;
-    u16* tb;          // workspace: per (b,h,chunk) two 64x64 bf16 planes (hi, lo)
+    u16* ws;          // per (b,h,chunk): NPLANES planes of 64 x 64 bf16
     int B, T, H, K, V;
     float scale;
     int vtiles;
@@ -62,72 +68,149 @@ __device__ __forceinline__ void tri_block(int n, int& i, int& j) {
     j = n - (i * (i + 1)) / 2;
 }
 
-// 8-byte LDS write of 4 bf16.
+// MTb output blocks (i, j) handled by each wave, five 16x16 block products per
+// wave: {(3,0),(0,0)}, {(2,0),(1,0)}, {(3,1),(2,1)}, {(3,2),(1,1),(2,2),(3,3)}.
+__device__ __forceinline__ void mtb_job(int wave, int q, int& i, int& j) {
+    i = -1;
+    j = -1;
+    switch (wave * 4 + q) {
+        case 0: i = 3; j = 0; break;
+        case 1: i = 0; j = 0; break;
+        case 4: i = 2; j = 0; break;
+        case 5: i = 1; j = 0; break;
+        case 8: i = 3; j = 1; break;
+        case 9: i = 2; j = 1; break;
+        case 12: i = 3; j = 2; break;
+        case 13: i = 1; j = 1; break;
+        case 14: i = 2; j = 2; break;
+        case 15: i = 3; j = 3; break;
+        default: break;
+    }
+}
+
 __device__ __forceinline__ void store4(u16* dst, u16 a, u16 b, u16 c, u16 d) {
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     u32x2 w = {a | (static_cast<uint32_t>(b) << 16), c | (static_cast<uint32_t>(d) << 16)};
     *reinterpret_cast<u32x2*>(dst) = w;
 }
 
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        u16 hh, ll;
+        split_bf16(x[e], hh, ll);
+        hi[e] = static_cast<short>(hh);
+        lo[e] = static_cast<short>(ll);
+    }
+}
+
+// acc += X * Y for 16 x 16 fp32 blocks with ~fp32 accuracy.  `xa` is X as the
+// left operand of v_mfma_f32_16x16x16_bf16 (lane: row lane%16, k = 4(lane/16)+e)
+// and `yb` is Y as the right operand (lane: column lane%16, same k) -- which is
+// also how a 16x16 result is laid out, so results chain without a shuffle.
+__device__ __forceinline__ f32x4 mm16(f32x4 xa, f32x4 yb, f32x4 acc) {
+    s16x4 ah, al, bh, bl;
+    split4(xa, ah, al);
+    split4(yb, bh, bl);
+    acc = mfma16k16(al, bh, acc);
+    acc = mfma16k16(ah, bl, acc);
+    return mfma16k16(ah, bh, acc);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+
+// 8 consecutive bf16 (columns c0..c0+7 of a row of n columns); zero past the
+// row count or past n.  Vector path: one buffer load at `off_bytes` within a
+// per-batch-row resource.  Scalar path: from `rowptr`.
+template <bool VEC>
+__device__ __forceinline__ u32x4 load_piece(BufRes r, const u16* rowptr, int off_bytes, int c0, int n,
+                                            bool row_ok) {
+    if constexpr (VEC) {
+        return buf_load16(r, c0 < n ? off_bytes : kBufOOB);
+    } else {
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (row_ok) x = load8_bf16(rowptr, c0, n, false);
+        return x;
+    }
+}
+
 // ---------------------------------------------------------------------------
-// prep: Tb = (I + strict_lower(diag(beta) K K^T))^{-1} diag(beta) per chunk
+// prep: Tb = (I + strict_lower(diag(beta) K K^T))^{-1} diag(beta), MTb = tril(Q K^T) Tb
 // ---------------------------------------------------------------------------
 template <int KP, bool VEC>
 __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     constexpr int LDK = KP + 8;
-    constexpr int LDA = L + 1;   // fp32 rows, odd stride
-    __shared__ __align__(16) u16 sK[L * LDK];
-    __shared__ float sA[L * LDA];
-    __shared__ float sT[L * LDA];
-    __shared__ float sY[16 * L];
+    constexpr int LDA = L + 4;                     // fp32 rows of 272 bytes
+    constexpr int QK_BYTES = 2 * L * LDK * 2;      // sQ, sK (bf16)
+    constexpr int AT_BYTES = 2 * L * LDA * 4;      // sA, sT (fp32) reuse the same space
+    constexpr int U_BYTES = QK_BYTES > AT_BYTES ? QK_BYTES : AT_BYTES;
+    __shared__ __align__(16) unsigned char sU[U_BYTES];
+    __shared__ __align__(16) float sM[L * LDA];
     __shared__ float sBeta[L];
+    u16* sQ = reinterpret_cast<u16*>(sU);
+    u16* sK = sQ + L * LDK;
+    float* sA = reinterpret_cast<float*>(sU);
+    float* sT = sA + L * LDA;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
     const int c = blockIdx.x % p.nchunks;
     const int bh = blockIdx.x / p.nchunks;
     const int b = bh / p.H, h = bh - b * p.H;
     const int64_t T = p.T, t0 = static_cast<int64_t>(c) * L;
-    const int K = p.K;
+    const int K = p.K, H = p.H;
 
-    const BufRes rk = make_rsrc(p.k + b * T * p.H * static_cast<int64_t>(K), T * p.H * static_cast<int64_t>(K) * 2);
+    const int64_t row_elems = static_cast<int64_t>(H) * K;
+    const BufRes rq = make_rsrc(p.q + b * T * row_elems, T * row_elems * 2);
+    const BufRes rk = make_rsrc(p.k + b * T * row_elems, T * row_elems * 2);
     for (int pi = tid; pi < L * KP / 8; pi += NT) {
         const int row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
         const int64_t t = t0 + row;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if constexpr (VEC) {
-            x = buf_load16(rk, c8 < K ? ((static_cast<int>(t) * p.H + h) * K + c8) * 2 : kBufOOB);
-        } else {
-            if (t < T) x = load8_bf16(p.k + ((b * T + t) * p.H + h) * static_cast<int64_t>(K), c8, K, false);
-        }
-        *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = x;
+        const int off = ((static_cast<int>(t) * H + h) * K + c8) * 2;
+        const int64_t goff = ((b * T + t) * H + h) * static_cast<int64_t>(K);
+        *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = load_piece<VEC>(rq, p.q + goff, off, c8, K, t < T);
+        *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = load_piece<VEC>(rk, p.k + goff, off, c8, K, t < T);
     }
-    if (tid < L) sBeta[tid] = (t0 + tid < T) ? p.beta[(b * T + t0 + tid) * p.H + h] : 0.0f;
-    for (int e = tid; e < L * LDA; e += NT) {
-        sA[e] = 0.0f;
-        sT[e] = 0.0f;
-    }
+    if (tid < L) sBeta[tid] = (t0 + tid < T) ? p.beta[(b * T + t0 + tid) * H + h] : 0.0f;
     __syncthreads();
 
-    // A = strict_lower(diag(beta) K K^T): keys are bf16, products exact in fp32
-    for (int n = wave; n < 10; n += 4) {
+    // A = K K^T and M = Q K^T lower-triangle blocks (20 jobs over 4 waves), kept in registers
+    f32x4 acc[5];
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int n = wave + 4 * m;
         int bi, bj;
-        tri_block(n, bi, bj);
-        f32x4 acc = zero4();
+        tri_block(n % 10, bi, bj);
+        const u16* left = n < 10 ? sK : sQ;
+        f32x4 a = zero4();
 #pragma unroll
         for (int k0 = 0; k0 < KP; k0 += 32)
-            acc = mfma16(frag<LDK>(sK, 16 * bi, k0, lane), frag<LDK>(sK, 16 * bj, k0, lane), acc);
-        const int tau = 16 * bj + (lane & 15);
+            a = mfma16(frag<LDK>(left, 16 * bi, k0, lane), frag<LDK>(sK, 16 * bj, k0, lane), a);
+        acc[m] = a;
+    }
+    __syncthreads();   // sQ / sK are overwritten by sA / sT below
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int n = wave + 4 * m;
+        int bi, bj;
+        tri_block(n % 10, bi, bj);
+        const int tau = 16 * bj + c16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 16 * bi + 4 * (lane >> 4) + r;
-            if (tau < t) sA[t * LDA + tau] = sBeta[t] * acc[r];
+            const int t = 16 * bi + 4 * g + r;
+            if (n < 10) sA[t * LDA + tau] = tau < t ? sBeta[t] * acc[m][r] : 0.0f;
+            else sM[t * LDA + tau] = tau <= t ? acc[m][r] : 0.0f;
         }
     }
     __syncthreads();
 
-    // diagonal 16x16 blocks of (I + A)^{-1}: forward substitution, one lane per column
-    if (tid < L) {
-        const int bk = tid / 16, col = tid % 16;
+    // diagonal 16x16 blocks of T = (I + A)^{-1}: one lane per column
+    if (wave == 0) {
+        const int bk = lane / 16, col = lane % 16;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -141,42 +224,65 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     }
     __syncthreads();
 
-    // off-diagonal blocks, block row by block row:
-    //   T[i][col] = T_ii * ( - sum_{m=j..i-1} A_im T_m[col] ),  col in block j < i
-    for (int bi = 1; bi < 4; ++bi) {
-        const int col = tid % L, qr = tid / L;   // qr: which 4 rows of the block
-        const bool act = col < 16 * bi;
-        if (act) {
-            const int bj = col / 16;
+    // off-diagonal blocks of T: column block j = wave, block rows i = j+1..3,
+    //   T_ij = -T_ii * sum_{m=j}^{i-1} A_im T_mj
+    // A wave's LDS writes are visible to its own later LDS reads, so a column
+    // block needs no barrier.
+    if (wave < 3) {
+        const int j = wave;
+        for (int i = j + 1; i < 4; ++i) {
+            f32x4 X = zero4();
+            for (int m = j; m < i; ++m) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(sA + (16 * i + c16) * LDA + 16 * m + 4 * g);
+                f32x4 bcol;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = 4 * qr + rr;
-                float y = 0.0f;
-                for (int m = 16 * bj; m < 16 * bi; ++m) y -= sA[(16 * bi + r) * LDA + m] * sT[m * LDA + col];
-                sY[r * L + col] = y;
+                for (int r = 0; r < 4; ++r) bcol[r] = sT[(16 * m + 4 * g + r) * LDA + 16 * j + c16];
+                X = mm16(a, bcol, X);
             }
-        }
-        __syncthreads();
-        if (act) {
+            const f32x4 tii = *reinterpret_cast<const f32x4*>(sT + (16 * i + c16) * LDA + 16 * i + 4 * g);
+            const f32x4 Y = mm16(tii, X, zero4());
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int r = 4 * qr + rr;
-                float x = 0.0f;
-#pragma unroll
-                for (int s2 = 0; s2 < 16; ++s2) x += sT[(16 * bi + r) * LDA + 16 * bi + s2] * sY[s2 * L + col];
-                sT[(16 * bi + r) * LDA + col] = x;
-            }
+            for (int r = 0; r < 4; ++r) sT[(16 * i + 4 * g + r) * LDA + 16 * j + c16] = -Y[r];
         }
-        __syncthreads();
     }
+    __syncthreads();
 
-    // Tb = T diag(beta) as hi/lo bf16 planes, row-major 64 x 64
-    u16* dst = p.tb + static_cast<int64_t>(blockIdx.x) * 2 * L * L;
+    u16* planes = p.ws + static_cast<int64_t>(blockIdx.x) * NPLANES * PLANE;
+    // MTb lower blocks (i, j): (sum_{m=j}^{i} M_im T_mj) diag(beta); five block
+    // products per wave
+    {
+        for (int qj = 0; qj < 4; ++qj) {
+            int bi, bj;
+            mtb_job(wave, qj, bi, bj);
+            if (bi < 0) continue;
+            f32x4 X = zero4();
+            for (int m = bj; m <= bi; ++m) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(sM + (16 * bi + c16) * LDA + 16 * m + 4 * g);
+                f32x4 bcol;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bcol[r] = sT[(16 * m + 4 * g + r) * LDA + 16 * bj + c16];
+                X = mm16(a, bcol, X);
+            }
+            const float beta_col = sBeta[16 * bj + c16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u16 hi, lo;
+                split_bf16(X[r] * beta_col, hi, lo);
+                const int idx = (16 * bi + 4 * g + r) * L + 16 * bj + c16;
+                planes[2 * PLANE + idx] = hi;
+                planes[3 * PLANE + idx] = lo;
+            }
+        }
+    }
+    // Tb = T diag(beta) (zero above the diagonal) and zeros for the upper blocks of MTb
     {
         const int row = tid / 4, c0 = (tid % 4) * 16;
         u16 hi[16], lo[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) split_bf16(sT[row * LDA + c0 + e] * sBeta[c0 + e], hi[e], lo[e]);
+        for (int e = 0; e < 16; ++e) {
+            const int col = c0 + e;
+            split_bf16(col <= row ? sT[row * LDA + col] * sBeta[col] : 0.0f, hi[e], lo[e]);
+        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             u32x4 wh, wl;
@@ -188,45 +294,42 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             wl.y = lo[8 * half + 2] | (static_cast<uint32_t>(lo[8 * half + 3]) << 16);
             wl.z = lo[8 * half + 4] | (static_cast<uint32_t>(lo[8 * half + 5]) << 16);
             wl.w = lo[8 * half + 6] | (static_cast<uint32_t>(lo[8 * half + 7]) << 16);
-            *reinterpret_cast<u32x4*>(dst + row * L + c0 + 8 * half) = wh;
-            *reinterpret_cast<u32x4*>(dst + L * L + row * L + c0 + 8 * half) = wl;
+            *reinterpret_cast<u32x4*>(planes + row * L + c0 + 8 * half) = wh;
+            *reinterpret_cast<u32x4*>(planes + PLANE + row * L + c0 + 8 * half) = wl;
+        }
+        if (c0 >= 16 * (row / 16 + 1)) {   // a 16-column group right of the diagonal block
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(planes + 2 * PLANE + row * L + c0) = z;
+            *reinterpret_cast<u32x4*>(planes + 2 * PLANE + row * L + c0 + 8) = z;
+            *reinterpret_cast<u32x4*>(planes + 3 * PLANE + row * L + c0) = z;
+            *reinterpret_cast<u32x4*>(planes + 3 * PLANE + row * L + c0 + 8) = z;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// scan: sequential over chunks per (batch, head, V-tile)
+// scan: sequential over chunks per (batch, head, 16-wide V-tile)
 // ---------------------------------------------------------------------------
-template <int KP, int VT, bool VEC>
+template <int KP, bool VEC>
 __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     constexpr int LDK = KP + 8;
     constexpr int LDL = L + 8;
     constexpr int LDV = VT + 8;
-    constexpr int KT = KP / 16;
-    constexpr int VTT = VT / 16;
-    constexpr int S_PER_WAVE = KT * VTT / 4;
-    constexpr int PQ = L * KP / 8 / NT;        // q/k pieces per thread
-    constexpr int NVP = L * VT / 8;            // v pieces per chunk
-    constexpr int PVT = (NVP + NT - 1) / NT;   // v pieces per thread
-    constexpr int PT = 2 * L * L / 8 / NT;     // Tb pieces per thread (hi + lo)
-    static_assert(PQ >= 1 && S_PER_WAVE >= 1, "tile shape");
+    constexpr int KS = KP / 32;          // k-steps over the key dimension
+    constexpr int STW = KP / 16 / 4;     // state row tiles per wave
+    static_assert(STW >= 1, "state tiles");
 
-    __shared__ __align__(16) u16 sQ[L * LDK];
-    __shared__ __align__(16) u16 sK[L * LDK];
-    __shared__ __align__(16) u16 sKT[KP * LDL];
-    __shared__ __align__(16) u16 sTh[L * LDL];
-    __shared__ __align__(16) u16 sTl[L * LDL];
-    __shared__ __align__(16) u16 sMh[L * LDL];
-    __shared__ __align__(16) u16 sMl[L * LDL];
-    __shared__ __align__(16) u16 sV[L * LDV];
-    __shared__ __align__(16) u16 sRTh[VT * LDL];
+    __shared__ __align__(16) u16 sK[L * LDK];        // K of the chunk, row-major
+    __shared__ __align__(16) u16 sV[L * LDV];        // V tile, row-major
+    __shared__ __align__(16) u16 sRTh[VT * LDL];     // R^T hi/lo
     __shared__ __align__(16) u16 sRTl[VT * LDL];
-    __shared__ __align__(16) u16 sDTh[VT * LDL];
+    __shared__ __align__(16) u16 sDTh[VT * LDL];     // Delta^T hi/lo
     __shared__ __align__(16) u16 sDTl[VT * LDL];
-    __shared__ __align__(16) u16 sSTh[VT * LDK];
-    __shared__ __align__(16) u16 sSTl[VT * LDK];
+    __shared__ __align__(16) u16 sSh[VT * LDK];      // S^T hi/lo entering the chunk
+    __shared__ __align__(16) u16 sSl[VT * LDK];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int vt = lid % p.vtiles;
     const int bh = lid / p.vtiles;
@@ -235,276 +338,212 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     const int64_t T = p.T;
     const int K = p.K, V = p.V, H = p.H;
     const int nchunks = p.nchunks;
-    const u16* tbase = p.tb + static_cast<int64_t>(bh) * nchunks * 2 * L * L;
 
-    // q/k pieces: row = pi % 64 (lanes along time), columns c8 = 8 * (pi / 64).
-    // Vector path: per-batch-row buffer resources; rows past T and columns past
-    // K / V read as zero in hardware, so the prefetch is a straight run of loads.
     const int64_t qk_row = static_cast<int64_t>(H) * K, v_row = static_cast<int64_t>(H) * V;
     const BufRes rq = make_rsrc(p.q + b * T * qk_row, T * qk_row * 2);
     const BufRes rk = make_rsrc(p.k + b * T * qk_row, T * qk_row * 2);
     const BufRes rv = make_rsrc(p.v + b * T * v_row, T * v_row * 2);
-    const BufRes rt = make_rsrc(tbase, static_cast<int64_t>(nchunks) * 2 * L * L * 2);
-    u32x4 cq[PQ], ck[PQ], nq[PQ], nk[PQ], cv[PVT], nv[PVT], ct[PT], nt[PT];
-    auto load_chunk = [&](int c, u32x4 (&Q)[PQ], u32x4 (&Kx)[PQ], u32x4 (&Vx)[PVT], u32x4 (&Tx)[PT]) {
-        const int64_t t0 = static_cast<int64_t>(c) * L;
-        if constexpr (VEC) {
+    const u16* wsb = p.ws + static_cast<int64_t>(bh) * nchunks * NPLANES * PLANE;
+    const BufRes rw = make_rsrc(wsb, static_cast<int64_t>(nchunks) * NPLANES * PLANE * 2);
+
+    // operand rows of this wave: t = 16 * wave + c16; columns 32 ks + 8 g
+    const int arow = 16 * wave + c16;
+    u32x4 qf[KS], kf[KS], tf[2][2], mf[2][2], vf;
+    u32x4 nqf[KS], nkf[KS], ntf[2][2], nmf[2][2], nvf;
+    auto load_chunk = [&](int c, u32x4 (&Q)[KS], u32x4 (&Kx)[KS], u32x4 (&Tb)[2][2], u32x4 (&Mb)[2][2],
+                          u32x4& Vx) {
+        const int64_t t = static_cast<int64_t>(c) * L + arow;
+        const int64_t goff = ((b * T + t) * H + h) * static_cast<int64_t>(K);
 #pragma unroll
-            for (int i = 0; i < PQ; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi % L, c8 = (pi / L) * 8;
-                const int t = static_cast<int>(t0) + row;
-                const int off = c8 < K ? ((t * H + h) * K + c8) * 2 : kBufOOB;
-                Q[i] = buf_load16(rq, off);
-                Kx[i] = buf_load16(rk, off);
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c8 = 32 * ks + 8 * g;
+            const int off = ((static_cast<int>(t) * H + h) * K + c8) * 2;
+            Q[ks] = load_piece<VEC>(rq, p.q + goff, off, c8, K, t < T);
+            Kx[ks] = load_piece<VEC>(rk, p.k + goff, off, c8, K, t < T);
+        }
+        const int pbase = c * NPLANES * PLANE;
 #pragma unroll
-            for (int i = 0; i < PVT; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi % L, c8 = (pi / L) * 8;
-                const int t = static_cast<int>(t0) + row;
-                const int off = (pi < NVP && v0 + c8 < V) ? ((t * H + h) * V + v0 + c8) * 2 : kBufOOB;
-                Vx[i] = buf_load16(rv, off);
-            }
-        } else {
+        for (int ks = 0; ks < 2; ++ks) {
+            const int e = arow * L + 32 * ks + 8 * g;
 #pragma unroll
-            for (int i = 0; i < PQ; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi % L, c8 = (pi / L) * 8;
-                const int64_t t = t0 + row;
-                Q[i] = u32x4{0u, 0u, 0u, 0u};
-                Kx[i] = u32x4{0u, 0u, 0u, 0u};
-                if (t < T) {
-                    const int64_t off = ((b * T + t) * H + h) * static_cast<int64_t>(K);
-                    Q[i] = load8_bf16(p.q + off, c8, K, false);
-                    Kx[i] = load8_bf16(p.k + off, c8, K, false);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < PVT; ++i) {
-                const int pi = tid + NT * i;
-                Vx[i] = u32x4{0u, 0u, 0u, 0u};
-                if (pi < NVP) {
-                    const int row = pi % L, c8 = (pi / L) * 8;
-                    const int64_t t = t0 + row;
-                    if (t < T)
-                        Vx[i] = load8_bf16(p.v + ((b * T + t) * H + h) * static_cast<int64_t>(V) + v0, c8,
-                                           V - v0, false);
-                }
+            for (int pl = 0; pl < 2; ++pl) {
+                Tb[ks][pl] = buf_load16(rw, (pbase + pl * PLANE + e) * 2);
+                Mb[ks][pl] = buf_load16(rw, (pbase + (2 + pl) * PLANE + e) * 2);
             }
         }
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int pi = tid + NT * i;   // hi plane pieces 0..511, lo plane 512..1023
-            Tx[i] = buf_load16(rt, (c * 2 * L * L + 8 * pi) * 2);
+        Vx = u32x4{0u, 0u, 0u, 0u};
+        if (tid < L * VT / 8) {
+            const int vr = tid / (VT / 8), c8 = (tid % (VT / 8)) * 8;
+            const int64_t tv = static_cast<int64_t>(c) * L + vr;
+            const int off = ((static_cast<int>(tv) * H + h) * V + v0 + c8) * 2;
+            Vx = load_piece<VEC>(rv, p.v + ((b * T + tv) * H + h) * static_cast<int64_t>(V) + v0, off, c8,
+                                 V - v0, tv < T);
         }
     };
 
-    // state tile from s0
-    f32x4 S[S_PER_WAVE];
+    // state: wave owns row tiles sr = STW * wave + st (keys 16 sr .. 16 sr + 15)
+    f32x4 S[STW];
 #pragma unroll
-    for (int m = 0; m < S_PER_WAVE; ++m) {
-        const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-        const int j = v0 + 16 * sc + (lane & 15);
+    for (int st = 0; st < STW; ++st) {
+        const int sr = STW * wave + st;
+        const int j = v0 + c16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int d = 16 * sr + 4 * (lane >> 4) + r;
+            const int d = 16 * sr + 4 * g + r;
             float x = 0.0f;
             if (p.s0 && d < K && j < V) x = p.s0[((static_cast<int64_t>(b) * H + h) * K + d) * V + j];
-            S[m][r] = x;
+            S[st][r] = x;
         }
     }
     auto write_state_lds = [&]() {
 #pragma unroll
-        for (int m = 0; m < S_PER_WAVE; ++m) {
-            const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-            const int j = 16 * sc + (lane & 15);
-            const int d = 16 * sr + 4 * (lane >> 4);
+        for (int st = 0; st < STW; ++st) {
+            const int d = 16 * (STW * wave + st) + 4 * g;
             u16 hi[4], lo[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) split_bf16(S[m][r], hi[r], lo[r]);
-            store4(sSTh + j * LDK + d, hi[0], hi[1], hi[2], hi[3]);
-            store4(sSTl + j * LDK + d, lo[0], lo[1], lo[2], lo[3]);
+            for (int r = 0; r < 4; ++r) split_bf16(S[st][r], hi[r], lo[r]);
+            store4(sSh + c16 * LDK + d, hi[0], hi[1], hi[2], hi[3]);
+            store4(sSl + c16 * LDK + d, lo[0], lo[1], lo[2], lo[3]);
         }
     };
     write_state_lds();
-    // blocks of M above the diagonal are never written and must read as zero
-    for (int e = tid; e < L * LDL; e += NT) {
-        sMh[e] = 0;
-        sMl[e] = 0;
-    }
-    load_chunk(0, cq, ck, cv, ct);
+    load_chunk(0, qf, kf, tf, mf, vf);
 
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
-        // ---- P0: chunk inputs into LDS ----
+        // ---- P0: K (row-major) and the V tile into LDS ----
 #pragma unroll
-        for (int i = 0; i < PQ; ++i) {
-            const int pi = tid + NT * i;
-            const int row = pi % L, c8 = (pi / L) * 8;
-            *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = cq[i];
-            *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = ck[i];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sKT[(c8 + e) * LDL + row] = piece_elem(ck[i], e);
-        }
-#pragma unroll
-        for (int i = 0; i < PVT; ++i) {
-            const int pi = tid + NT * i;
-            if (pi < NVP) {
-                const int row = pi % L, c8 = (pi / L) * 8;
-                *reinterpret_cast<u32x4*>(sV + row * LDV + c8) = cv[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < PT; ++i) {
-            const int pi = tid + NT * i;
-            const int plane = pi / (L * L / 8), pp = pi % (L * L / 8);
-            const int row = pp / (L / 8), c8 = (pp % (L / 8)) * 8;
-            *reinterpret_cast<u32x4*>((plane ? sTl : sTh) + row * LDL + c8) = ct[i];
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<u32x4*>(sK + arow * LDK + 32 * ks + 8 * g) = kf[ks];
+        if (tid < L * VT / 8)
+            *reinterpret_cast<u32x4*>(sV + (tid / (VT / 8)) * LDV + (tid % (VT / 8)) * 8) = vf;
         __syncthreads();
-        if (c + 1 < nchunks) load_chunk(c + 1, nq, nk, nv, nt);
+        if (c + 1 < nchunks) load_chunk(c + 1, nqf, nkf, ntf, nmf, nvf);
 
-        // ---- P1: M = tril(Q K^T) (exact), Y = K S0 -> R = V - Y, O1 = Q S0 ----
-        for (int n = wave; n < 10; n += 4) {
-            int bi, bj;
-            tri_block(n, bi, bj);
-            f32x4 acc = zero4();
+        // ---- P1: Y = K S0, O1 = Q S0 (row block = wave), R = V - Y ----
+        f32x4 y = zero4(), o1 = zero4();
 #pragma unroll
-            for (int k0 = 0; k0 < KP; k0 += 32)
-                acc = mfma16(frag<LDK>(sQ, 16 * bi, k0, lane), frag<LDK>(sK, 16 * bj, k0, lane), acc);
-            const int tau = 16 * bj + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * bi + 4 * (lane >> 4) + r;
-                u16 hi, lo;
-                split_bf16(tau <= t ? acc[r] : 0.0f, hi, lo);
-                sMh[t * LDL + tau] = hi;
-                sMl[t * LDL + tau] = lo;
-            }
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 sh = frag<LDK>(sSh, 0, 32 * ks, lane);
+            const bf16x8 sl = frag<LDK>(sSl, 0, 32 * ks, lane);
+            const bf16x8 ka = as_bf16x8(kf[ks]);
+            const bf16x8 qa = as_bf16x8(qf[ks]);
+            y = mfma16(ka, sl, y);
+            y = mfma16(ka, sh, y);
+            o1 = mfma16(qa, sl, o1);
+            o1 = mfma16(qa, sh, o1);
         }
-        const int ri = wave;
-        f32x4 O1[VTT];
-#pragma unroll
-        for (int cj = 0; cj < VTT; ++cj) {
-            f32x4 y = zero4(), o1 = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < KP; k0 += 32) {
-                const bf16x8 sh = frag<LDK>(sSTh, 16 * cj, k0, lane);
-                const bf16x8 sl = frag<LDK>(sSTl, 16 * cj, k0, lane);
-                const bf16x8 ka = frag<LDK>(sK, 16 * ri, k0, lane);
-                const bf16x8 qa = frag<LDK>(sQ, 16 * ri, k0, lane);
-                y = mfma16(ka, sl, y);
-                y = mfma16(ka, sh, y);
-                o1 = mfma16(qa, sl, o1);
-                o1 = mfma16(qa, sh, o1);
-            }
-            O1[cj] = o1;
-            const int j = 16 * cj + (lane & 15);
-            const int t = 16 * ri + 4 * (lane >> 4);
+        {
+            const int t = 16 * wave + 4 * g;
             u16 hi[4], lo[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) split_bf16(bf2f(sV[(t + r) * LDV + j]) - y[r], hi[r], lo[r]);
-            store4(sRTh + j * LDL + t, hi[0], hi[1], hi[2], hi[3]);
-            store4(sRTl + j * LDL + t, lo[0], lo[1], lo[2], lo[3]);
+            for (int r = 0; r < 4; ++r) split_bf16(bf2f(sV[(t + r) * LDV + c16]) - y[r], hi[r], lo[r]);
+            store4(sRTh + c16 * LDL + t, hi[0], hi[1], hi[2], hi[3]);
+            store4(sRTl + c16 * LDL + t, lo[0], lo[1], lo[2], lo[3]);
         }
         __syncthreads();
 
-        // ---- P2: Delta = Tb R (row block = wave) ----
+        // ---- P2: Delta = Tb R, O = scale (O1 + MTb R) ----
+        f32x4 dl = zero4(), o2 = zero4();
 #pragma unroll
-        for (int cj = 0; cj < VTT; ++cj) {
-            f32x4 dl = zero4();
-            for (int ks = 0; ks <= ri / 2; ++ks) {
-                const bf16x8 th = frag<LDL>(sTh, 16 * ri, 32 * ks, lane);
-                const bf16x8 tl = frag<LDL>(sTl, 16 * ri, 32 * ks, lane);
-                const bf16x8 rh = frag<LDL>(sRTh, 16 * cj, 32 * ks, lane);
-                const bf16x8 rl = frag<LDL>(sRTl, 16 * cj, 32 * ks, lane);
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks <= wave / 2) {   // Tb and MTb are lower triangular
+                const bf16x8 rh = frag<LDL>(sRTh, 0, 32 * ks, lane);
+                const bf16x8 rl = frag<LDL>(sRTl, 0, 32 * ks, lane);
+                const bf16x8 th = as_bf16x8(tf[ks][0]), tl = as_bf16x8(tf[ks][1]);
+                const bf16x8 mh = as_bf16x8(mf[ks][0]), ml = as_bf16x8(mf[ks][1]);
                 dl = mfma16(tl, rh, dl);
                 dl = mfma16(th, rl, dl);
                 dl = mfma16(th, rh, dl);
+                o2 = mfma16(ml, rh, o2);
+                o2 = mfma16(mh, rl, o2);
+                o2 = mfma16(mh, rh, o2);
             }
-            const int j = 16 * cj + (lane & 15);
-            const int t = 16 * ri + 4 * (lane >> 4);
+        }
+        {
+            const int t = 16 * wave + 4 * g;
+            const int j = v0 + c16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (t0 + t + r < T && j < V)
+                    p.o[((b * T + t0 + t + r) * H + h) * static_cast<int64_t>(V) + j] = p.scale * (o1[r] + o2[r]);
             u16 hi[4], lo[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) split_bf16(dl[r], hi[r], lo[r]);
-            store4(sDTh + j * LDL + t, hi[0], hi[1], hi[2], hi[3]);
-            store4(sDTl + j * LDL + t, lo[0], lo[1], lo[2], lo[3]);
+            store4(sDTh + c16 * LDL + t, hi[0], hi[1], hi[2], hi[3]);
+            store4(sDTl + c16 * LDL + t, lo[0], lo[1], lo[2], lo[3]);
         }
         __syncthreads();
 
-        // ---- P3: O = scale (O1 + M Delta); S += K^T Delta ----
+        // ---- P3: S += K^T Delta (K^T operands by transposing LDS reads) ----
+        {
+            const int i16 = lane & 15;
 #pragma unroll
-        for (int cj = 0; cj < VTT; ++cj) {
-            f32x4 o2 = zero4();
-            for (int ks = 0; ks <= ri / 2; ++ks) {
-                const bf16x8 mh = frag<LDL>(sMh, 16 * ri, 32 * ks, lane);
-                const bf16x8 ml = frag<LDL>(sMl, 16 * ri, 32 * ks, lane);
-                const bf16x8 dh = frag<LDL>(sDTh, 16 * cj, 32 * ks, lane);
-                const bf16x8 dlo = frag<LDL>(sDTl, 16 * cj, 32 * ks, lane);
-                o2 = mfma16(ml, dh, o2);
-                o2 = mfma16(mh, dlo, o2);
-                o2 = mfma16(mh, dh, o2);
-            }
-            const int j = v0 + 16 * cj + (lane & 15);
+            for (int st = 0; st < STW; ++st) {
+                const int d0 = 16 * (STW * wave + st);
+                f32x4 ds = zero4();
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * ri + 4 * (lane >> 4) + r;
-                if (t0 + t < T && j < V)
-                    p.o[((b * T + t0 + t) * H + h) * static_cast<int64_t>(V) + j] = p.scale * (O1[cj][r] + o2[r]);
+                for (int ks = 0; ks < 2; ++ks) {
+                    // lane i of a 16-lane group supplies row tau0 + i/4, columns d0 + 4(i%4)..+3;
+                    // lane j then holds K[tau0 .. tau0+3][d0 + j]
+                    const int tau0 = 32 * ks + 8 * g + (i16 >> 2);
+                    const u16* a0 = sK + tau0 * LDK + d0 + 4 * (i16 & 3);
+                    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 4 * LDK));
+                    const bf16x8 ka =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                    ds = mfma16(ka, frag<LDL>(sDTl, 0, 32 * ks, lane), ds);
+                    ds = mfma16(ka, frag<LDL>(sDTh, 0, 32 * ks, lane), ds);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[st][r] += ds[r];
             }
         }
-#pragma unroll
-        for (int m = 0; m < S_PER_WAVE; ++m) {
-            const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-            f32x4 ds = zero4();
-#pragma unroll
-            for (int ks = 0; ks < L / 32; ++ks) {
-                const bf16x8 ka = frag<LDL>(sKT, 16 * sr, 32 * ks, lane);
-                ds = mfma16(ka, frag<LDL>(sDTl, 16 * sc, 32 * ks, lane), ds);
-                ds = mfma16(ka, frag<LDL>(sDTh, 16 * sc, 32 * ks, lane), ds);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[m][r] += ds[r];
-        }
-        __syncthreads();
         write_state_lds();
+        __syncthreads();   // sK, sV are rewritten by the next chunk; sS is read by it
 
         if (c + 1 < nchunks) {
 #pragma unroll
-            for (int i = 0; i < PQ; ++i) { cq[i] = nq[i]; ck[i] = nk[i]; }
+            for (int ks = 0; ks < KS; ++ks) {
+                qf[ks] = nqf[ks];
+                kf[ks] = nkf[ks];
+            }
 #pragma unroll
-            for (int i = 0; i < PVT; ++i) cv[i] = nv[i];
+            for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < PT; ++i) ct[i] = nt[i];
+                for (int pl = 0; pl < 2; ++pl) {
+                    tf[ks][pl] = ntf[ks][pl];
+                    mf[ks][pl] = nmf[ks][pl];
+                }
+            vf = nvf;
         }
     }
 
 #pragma unroll
-    for (int m = 0; m < S_PER_WAVE; ++m) {
-        const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-        const int j = v0 + 16 * sc + (lane & 15);
+    for (int st = 0; st < STW; ++st) {
+        const int sr = STW * wave + st;
+        const int j = v0 + c16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int d = 16 * sr + 4 * (lane >> 4) + r;
-            if (d < K && j < V) p.s_final[((static_cast<int64_t>(b) * H + h) * K + d) * V + j] = S[m][r];
+            const int d = 16 * sr + 4 * g + r;
+            if (d < K && j < V) p.s_final[((static_cast<int64_t>(b) * H + h) * K + d) * V + j] = S[st][r];
         }
     }
 }
 
-template <int KP, int VT>
+template <int KP>
 hipError_t launch_t(const DeltaArgs& a, bool vec, hipStream_t stream) {
     const int64_t gprep = static_cast<int64_t>(a.B) * a.H * a.nchunks;
     const int64_t gscan = static_cast<int64_t>(a.B) * a.H * a.vtiles;
     if (vec) {
         hipLaunchKernelGGL((delta_prep_kernel<KP, true>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
                            stream, a);
-        hipLaunchKernelGGL((delta_scan_kernel<KP, VT, true>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
+        hipLaunchKernelGGL((delta_scan_kernel<KP, true>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
                            stream, a);
     } else {
         hipLaunchKernelGGL((delta_prep_kernel<KP, false>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
                            stream, a);
-        hipLaunchKernelGGL((delta_scan_kernel<KP, VT, false>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
+        hipLaunchKernelGGL((delta_scan_kernel<KP, false>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
                            stream, a);
     }
     return hipGetLastError();
@@ -512,11 +551,11 @@ hipError_t launch_t(const DeltaArgs& a, bool vec, hipStream_t stream) {
 
 }  // namespace
 
-int delta_vtile() { return 16; }
+int delta_vtile() { return VT; }
 
 size_t delta_workspace_bytes(int B, int T, int H) {
     const int64_t nchunks = (static_cast<int64_t>(T) + L - 1) / L;
-    return static_cast<size_t>(B) * H * nchunks * 2 * L * L * sizeof(u16);
+    return static_cast<size_t>(B) * H * nchunks * NPLANES * PLANE * sizeof(u16);
 }
 
 hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_t stream) {
@@ -528,16 +567,16 @@ hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_
     a.s0 = prm.s0;
     a.o = prm.o;
     a.s_final = prm.s_final;
-    a.tb = static_cast<u16*>(workspace);
+    a.ws = static_cast<u16*>(workspace);
     a.B = prm.B;
     a.T = prm.T;
     a.H = prm.H;
     a.K = prm.K;
     a.V = prm.V;
     a.scale = prm.scale;
-    a.vtiles = (prm.V + delta_vtile() - 1) / delta_vtile();
+    a.vtiles = (prm.V + VT - 1) / VT;
     a.nchunks = (prm.T + L - 1) / L;
-    return prm.K <= 64 ? launch_t<64, 16>(a, prm.vec != 0, stream) : launch_t<128, 16>(a, prm.vec != 0, stream);
+    return prm.K <= 64 ? launch_t<64>(a, prm.vec != 0, stream) : launch_t<128>(a, prm.vec != 0, stream);
 }
 
 }  // namespace lrs

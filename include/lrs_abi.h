@@ -129,8 +129,16 @@ void lrs_context_destroy(LrsContext* ctx);
  *                               tile and obtains its carry-in from earlier
  *                               tiles by a decoupled look-back.
  * Both give results within the documented tolerance of each other.
+ *
+ * LRS_PARAM_DIAG_SEGMENTS sets how many segments lrs_scan_diag_outer splits
+ * the time axis into (each a run of 64-step chunks processed by its own
+ * workgroups; a first pass reduces every segment but the last to a decay
+ * product and a state contribution, kept in the context's workspace):
+ *   0 (default)  as many as fill the device's resident workgroup slots once;
+ *   n >= 1       n segments (capped at the number of chunks).
+ * Any value gives results within the documented tolerance.
  * Errors: LRS_E_INVAL for a NULL context, unknown parameter or value. */
-enum { LRS_PARAM_ELEM_SCHEDULE = 1 };
+enum { LRS_PARAM_ELEM_SCHEDULE = 1, LRS_PARAM_DIAG_SEGMENTS = 2 };
 enum {
     LRS_ELEM_SCHEDULE_AUTO = 0,
     LRS_ELEM_SCHEDULE_STREAM = 1,
@@ -188,7 +196,11 @@ lrs_status lrs_scan_gated(LrsContext* ctx, const float* a, const float* u, const
  *
  * g is a log-decay and is expected to be <= 0 (decay factors in (0,1]); any
  * finite value is accepted.  Limits: 1 <= K <= 128 (LRS_E_UNSUPPORTED above),
- * H % Hg == 0 (LRS_E_INVAL otherwise), decay_mode in {0,1}.
+ * H % Hg == 0 (LRS_E_INVAL otherwise), decay_mode in {0,1}.  With more than
+ * one time segment (LRS_PARAM_DIAG_SEGMENTS) the context keeps a workspace of
+ * (segments - 1) * B * H * (ceil(V/64)*64*KP + KP) * 4 bytes, KP = 64 for
+ * K <= 64 and 128 otherwise, grown on demand (LRS_E_NOMEM if that allocation
+ * fails); growing it waits for the stream of the call.
  */
 lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                                const lrs_bf16* v, const float* g, int32_t decay_mode,

@@ -25,6 +25,7 @@ LRS_OK, LRS_E_INVAL, LRS_E_NOMEM, LRS_E_IO, LRS_E_FORMAT, LRS_E_UNSUPPORTED, LRS
     0, -1, -2, -3, -4, -5, -6)
 LRS_CAP_SCAN_FMA, LRS_CAP_SCAN_GATED, LRS_CAP_SCAN_DIAG_OUTER, LRS_CAP_SCAN_DELTA = 1, 2, 4, 8
 LRS_PARAM_ELEM_SCHEDULE = 1
+LRS_PARAM_DIAG_SEGMENTS = 2
 LRS_ELEM_SCHEDULE_AUTO, LRS_ELEM_SCHEDULE_STREAM, LRS_ELEM_SCHEDULE_LOOKBACK = 0, 1, 2
 
 # Every symbol the header declares, with (restype, argtypes).

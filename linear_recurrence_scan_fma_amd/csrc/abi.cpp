@@ -29,6 +29,10 @@ struct LrsContext {
     // delta-rule scratch (per-chunk UT-transform planes), grown on demand
     void* delta_ws = nullptr;
     size_t delta_ws_bytes = 0;
+    // diag-outer segment pairs (decay products and state contributions), grown on demand
+    int diag_segments = 0;   // 0: automatic
+    void* diag_ws = nullptr;
+    size_t diag_ws_bytes = 0;
     hipStream_t last_stream = nullptr;
     bool used = false;
 };
@@ -246,6 +250,7 @@ LRS_API void lrs_context_destroy(LrsContext* ctx) {
         (void)hipDeviceSynchronize();
         if (ctx->words) (void)hipFree(ctx->words);
         if (ctx->delta_ws) (void)hipFree(ctx->delta_ws);
+        if (ctx->diag_ws) (void)hipFree(ctx->diag_ws);
         if (ctx->fixed) (void)hipFree(ctx->fixed);
     }
     delete ctx;
@@ -258,6 +263,11 @@ LRS_API lrs_status lrs_context_set_param(LrsContext* ctx, int32_t param, int32_t
             value != LRS_ELEM_SCHEDULE_LOOKBACK)
             return LRS_E_INVAL;
         ctx->elem_schedule = value;
+        return LRS_OK;
+    }
+    if (param == LRS_PARAM_DIAG_SEGMENTS) {
+        if (value < 0) return LRS_E_INVAL;
+        ctx->diag_segments = value;
         return LRS_OK;
     }
     return LRS_E_INVAL;
@@ -293,6 +303,30 @@ LRS_API lrs_status lrs_scan_gated(LrsContext* ctx, const float* a, const float* 
                                   int32_t T, int32_t N, void* stream) {
     return scan_elem(ctx, true, a, u, s0, s, s_final, B, T, N, stream);
 }
+
+namespace {
+
+// Grows a context-owned device buffer to `need` bytes.  A buffer in use by
+// earlier work on `stream` is released only after that work finishes.
+lrs_status grow_workspace(void*& ptr, size_t& cap, size_t need, hipStream_t stream) {
+    if (need <= cap) return LRS_OK;
+    if (ptr) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return LRS_E_DEVICE;
+        (void)hipFree(ptr);
+        ptr = nullptr;
+        cap = 0;
+    }
+    void* fresh = nullptr;
+    if (hipMalloc(&fresh, need) != hipSuccess) {
+        (void)hipGetLastError();
+        return LRS_E_NOMEM;
+    }
+    ptr = fresh;
+    cap = need;
+    return LRS_OK;
+}
+
+}  // namespace
 
 LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                                        const lrs_bf16* v, const float* g, int32_t decay_mode,
@@ -341,12 +375,16 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
     // the vector path addresses one batch row of each tensor with 32-bit buffer offsets
     const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
-             aligned(g, 16) && row_bytes < (int64_t{1} << 31)) ? 1 : 0;
-    const int64_t grid = static_cast<int64_t>(B) * H * ((V + lrs::diag_outer_vtile(decay_mode) - 1) /
-                                                         lrs::diag_outer_vtile(decay_mode));
+             aligned(g, 16) && aligned(o, 16) && row_bytes < (int64_t{1} << 31)) ? 1 : 0;
+    const lrs::DiagPlan plan =
+        lrs::diag_outer_plan(B, T, H, V, K, decay_mode, p.vec != 0, ctx->num_cus, ctx->diag_segments);
+    const int64_t grid = static_cast<int64_t>(B) * H * plan.vtiles * plan.nseg;
     if (grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (lrs::launch_scan_diag_outer(p, st) != hipSuccess) return LRS_E_DEVICE;
+    const lrs_status ws = grow_workspace(ctx->diag_ws, ctx->diag_ws_bytes,
+                                         lrs::diag_outer_workspace_bytes(B, H, K, V, plan.nseg), st);
+    if (ws != LRS_OK) return ws;
+    if (lrs::launch_scan_diag_outer(p, plan, ctx->diag_ws, st) != hipSuccess) return LRS_E_DEVICE;
     ctx->last_stream = st;
     ctx->used = true;
     return LRS_OK;
@@ -384,22 +422,8 @@ LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_
     hipStream_t st = static_cast<hipStream_t>(stream);
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return LRS_E_DEVICE;
-    const size_t need = lrs::delta_workspace_bytes(B, T, H);
-    if (need > ctx->delta_ws_bytes) {
-        if (ctx->delta_ws) {
-            if (hipStreamSynchronize(st) != hipSuccess) return LRS_E_DEVICE;
-            (void)hipFree(ctx->delta_ws);
-            ctx->delta_ws = nullptr;
-            ctx->delta_ws_bytes = 0;
-        }
-        void* pws = nullptr;
-        if (hipMalloc(&pws, need) != hipSuccess) {
-            (void)hipGetLastError();
-            return LRS_E_NOMEM;
-        }
-        ctx->delta_ws = pws;
-        ctx->delta_ws_bytes = need;
-    }
+    const lrs_status ws = grow_workspace(ctx->delta_ws, ctx->delta_ws_bytes, lrs::delta_workspace_bytes(B, T, H), st);
+    if (ws != LRS_OK) return ws;
     lrs::DeltaParams p{};
     p.q = q;
     p.k = k;

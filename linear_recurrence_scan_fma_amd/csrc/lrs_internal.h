@@ -61,11 +61,26 @@ struct DiagParams {
     float* o;
     float* s_final;
     int B, T, H, Hg, K, V;
-    int vec;               // 16-byte vector loads allowed
+    int vec;               // 16-byte vector loads and stores allowed
 };
 
-int diag_outer_vtile(int decay_mode);
-hipError_t launch_scan_diag_outer(const DiagParams& p, hipStream_t stream);
+// Time-axis split of the diag-outer scan: chunks of 64 steps grouped into
+// segments; a segment count above one needs diag_outer_workspace_bytes().
+struct DiagPlan {
+    int nchunks;
+    int vtiles;
+    int nseg;
+    int cps;               // chunks per segment
+};
+
+int diag_outer_vtile();
+// requested_segments <= 0 picks as many segments as fill the chip's resident
+// workgroup slots once.
+DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool vec, int num_cus,
+                         int requested_segments);
+size_t diag_outer_workspace_bytes(int B, int H, int K, int V, int nseg);
+hipError_t launch_scan_diag_outer(const DiagParams& p, const DiagPlan& plan, void* workspace,
+                                  hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Delta-rule state scan.

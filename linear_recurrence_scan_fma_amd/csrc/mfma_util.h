@@ -34,6 +34,27 @@ __device__ __forceinline__ void split_bf16(float x, u16& hi, u16& lo) {
     lo = f2bf(x - bf2f(hi));
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two values at once: hi and lo come back as packed bf16 pairs (the first
+// value in the low half), with a + b ~= hi + lo as in split_bf16.
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+    const float ha = __uint_as_float(h << 16), hb = __uint_as_float(h & 0xffff0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
+    hi = h;
+}
+
+// Eight values (two groups of four) as hi and lo bf16x8 operands.
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split2(x[2 * i], x[2 * i + 1], h[i], l[i]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+}
+
 template <int LD>
 __device__ __forceinline__ bf16x8 frag(const u16* base, int r0, int k0, int lane) {
     return *reinterpret_cast<const bf16x8*>(base + (r0 + (lane & 15)) * LD + k0 + 8 * (lane >> 4));
@@ -89,6 +110,21 @@ __device__ __forceinline__ u32x4 buf_load16(BufRes r, int off) {
 
 __device__ __forceinline__ float buf_load_f32(BufRes r, int off) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// A resource over [base + skip, base + bytes): a loop over time steps moves its
+// window with scalar arithmetic only, keeping per-lane offsets loop-invariant.
+// The range check of a raw buffer access covers the per-lane offset (plus the
+// instruction's immediate), so accesses past the window read zero or are
+// dropped.
+__device__ __forceinline__ BufRes make_rsrc_window(const void* base, int64_t bytes, int64_t skip) {
+    const int64_t left = bytes > skip ? bytes - skip : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(static_cast<const char*>(base)) + skip,
+                                             static_cast<short>(0), static_cast<int>(left), 0x00020000);
+}
+
+__device__ __forceinline__ void buf_store16(u32x4 x, BufRes r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, off, 0, 0);
 }
 
 // XCD-aware workgroup order: the hardware hands consecutive workgroup ids to

@@ -10,28 +10,40 @@
 // "我拿同一份权重和 llama.cpp 正面比了一场：我手写的 C 内核，慢了 1.1–1.7 倍" §3].
 //
 // Chunked form (chunk of L = 64 steps, state S0 entering the chunk, G_t the
-// within-chunk cumulative log-decay including step t):
-//   o_t   = scale * ( sum_{tau<=t} P[t][tau] v_tau + sum_d q_t[d] e^{G_t[d]} S0[d][:] )
+// within-chunk cumulative log-decay including step t, G_L its last value):
+//   o_t = scale * ( sum_{tau<=t} P[t][tau] v_tau + sum_d q_t[d] e^{G_t[d]} S0[d][:] )
 //   P[t][tau] = kappa_tau sum_d q_t[d] k_tau[d] e^{G_t[d] - G_tau[d]}
-//   S_L   = diag(e^{G_L}) S0 + sum_tau diag(e^{G_L - G_tau}) kappa_tau k_tau v_tau^T
-// which is the sequential recurrence regrouped (no approximation).  The
-// contractions run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Inputs
-// q, k, v are bf16 and enter exactly; an fp32 operand (scaled keys, P, the
-// state) is split into hi + lo bf16 terms so its rounding error is ~2^-17.
+//   S_L = diag(e^{G_L}) S0 + sum_tau diag(e^{G_L - G_tau}) kappa_tau k_tau v_tau^T
+// which is the sequential recurrence regrouped (no approximation).  Across
+// chunks the state obeys S <- a (.) S + U with a diagonal `a`, so the time
+// axis also splits into segments: a first kernel reduces each segment to its
+// pair (a_seg, U_seg) from a zero state, and the output kernel starts each
+// segment from S0 folded through the pairs of the segments before it.
 //
-//  * scalar decay (mode 0): P = (Q K^T) masked by kappa_tau e^{G_t - G_tau},
-//    with Q K^T exact on the matrix cores and the mask exact per pair, so any
-//    decay strength is stable.  The e^{G_t} readout factor scales output rows.
-//  * per-key decay (mode 1): P = (Q o e^{G}) (K o kappa e^{-G})^T.  Both factors
-//    stay inside the fp32/bf16 exponent range while the chunk's total decay is
-//    below 60 nats on every key (GLA-shaped gates use a few nats); otherwise
-//    the chunk falls back to evaluating P pair by pair with exact exponentials.
+// Work split: a workgroup owns (batch, head, 64-column V-tile, segment); wave w
+// owns state columns 16w..16w+15 for all keys, as 16x16 fp32 accumulator tiles
+// held in registers for the whole segment.  Per chunk the raw inputs go to LDS
+// row-major (prefetched into registers during the previous chunk), then:
+//   scores  P^T = K Q^T on v_mfma_f32_16x16x32_bf16, masked and scaled, to LDS;
+//   readout O^T = S^T Q^T (the state tiles are the left operand in place) plus
+//           V^T P^T, with V^T and K^T taken by the transposing LDS read;
+//   update  S = a (.) S + K~^T V~.
+// The contraction index of a 16x16x32 product may be permuted as long as both
+// operands agree; here lane group g holds k-slots {4g..4g+3} u {16+4g..16+4g+3}
+// of each 32-wide step, which is exactly what two 16x16 accumulator tiles
+// (rows 4g..4g+3 each) hold, so the state never leaves its registers.
 //
-// Work split: one workgroup per (batch, head, V-tile of VT columns) walks the
-// chunks in order, holding its K x VT fp32 state tile in MFMA accumulator
-// registers across chunks, and prefetching the next chunk's inputs into
-// registers while it computes the current one.  V-tiles of one head run on
-// one XCD so that their shared q/k/g reads hit the same L2.
+// Precision: q, k, v are bf16 and enter the matrix cores exactly; fp32 operands
+// (the state, P, decay-scaled keys or values) are split into hi + lo bf16 terms.
+//  * scalar decay (mode 0): P = (K Q^T) scaled pair by pair by
+//    kappa_tau e^{G_t - G_tau}; the readout is scaled by e^{G_t} per row; the
+//    update weight kappa_tau e^{G_L - G_tau} goes on the values.  Stable for any
+//    decay strength.
+//  * per-key decay (mode 1): q~ = q o e^{G_t - G_L} and k~ = kappa k o e^{G_L - G_t}
+//    give P = q~ k~^T, readout q~ (e^{G_L} o S0), update k~^T v.  Both factors stay
+//    inside the fp32/bf16 range while the chunk's decay is below 60 nats on every
+//    key (GLA-shaped gates use a few nats); otherwise the chunk evaluates P pair
+//    by pair with exact exponentials and reads out with q o e^{G_t} and S0.
 #include "lrs_internal.h"
 #include "mfma_util.h"
 
@@ -40,7 +52,12 @@ namespace {
 
 constexpr int L = 64;     // chunk length
 constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr int VT = 64;    // V-tile width: 16 columns per wave
 constexpr float kFastPathMaxDecay = 60.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct DiagArgs {
     const u16* q;
@@ -51,251 +68,329 @@ struct DiagArgs {
     const float* s0;
     float* o;
     float* s_final;
+    float* agg_u;    // [nseg-1][unit][wave][KP/16][lane][4]: segment state contributions,
+                     // in the accumulator-tile order of the lanes that own them
+    float* agg_a;    // [nseg-1][B*H][KP]: segment decay products (1 past K)
     int B, T, H, Hg, K, V;
     float scale;
     int vtiles;
-    int vec;  // K % 8 == 0, V % 8 == 0 and 16-byte aligned bases: vector loads allowed
+    int nchunks, nseg, cps;   // chunks, segments, chunks per segment
 };
 
-// Lower-triangular 16x16 blocks (i, j), j <= i, of the 64 x 64 chunk score matrix.
-__device__ __forceinline__ void tri_block(int n, int& i, int& j) {
-    i = n < 1 ? 0 : (n < 3 ? 1 : (n < 6 ? 2 : 3));
-    j = n - (i * (i + 1)) / 2;
+__device__ __forceinline__ void store4(u16* dst, const u16 (&x)[4]) {
+    u32x2 w = {x[0] | (static_cast<uint32_t>(x[1]) << 16), x[2] | (static_cast<uint32_t>(x[3]) << 16)};
+    *reinterpret_cast<u32x2*>(dst) = w;
 }
 
-__device__ __forceinline__ void store8(u16* dst, const u16 (&x)[8]) {
-    u32x4 w = {x[0] | (static_cast<uint32_t>(x[1]) << 16), x[2] | (static_cast<uint32_t>(x[3]) << 16),
-               x[4] | (static_cast<uint32_t>(x[5]) << 16), x[6] | (static_cast<uint32_t>(x[7]) << 16)};
-    *reinterpret_cast<u32x4*>(dst) = w;
+__device__ __forceinline__ u16 half_elem(const u32x2& v, int e) {
+    const uint32_t w = e < 2 ? v.x : v.y;
+    return static_cast<u16>((e & 1) ? (w >> 16) : (w & 0xffff));
 }
 
-template <int MODE, int KP, int VT, bool VEC>
+// Operand with k-slots {k0 .. k0+3} u {k0+16 .. k0+19} of row `row`: two 8-byte LDS reads.
+__device__ __forceinline__ bf16x8 slot_frag(const u16* rowp) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(rowp);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(rowp + 16);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
+// Transposed operand from a row-major [k][n] bf16 array: lane j of 16-lane group
+// g receives M[k0 .. k0+3][n0 + j] and M[k0+16 .. k0+19][n0 + j] with k0 = kb + 4g
+// (ds_read_b64_tr_b16: lane i of a group supplies row k0 + i/4, columns n0 + 4(i%4)).
+template <int LD>
+__device__ __forceinline__ bf16x8 tr_frag(const u16* m, int kb, int n0, int lane) {
+    const int i16 = lane & 15, k0 = kb + 4 * (lane >> 4);
+    const u16* pa = m + (k0 + (i16 >> 2)) * LD + n0 + 4 * (i16 & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 16 * LD));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Score blocks (key block, query block), key block <= query block, per wave:
+// {(0,0),(0,1),(0,2)}, {(1,1),(1,2),(1,3)}, {(2,2),(2,3)}, {(0,3),(3,3)}.
+__device__ __forceinline__ bool score_job(int wave, int n, int& kb, int& qb) {
+    switch (wave * 3 + n) {
+        case 0: kb = 0; qb = 0; return true;
+        case 1: kb = 0; qb = 1; return true;
+        case 2: kb = 0; qb = 2; return true;
+        case 3: kb = 1; qb = 1; return true;
+        case 4: kb = 1; qb = 2; return true;
+        case 5: kb = 1; qb = 3; return true;
+        case 6: kb = 2; qb = 2; return true;
+        case 7: kb = 2; qb = 3; return true;
+        case 9: kb = 0; qb = 3; return true;
+        case 10: kb = 3; qb = 3; return true;
+        default: return false;
+    }
+}
+
+// AGG = true: segment reduction (a_seg, U_seg) from a zero state, no outputs.
+// AGG = false: outputs and the final state, starting from the folded segment state.
+template <int MODE, int KP, bool VEC, bool AGG>
 __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
-    constexpr int LDK = KP + 8;   // padded row length for [*][KP] bf16 arrays
-    constexpr int LDL = L + 8;    // padded row length for [*][L] bf16 arrays
-    constexpr int KT = KP / 16;
-    constexpr int VTT = VT / 16;
-    constexpr int S_PER_WAVE = KT * VTT / 4;
-    constexpr int PQ = L * KP / 8 / NT;   // q/k 16-byte pieces per thread
-    constexpr int PV = L * VT / 8 / NT;   // v pieces per thread
-    constexpr int KG = KP / 4;            // groups of 4 keys (per-key decay loads)
-    constexpr int RG = NT / KG;           // row groups
-    constexpr int RPG = L / RG;           // rows per group
-    constexpr int SK_ELEMS = (L * LDK > KP * LDL) ? L * LDK : KP * LDL;
-    static_assert(PQ >= 1 && PV >= 1 && S_PER_WAVE >= 1, "tile shape");
+    constexpr bool OUT = !AGG;
+    constexpr int LDK = KP + 8;   // row stride of the [L][KP] bf16 operands
+    constexpr int LDV = VT + 8;
+    constexpr int LDP = L + 8;
+    constexpr int KB = KP / 16;   // 16-row state tiles per wave
+    constexpr int KM = KP / 32;   // 32-wide steps over the key axis
+    constexpr int NPL = MODE == 1 ? 2 : 1;   // hi/lo planes of the q/k operands
+    constexpr int PQ = L * KP / 8 / NT;      // mode 0: 16-byte q/k pieces per thread
+    constexpr int PV = L * VT / 8 / NT;      // 16-byte v pieces per thread
+    constexpr int KG = KP / 4;               // mode 1: threads per row (4 keys each)
+    constexpr int RG = NT / KG;              // mode 1: row groups
+    constexpr int RPG = L / RG;              // mode 1: rows per thread
+    constexpr int NQ = MODE == 0 ? PQ : RPG;
+    static_assert(PQ >= 1 && PV >= 1 && RPG >= 1, "tile shape");
+    static_assert(MODE == 0 || NPL * L * LDK * 2 >= L * KP * 4, "fallback scores reuse the key operand space");
 
-    __shared__ __align__(16) u16 sQh[L * LDK];
-    __shared__ __align__(16) u16 sQl[L * LDK];
-    __shared__ __align__(16) u16 sKh[SK_ELEMS];   // [L][LDK] scores operand, then [KP][LDL] state update
-    __shared__ __align__(16) u16 sKl[SK_ELEMS];
-    __shared__ __align__(16) u16 sPh[L * LDL];
-    __shared__ __align__(16) u16 sPl[L * LDL];
-    __shared__ __align__(16) u16 sVT[VT * LDL];   // V^T, exact
-    __shared__ __align__(16) u16 sSTh[VT * LDK];  // S^T entering the chunk, hi/lo
-    __shared__ __align__(16) u16 sSTl[VT * LDK];
-    __shared__ float sG[MODE == 1 ? L * KP : L];
-    __shared__ float sGL[MODE == 1 ? KP : 1];
-    __shared__ float sKap[L];
-    __shared__ float sTot[MODE == 1 ? RG * KP : 1];
+    __shared__ __align__(16) u16 sQ[OUT ? NPL * L * LDK : 8];
+    __shared__ __align__(16) u16 sK[NPL * L * LDK];
+    __shared__ __align__(16) u16 sV[L * LDV];
+    __shared__ __align__(16) u16 sP[OUT ? 2 * L * LDP : 8];
+    __shared__ __align__(16) float sG[MODE == 0 ? L : 1];      // cumulative log decay
+    __shared__ float sEG[MODE == 0 ? L : 1];     // scale e^{G_t}
+    __shared__ __align__(16) float sW[MODE == 0 ? L : 1];   // kappa_t e^{G_L - G_t}
+    __shared__ __align__(16) float sKap[L];                    // scale kappa_t (scores)
+    __shared__ float sDec[1];                    // mode 0: e^{G_L}
+    __shared__ __align__(16) float sTot[MODE == 1 ? RG * KP : 1];
+    __shared__ float sGL[MODE == 1 ? KP : 1];    // G_L per key
+    __shared__ __align__(16) float sEGL[MODE == 1 ? KP : 1];   // e^{G_L} per key
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int g4 = lane >> 4;
+    const int c16 = lane & 15;
+    const int nsegk = AGG ? p.nseg - 1 : p.nseg;
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int vt = lid % p.vtiles;
-    const int bh = lid / p.vtiles;
+    const int seg = lid % nsegk;
+    const int rest = lid / nsegk;
+    const int vt = rest % p.vtiles;
+    const int bh = rest / p.vtiles;
     const int b = bh / p.H;
     const int h = bh - b * p.H;
     const int grp = h / (p.H / p.Hg);
     const int v0 = vt * VT;
-    constexpr bool vec = VEC;   // compile-time, so the vector path never waits on a scalar one
     const int64_t T = p.T;
     const int K = p.K, V = p.V, H = p.H, Hg = p.Hg;
-    const int nchunks = static_cast<int>((T + L - 1) / L);
+    const int c_begin = seg * p.cps;
+    const int c_end = min(c_begin + p.cps, p.nchunks);
+    const int jcol = v0 + 16 * wave + c16;   // this lane's state column
+    const float scale = p.scale;
 
-    u32x4 cq[PQ], ck[PQ], cv[PV];
-    u32x4 nq[PQ], nk[PQ], nv[PV];
-    float cg[MODE == 1 ? RPG : 1][4];
-    float ng[MODE == 1 ? RPG : 1][4];
-    float cgs = 0.0f, ngs = 0.0f, ckap = 0.0f, nkap = 0.0f;
+    // Batch-row bases and byte sizes; each chunk reads through a window that
+    // starts at its first step (vector path), so per-lane offsets are fixed.
+    const int64_t qk_row = static_cast<int64_t>(Hg) * K * 2;        // bytes per step
+    const int64_t v_row = static_cast<int64_t>(H) * V * 2;
+    const int64_t g_row = static_cast<int64_t>(H) * (MODE == 1 ? K : 1) * 4;
+    const int64_t s_row = static_cast<int64_t>(H) * 4;               // k_scale
+    const int64_t o_row = static_cast<int64_t>(H) * V * 4;
+    const u16* qb = p.q + b * T * Hg * static_cast<int64_t>(K);
+    const u16* kb_ = p.k + b * T * Hg * static_cast<int64_t>(K);
+    const u16* vb = p.v + b * T * H * static_cast<int64_t>(V);
+    const float* gb = p.g + b * T * H * static_cast<int64_t>(MODE == 1 ? K : 1);
+    const float* ksb = p.ks ? p.ks + b * T * H : nullptr;
+    float* ob = p.o + b * T * H * static_cast<int64_t>(V);
 
-    // Per-batch-row buffer resources (vector path): rows past T and columns
-    // past K / V fall outside and read as zero.
-    const BufRes rq = make_rsrc(p.q + b * T * Hg * static_cast<int64_t>(K), T * Hg * static_cast<int64_t>(K) * 2);
-    const BufRes rk = make_rsrc(p.k + b * T * Hg * static_cast<int64_t>(K), T * Hg * static_cast<int64_t>(K) * 2);
-    const BufRes rv = make_rsrc(p.v + b * T * H * static_cast<int64_t>(V), T * H * static_cast<int64_t>(V) * 2);
-    const int64_t gcols = MODE == 1 ? K : 1;
-    const BufRes rdec = make_rsrc(p.g + b * T * H * gcols, T * H * gcols * 4);
-    const BufRes rks = make_rsrc(p.ks ? p.ks + b * T * H : p.g, p.ks ? T * H * 4 : 0);
+    // per-lane offsets within a chunk window
+    int offq[NQ], offg[MODE == 1 ? NQ : 1], offs[MODE == 1 ? NQ : 1], offv[PV];
+    if constexpr (MODE == 0) {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) {
+            const int pi = tid + NT * i, row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
+            offq[i] = c8 < K ? ((row * Hg + grp) * K + c8) * 2 : kBufOOB;
+        }
+        offg[0] = (tid * H + h) * 4;
+    } else {
+        const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const int t = rg * RPG + r;
+            offq[r] = d0 < K ? ((t * Hg + grp) * K + d0) * 2 : kBufOOB;
+            offg[r] = d0 < K ? ((t * H + h) * K + d0) * 4 : kBufOOB;
+            offs[r] = (t * H + h) * 4;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PV; ++i) {
+        const int pi = tid + NT * i, row = pi / (VT / 8), c8 = (pi % (VT / 8)) * 8;
+        offv[i] = v0 + c8 < V ? ((row * H + h) * V + v0 + c8) * 2 : kBufOOB;
+    }
+    const int offo = jcol - c16 + 4 * g4 < V ? ((c16 * H + h) * V + v0 + 16 * wave + 4 * g4) * 4 : kBufOOB;
 
-    auto load_chunk = [&](int64_t t0, u32x4 (&Q)[PQ], u32x4 (&Kx)[PQ], u32x4 (&Vx)[PV],
-                          float (&Gx)[MODE == 1 ? RPG : 1][4], float& gs, float& kap) {
+    // ---- prefetch registers: raw inputs of one chunk ----
+    // mode 0: q/k as 16-byte row pieces; mode 1: 4 keys x RPG rows per thread
+    u32x4 cq[MODE == 0 ? NQ : 1], ck[MODE == 0 ? NQ : 1];
+    u32x2 cq2[MODE == 1 ? NQ : 1], ck2[MODE == 1 ? NQ : 1];
+    u32x4 cgv[MODE == 1 ? NQ : 1];
+    float ckp[MODE == 1 ? NQ : 1];
+    u32x4 cv[PV];
+    float cgs = 0.0f, ckap = 0.0f;
+
+    auto load_chunk = [&](int c) {
+        const int64_t t0 = static_cast<int64_t>(c) * L;
         if constexpr (VEC) {
+            const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
+            const BufRes wk = make_rsrc_window(kb_, T * qk_row, t0 * qk_row);
+            const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
+            const BufRes wg = make_rsrc_window(gb, T * g_row, t0 * g_row);
+            const BufRes ws = make_rsrc_window(ksb ? static_cast<const void*>(ksb) : gb, ksb ? T * s_row : 0,
+                                               t0 * s_row);
+            if constexpr (MODE == 0) {
 #pragma unroll
-            for (int i = 0; i < PQ; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi / (KP / 8);
-                const int c8 = (pi % (KP / 8)) * 8;
-                const int t = static_cast<int>(t0) + row;
-                const int off = c8 < K ? ((t * Hg + grp) * K + c8) * 2 : kBufOOB;
-                Q[i] = buf_load16(rq, off);
-                Kx[i] = buf_load16(rk, off);
-            }
+                for (int i = 0; i < NQ; ++i) {
+                    if constexpr (OUT) cq[i] = buf_load16(wq, offq[i]);
+                    ck[i] = buf_load16(wk, offq[i]);
+                }
+                if (tid < L) {
+                    cgs = buf_load_f32(wg, offg[0]);
+                    ckap = buf_load_f32(ws, offg[0]);   // raw; NULL k_scale handled at use
+                }
+            } else {
 #pragma unroll
-            for (int i = 0; i < PV; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi / (VT / 8);
-                const int c8 = (pi % (VT / 8)) * 8;
-                const int t = static_cast<int>(t0) + row;
-                const int off = v0 + c8 < V ? ((t * H + h) * V + v0 + c8) * 2 : kBufOOB;
-                Vx[i] = buf_load16(rv, off);
-            }
-            if constexpr (MODE == 1) {
-                const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
-#pragma unroll
-                for (int r = 0; r < RPG; ++r) {
-                    const int t = static_cast<int>(t0) + rg * RPG + r;
-                    const int off = d0 < K ? ((t * H + h) * K + d0) * 4 : kBufOOB;
-                    const u32x4 x = buf_load16(rdec, off);
-                    Gx[r][0] = __uint_as_float(x.x);
-                    Gx[r][1] = __uint_as_float(x.y);
-                    Gx[r][2] = __uint_as_float(x.z);
-                    Gx[r][3] = __uint_as_float(x.w);
+                for (int r = 0; r < NQ; ++r) {
+                    if constexpr (OUT) cq2[r] = __builtin_amdgcn_raw_buffer_load_b64(wq, offq[r], 0, 0);
+                    ck2[r] = __builtin_amdgcn_raw_buffer_load_b64(wk, offq[r], 0, 0);
+                    cgv[r] = buf_load16(wg, offg[r]);
+                    ckp[r] = buf_load_f32(ws, offs[r]);   // raw; NULL k_scale handled at use
                 }
             }
-            if (tid < L) {
-                const int t = static_cast<int>(t0) + tid;
-                if constexpr (MODE == 0) gs = buf_load_f32(rdec, (t * H + h) * 4);
-                kap = buf_load_f32(rks, (t * H + h) * 4);   // raw; NULL k_scale handled in phase 0
-            }
+#pragma unroll
+            for (int i = 0; i < PV; ++i) cv[i] = buf_load16(wv, offv[i]);
         } else {
+            if constexpr (MODE == 0) {
 #pragma unroll
-            for (int i = 0; i < PQ; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi / (KP / 8);
-                const int c8 = (pi % (KP / 8)) * 8;
-                const int64_t t = t0 + row;
-                Q[i] = u32x4{0u, 0u, 0u, 0u};
-                Kx[i] = u32x4{0u, 0u, 0u, 0u};
-                if (t < T) {
-                    const int64_t off = ((b * T + t) * Hg + grp) * static_cast<int64_t>(K);
-                    Q[i] = load8_bf16(p.q + off, c8, K, false);
-                    Kx[i] = load8_bf16(p.k + off, c8, K, false);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < PV; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi / (VT / 8);
-                const int c8 = (pi % (VT / 8)) * 8;
-                const int64_t t = t0 + row;
-                Vx[i] = u32x4{0u, 0u, 0u, 0u};
-                if (t < T) {
-                    const int64_t off = ((b * T + t) * H + h) * static_cast<int64_t>(V) + v0;
-                    Vx[i] = load8_bf16(p.v + off, c8, V - v0, false);
-                }
-            }
-            if constexpr (MODE == 1) {
-                const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
-#pragma unroll
-                for (int r = 0; r < RPG; ++r) {
-                    const int64_t t = t0 + rg * RPG + r;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) Gx[r][e] = 0.0f;
+                for (int i = 0; i < NQ; ++i) {
+                    const int pi = tid + NT * i, row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
+                    const int64_t t = t0 + row;
+                    cq[i] = u32x4{0u, 0u, 0u, 0u};
+                    ck[i] = u32x4{0u, 0u, 0u, 0u};
                     if (t < T) {
-                        const float* grow = p.g + ((b * T + t) * H + h) * static_cast<int64_t>(K);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) Gx[r][e] = d0 + e < K ? grow[d0 + e] : 0.0f;
+                        const int64_t off = (t * Hg + grp) * static_cast<int64_t>(K);
+                        if constexpr (OUT) cq[i] = load8_bf16(qb + off, c8, K, false);
+                        ck[i] = load8_bf16(kb_ + off, c8, K, false);
                     }
                 }
-            }
-            if (tid < L) {
-                const int64_t t = t0 + tid;
-                gs = 0.0f;
-                kap = 0.0f;
-                if (t < T) {
-                    const int64_t idx = (b * T + t) * H + h;
-                    if constexpr (MODE == 0) gs = p.g[idx];
-                    kap = p.ks ? p.ks[idx] : 1.0f;
+                if (tid < L) {
+                    const int64_t t = t0 + tid;
+                    cgs = 0.0f;
+                    ckap = 0.0f;
+                    if (t < T) {
+                        cgs = gb[t * H + h];
+                        ckap = ksb ? ksb[t * H + h] : 1.0f;
+                    }
+                }
+            } else {
+                const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
+#pragma unroll
+                for (int r = 0; r < NQ; ++r) {
+                    const int64_t t = t0 + rg * RPG + r;
+                    u16 qe[4] = {0, 0, 0, 0}, ke[4] = {0, 0, 0, 0};
+                    float ge[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    float kp = 0.0f;
+                    if (t < T) {
+                        const int64_t oq = (t * Hg + grp) * static_cast<int64_t>(K);
+                        const int64_t og = (t * H + h) * static_cast<int64_t>(K);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (d0 + e < K) {
+                                if constexpr (OUT) qe[e] = qb[oq + d0 + e];
+                                ke[e] = kb_[oq + d0 + e];
+                                ge[e] = gb[og + d0 + e];
+                            }
+                        }
+                        kp = ksb ? ksb[t * H + h] : 1.0f;
+                    }
+                    cq2[r] = u32x2{qe[0] | (static_cast<uint32_t>(qe[1]) << 16),
+                                   qe[2] | (static_cast<uint32_t>(qe[3]) << 16)};
+                    ck2[r] = u32x2{ke[0] | (static_cast<uint32_t>(ke[1]) << 16),
+                                   ke[2] | (static_cast<uint32_t>(ke[3]) << 16)};
+                    cgv[r] = u32x4{__float_as_uint(ge[0]), __float_as_uint(ge[1]), __float_as_uint(ge[2]),
+                                   __float_as_uint(ge[3])};
+                    ckp[r] = kp;
                 }
             }
-        }
-    };
-
-    // ---- prologue: state tile from s0 into registers and into S^T (LDS) ----
-    f32x4 S[S_PER_WAVE];
 #pragma unroll
-    for (int m = 0; m < S_PER_WAVE; ++m) {
-        const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-        const int j = v0 + 16 * sc + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d = 16 * sr + 4 * (lane >> 4) + r;
-            float x = 0.0f;
-            if (p.s0 && d < K && j < V) x = p.s0[((static_cast<int64_t>(b) * H + h) * K + d) * V + j];
-            S[m][r] = x;
-        }
-    }
-    auto write_state_lds = [&]() {
-#pragma unroll
-        for (int m = 0; m < S_PER_WAVE; ++m) {
-            const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-            const int j = 16 * sc + (lane & 15);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int d = 16 * sr + 4 * (lane >> 4) + r;
-                u16 hi, lo;
-                split_bf16(S[m][r], hi, lo);
-                sSTh[j * LDK + d] = hi;
-                sSTl[j * LDK + d] = lo;
+            for (int i = 0; i < PV; ++i) {
+                const int pi = tid + NT * i, row = pi / (VT / 8), c8 = (pi % (VT / 8)) * 8;
+                const int64_t t = t0 + row;
+                cv[i] = u32x4{0u, 0u, 0u, 0u};
+                if (t < T) cv[i] = load8_bf16(vb + (t * H + h) * static_cast<int64_t>(V) + v0, c8, V - v0, false);
             }
         }
     };
-    write_state_lds();
-    for (int e = tid; e < L * LDL; e += NT) {
-        sPh[e] = 0;
-        sPl[e] = 0;
+
+    // ---- state: S0 folded through the earlier segments (output pass) or zero ----
+    f32x4 S[KB];
+#pragma unroll
+    for (int db = 0; db < KB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int d = 16 * db + 4 * g4 + r;
+            float x = 0.0f;
+            if (OUT && p.s0 && d < K && jcol < V) x = p.s0[((static_cast<int64_t>(b) * H + h) * K + d) * V + jcol];
+            S[db][r] = x;
+        }
     }
-    load_chunk(0, cq, ck, cv, cg, cgs, ckap);
+    if constexpr (OUT) {
+        if (seg > 0) {
+            // S = (prod_s a_s) o S0 + sum_s (prod_{s' > s} a_s') o U_s over the earlier
+            // segments, newest first: every segment's loads are independent of the
+            // running result, so they overlap
+            const int units = p.B * H * p.vtiles;
+            f32x4 acc[KB], pr[KB];
+#pragma unroll
+            for (int db = 0; db < KB; ++db) {
+                acc[db] = zero4();
+                pr[db] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+            }
+#pragma unroll 2
+            for (int s2 = seg - 1; s2 >= 0; --s2) {
+                const float* ub = p.agg_u + ((static_cast<int64_t>(s2) * units + rest) * 4 + wave) * (KB * 256);
+                const float* ab = p.agg_a + (static_cast<int64_t>(s2) * p.B * H + bh) * KP;
+#pragma unroll
+                for (int db = 0; db < KB; ++db) {
+                    const f32x4 u = *reinterpret_cast<const f32x4*>(ub + (db * 64 + lane) * 4);
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(ab + 16 * db + 4 * g4);
+                    acc[db] += pr[db] * u;
+                    pr[db] *= a;
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < KB; ++db) S[db] = pr[db] * S[db] + acc[db];
+        }
+        // score blocks right of the diagonal that the readout reads: always zero
+        {
+            const int blk = tid >> 7, plane = (tid >> 6) & 1, row = (tid >> 2) & 15, quad = tid & 3;
+            const int t = 32 * blk + row, c0 = 32 * blk + 16 + 4 * quad;
+            const u16 z[4] = {0, 0, 0, 0};
+            store4(sP + plane * L * LDP + t * LDP + c0, z);
+        }
+    }
+    float lsum = 0.0f;   // segment log-decay (mode 0: uniform; mode 1: key `tid`)
 
-    for (int c = 0; c < nchunks; ++c) {
+    if (c_begin < c_end) load_chunk(c_begin);
+
+    for (int c = c_begin; c < c_end; ++c) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
+        bool fast = true;
 
-        // ---- phase 0: V^T, cumulative decay, kappa into LDS ----
+        // ---- stage: raw or decay-scaled operands into LDS ----
 #pragma unroll
         for (int i = 0; i < PV; ++i) {
             const int pi = tid + NT * i;
-            const int row = pi / (VT / 8);
-            const int c8 = (pi % (VT / 8)) * 8;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sVT[(c8 + e) * LDL + row] = piece_elem(cv[i], e);
+            *reinterpret_cast<u32x4*>(sV + (pi / (VT / 8)) * LDV + (pi % (VT / 8)) * 8) = cv[i];
         }
-        if (tid < L) sKap[tid] = (VEC && !p.ks) ? (t0 + tid < T ? 1.0f : 0.0f) : ckap;
-        if constexpr (MODE == 1) {
-            const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (MODE == 0) {
 #pragma unroll
-            for (int r = 0; r < RPG; ++r)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    acc[e] += cg[r][e];
-                    cg[r][e] = acc[e];   // local inclusive sums
-                }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sTot[rg * KP + d0 + e] = acc[e];
-            __syncthreads();
-            float pre[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            for (int r2 = 0; r2 < rg; ++r2)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pre[e] += sTot[r2 * KP + d0 + e];
-#pragma unroll
-            for (int r = 0; r < RPG; ++r)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sG[(rg * RPG + r) * KP + d0 + e] = cg[r][e] + pre[e];
-            if (rg == RG - 1)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sGL[d0 + e] = cg[RPG - 1][e] + pre[e];
-        } else {
+            for (int i = 0; i < NQ; ++i) {
+                const int pi = tid + NT * i;
+                const int row = pi / (KP / 8);
+                const int c8 = (pi % (KP / 8)) * 8;
+                if constexpr (OUT) *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = cq[i];
+                *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = ck[i];
+            }
             if (wave == 0) {
                 float x = cgs;
 #pragma unroll
@@ -303,237 +398,369 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
                     const float y = __shfl_up(x, off);
                     if (lane >= off) x += y;
                 }
+                const float gl = __shfl(x, 63);
+                const float kap = (VEC && !p.ks) ? (t0 + lane < T ? 1.0f : 0.0f) : ckap;
                 sG[lane] = x;
-                if (lane == 63) sGL[0] = x;
-            }
-        }
-        __syncthreads();
-
-        // prefetch the next chunk while this one is computed
-        if (c + 1 < nchunks) load_chunk(t0 + L, nq, nk, nv, ng, ngs, nkap);
-
-        // ---- phase 1: score operands ----
-        bool fast = true;
-        if constexpr (MODE == 1) {
-            int bad = 0;
-            if (tid < KP) bad = -sGL[tid] > kFastPathMaxDecay;
-            fast = !__syncthreads_or(bad);
-        }
-#pragma unroll
-        for (int i = 0; i < PQ; ++i) {
-            const int pi = tid + NT * i;
-            const int row = pi / (KP / 8);
-            const int c8 = (pi % (KP / 8)) * 8;
-            if (MODE == 1 && fast) {
-                u16 qh[8], ql[8], kh[8], kl[8];
-                const float kap = sKap[row];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float Gt = sG[row * KP + c8 + e];
-                    split_bf16(bf2f(piece_elem(cq[i], e)) * __expf(Gt), qh[e], ql[e]);
-                    split_bf16(bf2f(piece_elem(ck[i], e)) * kap * __expf(-Gt), kh[e], kl[e]);
-                }
-                store8(sQh + row * LDK + c8, qh);
-                store8(sQl + row * LDK + c8, ql);
-                store8(sKh + row * LDK + c8, kh);
-                store8(sKl + row * LDK + c8, kl);
-            } else {
-                *reinterpret_cast<u32x4*>(sQh + row * LDK + c8) = cq[i];
-                *reinterpret_cast<u32x4*>(sKh + row * LDK + c8) = ck[i];
-            }
-        }
-        __syncthreads();
-
-        // ---- phase 2: intra-chunk scores P (lower triangle) ----
-        if (MODE == 1 && !fast) {
-            // exact fallback for very strong decay: every pair with its own exponentials
-            for (int idx = tid; idx < L * L; idx += NT) {
-                const int t = idx / L, tau = idx % L;
-                float acc = 0.0f;
-                if (tau <= t) {
-                    for (int d = 0; d < KP; ++d)
-                        acc += bf2f(sQh[t * LDK + d]) * bf2f(sKh[tau * LDK + d]) *
-                               __expf(sG[t * KP + d] - sG[tau * KP + d]);
-                    acc *= sKap[tau];
-                }
-                u16 hi, lo;
-                split_bf16(acc, hi, lo);
-                sPh[t * LDL + tau] = hi;
-                sPl[t * LDL + tau] = lo;
-            }
-            __syncthreads();
-            // the readout needs q o e^{G_t}
-#pragma unroll
-            for (int i = 0; i < PQ; ++i) {
-                const int pi = tid + NT * i;
-                const int row = pi / (KP / 8);
-                const int c8 = (pi % (KP / 8)) * 8;
-                u16 qh[8], ql[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    split_bf16(bf2f(piece_elem(cq[i], e)) * __expf(sG[row * KP + c8 + e]), qh[e], ql[e]);
-                store8(sQh + row * LDK + c8, qh);
-                store8(sQl + row * LDK + c8, ql);
+                sEG[lane] = scale * __expf(x);
+                sW[lane] = kap * __expf(gl - x);
+                sKap[lane] = scale * kap;
+                if (lane == 0) sDec[0] = __expf(gl);
             }
         } else {
-            for (int n = wave; n < 10; n += 4) {
-                int bi, bj;
-                tri_block(n, bi, bj);
+            const int kg = tid % KG, rg = tid / KG, d0 = kg * 4;
+            float G[NQ][4];
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+                const float ge[4] = {__uint_as_float(cgv[r].x), __uint_as_float(cgv[r].y),
+                                     __uint_as_float(cgv[r].z), __uint_as_float(cgv[r].w)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[e] += ge[e];
+                    G[r][e] = acc[e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sTot[rg * KP + d0 + e] = acc[e];
+            __syncthreads();
+            float pre[4] = {0.0f, 0.0f, 0.0f, 0.0f}, tot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int r2 = 0; r2 < RG; ++r2) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sTot + r2 * KP + d0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (r2 < rg) pre[e] += x[e];
+                    tot[e] += x[e];
+                }
+            }
+            bool bad = false;
+#pragma unroll
+            for (int r = 0; r < NQ; ++r)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) G[r][e] += pre[e];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bad = bad || (-tot[e] > kFastPathMaxDecay);
+            if constexpr (OUT) fast = !__syncthreads_or(bad);
+            if (rg == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sGL[d0 + e] = tot[e];
+                    sEGL[d0 + e] = __expf(tot[e]);
+                }
+            }
+            float kapr[NQ];
+#pragma unroll
+            for (int r = 0; r < NQ; ++r)
+                kapr[r] = (VEC && !p.ks) ? (t0 + rg * RPG + r < T ? 1.0f : 0.0f) : ckp[r];
+            if (OUT && !fast) {
+                // exact scores pair by pair: raw q, k and G into the operand space
+                float* sGf = reinterpret_cast<float*>(sK);
+#pragma unroll
+                for (int r = 0; r < NQ; ++r) {
+                    const int t = rg * RPG + r;
+                    *reinterpret_cast<u32x2*>(sQ + t * LDK + d0) = cq2[r];
+                    *reinterpret_cast<u32x2*>(sQ + L * LDK + t * LDK + d0) = ck2[r];
+                    *reinterpret_cast<f32x4*>(sGf + t * KP + d0) = f32x4{G[r][0], G[r][1], G[r][2], G[r][3]};
+                    if (kg == 0) sKap[t] = scale * kapr[r];
+                }
+                __syncthreads();
+                for (int idx = tid; idx < L * L; idx += NT) {
+                    const int t = idx / L, tau = idx % L;
+                    float a = 0.0f;
+                    if (tau <= t) {
+                        for (int d = 0; d < KP; ++d)
+                            a += bf2f(sQ[t * LDK + d]) * bf2f(sQ[L * LDK + tau * LDK + d]) *
+                                 __expf(sGf[t * KP + d] - sGf[tau * KP + d]);
+                        a *= sKap[tau];
+                    }
+                    u16 hi, lo;
+                    split_bf16(a, hi, lo);
+                    sP[t * LDP + tau] = hi;
+                    sP[L * LDP + t * LDP + tau] = lo;
+                }
+                __syncthreads();
+            }
+            // q~ = scale q e^{G_t - G_L} (fallback: scale q e^{G_t}), k~ = kappa k e^{G_L - G_t}
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+                const int t = rg * RPG + r;
+                float qv[4], kv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (OUT) qv[e] = bf2f(half_elem(cq2[r], e)) * (scale * __expf(fast ? G[r][e] - tot[e] : G[r][e]));
+                    kv[e] = bf2f(half_elem(ck2[r], e)) * (kapr[r] * __expf(tot[e] - G[r][e]));
+                }
+                uint32_t hq[2], lq[2], hk[2], lk[2];
+                if constexpr (OUT) {
+                    split2(qv[0], qv[1], hq[0], lq[0]);
+                    split2(qv[2], qv[3], hq[1], lq[1]);
+                    *reinterpret_cast<u32x2*>(sQ + t * LDK + d0) = u32x2{hq[0], hq[1]};
+                    *reinterpret_cast<u32x2*>(sQ + L * LDK + t * LDK + d0) = u32x2{lq[0], lq[1]};
+                }
+                split2(kv[0], kv[1], hk[0], lk[0]);
+                split2(kv[2], kv[3], hk[1], lk[1]);
+                *reinterpret_cast<u32x2*>(sK + t * LDK + d0) = u32x2{hk[0], hk[1]};
+                *reinterpret_cast<u32x2*>(sK + L * LDK + t * LDK + d0) = u32x2{lk[0], lk[1]};
+            }
+        }
+        __syncthreads();
+
+        // the prefetch registers were consumed by the staging: load the next chunk
+        if (c + 1 < c_end) load_chunk(c + 1);
+        if constexpr (AGG) {
+            if constexpr (MODE == 0) lsum += sG[L - 1];
+            else if (tid < KP) lsum += sGL[tid];
+        }
+
+        // ---- scores P (key block kb, query block qb) -> LDS as P[t][tau] ----
+        if (OUT && fast) {
+#pragma unroll
+            for (int n = 0; n < 3; ++n) {
+                int kb, qbk;
+                if (!score_job(wave, n, kb, qbk)) continue;
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int k0 = 0; k0 < KP; k0 += 32) {
-                    const bf16x8 ah = frag<LDK>(sQh, 16 * bi, k0, lane);
-                    const bf16x8 bh_ = frag<LDK>(sKh, 16 * bj, k0, lane);
+                for (int ks = 0; ks < KM; ++ks) {
+                    const bf16x8 ah = frag<LDK>(sK, 16 * kb, 32 * ks, lane);
+                    const bf16x8 bh_ = frag<LDK>(sQ, 16 * qbk, 32 * ks, lane);
                     if constexpr (MODE == 1) {
-                        const bf16x8 al = frag<LDK>(sQl, 16 * bi, k0, lane);
-                        const bf16x8 bl = frag<LDK>(sKl, 16 * bj, k0, lane);
+                        const bf16x8 al = frag<LDK>(sK + L * LDK, 16 * kb, 32 * ks, lane);
+                        const bf16x8 bl = frag<LDK>(sQ + L * LDK, 16 * qbk, 32 * ks, lane);
                         acc = mfma16(al, bh_, acc);
                         acc = mfma16(ah, bl, acc);
                     }
                     acc = mfma16(ah, bh_, acc);
                 }
-                const int tau = 16 * bj + (lane & 15);
+                const int t = 16 * qbk + c16;
+                const int tau0 = 16 * kb + 4 * g4;
+                float val[4];
+                if constexpr (MODE == 0) {
+                    const float gt = sG[t];
+                    const f32x4 gtau = *reinterpret_cast<const f32x4*>(sG + tau0);
+                    const f32x4 ktau = *reinterpret_cast<const f32x4*>(sKap + tau0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * bi + 4 * (lane >> 4) + r;
-                    float val = acc[r];
-                    if (tau > t) {
-                        val = 0.0f;
-                    } else if constexpr (MODE == 0) {
-                        val *= sKap[tau] * __expf(sG[t] - sG[tau]);
+                    for (int r = 0; r < 4; ++r) {
+                        const float f = ktau[r] * __expf(gt - gtau[r]);   // unused (maybe inf) above the diagonal
+                        val[r] = tau0 + r <= t ? acc[r] * f : 0.0f;
                     }
-                    u16 hi, lo;
-                    split_bf16(val, hi, lo);
-                    sPh[t * LDL + tau] = hi;
-                    sPl[t * LDL + tau] = lo;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) val[r] = tau0 + r <= t ? acc[r] : 0.0f;
                 }
+                uint32_t hi[2], lo[2];
+                split2(val[0], val[1], hi[0], lo[0]);
+                split2(val[2], val[3], hi[1], lo[1]);
+                *reinterpret_cast<u32x2*>(sP + t * LDP + tau0) = u32x2{hi[0], hi[1]};
+                *reinterpret_cast<u32x2*>(sP + L * LDP + t * LDP + tau0) = u32x2{lo[0], lo[1]};
             }
         }
-        __syncthreads();
+        if constexpr (OUT) __syncthreads();
 
-        // ---- phase 3: state-update operand (kappa k o e^{G_L - G_tau})^T into sK ----
+        // ---- per wave: readout of its 16 columns and the state update ----
+        bf16x8 vA[2];
 #pragma unroll
-        for (int i = 0; i < PQ; ++i) {
-            const int pi = tid + NT * i;
-            const int row = pi / (KP / 8);
-            const int c8 = (pi % (KP / 8)) * 8;
-            const float kap = sKap[row];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = c8 + e;
-                const float w = MODE == 1 ? __expf(sGL[d] - sG[row * KP + d]) : __expf(sGL[0] - sG[row]);
-                u16 hi, lo;
-                split_bf16(bf2f(piece_elem(ck[i], e)) * kap * w, hi, lo);
-                sKh[d * LDL + row] = hi;
-                sKl[d * LDL + row] = lo;
-            }
-        }
-        __syncthreads();
+        for (int ks = 0; ks < 2; ++ks) vA[ks] = tr_frag<LDV>(sV, 32 * ks, 16 * wave, lane);
 
-        // ---- phase 4: outputs (row block = wave) and the state update ----
-        {
-            const int ri = wave;
-#pragma unroll
-            for (int cj = 0; cj < VTT; ++cj) {
-                f32x4 a1 = zero4(), a2 = zero4();
-                for (int ks = 0; ks <= ri / 2; ++ks) {
-                    const bf16x8 ph = frag<LDL>(sPh, 16 * ri, 32 * ks, lane);
-                    const bf16x8 pl = frag<LDL>(sPl, 16 * ri, 32 * ks, lane);
-                    const bf16x8 vb = frag<LDL>(sVT, 16 * cj, 32 * ks, lane);
-                    a1 = mfma16(pl, vb, a1);
-                    a1 = mfma16(ph, vb, a1);
-                }
-#pragma unroll
-                for (int k0 = 0; k0 < KP; k0 += 32) {
-                    const bf16x8 qh = frag<LDK>(sQh, 16 * ri, k0, lane);
-                    const bf16x8 sh = frag<LDK>(sSTh, 16 * cj, k0, lane);
-                    const bf16x8 sl = frag<LDK>(sSTl, 16 * cj, k0, lane);
-                    if constexpr (MODE == 1) {
-                        const bf16x8 ql = frag<LDK>(sQl, 16 * ri, k0, lane);
-                        a2 = mfma16(ql, sh, a2);
-                    }
-                    a2 = mfma16(qh, sl, a2);
-                    a2 = mfma16(qh, sh, a2);
-                }
-                const int j = v0 + 16 * cj + (lane & 15);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * ri + 4 * (lane >> 4) + r;
-                    const float y = MODE == 0 ? a1[r] + __expf(sG[t]) * a2[r] : a1[r] + a2[r];
-                    if (t0 + t < T && j < V)
-                        p.o[((b * T + t0 + t) * H + h) * static_cast<int64_t>(V) + j] = p.scale * y;
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < S_PER_WAVE; ++m) {
-                const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-                f32x4 ds = zero4();
-#pragma unroll
-                for (int ks = 0; ks < L / 32; ++ks) {
-                    const bf16x8 kh = frag<LDL>(sKh, 16 * sr, 32 * ks, lane);
-                    const bf16x8 kl = frag<LDL>(sKl, 16 * sr, 32 * ks, lane);
-                    const bf16x8 vb = frag<LDL>(sVT, 16 * sc, 32 * ks, lane);
-                    ds = mfma16(kl, vb, ds);
-                    ds = mfma16(kh, vb, ds);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int d = 16 * sr + 4 * (lane >> 4) + r;
-                    const float decay = MODE == 1 ? __expf(sGL[d]) : __expf(sGL[0]);
-                    S[m][r] = decay * S[m][r] + ds[r];
-                }
-            }
-        }
-        __syncthreads();
-        write_state_lds();   // S^T for the next chunk's readout
-
-        if (c + 1 < nchunks) {
-#pragma unroll
-            for (int i = 0; i < PQ; ++i) { cq[i] = nq[i]; ck[i] = nk[i]; }
-#pragma unroll
-            for (int i = 0; i < PV; ++i) cv[i] = nv[i];
+        if constexpr (OUT) {
+            // per-key decay reads out from e^{G_L} o S0 (and the update then adds to it)
             if constexpr (MODE == 1) {
+                if (fast) {
 #pragma unroll
-                for (int r = 0; r < RPG; ++r)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) cg[r][e] = ng[r][e];
+                    for (int db = 0; db < KB; ++db) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(sEGL + 16 * db + 4 * g4);
+                        S[db] *= a;
+                    }
+                }
             }
-            cgs = ngs;
-            ckap = nkap;
+            bf16x8 sh[KM], sl[KM];
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+                const float x[8] = {S[2 * m][0],     S[2 * m][1],     S[2 * m][2],     S[2 * m][3],
+                                    S[2 * m + 1][0], S[2 * m + 1][1], S[2 * m + 1][2], S[2 * m + 1][3]};
+                split8(x, sh[m], sl[m]);
+            }
+            f32x4 acc[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) acc[tb] = zero4();
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const u16* qrow = sQ + (16 * tb + c16) * LDK + 4 * g4 + 32 * m;
+                    const bf16x8 qh = slot_frag(qrow);
+                    acc[tb] = mfma16(sl[m], qh, acc[tb]);
+                    acc[tb] = mfma16(sh[m], qh, acc[tb]);
+                    if constexpr (MODE == 1) acc[tb] = mfma16(sh[m], slot_frag(qrow + L * LDK), acc[tb]);
+                }
+            }
+            if constexpr (MODE == 0) {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[tb] *= sEG[16 * tb + c16];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+                for (int tb = 2 * ks; tb < 4; ++tb) {
+                    const u16* prow = sP + (16 * tb + c16) * LDP + 4 * g4 + 32 * ks;
+                    acc[tb] = mfma16(vA[ks], slot_frag(prow + L * LDP), acc[tb]);
+                    acc[tb] = mfma16(vA[ks], slot_frag(prow), acc[tb]);
+                }
+            }
+            // acc[tb]: rows = columns v0 + 16 wave + 4 g4 + r, column = step t0 + 16 tb + c16
+            if constexpr (VEC) {
+                const BufRes wo = make_rsrc_window(ob, T * o_row, t0 * o_row);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+                    buf_store16(__builtin_bit_cast(u32x4, acc[tb]), wo,
+                                offo == kBufOOB ? kBufOOB : offo + tb * 16 * static_cast<int>(o_row));
+            } else {
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    const int64_t t = t0 + 16 * tb + c16;
+                    const int col = v0 + 16 * wave + 4 * g4;
+                    if (t < T) {
+                        float* dst = ob + t * H * static_cast<int64_t>(V) + h * static_cast<int64_t>(V) + col;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (col + r < V) dst[r] = acc[tb][r];
+                    }
+                }
+            }
         }
+
+        // state update: S = e^{G_L} o S + K~^T V~
+        if constexpr (MODE == 0) {
+            const float a = sDec[0];
+#pragma unroll
+            for (int db = 0; db < KB; ++db) S[db] *= a;
+        } else {
+            if (AGG || !fast) {
+#pragma unroll
+                for (int db = 0; db < KB; ++db) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(sEGL + 16 * db + 4 * g4);
+                    S[db] *= a;
+                }
+            }
+        }
+        bf16x8 wBh[2], wBl[2];
+        if constexpr (MODE == 0) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(sW + 32 * ks + 4 * g4);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(sW + 32 * ks + 16 + 4 * g4);
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(vA[ks][e]) * (e < 4 ? w0[e & 3] : w1[e & 3]);
+                split8(x, wBh[ks], wBl[ks]);
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int db = 0; db < KB; ++db) {
+                const bf16x8 kh = tr_frag<LDK>(sK, 32 * ks, 16 * db, lane);
+                if constexpr (MODE == 0) {
+                    S[db] = mfma16(kh, wBl[ks], S[db]);
+                    S[db] = mfma16(kh, wBh[ks], S[db]);
+                } else {
+                    const bf16x8 kl = tr_frag<LDK>(sK + L * LDK, 32 * ks, 16 * db, lane);
+                    S[db] = mfma16(kl, vA[ks], S[db]);
+                    S[db] = mfma16(kh, vA[ks], S[db]);
+                }
+            }
+        }
+        __syncthreads();   // LDS operands are restaged by the next chunk
     }
 
-    // ---- epilogue: final state ----
+    // ---- epilogue ----
+    if constexpr (AGG) {
+        const int units = p.B * H * p.vtiles;
+        float* ub = p.agg_u + ((static_cast<int64_t>(seg) * units + rest) * 4 + wave) * (KB * 256);
 #pragma unroll
-    for (int m = 0; m < S_PER_WAVE; ++m) {
-        const int s = wave * S_PER_WAVE + m, sr = s / VTT, sc = s % VTT;
-        const int j = v0 + 16 * sc + (lane & 15);
+        for (int db = 0; db < KB; ++db) *reinterpret_cast<f32x4*>(ub + (db * 64 + lane) * 4) = S[db];
+        if (vt == 0 && tid < KP) p.agg_a[(static_cast<int64_t>(seg) * p.B * H + bh) * KP + tid] = __expf(lsum);
+    } else {
+        if (seg == p.nseg - 1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d = 16 * sr + 4 * (lane >> 4) + r;
-            if (d < K && j < V) p.s_final[((static_cast<int64_t>(b) * H + h) * K + d) * V + j] = S[m][r];
+            for (int db = 0; db < KB; ++db) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int d = 16 * db + 4 * g4 + r;
+                    if (d < K && jcol < V)
+                        p.s_final[((static_cast<int64_t>(b) * H + h) * K + d) * V + jcol] = S[db][r];
+                }
+            }
         }
     }
 }
 
-template <int MODE, int KP, int VT>
-hipError_t launch_t(const DiagArgs& a, hipStream_t stream) {
-    const int64_t grid = static_cast<int64_t>(a.B) * a.H * a.vtiles;
-    if (a.vec) {
-        hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, VT, true>), dim3(static_cast<unsigned>(grid)),
-                           dim3(NT), 0, stream, a);
-    } else {
-        hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, VT, false>), dim3(static_cast<unsigned>(grid)),
-                           dim3(NT), 0, stream, a);
+template <int MODE, int KP>
+hipError_t launch_t(const DiagArgs& a, bool vec, hipStream_t stream) {
+    const int64_t units = static_cast<int64_t>(a.B) * a.H * a.vtiles;
+    if (a.nseg > 1) {
+        const dim3 grid(static_cast<unsigned>(units * (a.nseg - 1)));
+        if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, true, true>), grid, dim3(NT), 0, stream, a);
+        else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, false, true>), grid, dim3(NT), 0, stream, a);
     }
+    const dim3 grid(static_cast<unsigned>(units * a.nseg));
+    if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, true, false>), grid, dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, false, false>), grid, dim3(NT), 0, stream, a);
     return hipGetLastError();
+}
+
+// Output-pass workgroups that fit on one compute unit at once (LDS and
+// registers), measured once per kernel variant.
+template <int MODE, int KP, bool VEC>
+int resident_blocks() {
+    static int n = 0;
+    if (n == 0) {
+        int m = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, diag_outer_kernel<MODE, KP, VEC, false>, NT, 0) !=
+                hipSuccess || m < 1)
+            m = 1;
+        n = m;
+    }
+    return n;
+}
+
+int resident_blocks(int decay_mode, int K, bool vec) {
+    if (decay_mode == 0) {
+        if (K <= 64) return vec ? resident_blocks<0, 64, true>() : resident_blocks<0, 64, false>();
+        return vec ? resident_blocks<0, 128, true>() : resident_blocks<0, 128, false>();
+    }
+    if (K <= 64) return vec ? resident_blocks<1, 64, true>() : resident_blocks<1, 64, false>();
+    return vec ? resident_blocks<1, 128, true>() : resident_blocks<1, 128, false>();
 }
 
 }  // namespace
 
-int diag_outer_vtile(int decay_mode) { return decay_mode == 0 ? 64 : 32; }
+int diag_outer_vtile() { return VT; }
 
-hipError_t launch_scan_diag_outer(const DiagParams& prm, hipStream_t stream) {
+DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool vec, int num_cus,
+                         int requested_segments) {
+    DiagPlan pl{};
+    pl.nchunks = (T + L - 1) / L;
+    pl.vtiles = (V + VT - 1) / VT;
+    const int64_t units = static_cast<int64_t>(B) * H * pl.vtiles;
+    int64_t nseg = requested_segments;
+    if (nseg <= 0) {
+        // as many segments as keep every resident slot of the chip busy in one round
+        const int64_t slots = static_cast<int64_t>(num_cus) * resident_blocks(decay_mode, K, vec);
+        nseg = slots / units;
+    }
+    if (nseg > pl.nchunks) nseg = pl.nchunks;
+    if (nseg < 1) nseg = 1;
+    pl.cps = static_cast<int>((pl.nchunks + nseg - 1) / nseg);
+    pl.nseg = (pl.nchunks + pl.cps - 1) / pl.cps;
+    return pl;
+}
+
+size_t diag_outer_workspace_bytes(int B, int H, int K, int V, int nseg) {
+    if (nseg <= 1) return 0;
+    const size_t kp = K <= 64 ? 64 : 128, vtiles = (static_cast<size_t>(V) + VT - 1) / VT;
+    return static_cast<size_t>(nseg - 1) * B * H * (vtiles * kp * VT + kp) * sizeof(float);
+}
+
+hipError_t launch_scan_diag_outer(const DiagParams& prm, const DiagPlan& pl, void* workspace, hipStream_t stream) {
     DiagArgs a{};
     a.q = reinterpret_cast<const u16*>(prm.q);
     a.k = reinterpret_cast<const u16*>(prm.k);
@@ -550,14 +777,19 @@ hipError_t launch_scan_diag_outer(const DiagParams& prm, hipStream_t stream) {
     a.K = prm.K;
     a.V = prm.V;
     a.scale = prm.scale;
-    const int vtw = diag_outer_vtile(prm.decay_mode);
-    a.vtiles = (prm.V + vtw - 1) / vtw;
-    a.vec = prm.vec;
-    const bool k64 = prm.K <= 64;
-    if (prm.decay_mode == 0) {
-        return k64 ? launch_t<0, 64, 64>(a, stream) : launch_t<0, 128, 64>(a, stream);
+    a.vtiles = pl.vtiles;
+    a.nchunks = pl.nchunks;
+    a.nseg = pl.nseg;
+    a.cps = pl.cps;
+    if (pl.nseg > 1) {
+        a.agg_u = static_cast<float*>(workspace);
+        const size_t kp = prm.K <= 64 ? 64 : 128;
+        a.agg_a = a.agg_u + static_cast<size_t>(pl.nseg - 1) * prm.B * prm.H * pl.vtiles * kp * VT;
     }
-    return k64 ? launch_t<1, 64, 32>(a, stream) : launch_t<1, 128, 32>(a, stream);
+    const bool vec = prm.vec != 0;
+    const bool k64 = prm.K <= 64;
+    if (prm.decay_mode == 0) return k64 ? launch_t<0, 64>(a, vec, stream) : launch_t<0, 128>(a, vec, stream);
+    return k64 ? launch_t<1, 64>(a, vec, stream) : launch_t<1, 128>(a, vec, stream);
 }
 
 }  // namespace lrs

@@ -105,16 +105,47 @@ def test_key_decay_with_k_scale_and_groups(ctx):
     _check(ctx, d, inputs.random_state((B, H, K, V), 3))
 
 
+class _Segments:
+    """Sets LRS_PARAM_DIAG_SEGMENTS for a block and restores the default."""
+
+    def __init__(self, ctx, n):
+        self.ctx, self.n = ctx, n
+
+    def __enter__(self):
+        binding.lrs_context_set_param(self.ctx, binding.LRS_PARAM_DIAG_SEGMENTS, self.n)
+
+    def __exit__(self, *exc):
+        binding.lrs_context_set_param(self.ctx, binding.LRS_PARAM_DIAG_SEGMENTS, 0)
+
+
+@pytest.mark.parametrize("segments", [0, 1])
 @pytest.mark.parametrize("gval", [-1.5, -4.0])
-def test_key_decay_strong_gates_exact_fallback(ctx, gval):
+def test_key_decay_strong_gates_exact_fallback(ctx, gval, segments):
     # chunk decay of 64 * |g| nats exceeds the factorised path's range: the
     # kernel must switch to per-pair exponentials and stay accurate
     B, T, H, K, V = 1, 200, 2, 128, 64
     d = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=31)
     rng = np.random.default_rng(32)
     d["g"] = torch.from_numpy((gval * rng.uniform(0.5, 1.0, (B, T, H, K))).astype(np.float32))
-    say(f"diag strong gates g~{gval}")
-    _check(ctx, d, inputs.random_state((B, H, K, V), 4))
+    say(f"diag strong gates g~{gval} segments={segments}")
+    with _Segments(ctx, segments):
+        _check(ctx, d, inputs.random_state((B, H, K, V), 4))
+
+
+@pytest.mark.parametrize("segments", [1, 2, 3, 7, 0])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_time_segments(ctx, mode, segments):
+    # each segment starts from s0 folded through the (decay product, state
+    # contribution) pairs of the segments before it; any count must agree
+    # with the sequential oracle, including segments of unequal length
+    B, T, H, K, V = 2, 650, 2, 128, 64
+    if mode == 0:
+        d = _mamba(B, T, H, K, V, seed=61)
+    else:
+        d = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=62)
+    say(f"diag mode{mode} segments={segments}")
+    with _Segments(ctx, segments):
+        _check(ctx, d, inputs.random_state((B, H, K, V), 8))
 
 
 def test_scalar_decay_strong_gates(ctx):

@@ -130,7 +130,7 @@ def main():
     achieved = nbytes / (ms_kernel * 1e-3) / 1e9
     traffic = measured_traffic("scan_elem_gated_B16_T8192_N2048", "scan_elem.hip")
     line = {
-        "metric": "gated elementwise scan throughput (algorithmic HBM GB/s)",
+        "metric": "scan throughput: GB/s & % HBM peak (elementwise); tokens/s·head & MFMA util",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -281,9 +281,10 @@ def run_rows(ctx, args, binding, inputs, dev):
     specs = [
         ("scan_diag_outer Mamba-2 B=8 T=4096 H=24 P=64 N=128 (scalar decay, 1 group)", "diag",
          lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}),
-         ["diag_outer_mamba2_B8_T4096_H24_P64_N128"]),
+         ["diag_outer_agg_mamba2_B8_T4096_H24_P64_N128", "diag_outer_out_mamba2_B8_T4096_H24_P64_N128"]),
         ("scan_diag_outer GLA B=4 T=4096 H=4 K=128 V=128 (per-key decay)", "diag",
-         lambda: inputs.gla(**inputs.GLA), ["diag_outer_gla_B4_T4096_H4_K128_V128"]),
+         lambda: inputs.gla(**inputs.GLA),
+         ["diag_outer_agg_gla_B4_T4096_H4_K128_V128", "diag_outer_out_gla_B4_T4096_H4_K128_V128"]),
         ("scan_delta DeltaNet B=4 T=4096 H=8 K=128 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET),
          ["delta_prep_deltanet_B4_T4096_H8_K128", "delta_scan_deltanet_B4_T4096_H8_K128_V128"]),
         ("scan_delta DeltaNet B=4 T=4096 H=8 K=64 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET_K64),

@@ -34,6 +34,9 @@ __device__ __forceinline__ void split_bf16(float x, u16& hi, u16& lo) {
     lo = f2bf(x - bf2f(hi));
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -58,6 +61,33 @@ __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& 
 template <int LD>
 __device__ __forceinline__ bf16x8 frag(const u16* base, int r0, int k0, int lane) {
     return *reinterpret_cast<const bf16x8*>(base + (r0 + (lane & 15)) * LD + k0 + 8 * (lane >> 4));
+}
+
+// The contraction index of a 16x16x32 product may be permuted as long as both
+// operands agree.  "Slot" operands give lane group g the contraction indices
+// {k0 + 4g .. k0 + 4g + 3} u {k0 + 16 + 4g .. k0 + 16 + 4g + 3}: exactly what
+// two 16x16 accumulator tiles hold in rows 4g .. 4g + 3, so accumulators can
+// feed the next product without leaving their registers.
+
+// Slot operand from a row-major array: row `rowp` at column k0 + 4g (the
+// caller adds k0 + 4g), two 8-byte LDS reads.
+__device__ __forceinline__ bf16x8 slot_frag(const u16* rowp) {
+    const u32x2 a = *reinterpret_cast<const u32x2*>(rowp);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(rowp + 16);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
+// Transposed slot operand from a row-major [k][n] bf16 array in LDS: lane j of
+// 16-lane group g receives M[k0 .. k0+3][n0 + j] and M[k0+16 .. k0+19][n0 + j]
+// with k0 = kb + 4g (ds_read_b64_tr_b16: lane i of a group supplies row
+// k0 + i/4, columns n0 + 4(i%4)).
+template <int LD>
+__device__ __forceinline__ bf16x8 tr_frag(const u16* m, int kb, int n0, int lane) {
+    const int i16 = lane & 15, k0 = kb + 4 * (lane >> 4);
+    const u16* pa = m + (k0 + (i16 >> 2)) * LD + n0 + 4 * (i16 & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 16 * LD));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -45,8 +45,6 @@ constexpr int PLANE = L * L;   // elements of one 64 x 64 bf16 plane
 constexpr int NPLANES = 4;     // per chunk: Tb hi, Tb lo, MTb hi, MTb lo
 constexpr int VT = 16;         // V-tile width of the scan kernel
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 struct DeltaArgs {
     const u16* q;
@@ -89,7 +87,6 @@ __device__ __forceinline__ void mtb_job(int wave, int q, int& i, int& j) {
 }
 
 __device__ __forceinline__ void store4(u16* dst, u16 a, u16 b, u16 c, u16 d) {
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     u32x2 w = {a | (static_cast<uint32_t>(b) << 16), c | (static_cast<uint32_t>(d) << 16)};
     *reinterpret_cast<u32x2*>(dst) = w;
 }
@@ -310,17 +307,42 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
 // ---------------------------------------------------------------------------
 // scan: sequential over chunks per (batch, head, 16-wide V-tile)
 // ---------------------------------------------------------------------------
+// Byte offset of 16-byte piece `p` of row `r` in a row-major tile whose rows
+// hold PPR pieces, with the pieces of each row rotated by an XOR of the row
+// index: 16 consecutive rows read at one column then hit different banks.
+template <int PPR>
+__device__ __forceinline__ int swz(int r, int p) {
+    return r * (PPR * 16) + ((p ^ (r & (PPR - 1))) << 4);
+}
+
+// Wave w owns chunk rows 16w .. 16w+15 (Y, R, Delta, outputs) and state keys
+// 16 STW w .. (row tiles of S).  The chunk's q, k, Tb / MTb planes and V tile
+// are fetched one chunk ahead straight into LDS (buffer loads with an LDS
+// destination: whole 1 KB runs per instruction, no registers held), double
+// buffered by chunk parity, into swizzled tiles read as matrix-core operands.
+// Per chunk, three barriers:
+//   -- inputs of chunk c visible --
+//   1. Y = K S0, O1 = Q S0 (rows of this wave); R = V - Y -> LDS
+//   -- barrier --
+//   2. Delta = Tb R, O = scale (O1 + MTb R) -> outputs; Delta -> LDS
+//   -- barrier --
+//   3. S += K^T Delta (tiles of this wave) -> LDS as the next chunk's operand
 template <int KP, bool VEC>
 __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
+    constexpr int PPR = KP / 8;          // 16-byte pieces per q / k row
+    constexpr int QB = L * KP * 2;       // bytes of a q or k tile
+    constexpr int PB = L * L * 2;        // bytes of a Tb / MTb plane
+    constexpr int VB = L * VT * 2;       // bytes of the V tile
+    constexpr int STAGE = 2 * QB + 4 * PB + VB;
+    constexpr int OFF_K = QB, OFF_P = 2 * QB, OFF_V = 2 * QB + 4 * PB;
     constexpr int LDK = KP + 8;
     constexpr int LDL = L + 8;
-    constexpr int LDV = VT + 8;
     constexpr int KS = KP / 32;          // k-steps over the key dimension
     constexpr int STW = KP / 16 / 4;     // state row tiles per wave
     static_assert(STW >= 1, "state tiles");
+    static_assert(QB % 1024 == 0 && PB % 1024 == 0 && VB == 2048, "1 KB load runs");
 
-    __shared__ __align__(16) u16 sK[L * LDK];        // K of the chunk, row-major
-    __shared__ __align__(16) u16 sV[L * LDV];        // V tile, row-major
+    __shared__ __align__(16) unsigned char sIn[2 * STAGE];
     __shared__ __align__(16) u16 sRTh[VT * LDL];     // R^T hi/lo
     __shared__ __align__(16) u16 sRTl[VT * LDL];
     __shared__ __align__(16) u16 sDTh[VT * LDL];     // Delta^T hi/lo
@@ -339,45 +361,78 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     const int K = p.K, V = p.V, H = p.H;
     const int nchunks = p.nchunks;
 
-    const int64_t qk_row = static_cast<int64_t>(H) * K, v_row = static_cast<int64_t>(H) * V;
-    const BufRes rq = make_rsrc(p.q + b * T * qk_row, T * qk_row * 2);
-    const BufRes rk = make_rsrc(p.k + b * T * qk_row, T * qk_row * 2);
-    const BufRes rv = make_rsrc(p.v + b * T * v_row, T * v_row * 2);
+    const int64_t qk_row = static_cast<int64_t>(H) * K * 2, v_row = static_cast<int64_t>(H) * V * 2;   // bytes per step
+    const u16* qb = p.q + b * T * H * static_cast<int64_t>(K);
+    const u16* kb = p.k + b * T * H * static_cast<int64_t>(K);
+    const u16* vb = p.v + b * T * H * static_cast<int64_t>(V);
     const u16* wsb = p.ws + static_cast<int64_t>(bh) * nchunks * NPLANES * PLANE;
-    const BufRes rw = make_rsrc(wsb, static_cast<int64_t>(nchunks) * NPLANES * PLANE * 2);
 
-    // operand rows of this wave: t = 16 * wave + c16; columns 32 ks + 8 g
-    const int arow = 16 * wave + c16;
-    u32x4 qf[KS], kf[KS], tf[2][2], mf[2][2], vf;
-    u32x4 nqf[KS], nkf[KS], ntf[2][2], nmf[2][2], nvf;
-    auto load_chunk = [&](int c, u32x4 (&Q)[KS], u32x4 (&Kx)[KS], u32x4 (&Tb)[2][2], u32x4 (&Mb)[2][2],
-                          u32x4& Vx) {
-        const int64_t t = static_cast<int64_t>(c) * L + arow;
-        const int64_t goff = ((b * T + t) * H + h) * static_cast<int64_t>(K);
+    // ---- fetch of one chunk's inputs into stage `buf` ----
+    // Load run i (64 lanes x 16 bytes) fills bytes 1024 i .. of a tile: lane l
+    // takes slot s = 64 i + l, i.e. row s / PPR, stored piece s % PPR, which
+    // holds the row's piece (s % PPR) ^ (row & (PPR - 1)).
+    auto fetch = [&](int c, int buf) {
+        unsigned char* st = sIn + buf * STAGE;
+        const int64_t t0 = static_cast<int64_t>(c) * L;
+        if constexpr (VEC) {
+            const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
+            const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
+            const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
+            const BufRes wp = make_rsrc_window(wsb, static_cast<int64_t>(nchunks) * NPLANES * PLANE * 2,
+                                               static_cast<int64_t>(c) * NPLANES * PLANE * 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c8 = 32 * ks + 8 * g;
-            const int off = ((static_cast<int>(t) * H + h) * K + c8) * 2;
-            Q[ks] = load_piece<VEC>(rq, p.q + goff, off, c8, K, t < T);
-            Kx[ks] = load_piece<VEC>(rk, p.k + goff, off, c8, K, t < T);
-        }
-        const int pbase = c * NPLANES * PLANE;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int e = arow * L + 32 * ks + 8 * g;
-#pragma unroll
-            for (int pl = 0; pl < 2; ++pl) {
-                Tb[ks][pl] = buf_load16(rw, (pbase + pl * PLANE + e) * 2);
-                Mb[ks][pl] = buf_load16(rw, (pbase + (2 + pl) * PLANE + e) * 2);
+            for (int j = 0; j < QB / 1024 / 4; ++j) {
+                const int i = wave + 4 * j, sl = 64 * i + lane;
+                const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
+                const int off = col < K ? ((row * H + h) * K + col) * 2 : kBufOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wq, (__attribute__((address_space(3))) void*)(st + 1024 * i),
+                                                         16, off, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wk, (__attribute__((address_space(3))) void*)(st + OFF_K + 1024 * i), 16, off, 0, 0, 0);
             }
-        }
-        Vx = u32x4{0u, 0u, 0u, 0u};
-        if (tid < L * VT / 8) {
-            const int vr = tid / (VT / 8), c8 = (tid % (VT / 8)) * 8;
-            const int64_t tv = static_cast<int64_t>(c) * L + vr;
-            const int off = ((static_cast<int>(tv) * H + h) * V + v0 + c8) * 2;
-            Vx = load_piece<VEC>(rv, p.v + ((b * T + tv) * H + h) * static_cast<int64_t>(V) + v0, off, c8,
-                                 V - v0, tv < T);
+#pragma unroll
+            for (int j = 0; j < 4 * PB / 1024 / 4; ++j) {
+                const int i = wave + 4 * j;                 // run over the four planes
+                const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
+                const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
+                const int off = (pl * PLANE + row * L + col) * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wp, (__attribute__((address_space(3))) void*)(st + OFF_P + 1024 * i), 16, off, 0, 0, 0);
+            }
+            if (wave < 2) {
+                const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
+                const int off = v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wv, (__attribute__((address_space(3))) void*)(st + OFF_V + 1024 * wave), 16, off, 0, 0, 0);
+            }
+        } else {
+            // same slots, filled through registers (odd sizes or alignment)
+            for (int sl = tid; sl < L * PPR; sl += NT) {
+                const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
+                const int64_t t = t0 + row;
+                u32x4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
+                if (t < T) {
+                    const int64_t o = (t * H + h) * static_cast<int64_t>(K);
+                    xq = load8_bf16(qb + o, col, K, false);
+                    xk = load8_bf16(kb + o, col, K, false);
+                }
+                *reinterpret_cast<u32x4*>(st + 16 * sl) = xq;
+                *reinterpret_cast<u32x4*>(st + OFF_K + 16 * sl) = xk;
+            }
+            const u16* pw = wsb + static_cast<int64_t>(c) * NPLANES * PLANE;
+            for (int sl = tid; sl < 4 * L * 8; sl += NT) {
+                const int pl = sl / (L * 8), s2 = sl % (L * 8);
+                const int row = s2 / 8, col = ((s2 % 8) ^ (row & 7)) * 8;
+                *reinterpret_cast<u32x4*>(st + OFF_P + 16 * sl) =
+                    *reinterpret_cast<const u32x4*>(pw + pl * PLANE + row * L + col);
+            }
+            if (tid < L * 2) {
+                const int row = tid / 2, col = ((tid % 2) ^ (row & 1)) * 8;
+                const int64_t t = t0 + row;
+                u32x4 xv = {0u, 0u, 0u, 0u};
+                if (t < T) xv = load8_bf16(vb + (t * H + h) * static_cast<int64_t>(V) + v0, col, V - v0, false);
+                *reinterpret_cast<u32x4*>(st + OFF_V + 16 * tid) = xv;
+            }
         }
     };
 
@@ -399,59 +454,66 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
 #pragma unroll
         for (int st = 0; st < STW; ++st) {
             const int d = 16 * (STW * wave + st) + 4 * g;
-            u16 hi[4], lo[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) split_bf16(S[st][r], hi[r], lo[r]);
-            store4(sSh + c16 * LDK + d, hi[0], hi[1], hi[2], hi[3]);
-            store4(sSl + c16 * LDK + d, lo[0], lo[1], lo[2], lo[3]);
+            uint32_t hi[2], lo[2];
+            split2(S[st][0], S[st][1], hi[0], lo[0]);
+            split2(S[st][2], S[st][3], hi[1], lo[1]);
+            *reinterpret_cast<u32x2*>(sSh + c16 * LDK + d) = u32x2{hi[0], hi[1]};
+            *reinterpret_cast<u32x2*>(sSl + c16 * LDK + d) = u32x2{lo[0], lo[1]};
         }
     };
     write_state_lds();
-    load_chunk(0, qf, kf, tf, mf, vf);
+    fetch(0, 0);
 
+    const int arow = 16 * wave + c16;    // operand row of this wave
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
-        // ---- P0: K (row-major) and the V tile into LDS ----
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            *reinterpret_cast<u32x4*>(sK + arow * LDK + 32 * ks + 8 * g) = kf[ks];
-        if (tid < L * VT / 8)
-            *reinterpret_cast<u32x4*>(sV + (tid / (VT / 8)) * LDV + (tid % (VT / 8)) * 8) = vf;
-        __syncthreads();
-        if (c + 1 < nchunks) load_chunk(c + 1, nqf, nkf, ntf, nmf, nvf);
+        const unsigned char* st = sIn + (c & 1) * STAGE;
+        if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads into LDS are done
+        __syncthreads();                                         // ... and every wave's
+        if (c + 1 < nchunks) fetch(c + 1, (c + 1) & 1);
 
-        // ---- P1: Y = K S0, O1 = Q S0 (row block = wave), R = V - Y ----
+        // ---- 1: Y = K S0, O1 = Q S0 (row block = wave), R = V - Y ----
         f32x4 y = zero4(), o1 = zero4();
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 sh = frag<LDK>(sSh, 0, 32 * ks, lane);
             const bf16x8 sl = frag<LDK>(sSl, 0, 32 * ks, lane);
-            const bf16x8 ka = as_bf16x8(kf[ks]);
-            const bf16x8 qa = as_bf16x8(qf[ks]);
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + OFF_K + swz<PPR>(arow, 4 * ks + g));
+            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st + swz<PPR>(arow, 4 * ks + g));
             y = mfma16(ka, sl, y);
             y = mfma16(ka, sh, y);
             o1 = mfma16(qa, sl, o1);
             o1 = mfma16(qa, sh, o1);
         }
         {
-            const int t = 16 * wave + 4 * g;
-            u16 hi[4], lo[4];
+            // V rows 16 wave + 4g .. +3 at column c16, by the transposing read
+            const int vr = 16 * wave + 4 * g + (c16 >> 2), vc = 4 * (c16 & 3);
+            const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(st + OFF_V + swz<2>(vr, vc >> 3) + (vc & 4) * 2));
+            float rr[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) split_bf16(bf2f(sV[(t + r) * LDV + c16]) - y[r], hi[r], lo[r]);
-            store4(sRTh + c16 * LDL + t, hi[0], hi[1], hi[2], hi[3]);
-            store4(sRTl + c16 * LDL + t, lo[0], lo[1], lo[2], lo[3]);
+            for (int r = 0; r < 4; ++r) rr[r] = bf2f(static_cast<u16>(v4[r])) - y[r];
+            uint32_t hi[2], lo[2];
+            split2(rr[0], rr[1], hi[0], lo[0]);
+            split2(rr[2], rr[3], hi[1], lo[1]);
+            const int t = 16 * wave + 4 * g;
+            *reinterpret_cast<u32x2*>(sRTh + c16 * LDL + t) = u32x2{hi[0], hi[1]};
+            *reinterpret_cast<u32x2*>(sRTl + c16 * LDL + t) = u32x2{lo[0], lo[1]};
         }
         __syncthreads();
 
-        // ---- P2: Delta = Tb R, O = scale (O1 + MTb R) ----
+        // ---- 2: Delta = Tb R, O = scale (O1 + MTb R) ----
         f32x4 dl = zero4(), o2 = zero4();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks <= wave / 2) {   // Tb and MTb are lower triangular
                 const bf16x8 rh = frag<LDL>(sRTh, 0, 32 * ks, lane);
                 const bf16x8 rl = frag<LDL>(sRTl, 0, 32 * ks, lane);
-                const bf16x8 th = as_bf16x8(tf[ks][0]), tl = as_bf16x8(tf[ks][1]);
-                const bf16x8 mh = as_bf16x8(mf[ks][0]), ml = as_bf16x8(mf[ks][1]);
+                const int po = swz<8>(arow, 4 * ks + g);
+                const bf16x8 th = *reinterpret_cast<const bf16x8*>(st + OFF_P + po);
+                const bf16x8 tl = *reinterpret_cast<const bf16x8*>(st + OFF_P + PB + po);
+                const bf16x8 mh = *reinterpret_cast<const bf16x8*>(st + OFF_P + 2 * PB + po);
+                const bf16x8 ml = *reinterpret_cast<const bf16x8*>(st + OFF_P + 3 * PB + po);
                 dl = mfma16(tl, rh, dl);
                 dl = mfma16(th, rl, dl);
                 dl = mfma16(th, rh, dl);
@@ -467,66 +529,51 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             for (int r = 0; r < 4; ++r)
                 if (t0 + t + r < T && j < V)
                     p.o[((b * T + t0 + t + r) * H + h) * static_cast<int64_t>(V) + j] = p.scale * (o1[r] + o2[r]);
-            u16 hi[4], lo[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) split_bf16(dl[r], hi[r], lo[r]);
-            store4(sDTh + c16 * LDL + t, hi[0], hi[1], hi[2], hi[3]);
-            store4(sDTl + c16 * LDL + t, lo[0], lo[1], lo[2], lo[3]);
+            uint32_t hi[2], lo[2];
+            split2(dl[0], dl[1], hi[0], lo[0]);
+            split2(dl[2], dl[3], hi[1], lo[1]);
+            *reinterpret_cast<u32x2*>(sDTh + c16 * LDL + t) = u32x2{hi[0], hi[1]};
+            *reinterpret_cast<u32x2*>(sDTl + c16 * LDL + t) = u32x2{lo[0], lo[1]};
         }
         __syncthreads();
 
-        // ---- P3: S += K^T Delta (K^T operands by transposing LDS reads) ----
+        // ---- 3: S += K^T Delta (K^T operands by transposing LDS reads) ----
         {
             const int i16 = lane & 15;
 #pragma unroll
-            for (int st = 0; st < STW; ++st) {
-                const int d0 = 16 * (STW * wave + st);
+            for (int s2 = 0; s2 < STW; ++s2) {
+                const int d0 = 16 * (STW * wave + s2);
+                const int col = d0 + 4 * (i16 & 3);
                 f32x4 ds = zero4();
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     // lane i of a 16-lane group supplies row tau0 + i/4, columns d0 + 4(i%4)..+3;
                     // lane j then holds K[tau0 .. tau0+3][d0 + j]
                     const int tau0 = 32 * ks + 8 * g + (i16 >> 2);
-                    const u16* a0 = sK + tau0 * LDK + d0 + 4 * (i16 & 3);
+                    const unsigned char* a0 = st + OFF_K + swz<PPR>(tau0, col >> 3) + (col & 4) * 2;
+                    const unsigned char* a1 = st + OFF_K + swz<PPR>(tau0 + 4, col >> 3) + (col & 4) * 2;
                     const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 4 * LDK));
+                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
                     const bf16x8 ka =
                         __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
                     ds = mfma16(ka, frag<LDL>(sDTl, 0, 32 * ks, lane), ds);
                     ds = mfma16(ka, frag<LDL>(sDTh, 0, 32 * ks, lane), ds);
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[st][r] += ds[r];
+                for (int r = 0; r < 4; ++r) S[s2][r] += ds[r];
             }
         }
         write_state_lds();
-        __syncthreads();   // sK, sV are rewritten by the next chunk; sS is read by it
-
-        if (c + 1 < nchunks) {
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qf[ks] = nqf[ks];
-                kf[ks] = nkf[ks];
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-                for (int pl = 0; pl < 2; ++pl) {
-                    tf[ks][pl] = ntf[ks][pl];
-                    mf[ks][pl] = nmf[ks][pl];
-                }
-            vf = nvf;
-        }
     }
 
 #pragma unroll
-    for (int st = 0; st < STW; ++st) {
-        const int sr = STW * wave + st;
+    for (int s2 = 0; s2 < STW; ++s2) {
+        const int sr = STW * wave + s2;
         const int j = v0 + c16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int d = 16 * sr + 4 * g + r;
-            if (d < K && j < V) p.s_final[((static_cast<int64_t>(b) * H + h) * K + d) * V + j] = S[st][r];
+            if (d < K && j < V) p.s_final[((static_cast<int64_t>(b) * H + h) * K + d) * V + j] = S[s2][r];
         }
     }
 }

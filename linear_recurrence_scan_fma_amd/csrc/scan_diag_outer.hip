@@ -28,10 +28,9 @@
 //   readout O^T = S^T Q^T (the state tiles are the left operand in place) plus
 //           V^T P^T, with V^T and K^T taken by the transposing LDS read;
 //   update  S = a (.) S + K~^T V~.
-// The contraction index of a 16x16x32 product may be permuted as long as both
-// operands agree; here lane group g holds k-slots {4g..4g+3} u {16+4g..16+4g+3}
-// of each 32-wide step, which is exactly what two 16x16 accumulator tiles
-// (rows 4g..4g+3 each) hold, so the state never leaves its registers.
+// With the contraction slots of mfma_util.h (lane group g holds {4g..4g+3} u
+// {16+4g..16+4g+3} of each 32-wide step), two accumulator tiles are exactly a
+// left operand, so the state never leaves its registers.
 //
 // Precision: q, k, v are bf16 and enter the matrix cores exactly; fp32 operands
 // (the state, P, decay-scaled keys or values) are split into hi + lo bf16 terms.
@@ -54,10 +53,6 @@ constexpr int L = 64;     // chunk length
 constexpr int NT = 256;   // threads per workgroup (4 waves)
 constexpr int VT = 64;    // V-tile width: 16 columns per wave
 constexpr float kFastPathMaxDecay = 60.0f;
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 struct DiagArgs {
     const u16* q;
@@ -85,25 +80,6 @@ __device__ __forceinline__ void store4(u16* dst, const u16 (&x)[4]) {
 __device__ __forceinline__ u16 half_elem(const u32x2& v, int e) {
     const uint32_t w = e < 2 ? v.x : v.y;
     return static_cast<u16>((e & 1) ? (w >> 16) : (w & 0xffff));
-}
-
-// Operand with k-slots {k0 .. k0+3} u {k0+16 .. k0+19} of row `row`: two 8-byte LDS reads.
-__device__ __forceinline__ bf16x8 slot_frag(const u16* rowp) {
-    const u32x2 a = *reinterpret_cast<const u32x2*>(rowp);
-    const u32x2 b = *reinterpret_cast<const u32x2*>(rowp + 16);
-    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
-}
-
-// Transposed operand from a row-major [k][n] bf16 array: lane j of 16-lane group
-// g receives M[k0 .. k0+3][n0 + j] and M[k0+16 .. k0+19][n0 + j] with k0 = kb + 4g
-// (ds_read_b64_tr_b16: lane i of a group supplies row k0 + i/4, columns n0 + 4(i%4)).
-template <int LD>
-__device__ __forceinline__ bf16x8 tr_frag(const u16* m, int kb, int n0, int lane) {
-    const int i16 = lane & 15, k0 = kb + 4 * (lane >> 4);
-    const u16* pa = m + (k0 + (i16 >> 2)) * LD + n0 + 4 * (i16 & 3);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(pa + 16 * LD));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Score blocks (key block, query block), key block <= query block, per wave:
@@ -228,7 +204,10 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
     u32x4 cv[PV];
     float cgs = 0.0f, ckap = 0.0f;
 
-    auto load_chunk = [&](int c) {
+    // part 0: q, k; part 1: v, g, kappa (vector path; the scalar path loads
+    // everything in part 0).  Two short bursts issued after two different
+    // barriers keep the memory queue from stalling a wave behind one long one.
+    auto load_chunk = [&](int c, int part) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
         if constexpr (VEC) {
             const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
@@ -237,28 +216,37 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
             const BufRes wg = make_rsrc_window(gb, T * g_row, t0 * g_row);
             const BufRes ws = make_rsrc_window(ksb ? static_cast<const void*>(ksb) : gb, ksb ? T * s_row : 0,
                                                t0 * s_row);
-            if constexpr (MODE == 0) {
+            if (part == 0) {
+                if constexpr (MODE == 0) {
 #pragma unroll
-                for (int i = 0; i < NQ; ++i) {
-                    if constexpr (OUT) cq[i] = buf_load16(wq, offq[i]);
-                    ck[i] = buf_load16(wk, offq[i]);
-                }
-                if (tid < L) {
-                    cgs = buf_load_f32(wg, offg[0]);
-                    ckap = buf_load_f32(ws, offg[0]);   // raw; NULL k_scale handled at use
+                    for (int i = 0; i < NQ; ++i) {
+                        if constexpr (OUT) cq[i] = buf_load16(wq, offq[i]);
+                        ck[i] = buf_load16(wk, offq[i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < NQ; ++r) {
+                        if constexpr (OUT) cq2[r] = __builtin_amdgcn_raw_buffer_load_b64(wq, offq[r], 0, 0);
+                        ck2[r] = __builtin_amdgcn_raw_buffer_load_b64(wk, offq[r], 0, 0);
+                    }
                 }
             } else {
+                if constexpr (MODE == 0) {
+                    if (tid < L) {
+                        cgs = buf_load_f32(wg, offg[0]);
+                        ckap = buf_load_f32(ws, offg[0]);   // raw; NULL k_scale handled at use
+                    }
+                } else {
 #pragma unroll
-                for (int r = 0; r < NQ; ++r) {
-                    if constexpr (OUT) cq2[r] = __builtin_amdgcn_raw_buffer_load_b64(wq, offq[r], 0, 0);
-                    ck2[r] = __builtin_amdgcn_raw_buffer_load_b64(wk, offq[r], 0, 0);
-                    cgv[r] = buf_load16(wg, offg[r]);
-                    ckp[r] = buf_load_f32(ws, offs[r]);   // raw; NULL k_scale handled at use
+                    for (int r = 0; r < NQ; ++r) {
+                        cgv[r] = buf_load16(wg, offg[r]);
+                        ckp[r] = buf_load_f32(ws, offs[r]);   // raw; NULL k_scale handled at use
+                    }
                 }
-            }
 #pragma unroll
-            for (int i = 0; i < PV; ++i) cv[i] = buf_load16(wv, offv[i]);
-        } else {
+                for (int i = 0; i < PV; ++i) cv[i] = buf_load16(wv, offv[i]);
+            }
+        } else if (part == 0) {
             if constexpr (MODE == 0) {
 #pragma unroll
                 for (int i = 0; i < NQ; ++i) {
@@ -370,7 +358,10 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
     }
     float lsum = 0.0f;   // segment log-decay (mode 0: uniform; mode 1: key `tid`)
 
-    if (c_begin < c_end) load_chunk(c_begin);
+    if (c_begin < c_end) {
+        load_chunk(c_begin, 0);
+        load_chunk(c_begin, 1);
+    }
 
     for (int c = c_begin; c < c_end; ++c) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
@@ -505,7 +496,7 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
         __syncthreads();
 
         // the prefetch registers were consumed by the staging: load the next chunk
-        if (c + 1 < c_end) load_chunk(c + 1);
+        if (c + 1 < c_end) load_chunk(c + 1, 0);
         if constexpr (AGG) {
             if constexpr (MODE == 0) lsum += sG[L - 1];
             else if (tid < KP) lsum += sGL[tid];
@@ -554,6 +545,7 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
             }
         }
         if constexpr (OUT) __syncthreads();
+        if (c + 1 < c_end) load_chunk(c + 1, 1);
 
         // ---- per wave: readout of its 16 columns and the state update ----
         bf16x8 vA[2];

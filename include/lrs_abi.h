@@ -134,7 +134,8 @@ void lrs_context_destroy(LrsContext* ctx);
  * the time axis into (each a run of 64-step chunks processed by its own
  * workgroups; a first pass reduces every segment but the last to a decay
  * product and a state contribution, kept in the context's workspace):
- *   0 (default)  as many as fill the device's resident workgroup slots once;
+ *   0 (default)  about two workgroups per resident workgroup slot of the
+ *                device, but at least 5 chunks (320 steps) per segment;
  *   n >= 1       n segments (capped at the number of chunks).
  * Any value gives results within the documented tolerance.
  * Errors: LRS_E_INVAL for a NULL context, unknown parameter or value. */

@@ -67,13 +67,13 @@ struct DiagParams {
 // Time-axis split of the diag-outer scan: chunks of 64 steps grouped into
 // segments; a segment count above one needs diag_outer_workspace_bytes().
 struct DiagPlan {
+    int waves;             // waves per workgroup (16 state columns each)
     int nchunks;
     int vtiles;
     int nseg;
     int cps;               // chunks per segment
 };
 
-int diag_outer_vtile();
 // requested_segments <= 0 picks as many segments as fill the chip's resident
 // workgroup slots once.
 DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool vec, int num_cus,

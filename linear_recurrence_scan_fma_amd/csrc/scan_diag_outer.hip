@@ -50,8 +50,11 @@ namespace lrs {
 namespace {
 
 constexpr int L = 64;     // chunk length
-constexpr int NT = 256;   // threads per workgroup (4 waves)
-constexpr int VT = 64;    // V-tile width: 16 columns per wave
+// A workgroup has WPB waves (4 or 8); wave w owns 16 state columns, so a
+// workgroup covers a V-tile of 16 WPB columns.  Heads wider than 64 columns use
+// 8 waves, so that the per-chunk staging and scores are shared by all columns.
+inline int waves_for(int V) { return V > 64 ? 8 : 4; }
+constexpr int kMinChunksPerSegment = 5;
 constexpr float kFastPathMaxDecay = 60.0f;
 
 struct DiagArgs {
@@ -100,11 +103,24 @@ __device__ __forceinline__ bool score_job(int wave, int n, int& kb, int& qb) {
     }
 }
 
+// Score blocks with 8 waves: block wave (and wave + 8) of the list
+// (0,0),(0,1),(0,2),(0,3),(1,1),(1,2),(1,3),(2,2),(2,3),(3,3).
+__device__ __forceinline__ bool score_job8(int wave, int n, int& kb, int& qb) {
+    const int idx = wave + 8 * n;
+    if (idx >= 10) return false;
+    kb = idx < 4 ? 0 : (idx < 7 ? 1 : (idx < 9 ? 2 : 3));
+    const int first = kb == 0 ? 0 : (kb == 1 ? 4 : (kb == 2 ? 7 : 9));
+    qb = kb + (idx - first);
+    return true;
+}
+
 // AGG = true: segment reduction (a_seg, U_seg) from a zero state, no outputs.
 // AGG = false: outputs and the final state, starting from the folded segment state.
-template <int MODE, int KP, bool VEC, bool AGG>
-__global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
+template <int MODE, int KP, int WPB, bool VEC, bool AGG>
+__global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     constexpr bool OUT = !AGG;
+    constexpr int NT = 64 * WPB;   // threads per workgroup
+    constexpr int VT = 16 * WPB;   // V-tile width
     constexpr int LDK = KP + 8;   // row stride of the [L][KP] bf16 operands
     constexpr int LDV = VT + 8;
     constexpr int LDP = L + 8;
@@ -335,7 +351,7 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
             }
 #pragma unroll 2
             for (int s2 = seg - 1; s2 >= 0; --s2) {
-                const float* ub = p.agg_u + ((static_cast<int64_t>(s2) * units + rest) * 4 + wave) * (KB * 256);
+                const float* ub = p.agg_u + ((static_cast<int64_t>(s2) * units + rest) * WPB + wave) * (KB * 256);
                 const float* ab = p.agg_a + (static_cast<int64_t>(s2) * p.B * H + bh) * KP;
 #pragma unroll
                 for (int db = 0; db < KB; ++db) {
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
             for (int db = 0; db < KB; ++db) S[db] = pr[db] * S[db] + acc[db];
         }
         // score blocks right of the diagonal that the readout reads: always zero
-        {
+        if (tid < 256) {
             const int blk = tid >> 7, plane = (tid >> 6) & 1, row = (tid >> 2) & 15, quad = tid & 3;
             const int t = 32 * blk + row, c0 = 32 * blk + 16 + 4 * quad;
             const u16 z[4] = {0, 0, 0, 0};
@@ -505,9 +521,9 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
         // ---- scores P (key block kb, query block qb) -> LDS as P[t][tau] ----
         if (OUT && fast) {
 #pragma unroll
-            for (int n = 0; n < 3; ++n) {
+            for (int n = 0; n < (WPB == 4 ? 3 : 2); ++n) {
                 int kb, qbk;
-                if (!score_job(wave, n, kb, qbk)) continue;
+                if (!(WPB == 4 ? score_job(wave, n, kb, qbk) : score_job8(wave, n, kb, qbk))) continue;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int ks = 0; ks < KM; ++ks) {
@@ -666,7 +682,7 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
     // ---- epilogue ----
     if constexpr (AGG) {
         const int units = p.B * H * p.vtiles;
-        float* ub = p.agg_u + ((static_cast<int64_t>(seg) * units + rest) * 4 + wave) * (KB * 256);
+        float* ub = p.agg_u + ((static_cast<int64_t>(seg) * units + rest) * WPB + wave) * (KB * 256);
 #pragma unroll
         for (int db = 0; db < KB; ++db) *reinterpret_cast<f32x4*>(ub + (db * 64 + lane) * 4) = S[db];
         if (vt == 0 && tid < KP) p.agg_a[(static_cast<int64_t>(seg) * p.B * H + bh) * KP + tid] = __expf(lsum);
@@ -685,59 +701,72 @@ __global__ __launch_bounds__(NT) void diag_outer_kernel(DiagArgs p) {
     }
 }
 
-template <int MODE, int KP>
+template <int MODE, int KP, int WPB>
 hipError_t launch_t(const DiagArgs& a, bool vec, hipStream_t stream) {
     const int64_t units = static_cast<int64_t>(a.B) * a.H * a.vtiles;
+    const dim3 block(64 * WPB);
     if (a.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(units * (a.nseg - 1)));
-        if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, true, true>), grid, dim3(NT), 0, stream, a);
-        else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, false, true>), grid, dim3(NT), 0, stream, a);
+        if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, true>), grid, block, 0, stream, a);
     }
     const dim3 grid(static_cast<unsigned>(units * a.nseg));
-    if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, true, false>), grid, dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, false, false>), grid, dim3(NT), 0, stream, a);
+    if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, false>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 // Output-pass workgroups that fit on one compute unit at once (LDS and
 // registers), measured once per kernel variant.
-template <int MODE, int KP, bool VEC>
+template <int MODE, int KP, int WPB, bool VEC>
 int resident_blocks() {
     static int n = 0;
     if (n == 0) {
         int m = 1;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, diag_outer_kernel<MODE, KP, VEC, false>, NT, 0) !=
-                hipSuccess || m < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, diag_outer_kernel<MODE, KP, WPB, VEC, false>, 64 * WPB,
+                                                         0) != hipSuccess ||
+            m < 1)
             m = 1;
         n = m;
     }
     return n;
 }
 
-int resident_blocks(int decay_mode, int K, bool vec) {
-    if (decay_mode == 0) {
-        if (K <= 64) return vec ? resident_blocks<0, 64, true>() : resident_blocks<0, 64, false>();
-        return vec ? resident_blocks<0, 128, true>() : resident_blocks<0, 128, false>();
-    }
-    if (K <= 64) return vec ? resident_blocks<1, 64, true>() : resident_blocks<1, 64, false>();
-    return vec ? resident_blocks<1, 128, true>() : resident_blocks<1, 128, false>();
+template <int MODE, int KP>
+int resident_blocks_w(int wpb, bool vec) {
+    if (wpb == 8) return vec ? resident_blocks<MODE, KP, 8, true>() : resident_blocks<MODE, KP, 8, false>();
+    return vec ? resident_blocks<MODE, KP, 4, true>() : resident_blocks<MODE, KP, 4, false>();
+}
+
+int resident_blocks(int decay_mode, int K, int wpb, bool vec) {
+    if (decay_mode == 0) return K <= 64 ? resident_blocks_w<0, 64>(wpb, vec) : resident_blocks_w<0, 128>(wpb, vec);
+    return K <= 64 ? resident_blocks_w<1, 64>(wpb, vec) : resident_blocks_w<1, 128>(wpb, vec);
+}
+
+template <int MODE, int KP>
+hipError_t launch_w(const DiagArgs& a, int wpb, bool vec, hipStream_t stream) {
+    return wpb == 8 ? launch_t<MODE, KP, 8>(a, vec, stream) : launch_t<MODE, KP, 4>(a, vec, stream);
 }
 
 }  // namespace
 
-int diag_outer_vtile() { return VT; }
-
 DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool vec, int num_cus,
                          int requested_segments) {
     DiagPlan pl{};
+    pl.waves = waves_for(V);
+    const int vt = 16 * pl.waves;
     pl.nchunks = (T + L - 1) / L;
-    pl.vtiles = (V + VT - 1) / VT;
+    pl.vtiles = (V + vt - 1) / vt;
     const int64_t units = static_cast<int64_t>(B) * H * pl.vtiles;
     int64_t nseg = requested_segments;
     if (nseg <= 0) {
-        // as many segments as keep every resident slot of the chip busy in one round
-        const int64_t slots = static_cast<int64_t>(num_cus) * resident_blocks(decay_mode, K, vec);
-        nseg = slots / units;
+        // enough segments for two workgroups per resident slot of the chip (a
+        // second round covers the tail of the first), but at least
+        // kMinChunksPerSegment chunks each: every extra segment costs a
+        // reduction pass over its chunks and a longer fold
+        const int64_t slots = static_cast<int64_t>(num_cus) * resident_blocks(decay_mode, K, pl.waves, vec);
+        nseg = 2 * slots / units;
+        if (nseg > pl.nchunks / kMinChunksPerSegment) nseg = pl.nchunks / kMinChunksPerSegment;
     }
     if (nseg > pl.nchunks) nseg = pl.nchunks;
     if (nseg < 1) nseg = 1;
@@ -748,8 +777,9 @@ DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool
 
 size_t diag_outer_workspace_bytes(int B, int H, int K, int V, int nseg) {
     if (nseg <= 1) return 0;
-    const size_t kp = K <= 64 ? 64 : 128, vtiles = (static_cast<size_t>(V) + VT - 1) / VT;
-    return static_cast<size_t>(nseg - 1) * B * H * (vtiles * kp * VT + kp) * sizeof(float);
+    const size_t kp = K <= 64 ? 64 : 128, vt = 16 * static_cast<size_t>(waves_for(V));
+    const size_t vtiles = (static_cast<size_t>(V) + vt - 1) / vt;
+    return static_cast<size_t>(nseg - 1) * B * H * (vtiles * kp * vt + kp) * sizeof(float);
 }
 
 hipError_t launch_scan_diag_outer(const DiagParams& prm, const DiagPlan& pl, void* workspace, hipStream_t stream) {
@@ -774,14 +804,15 @@ hipError_t launch_scan_diag_outer(const DiagParams& prm, const DiagPlan& pl, voi
     a.nseg = pl.nseg;
     a.cps = pl.cps;
     if (pl.nseg > 1) {
-        a.agg_u = static_cast<float*>(workspace);
         const size_t kp = prm.K <= 64 ? 64 : 128;
-        a.agg_a = a.agg_u + static_cast<size_t>(pl.nseg - 1) * prm.B * prm.H * pl.vtiles * kp * VT;
+        a.agg_u = static_cast<float*>(workspace);
+        a.agg_a = a.agg_u + static_cast<size_t>(pl.nseg - 1) * prm.B * prm.H * pl.vtiles * kp * (16 * pl.waves);
     }
     const bool vec = prm.vec != 0;
     const bool k64 = prm.K <= 64;
-    if (prm.decay_mode == 0) return k64 ? launch_t<0, 64>(a, vec, stream) : launch_t<0, 128>(a, vec, stream);
-    return k64 ? launch_t<1, 64>(a, vec, stream) : launch_t<1, 128>(a, vec, stream);
+    if (prm.decay_mode == 0)
+        return k64 ? launch_w<0, 64>(a, pl.waves, vec, stream) : launch_w<0, 128>(a, pl.waves, vec, stream);
+    return k64 ? launch_w<1, 64>(a, pl.waves, vec, stream) : launch_w<1, 128>(a, pl.waves, vec, stream);
 }
 
 }  // namespace lrs

@@ -64,6 +64,8 @@ def _mamba(B, T, H, K, V, seed, Hg=1):
     (1, 130, 3, 3, 100, 37),    # K, V not multiples of 8 (scalar loads)
     (1, 1, 2, 1, 128, 64),      # T = 1
     (2, 70, 2, 2, 1, 1),        # K = V = 1
+    (1, 200, 2, 1, 128, 128),   # wide heads: 8 waves per workgroup
+    (1, 150, 2, 2, 64, 100),    # wide, ragged V tile, K = 64
 ], ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("with_s0", [False, True])
 def test_scalar_decay_parity(ctx, shape, with_s0):
@@ -118,7 +120,7 @@ class _Segments:
         binding.lrs_context_set_param(self.ctx, binding.LRS_PARAM_DIAG_SEGMENTS, 0)
 
 
-@pytest.mark.parametrize("segments", [0, 1])
+@pytest.mark.parametrize("segments", [3, 1])
 @pytest.mark.parametrize("gval", [-1.5, -4.0])
 def test_key_decay_strong_gates_exact_fallback(ctx, gval, segments):
     # chunk decay of 64 * |g| nats exceeds the factorised path's range: the
@@ -133,17 +135,17 @@ def test_key_decay_strong_gates_exact_fallback(ctx, gval, segments):
 
 
 @pytest.mark.parametrize("segments", [1, 2, 3, 7, 0])
-@pytest.mark.parametrize("mode", [0, 1])
-def test_time_segments(ctx, mode, segments):
+@pytest.mark.parametrize("mode,V", [(0, 64), (1, 64), (0, 128), (1, 128)])
+def test_time_segments(ctx, mode, V, segments):
     # each segment starts from s0 folded through the (decay product, state
     # contribution) pairs of the segments before it; any count must agree
     # with the sequential oracle, including segments of unequal length
-    B, T, H, K, V = 2, 650, 2, 128, 64
+    B, T, H, K = 2, 650, 2, 128
     if mode == 0:
         d = _mamba(B, T, H, K, V, seed=61)
     else:
         d = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=62)
-    say(f"diag mode{mode} segments={segments}")
+    say(f"diag mode{mode} V={V} segments={segments}")
     with _Segments(ctx, segments):
         _check(ctx, d, inputs.random_state((B, H, K, V), 8))
 

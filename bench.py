@@ -43,9 +43,9 @@ def source_sha(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, source_file):
-    """HBM bytes per launch measured by rocprofv3 counters, if the record in
-    profiles/traffic.json was taken on the current kernel source; else None."""
+def profile_record(kernel_key, source_file):
+    """The rocprofv3 counter record of a kernel in profiles/traffic.json, if it
+    was taken on the current kernel source; else None."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
@@ -53,7 +53,25 @@ def measured_traffic(kernel_key, source_file):
         rec = json.load(f).get(kernel_key)
     if not rec or rec.get("source_sha") != source_sha(source_file):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def measured_traffic(kernel_key, source_file):
+    """HBM bytes per launch measured by rocprofv3 counters (current source only)."""
+    rec = profile_record(kernel_key, source_file)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def measured_mfma_util(kernel_keys, source_file):
+    """Matrix-core busy fraction of SIMD cycles over a call's kernels (busy
+    cycles summed over kernels / active cycles x SIMDs), from counters taken
+    on the current source; else None."""
+    recs = [profile_record(k, source_file) for k in kernel_keys]
+    if any(r is None or "mfma_busy_cycles" not in r for r in recs):
+        return None
+    busy = sum(r["mfma_busy_cycles"] for r in recs)
+    active = sum(r["gui_active_cycles_sum_xcd"] for r in recs)
+    return round(busy * 8 / (active * 1024), 4) if active else None
 
 
 def elem_bytes(B, T, N, with_s0=True):
@@ -322,6 +340,7 @@ def run_rows(ctx, args, binding, inputs, dev):
         src = "scan_diag_outer.hip" if kind == "diag" else "scan_delta.hip"
         tr = [measured_traffic(key, src) for key in traffic_keys]
         row["roofline"]["traffic"] = None if any(t is None for t in tr) else sum(tr)
+        row["mfma_util"] = measured_mfma_util(traffic_keys, src)
         # parity and the CPU oracle on sampled heads (full time axis)
         errs = []
         t_cpu = 0.0

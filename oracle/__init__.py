@@ -63,6 +63,12 @@ def _load():
             f = getattr(lib, name + sfx)
             f.argtypes = [P, P, P, P, P, I64, I64, I64, I]
             f.restype = None
+        f = getattr(lib, "orc_scan_fma_bwd" + sfx)
+        f.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I]
+        f.restype = None
+        f = getattr(lib, "orc_scan_gated_bwd" + sfx)
+        f.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I]
+        f.restype = None
         f = getattr(lib, "orc_scan_diag_outer" + sfx)
         f.argtypes = [P, P, P, P, I, P, R, P, P, P, I64, I64, I64, I64, I64, I64, I]
         f.restype = None
@@ -135,6 +141,53 @@ def scan_fma(a, b, s0=None, dtype=np.float64, nthreads=None):
 def scan_gated(a, u, s0=None, dtype=np.float64, nthreads=None):
     """s_t = a_t s_{t-1} + (1 - a_t) u_t over [B,T,N] inputs [SunnyNet log §2.1]."""
     return _elementwise("orc_scan_gated", a, u, s0, dtype, nthreads)
+
+
+def _elementwise_bwd(gated, a, u, s0, s, ds, ds_final, dtype, nthreads):
+    a = _arr(a, dtype)
+    if a.ndim != 3:
+        raise ValueError("a must be [B,T,N]")
+    B, T, N = a.shape
+    s = _arr(s, dtype)
+    ds = _arr(ds, dtype)
+    _check_shape("s", s, (B, T, N))
+    _check_shape("ds", ds, (B, T, N))
+    s0 = _arr(s0, dtype)
+    _check_shape("s0", s0, (B, N))
+    ds_final = _arr(ds_final, dtype)
+    _check_shape("ds_final", ds_final, (B, N))
+    da = np.empty((B, T, N), dtype=dtype)
+    dx = np.empty((B, T, N), dtype=dtype)
+    ds0 = np.empty((B, N), dtype=dtype)
+    nth = nthreads or default_threads()
+    if gated:
+        u = _arr(u, dtype)
+        _check_shape("u", u, (B, T, N))
+        fn = getattr(_load(), "orc_scan_gated_bwd" + _sfx(dtype))
+        fn(_ptr(a), _ptr(u), _ptr(s0), _ptr(s), _ptr(ds), _ptr(ds_final), _ptr(da), _ptr(dx),
+           _ptr(ds0), B, T, N, nth)
+    else:
+        fn = getattr(_load(), "orc_scan_fma_bwd" + _sfx(dtype))
+        fn(_ptr(a), _ptr(s0), _ptr(s), _ptr(ds), _ptr(ds_final), _ptr(da), _ptr(dx), _ptr(ds0),
+           B, T, N, nth)
+    return da, dx, ds0
+
+
+def scan_fma_backward(a, s, ds, s0=None, ds_final=None, dtype=np.float64, nthreads=None):
+    """Reverse (gradient) pass of ``scan_fma`` [SunnyNet log §8, reverse-scan entry].
+
+    ``s`` are the forward states, ``ds`` the loss gradient with respect to each
+    of them and ``ds_final`` with respect to the returned final state.
+    gs_t = ds_t + a_{t+1} gs_{t+1} (gs_T = ds_T + ds_final); returns
+    ``(da, db, ds0)`` with da_t = gs_t s_{t-1}, db_t = gs_t, ds0 = a_1 gs_1.
+    """
+    return _elementwise_bwd(False, a, None, s0, s, ds, ds_final, dtype, nthreads)
+
+
+def scan_gated_backward(a, u, s, ds, s0=None, ds_final=None, dtype=np.float64, nthreads=None):
+    """Reverse (gradient) pass of ``scan_gated``: as ``scan_fma_backward`` but
+    da_t = gs_t (s_{t-1} - u_t) and du_t = gs_t (1 - a_t); returns ``(da, du, ds0)``."""
+    return _elementwise_bwd(True, a, u, s0, s, ds, ds_final, dtype, nthreads)
 
 
 def scan_diag_outer(q, k, v, g, decay_mode, k_scale=None, scale=1.0, s0=None,

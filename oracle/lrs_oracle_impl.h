@@ -74,6 +74,69 @@ void ORC_FN(orc_scan_gated)(const REAL* a, const REAL* u, const REAL* s0, REAL* 
 }
 
 /*
+ * Reverse (adjoint) pass of the two elementwise recurrences, per channel (b, n):
+ * the back-ends' reverse-scan entry [SunnyNet log §8], read as the gradient
+ * pass used in training.  Given the forward states s_t and the gradient ds_t
+ * of a loss with respect to each output s_t (plus ds_final with respect to
+ * the returned final state), the total derivative with respect to s_t is
+ *     gs_T = ds_T + ds_final,     gs_t = ds_t + a_{t+1} * gs_{t+1}   (t < T)
+ * because s_t enters the loss directly and through s_{t+1} = a_{t+1} s_t + ...
+ * The input gradients follow from one step's partial derivatives:
+ *     FMA   s_t = a_t s_{t-1} + b_t:           da_t = gs_t * s_{t-1},  db_t = gs_t
+ *     gated s_t = a_t s_{t-1} + (1-a_t) u_t:   da_t = gs_t * (s_{t-1} - u_t),
+ *                                               du_t = gs_t * (1 - a_t)
+ *     both: ds0 = a_1 * gs_1
+ * with s_0 = s0 (0 when s0 is NULL).  Layout: a, u, s, ds, da, dx are
+ * [B,T,N] (memory row t-1 holds step t); s0, ds_final, ds0 are [B,N];
+ * ds_final NULL means zero, ds0 NULL means not wanted.  `u` is read only by
+ * the gated form (pass NULL for the FMA form, whose dx is db).
+ */
+static void ORC_FN(orc_elem_bwd)(int gated, const REAL* a, const REAL* u, const REAL* s0,
+                                 const REAL* s, const REAL* ds, const REAL* ds_final, REAL* da,
+                                 REAL* dx, REAL* ds0, int64_t B, int64_t T, int64_t N,
+                                 int nthreads) {
+    int64_t nblk = (N + ORC_NBLK - 1) / ORC_NBLK;
+#pragma omp parallel for schedule(static) num_threads(nthreads)
+    for (int64_t w = 0; w < B * nblk; ++w) {
+        int64_t b = w / nblk, n_lo = (w % nblk) * ORC_NBLK;
+        int64_t n_hi = n_lo + ORC_NBLK < N ? n_lo + ORC_NBLK : N;
+        REAL gs[ORC_NBLK];
+        for (int64_t t = T - 1; t >= 0; --t) {
+            int64_t row = (b * T + t) * N;
+            for (int64_t n = n_lo; n < n_hi; ++n) {
+                REAL later;
+                if (t == T - 1) later = ds_final ? ds_final[b * N + n] : (REAL)0;
+                else later = a[row + N + n] * gs[n - n_lo];
+                REAL g = ds[row + n] + later;
+                gs[n - n_lo] = g;
+                REAL prev = t > 0 ? s[row - N + n] : (s0 ? s0[b * N + n] : (REAL)0);
+                if (gated) {
+                    da[row + n] = g * (prev - u[row + n]);
+                    dx[row + n] = g * ((REAL)1 - a[row + n]);
+                } else {
+                    da[row + n] = g * prev;
+                    dx[row + n] = g;
+                }
+            }
+        }
+        if (ds0)
+            for (int64_t n = n_lo; n < n_hi; ++n) ds0[b * N + n] = a[b * T * N + n] * gs[n - n_lo];
+    }
+}
+
+void ORC_FN(orc_scan_fma_bwd)(const REAL* a, const REAL* s0, const REAL* s, const REAL* ds,
+                              const REAL* ds_final, REAL* da, REAL* db, REAL* ds0, int64_t B,
+                              int64_t T, int64_t N, int nthreads) {
+    ORC_FN(orc_elem_bwd)(0, a, NULL, s0, s, ds, ds_final, da, db, ds0, B, T, N, nthreads);
+}
+
+void ORC_FN(orc_scan_gated_bwd)(const REAL* a, const REAL* u, const REAL* s0, const REAL* s,
+                                const REAL* ds, const REAL* ds_final, REAL* da, REAL* du,
+                                REAL* ds0, int64_t B, int64_t T, int64_t N, int nthreads) {
+    ORC_FN(orc_elem_bwd)(1, a, u, s0, s, ds, ds_final, da, du, ds0, B, T, N, nthreads);
+}
+
+/*
  * Decay-separable outer-product state recurrence with readout, per (b, h):
  *     alpha_t[i] = exp(g[b,t,h])        (decay_mode 0: one decay per head and step)
  *     alpha_t[i] = exp(g[b,t,h,i])      (decay_mode 1: one decay per key row)

@@ -201,6 +201,189 @@ def test_gated_double_sum_exact_rational_and_convexity():
 
 
 # ----------------------------------------------------------------------------
+# Reverse (gradient) pass of the elementwise scans [SunnyNet log §8: the
+# back-ends' reverse-scan entry].  The loss is L = sum_t <W_t, s_t> + <w_f, s_T>,
+# so (W, w_f) are the incoming gradients (ds, ds_final).  Each pin derives the
+# gradient without the backward recursion: every forward state is affine in
+# any single input, so a unit difference of L is that input's exact partial
+# derivative, and L is jointly linear in (b or u, s0).
+# ----------------------------------------------------------------------------
+
+def _states_exact(a, x, s0, gated):
+    """All states of one channel in exact rationals, from the double-sum closed
+    form (not the step-by-step recursion)."""
+    T = len(a)
+    out = []
+    for t in range(T):
+        val = s0
+        for j in range(t + 1):
+            val *= a[j]
+        for i in range(t + 1):
+            term = (1 - a[i]) * x[i] if gated else x[i]
+            for j in range(i + 1, t + 1):
+                term *= a[j]
+            val += term
+        out.append(val)
+    return out
+
+
+def _loss_exact(a, x, s0, W, wf, gated):
+    st = _states_exact(a, x, s0, gated)
+    return sum(w * v for w, v in zip(W, st)) + wf * st[-1]
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_elem_backward_exact_unit_differences(gated):
+    r = _rng(8 + gated)
+    B, T, N = 2, 6, 2
+    a = r.integers(-6, 7, (B, T, N)) / 4.0
+    x = r.integers(-8, 9, (B, T, N)) / 8.0
+    s0 = r.integers(-4, 5, (B, N)) / 2.0
+    ds = r.integers(-4, 5, (B, T, N)) / 4.0
+    dsf = r.integers(-4, 5, (B, N)) / 2.0
+    fwd = oracle.scan_gated if gated else oracle.scan_fma
+    s, _ = fwd(a, x, s0)
+    if gated:
+        da, dx, ds0 = oracle.scan_gated_backward(a, x, s, ds, s0, dsf)
+    else:
+        da, dx, ds0 = oracle.scan_fma_backward(a, s, ds, s0, dsf)
+    for bi in range(B):
+        for n in range(N):
+            A = [Fraction(v) for v in a[bi, :, n]]
+            X = [Fraction(v) for v in x[bi, :, n]]
+            W = [Fraction(v) for v in ds[bi, :, n]]
+            S0, WF = Fraction(s0[bi, n]), Fraction(dsf[bi, n])
+            L0 = _loss_exact(A, X, S0, W, WF, gated)
+            for t in range(T):
+                Ap = list(A); Ap[t] += 1
+                Xp = list(X); Xp[t] += 1
+                assert da[bi, t, n] == pytest.approx(float(_loss_exact(Ap, X, S0, W, WF, gated) - L0),
+                                                     rel=1e-14, abs=1e-14)
+                assert dx[bi, t, n] == pytest.approx(float(_loss_exact(A, Xp, S0, W, WF, gated) - L0),
+                                                     rel=1e-14, abs=1e-14)
+            assert ds0[bi, n] == pytest.approx(float(_loss_exact(A, X, S0 + 1, W, WF, gated) - L0),
+                                               rel=1e-14, abs=1e-14)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_elem_backward_central_differences(gated):
+    # longer sequences in float64: L is affine in each single input, so the
+    # central difference is exact up to the rounding of L itself
+    r = _rng(10 + gated)
+    B, T, N = 2, 64, 3
+    a = r.uniform(0.5, 1.0, (B, T, N)) if gated else r.uniform(-1.1, 1.1, (B, T, N))
+    x = r.standard_normal((B, T, N))
+    s0 = r.standard_normal((B, N))
+    ds = r.standard_normal((B, T, N))
+    dsf = r.standard_normal((B, N))
+    fwd = oracle.scan_gated if gated else oracle.scan_fma
+
+    def loss(a_, x_, s0_):
+        s_, fin_ = fwd(a_, x_, s0_)
+        return np.sum(ds * s_, axis=(1, 2)) + np.sum(dsf * fin_, axis=1)   # one loss per batch row
+
+    s, _ = fwd(a, x, s0)
+    bwd = (lambda: oracle.scan_gated_backward(a, x, s, ds, s0, dsf)) if gated else \
+          (lambda: oracle.scan_fma_backward(a, s, ds, s0, dsf))
+    da, dx, ds0 = bwd()
+    h = 0.25
+    scale = np.max(np.abs(ds)) * T
+    for t in (0, 1, T // 2, T - 2, T - 1):
+        for n in range(N):
+            e = np.zeros((B, T, N)); e[:, t, n] = h
+            fd_a = (loss(a + e, x, s0) - loss(a - e, x, s0)) / (2 * h)
+            fd_x = (loss(a, x + e, s0) - loss(a, x - e, s0)) / (2 * h)
+            assert np.max(np.abs(fd_a - da[:, t, n])) < 1e-11 * scale
+            assert np.max(np.abs(fd_x - dx[:, t, n])) < 1e-11 * scale
+    for n in range(N):
+        e = np.zeros((B, N)); e[:, n] = h
+        fd = (loss(a, x, s0 + e) - loss(a, x, s0 - e)) / (2 * h)
+        assert np.max(np.abs(fd - ds0[:, n])) < 1e-11 * scale
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_elem_backward_linearity_identity(gated):
+    # For fixed a the states are linear in (b or u, s0) jointly, so the loss
+    # equals <dx, x> + <ds0, s0> exactly (Euler's identity for a linear map).
+    r = _rng(12 + gated)
+    B, T, N = 3, 200, 4
+    a = r.uniform(0.5, 1.0, (B, T, N))
+    x = r.standard_normal((B, T, N))
+    s0 = r.standard_normal((B, N))
+    ds = r.standard_normal((B, T, N))
+    dsf = r.standard_normal((B, N))
+    if gated:
+        s, fin = oracle.scan_gated(a, x, s0)
+        _, dx, ds0 = oracle.scan_gated_backward(a, x, s, ds, s0, dsf)
+    else:
+        s, fin = oracle.scan_fma(a, x, s0)
+        _, dx, ds0 = oracle.scan_fma_backward(a, s, ds, s0, dsf)
+    lhs = np.sum(ds * s, axis=(1, 2)) + np.sum(dsf * fin, axis=1)
+    rhs = np.sum(dx * x, axis=(1, 2)) + np.sum(ds0 * s0, axis=1)
+    assert np.max(np.abs(lhs - rhs)) < 1e-11 * np.max(np.abs(lhs))
+
+
+def test_elem_backward_closed_forms():
+    r = _rng(14)
+    B, T, N = 2, 30, 3
+    x = r.standard_normal((B, T, N))
+    s0 = r.standard_normal((B, N))
+    ds = r.standard_normal((B, T, N))
+    dsf = r.standard_normal((B, N))
+    # a = 1: the gradient of every state is the suffix sum of the incoming ones
+    ones = np.ones((B, T, N))
+    s, _ = oracle.scan_fma(ones, x, s0)
+    _, db, ds0 = oracle.scan_fma_backward(ones, s, ds, s0, dsf)
+    suffix = np.flip(np.cumsum(np.flip(ds, axis=1), axis=1), axis=1) + dsf[:, None, :]
+    assert rel(db, suffix) < 1e-14
+    assert rel(ds0, suffix[:, 0]) < 1e-14
+    # a = 0: each state forgets the past, so only its own gradient reaches it
+    zeros = np.zeros((B, T, N))
+    s, _ = oracle.scan_fma(zeros, x, s0)
+    da, db, ds0 = oracle.scan_fma_backward(zeros, s, ds, s0, dsf)
+    own = ds.copy()
+    own[:, -1] += dsf
+    assert np.array_equal(db, own)
+    assert np.array_equal(ds0, np.zeros((B, N)))
+    # constant a = c with a single unit gradient at step k: gs_t = c^(k-t) for t <= k
+    c, k = 0.8, 17
+    ds1 = np.zeros((B, T, N)); ds1[:, k, :] = 1.0
+    s, _ = oracle.scan_fma(np.full((B, T, N), c), x, s0)
+    da, db, ds0 = oracle.scan_fma_backward(np.full((B, T, N), c), s, ds1, s0, None)
+    t = np.arange(T)[None, :, None]
+    ref = np.where(t <= k, c ** np.maximum(k - t, 0), 0.0) * np.ones((B, T, N))
+    assert rel(db, ref) < 1e-14
+    assert rel(ds0, np.full((B, N), c ** (k + 1))) < 1e-14
+    # gated with a = 0: s_t = u_t, so du = ds (plus ds_final at the end) and da = ds (s_{t-1} - u_t)
+    s, _ = oracle.scan_gated(zeros, x, s0)
+    da, du, ds0 = oracle.scan_gated_backward(zeros, x, s, ds, s0, dsf)
+    assert np.array_equal(du, own)
+    prev = np.concatenate([s0[:, None, :], x[:, :-1]], axis=1)
+    assert rel(da, own * (prev - x)) < 1e-15
+    # gated with a = 1: the state never moves, so du = 0 and ds0 collects every gradient
+    s, _ = oracle.scan_gated(ones, x, s0)
+    da, du, ds0 = oracle.scan_gated_backward(ones, x, s, ds, s0, dsf)
+    assert np.array_equal(du, np.zeros((B, T, N)))
+    assert rel(ds0, ds.sum(axis=1) + dsf) < 1e-14
+
+
+def test_elem_backward_float32_mode_and_nulls():
+    r = _rng(15)
+    a = r.uniform(0.5, 1.0, (2, 512, 8))
+    x = r.standard_normal((2, 512, 8))
+    ds = r.standard_normal((2, 512, 8))
+    s, _ = oracle.scan_gated(a, x)
+    g64 = oracle.scan_gated_backward(a, x, s, ds)
+    g32 = oracle.scan_gated_backward(a, x, s, ds, dtype=np.float32)
+    for u, v in zip(g32, g64):
+        assert u.dtype == np.float32 and rel(u, v) < 5e-6
+    # NULL s0 and ds_final mean zeros
+    z = oracle.scan_gated_backward(a, x, s, ds, np.zeros((2, 8)), np.zeros((2, 8)))
+    for u, v in zip(z, g64):
+        assert np.array_equal(u, v)
+
+
+# ----------------------------------------------------------------------------
 # Decay-separable state scan [SunnyNet log §4.1, §4.3]
 # ----------------------------------------------------------------------------
 

@@ -214,7 +214,25 @@ def profile_run(ctx, binding, inputs, dev, steps):
     for _ in range(steps):
         binding.lrs_scan_gated(ctx, a, u, s0, s, fin)
     torch.cuda.synchronize()
-    del a, u, s, d
+    # the gradient pass of the same workload (both forms)
+    g = elem_grad_inputs(inputs, dev)
+    da = torch.empty_like(a)
+    dx = torch.empty_like(a)
+    ds0 = torch.empty_like(s0)
+    for _ in range(steps):
+        binding.lrs_scan_gated_backward(ctx, a, u, s0, g["s"], g["ds"], g["dsf"], da, dx, ds0)
+    for _ in range(steps):
+        binding.lrs_scan_fma_backward(ctx, a, s0, g["s"], g["ds"], g["dsf"], da, dx, ds0)
+    torch.cuda.synchronize()
+    del a, u, s, d, g, da, dx
+    # one large single step (a pure 16 B per channel stream)
+    sa = torch.full(STEP_LARGE, 0.5, device=dev)
+    sx = torch.ones(STEP_LARGE, device=dev)
+    st = torch.zeros(STEP_LARGE, device=dev)
+    for _ in range(steps):
+        binding.lrs_step_gated(ctx, sa, sx, st)
+    torch.cuda.synchronize()
+    del sa, sx, st
     for gen, kind in ((lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}), "diag"),
                       (lambda: inputs.gla(**inputs.GLA), "diag"),
                       (lambda: inputs.deltanet(**inputs.DELTANET), "delta"),
@@ -230,6 +248,123 @@ def profile_run(ctx, binding, inputs, dev, steps):
         torch.cuda.synchronize()
     assert binding.lrs_context_check(ctx) == binding.LRS_OK
     log("[bench] profile run done")
+
+
+STEP_SMALL = (16, 2048)        # one decode step of the gated workload's state
+STEP_LARGE = (16, 4194304)     # 2^26 channels: 1 GiB moved per step
+
+
+def elem_grad_inputs(inputs, dev):
+    """Stand-in forward states and incoming gradients of the gated workload for
+    the gradient pass (the pass is defined for any given states)."""
+    cfg = inputs.GATED_LARGE
+    B, T, N = cfg["B"], cfg["T"], cfg["N"]
+    return {"s": inputs.random_normal((B, T, N), 2001).to(dev),
+            "ds": inputs.random_normal((B, T, N), 2002).to(dev),
+            "dsf": inputs.random_state((B, N), 2003).to(dev)}
+
+
+def elem_rows(ctx, binding, inputs, dev, flush):
+    """The gradient pass of the gated workload (both forms) and the single
+    step, each with a roofline figure, parity on sampled batch rows and the
+    CPU oracle timed on the same sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    rows = []
+    cfg = inputs.GATED_LARGE
+    B, T, N = cfg["B"], cfg["T"], cfg["N"]
+    log("[bench] row: gradient pass of the gated workload")
+    d = inputs.gated_large(**cfg)
+    a, u, s0 = d["a"].to(dev), d["u"].to(dev), d["s0"].to(dev)
+    g = elem_grad_inputs(inputs, dev)
+    da = torch.empty_like(a)
+    dx = torch.empty_like(a)
+    ds0 = torch.empty_like(s0)
+    nth = oracle.default_threads()
+    # parity and the CPU oracle on the whole workload
+    host = {k: v.cpu().numpy() for k, v in (("a", a), ("u", u), ("s", g["s"]), ("ds", g["ds"]))}
+    host0 = {k: v.cpu().numpy() for k, v in (("s0", s0), ("dsf", g["dsf"]))}
+    for kind in ("gated", "fma"):
+        if kind == "gated":
+            fn = lambda: binding.lrs_scan_gated_backward(ctx, a, u, s0, g["s"], g["ds"], g["dsf"],  # noqa: E731
+                                                         da, dx, ds0)
+            per_elem = 24
+        else:
+            fn = lambda: binding.lrs_scan_fma_backward(ctx, a, s0, g["s"], g["ds"], g["dsf"],  # noqa: E731
+                                                       da, dx, ds0)
+            per_elem = 20
+        med, mn = time_launches(fn, 10, 2, flush)
+        torch.cuda.synchronize()
+        assert binding.lrs_context_check(ctx) == binding.LRS_OK
+        nbytes = per_elem * B * T * N + 3 * 4 * B * N
+        achieved = nbytes / (med * 1e-3) / 1e9
+        key = f"scan_elem_{kind}_bwd_B16_T8192_N2048"
+        row = {"row": f"scan_{kind}_backward B=16 T=8192 N=2048 fp32 (gradient pass: reads a, ds, s"
+                      f"{', u' if kind == 'gated' else ''}; writes da, d{'u' if kind == 'gated' else 'b'}, ds0)",
+               "us_median": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+               "elements_per_s": round(B * T * N / (med * 1e-3), 1),
+               "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                            "bytes_per_call": nbytes,
+                            "traffic": measured_traffic(key, "scan_elem.hip")}}
+        t0 = time.perf_counter()
+        if kind == "gated":
+            r = oracle.scan_gated_backward(host["a"], host["u"], host["s"], host["ds"], host0["s0"],
+                                           host0["dsf"], nthreads=nth)
+        else:
+            r = oracle.scan_fma_backward(host["a"], host["s"], host["ds"], host0["s0"], host0["dsf"],
+                                         nthreads=nth)
+        dt = time.perf_counter() - t0
+        gpu = (da.cpu().numpy(), dx.cpu().numpy(), ds0.cpu().numpy())
+        row["parity_max_rel_err"] = max(float(np.max(np.abs(x - y)) / np.max(np.abs(y))) for x, y in zip(gpu, r))
+        del gpu, r
+        row["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s",
+                               "cores": nth, "kind": "oracle",
+                               "sample": "the whole workload (B=16,T=8192,N=2048), sequential fp64 oracle "
+                                         "incl. fp32->fp64 upcast, OpenMP over (batch, channel-block)",
+                               "seconds": round(dt, 3)}
+        rows.append(row)
+    del a, u, s0, g, da, dx, ds0, d, host, host0
+
+    log("[bench] row: single step")
+    for shape in (STEP_SMALL, STEP_LARGE):
+        n = shape[0] * shape[1]
+        sd = inputs.elementwise_small(shape[0], 1, shape[1], seed=2010) if n <= 1 << 20 else None
+        if sd is not None:
+            sa, sx = sd["a"][:, 0].to(dev), sd["u"][:, 0].to(dev)
+        else:
+            sa = torch.full(shape, 0.75, device=dev)
+            sx = torch.ones(shape, device=dev)
+        st0 = inputs.random_state(shape, 2011) if n <= 1 << 20 else None
+        st = st0.to(dev) if st0 is not None else torch.zeros(shape, device=dev)
+        if st0 is not None:
+            # parity: one step against the oracle's one-step scan
+            binding.lrs_step_gated(ctx, sa, sx, st)
+            ref = oracle.scan_gated(sd["a"], sd["u"], st0)[1]
+            err = float(np.max(np.abs(st.cpu().numpy() - ref)) / np.max(np.abs(ref)))
+        fn = lambda: binding.lrs_step_gated(ctx, sa, sx, st)  # noqa: E731
+        if n <= 1 << 20:
+            ms_call, ms_kernel = time_steps(fn, 200, 10)
+            row = {"row": f"step_gated B={shape[0]} N={shape[1]} fp32 (one in-place decode step)",
+                   "us_per_call": round(ms_call * 1e3, 3), "us_kernel_events": round(ms_kernel * 1e3, 3),
+                   "channels_per_s": round(n / (ms_kernel * 1e-3), 1),
+                   "parity_max_rel_err": err,
+                   "note": f"{16 * n / 1e6:.2f} MB per step: launch-latency bound; no roofline claim"}
+        else:
+            med, mn = time_launches(fn, 10, 2, flush)
+            achieved = 16 * n / (med * 1e-3) / 1e9
+            row = {"row": f"step_gated B={shape[0]} N={shape[1]} fp32 (one in-place step, 1 GiB stream)",
+                   "us_median": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+                   "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                                "bytes_per_call": 16 * n,
+                                "traffic": measured_traffic("step_elem_gated_B16_N4194304", "scan_elem.hip")}}
+        rows.append(row)
+        del sa, sx, st
+    return rows
 
 
 def diag_bytes(d):
@@ -294,6 +429,7 @@ def run_rows(ctx, args, binding, inputs, dev):
                      "note": "launch-latency bound (394 KB per call); no roofline claim"})
 
     flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
+    rows += elem_rows(ctx, binding, inputs, dev, flush)
     nth = oracle.default_threads()
     heads = [(0, 0), (1, 1)]
     specs = [

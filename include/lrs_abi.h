@@ -10,6 +10,10 @@
  *   lrs_scan_delta       S_t = S_{t-1} + k_t [beta_t (v_t - S_{t-1}^T k_t)]^T,
  *                        o_t = scale S_t^T q_t                     (per head)
  *
+ * plus, for the two elementwise forms, the reverse (gradient) pass
+ * (lrs_scan_fma_backward, lrs_scan_gated_backward) and the in-place single
+ * step (lrs_step_fma, lrs_step_gated).
+ *
  * Every scan takes an initial state and returns the final state, so a long
  * sequence can be processed in segments: running [0,T1) and then [T1,T) with
  * the first call's final state as the second call's initial state gives the
@@ -68,7 +72,7 @@ extern "C" {
 
 /* ---- version and capabilities [SunnyNet log §6] ------------------------ */
 #define LRS_ABI_VERSION_MAJOR 1
-#define LRS_ABI_VERSION_MINOR 0
+#define LRS_ABI_VERSION_MINOR 1
 #define LRS_ABI_VERSION_PATCH 0
 #define LRS_ABI_VERSION \
     ((LRS_ABI_VERSION_MAJOR << 16) | (LRS_ABI_VERSION_MINOR << 8) | LRS_ABI_VERSION_PATCH)
@@ -88,6 +92,8 @@ enum {
 #define LRS_CAP_SCAN_GATED      (1u << 1)
 #define LRS_CAP_SCAN_DIAG_OUTER (1u << 2)
 #define LRS_CAP_SCAN_DELTA      (1u << 3)
+#define LRS_CAP_ELEM_BACKWARD   (1u << 4)   /* since 1.1 */
+#define LRS_CAP_ELEM_STEP       (1u << 5)   /* since 1.1 */
 
 /* Packed version of the library actually loaded. */
 uint32_t lrs_abi_version(void);
@@ -174,6 +180,60 @@ lrs_status lrs_scan_fma(LrsContext* ctx, const float* a, const float* b, const f
 lrs_status lrs_scan_gated(LrsContext* ctx, const float* a, const float* u, const float* s0,
                           float* s, float* s_final, int32_t B, int32_t T, int32_t N,
                           void* stream);
+
+/* ---- reverse (gradient) pass of the elementwise scans -------------------
+ * The back-ends' reverse-scan entry [SunnyNet log §8], read as the gradient
+ * pass that training needs.  Given the forward call's inputs and states and
+ * the gradient of a loss with respect to its outputs, returns the gradients
+ * with respect to its inputs.  With gs_t the total gradient reaching s_t,
+ *
+ *   gs_T = ds_T + ds_final,    gs_t = ds_t + a_{t+1} gs_{t+1}   (t < T)
+ *   FMA form:    da_t = gs_t s_{t-1},           db_t = gs_t
+ *   gated form:  da_t = gs_t (s_{t-1} - u_t),    du_t = gs_t (1 - a_t)
+ *   ds0 = a_1 gs_1,                             s_0 = s0
+ *
+ *   a, u          fp32 [B,T,N]   the forward inputs (u: gated form only)
+ *   s0            fp32 [B,N]     the forward initial state; NULL means zeros
+ *   s             fp32 [B,T,N]   the forward states (s[:,t-1,:] = s_t)
+ *   ds            fp32 [B,T,N]   gradient with respect to s
+ *   ds_final      fp32 [B,N]     gradient with respect to s_final; NULL means zeros
+ *   da, db (du)   fp32 [B,T,N]   outputs
+ *   ds0           fp32 [B,N]     output; NULL skips it
+ *
+ * One pass over the data: a, ds and s (and u) are read once and da, db (du)
+ * written once, 20 (24) bytes per element.  The gradient recursion runs as a
+ * scan over reversed time with the same chunking and look-back as the
+ * forward scans (and the same context workspace); errors, limits and
+ * alignment rules are those of lrs_scan_fma.
+ */
+lrs_status lrs_scan_fma_backward(LrsContext* ctx, const float* a, const float* s0,
+                                 const float* s, const float* ds, const float* ds_final,
+                                 float* da, float* db, float* ds0, int32_t B, int32_t T,
+                                 int32_t N, void* stream);
+
+lrs_status lrs_scan_gated_backward(LrsContext* ctx, const float* a, const float* u,
+                                   const float* s0, const float* s, const float* ds,
+                                   const float* ds_final, float* da, float* du, float* ds0,
+                                   int32_t B, int32_t T, int32_t N, void* stream);
+
+/* ---- single step of the elementwise scans --------------------------------
+ * The back-ends' single-step entry [SunnyNet log §8]: one time step for every
+ * channel, updating the state in place (decode).  A single-sequence step is
+ * tiny and costs mostly call overhead [SunnyNet log §2.4], so one call should
+ * carry every channel of every sequence and layer that steps together.
+ *
+ *   a, b (or u)   fp32 [B,N]   this step's inputs
+ *   s             fp32 [B,N]   state, read and overwritten:
+ *                              s = a s + b   or   s = fma(a, s - u, u)
+ *
+ * Bit-identical to lrs_scan_fma / lrs_scan_gated with T = 1.  s must not
+ * overlap a or b (u).  Errors as lrs_scan_fma.
+ */
+lrs_status lrs_step_fma(LrsContext* ctx, const float* a, const float* b, float* s, int32_t B,
+                        int32_t N, void* stream);
+
+lrs_status lrs_step_gated(LrsContext* ctx, const float* a, const float* u, float* s, int32_t B,
+                          int32_t N, void* stream);
 
 /* ---- decay-separable outer-product state scan ---------------------------
  * Mamba-2 [SunnyNet log §4.1]: one decay exp(dt*A) per head and step shared by

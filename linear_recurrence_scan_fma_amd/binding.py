@@ -24,6 +24,7 @@ LRS_ABI_VERSION_MAJOR = 1
 LRS_OK, LRS_E_INVAL, LRS_E_NOMEM, LRS_E_IO, LRS_E_FORMAT, LRS_E_UNSUPPORTED, LRS_E_DEVICE = (
     0, -1, -2, -3, -4, -5, -6)
 LRS_CAP_SCAN_FMA, LRS_CAP_SCAN_GATED, LRS_CAP_SCAN_DIAG_OUTER, LRS_CAP_SCAN_DELTA = 1, 2, 4, 8
+LRS_CAP_ELEM_BACKWARD, LRS_CAP_ELEM_STEP = 16, 32
 LRS_PARAM_ELEM_SCHEDULE = 1
 LRS_PARAM_DIAG_SEGMENTS = 2
 LRS_ELEM_SCHEDULE_AUTO, LRS_ELEM_SCHEDULE_STREAM, LRS_ELEM_SCHEDULE_LOOKBACK = 0, 1, 2
@@ -44,6 +45,11 @@ SIGNATURES = {
     "lrs_context_check": (_I32, [_P]),
     "lrs_scan_fma": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
     "lrs_scan_gated": (_I32, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "lrs_scan_fma_backward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
+    "lrs_scan_gated_backward": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _I32, _I32, _I32, _P]),
+    "lrs_step_fma": (_I32, [_P, _P, _P, _P, _I32, _I32, _P]),
+    "lrs_step_gated": (_I32, [_P, _P, _P, _P, _I32, _I32, _P]),
     "lrs_scan_diag_outer": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _F, _P, _P, _P,
                                    _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_delta": (_I32, [_P, _P, _P, _P, _P, _F, _P, _P, _P,
@@ -198,6 +204,64 @@ def lrs_scan_gated(ctx, a, u, s0, s, s_final, stream=None) -> None:
     _elem("lrs_scan_gated", ctx, a, u, s0, s, s_final, stream)
 
 
+def lrs_scan_fma_backward(ctx, a, s0, s, ds, ds_final, da, db, ds0, stream=None) -> None:
+    """Gradient pass of lrs_scan_fma: a, s, ds, da, db [B,T,N] fp32; s0,
+    ds_final (None = zeros) and ds0 (None = not computed) [B,N] fp32."""
+    import torch
+
+    B, T, N = a.shape
+    d = ctx.device
+    f32 = torch.float32
+    args = (
+        _ptr(a, f32, (B, T, N), "a", d), _ptr(s0, f32, (B, N), "s0", d),
+        _ptr(s, f32, (B, T, N), "s", d), _ptr(ds, f32, (B, T, N), "ds", d),
+        _ptr(ds_final, f32, (B, N), "ds_final", d), _ptr(da, f32, (B, T, N), "da", d),
+        _ptr(db, f32, (B, T, N), "db", d), _ptr(ds0, f32, (B, N), "ds0", d),
+    )
+    st = lib().lrs_scan_fma_backward(ctx.handle, *args, B, T, N, _stream(stream, d))
+    _check("lrs_scan_fma_backward", st)
+
+
+def lrs_scan_gated_backward(ctx, a, u, s0, s, ds, ds_final, da, du, ds0, stream=None) -> None:
+    """Gradient pass of lrs_scan_gated; u, du [B,T,N] fp32, the rest as
+    lrs_scan_fma_backward."""
+    import torch
+
+    B, T, N = a.shape
+    d = ctx.device
+    f32 = torch.float32
+    args = (
+        _ptr(a, f32, (B, T, N), "a", d), _ptr(u, f32, (B, T, N), "u", d),
+        _ptr(s0, f32, (B, N), "s0", d), _ptr(s, f32, (B, T, N), "s", d),
+        _ptr(ds, f32, (B, T, N), "ds", d), _ptr(ds_final, f32, (B, N), "ds_final", d),
+        _ptr(da, f32, (B, T, N), "da", d), _ptr(du, f32, (B, T, N), "du", d),
+        _ptr(ds0, f32, (B, N), "ds0", d),
+    )
+    st = lib().lrs_scan_gated_backward(ctx.handle, *args, B, T, N, _stream(stream, d))
+    _check("lrs_scan_gated_backward", st)
+
+
+def _step(name, ctx, a, x, s, stream):
+    import torch
+
+    B, N = a.shape
+    d = ctx.device
+    f32 = torch.float32
+    args = (_ptr(a, f32, (B, N), "a", d), _ptr(x, f32, (B, N), "b/u", d), _ptr(s, f32, (B, N), "s", d))
+    st = getattr(lib(), name)(ctx.handle, *args, B, N, _stream(stream, d))
+    _check(name, st)
+
+
+def lrs_step_fma(ctx, a, b, s, stream=None) -> None:
+    """One step in place, s = a s + b; a, b, s [B,N] fp32."""
+    _step("lrs_step_fma", ctx, a, b, s, stream)
+
+
+def lrs_step_gated(ctx, a, u, s, stream=None) -> None:
+    """One step in place, s = a s + (1 - a) u; a, u, s [B,N] fp32."""
+    _step("lrs_step_gated", ctx, a, u, s, stream)
+
+
 def lrs_scan_diag_outer(ctx, q, k, v, g, decay_mode, k_scale, scale, s0, o, s_final,
                         stream=None) -> None:
     """S_t = diag(exp(g_t)) S_{t-1} + (kappa_t k_t) v_t^T, o_t = scale S_t^T q_t.
@@ -256,6 +320,21 @@ def scan_elementwise(ctx, kind, a, x, s0=None, stream=None):
     fn = lrs_scan_fma if kind == "fma" else lrs_scan_gated
     fn(ctx, a, x, s0, s, s_final, stream)
     return s, s_final
+
+
+def scan_elementwise_backward(ctx, kind, a, x, s, ds, s0=None, ds_final=None, stream=None):
+    """Allocates da, dx, ds0 and runs the gradient pass of scan_elementwise
+    (x = b for kind 'fma', unused there; x = u for 'gated').  Returns (da, dx, ds0)."""
+    import torch
+
+    da = torch.empty_like(a)
+    dx = torch.empty_like(a)
+    ds0 = torch.empty((a.shape[0], a.shape[2]), dtype=a.dtype, device=a.device)
+    if kind == "fma":
+        lrs_scan_fma_backward(ctx, a, s0, s, ds, ds_final, da, dx, ds0, stream)
+    else:
+        lrs_scan_gated_backward(ctx, a, x, s0, s, ds, ds_final, da, dx, ds0, stream)
+    return da, dx, ds0
 
 
 def scan_diag_outer(ctx, q, k, v, g, decay_mode, k_scale=None, scale=1.0, s0=None, stream=None):

@@ -123,39 +123,17 @@ lrs_status next_epoch(LrsContext* ctx, hipStream_t stream, unsigned int* out) {
     return LRS_OK;
 }
 
-lrs_status scan_elem(LrsContext* ctx, bool gated, const float* a, const float* x,
-                     const float* s0, float* s, float* s_final, int32_t B, int32_t T, int32_t N,
-                     void* stream_ptr) {
-    if (!ctx || !a || !x || !s || !s_final) return LRS_E_INVAL;
-    if (B < 1 || T < 1 || N < 1) return LRS_E_INVAL;
-    if (!aligned(a, 4) || !aligned(x, 4) || !aligned(s0, 4) || !aligned(s, 4) || !aligned(s_final, 4))
-        return LRS_E_INVAL;
-    int64_t seq = B;
-    if (!mul_ok(seq, T) || !mul_ok(seq, N) || seq > INT64_MAX / 8) return LRS_E_INVAL;
-    const size_t seq_bytes = static_cast<size_t>(seq) * sizeof(float);
-    const size_t st_bytes = static_cast<size_t>(B) * N * sizeof(float);
-    const Span ins[] = {{a, seq_bytes}, {x, seq_bytes}, {s0, st_bytes}};
-    const Span outs[] = {{s, seq_bytes}, {s_final, st_bytes}};
-    if (!outputs_disjoint(outs, 2, ins, 3)) return LRS_E_INVAL;
-
-    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    DeviceGuard guard(ctx->device);
-    if (!guard.ok()) return LRS_E_DEVICE;
-
-    const bool al16 = aligned(a, 16) && aligned(x, 16) && aligned(s, 16);
+// Resolves the schedule and plan of an elementwise pass over [B,T,N] and, for
+// the look-back schedule, sizes the status words and takes a fresh epoch.
+// Fills p.B/T/N, p.gated, p.schedule and the look-back fields.
+lrs_status elem_prepare(LrsContext* ctx, bool gated, int32_t B, int32_t T, int32_t N, bool al16,
+                        hipStream_t stream, lrs::ElemPlan& plan, lrs::ElemParams& p) {
     int schedule = ctx->elem_schedule;
     if (schedule == LRS_ELEM_SCHEDULE_AUTO)
         schedule = lrs::elem_auto_schedule(B, T, N, al16, ctx->num_cus);
     const int ksched = schedule == LRS_ELEM_SCHEDULE_LOOKBACK ? lrs::kElemLookback : lrs::kElemStream;
-    const lrs::ElemPlan plan = lrs::elem_plan(B, T, N, al16, ksched);
+    plan = lrs::elem_plan(B, T, N, al16, ksched);
     if (plan.grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
-
-    lrs::ElemParams p{};
-    p.a = a;
-    p.x = x;
-    p.s0 = s0;
-    p.s = s;
-    p.s_final = s_final;
     p.B = B;
     p.T = T;
     p.N = N;
@@ -171,8 +149,116 @@ lrs_status scan_elem(LrsContext* ctx, bool gated, const float* a, const float* x
         p.counter_base = ctx->counter_base;
         p.error_flag = reinterpret_cast<unsigned int*>(ctx->fixed + 1);
     }
+    return LRS_OK;
+}
+
+// Bookkeeping after a successful elementwise launch.
+void elem_launched(LrsContext* ctx, const lrs::ElemPlan& plan, const lrs::ElemParams& p,
+                   hipStream_t stream) {
+    if (p.schedule == lrs::kElemLookback) ctx->counter_base += static_cast<unsigned long long>(plan.grid);
+    ctx->last_stream = stream;
+    ctx->used = true;
+}
+
+// Shared size checks of the elementwise calls: dims >= 1 and B*T*N*8 bytes
+// representable.  Returns the element count in `seq`.
+bool elem_dims_ok(int32_t B, int32_t T, int32_t N, int64_t& seq) {
+    if (B < 1 || T < 1 || N < 1) return false;
+    seq = B;
+    return mul_ok(seq, T) && mul_ok(seq, N) && seq <= INT64_MAX / 8;
+}
+
+lrs_status scan_elem(LrsContext* ctx, bool gated, const float* a, const float* x,
+                     const float* s0, float* s, float* s_final, int32_t B, int32_t T, int32_t N,
+                     void* stream_ptr) {
+    if (!ctx || !a || !x || !s || !s_final) return LRS_E_INVAL;
+    int64_t seq = 0;
+    if (!elem_dims_ok(B, T, N, seq)) return LRS_E_INVAL;
+    if (!aligned(a, 4) || !aligned(x, 4) || !aligned(s0, 4) || !aligned(s, 4) || !aligned(s_final, 4))
+        return LRS_E_INVAL;
+    const size_t seq_bytes = static_cast<size_t>(seq) * sizeof(float);
+    const size_t st_bytes = static_cast<size_t>(B) * N * sizeof(float);
+    const Span ins[] = {{a, seq_bytes}, {x, seq_bytes}, {s0, st_bytes}};
+    const Span outs[] = {{s, seq_bytes}, {s_final, st_bytes}};
+    if (!outputs_disjoint(outs, 2, ins, 3)) return LRS_E_INVAL;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+
+    const bool al16 = aligned(a, 16) && aligned(x, 16) && aligned(s, 16);
+    lrs::ElemPlan plan{};
+    lrs::ElemParams p{};
+    const lrs_status st = elem_prepare(ctx, gated, B, T, N, al16, stream, plan, p);
+    if (st != LRS_OK) return st;
+    p.a = a;
+    p.x = x;
+    p.s0 = s0;
+    p.s = s;
+    p.s_final = s_final;
     if (lrs::launch_scan_elem(p, plan, stream) != hipSuccess) return LRS_E_DEVICE;
-    if (ksched == lrs::kElemLookback) ctx->counter_base += static_cast<unsigned long long>(plan.grid);
+    elem_launched(ctx, plan, p, stream);
+    return LRS_OK;
+}
+
+lrs_status scan_elem_bwd(LrsContext* ctx, bool gated, const float* a, const float* u,
+                         const float* s0, const float* s, const float* ds, const float* ds_final,
+                         float* da, float* dx, float* ds0, int32_t B, int32_t T, int32_t N,
+                         void* stream_ptr) {
+    if (!ctx || !a || !s || !ds || !da || !dx || (gated && !u)) return LRS_E_INVAL;
+    int64_t seq = 0;
+    if (!elem_dims_ok(B, T, N, seq)) return LRS_E_INVAL;
+    if (!aligned(a, 4) || !aligned(u, 4) || !aligned(s0, 4) || !aligned(s, 4) || !aligned(ds, 4) ||
+        !aligned(ds_final, 4) || !aligned(da, 4) || !aligned(dx, 4) || !aligned(ds0, 4))
+        return LRS_E_INVAL;
+    const size_t seq_bytes = static_cast<size_t>(seq) * sizeof(float);
+    const size_t st_bytes = static_cast<size_t>(B) * N * sizeof(float);
+    const Span ins[] = {{a, seq_bytes}, {u, seq_bytes}, {s0, st_bytes}, {s, seq_bytes},
+                        {ds, seq_bytes}, {ds_final, st_bytes}};
+    const Span outs[] = {{da, seq_bytes}, {dx, seq_bytes}, {ds0, st_bytes}};
+    if (!outputs_disjoint(outs, 3, ins, 6)) return LRS_E_INVAL;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+
+    const bool al16 = aligned(a, 16) && aligned(u, 16) && aligned(s, 16) && aligned(ds, 16) &&
+                      aligned(da, 16) && aligned(dx, 16);
+    lrs::ElemBwdParams p{};
+    lrs::ElemPlan plan{};
+    const lrs_status st = elem_prepare(ctx, gated, B, T, N, al16, stream, plan, p.scan);
+    if (st != LRS_OK) return st;
+    p.scan.s0 = ds_final;   // the reversed scan starts from the final state's gradient
+    p.a = a;
+    p.u = gated ? u : nullptr;
+    p.s0 = s0;
+    p.s = s;
+    p.ds = ds;
+    p.da = da;
+    p.dx = dx;
+    p.ds0 = ds0;
+    if (lrs::launch_scan_elem_bwd(p, plan, stream) != hipSuccess) return LRS_E_DEVICE;
+    elem_launched(ctx, plan, p.scan, stream);
+    return LRS_OK;
+}
+
+lrs_status step_elem(LrsContext* ctx, bool gated, const float* a, const float* x, float* s,
+                     int32_t B, int32_t N, void* stream_ptr) {
+    if (!ctx || !a || !x || !s) return LRS_E_INVAL;
+    int64_t n = 0;
+    if (!elem_dims_ok(B, 1, N, n)) return LRS_E_INVAL;
+    if (!aligned(a, 4) || !aligned(x, 4) || !aligned(s, 4)) return LRS_E_INVAL;
+    const size_t bytes = static_cast<size_t>(n) * sizeof(float);
+    const Span ins[] = {{a, bytes}, {x, bytes}};
+    const Span outs[] = {{s, bytes}};
+    if (!outputs_disjoint(outs, 1, ins, 2)) return LRS_E_INVAL;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    DeviceGuard guard(ctx->device);
+    if (!guard.ok()) return LRS_E_DEVICE;
+    const bool al16 = aligned(a, 16) && aligned(x, 16) && aligned(s, 16);
+    if (lrs::launch_step_elem(gated, a, x, s, n, al16, ctx->num_cus, stream) != hipSuccess)
+        return LRS_E_DEVICE;
     ctx->last_stream = stream;
     ctx->used = true;
     return LRS_OK;
@@ -190,7 +276,8 @@ LRS_API lrs_status lrs_abi_check(int32_t caller_major) {
 }
 
 LRS_API uint32_t lrs_abi_caps(void) {
-    return LRS_CAP_SCAN_FMA | LRS_CAP_SCAN_GATED | LRS_CAP_SCAN_DIAG_OUTER | LRS_CAP_SCAN_DELTA;
+    return LRS_CAP_SCAN_FMA | LRS_CAP_SCAN_GATED | LRS_CAP_SCAN_DIAG_OUTER | LRS_CAP_SCAN_DELTA |
+           LRS_CAP_ELEM_BACKWARD | LRS_CAP_ELEM_STEP;
 }
 
 LRS_API const char* lrs_status_string(lrs_status status) {
@@ -302,6 +389,30 @@ LRS_API lrs_status lrs_scan_gated(LrsContext* ctx, const float* a, const float* 
                                   const float* s0, float* s, float* s_final, int32_t B,
                                   int32_t T, int32_t N, void* stream) {
     return scan_elem(ctx, true, a, u, s0, s, s_final, B, T, N, stream);
+}
+
+LRS_API lrs_status lrs_scan_fma_backward(LrsContext* ctx, const float* a, const float* s0,
+                                         const float* s, const float* ds, const float* ds_final,
+                                         float* da, float* db, float* ds0, int32_t B, int32_t T,
+                                         int32_t N, void* stream) {
+    return scan_elem_bwd(ctx, false, a, nullptr, s0, s, ds, ds_final, da, db, ds0, B, T, N, stream);
+}
+
+LRS_API lrs_status lrs_scan_gated_backward(LrsContext* ctx, const float* a, const float* u,
+                                           const float* s0, const float* s, const float* ds,
+                                           const float* ds_final, float* da, float* du, float* ds0,
+                                           int32_t B, int32_t T, int32_t N, void* stream) {
+    return scan_elem_bwd(ctx, true, a, u, s0, s, ds, ds_final, da, du, ds0, B, T, N, stream);
+}
+
+LRS_API lrs_status lrs_step_fma(LrsContext* ctx, const float* a, const float* b, float* s,
+                                int32_t B, int32_t N, void* stream) {
+    return step_elem(ctx, false, a, b, s, B, N, stream);
+}
+
+LRS_API lrs_status lrs_step_gated(LrsContext* ctx, const float* a, const float* u, float* s,
+                                  int32_t B, int32_t N, void* stream) {
+    return step_elem(ctx, true, a, u, s, B, N, stream);
 }
 
 namespace {

@@ -46,6 +46,28 @@ ElemPlan elem_plan(int64_t B, int64_t T, int64_t N, bool aligned16, int schedule
 int elem_auto_schedule(int64_t B, int64_t T, int64_t N, bool aligned16, int num_cus);
 hipError_t launch_scan_elem(const ElemParams& p, const ElemPlan& plan, hipStream_t stream);
 
+// Reverse (gradient) pass of an elementwise scan: the reversed FMA scan of the
+// incoming gradients, fused with the input gradients.  `scan` carries the
+// shape, form (gated), schedule and look-back state; scan.s0 is the gradient
+// of the final state (nullable) and scan.a/x/s/s_final are unused.  The plan
+// is elem_plan() of the same shape.
+struct ElemBwdParams {
+    ElemParams scan;
+    const float* a;
+    const float* u;      // gated form only
+    const float* s0;     // forward initial state, nullable
+    const float* s;      // forward states
+    const float* ds;
+    float* da;
+    float* dx;           // db (FMA form) or du (gated form)
+    float* ds0;          // nullable
+};
+hipError_t launch_scan_elem_bwd(const ElemBwdParams& p, const ElemPlan& plan, hipStream_t stream);
+
+// One in-place step s = a s + x (or the gated form) over n channels.
+hipError_t launch_step_elem(bool gated, const float* a, const float* x, float* s, int64_t n, bool aligned16,
+                            int num_cus, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Decay-separable outer-product state scan.
 // ---------------------------------------------------------------------------

@@ -10,6 +10,9 @@ float64 -> float32 -> bfloat16, each step round-to-nearest-even):
 
 * elementwise, small:  a ~ U(0.5, 1), b ~ N(0, 1), u ~ N(0, 1), s0 = none, [B,T,N]
 * elementwise, gated:  a = sigmoid(z), z ~ N(2, 1); u ~ N(0, 1); s0 ~ N(0, 1)
+* gradient pass:       incoming gradients ds, ds_final ~ N(0, 1); at the full
+                       size the forward states it reads are stand-in N(0, 1)
+                       draws (the pass is defined for any given states)
 * Mamba-2 shaped:      dt = softplus(N(0,1)) [B,T,H]; A_h = -exp(U(0,2)) [H];
                        g = dt * A_h (one log-decay per head and step);
                        B, C ~ N(0,1) bf16 [B,T,1,K]; x ~ N(0,1) bf16 [B,T,H,V]
@@ -141,3 +144,13 @@ def random_state(shape, seed, std=1.0):
     """An fp32 initial state ~ N(0, std^2) for continuation and unit tests."""
     rng = np.random.default_rng(seed)
     return _f32(rng.standard_normal(shape) * std)
+
+
+def random_normal(shape, seed):
+    """An fp32 N(0, 1) tensor of any size, drawn one leading-axis slice at a
+    time (incoming gradients, stand-in states of the gradient pass)."""
+    rng = np.random.default_rng(seed)
+    out = torch.empty(tuple(shape), dtype=torch.float32)
+    for i in range(shape[0]):
+        out[i] = _f32(rng.standard_normal(tuple(shape[1:])))
+    return out

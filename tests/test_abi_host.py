@@ -21,6 +21,9 @@ def _declared_functions():
 
 def _header_int(name):
     src = open(HEADER).read()
+    m = re.search(rf"#define {name}\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    if m:
+        return int(m.group(1)) << int(m.group(2))
     m = re.search(rf"\b{name}\s*=\s*(-?\d+)", src) or re.search(rf"#define {name}\s+\(?(\d+)", src)
     return int(m.group(1))
 
@@ -34,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 12
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), f"{n} declared in lrs_abi.h but not exported"
     assert set(names) == set(binding.SIGNATURES), "binding and header disagree"
@@ -43,14 +46,17 @@ def test_exports_every_declared_symbol(lib):
 def test_python_mirrors_header_constants():
     for name in ("LRS_OK", "LRS_E_INVAL", "LRS_E_NOMEM", "LRS_E_UNSUPPORTED", "LRS_E_DEVICE",
                  "LRS_PARAM_ELEM_SCHEDULE", "LRS_ELEM_SCHEDULE_STREAM",
-                 "LRS_ELEM_SCHEDULE_LOOKBACK"):
+                 "LRS_ELEM_SCHEDULE_LOOKBACK", "LRS_PARAM_DIAG_SEGMENTS", "LRS_CAP_SCAN_FMA",
+                 "LRS_CAP_SCAN_GATED", "LRS_CAP_SCAN_DIAG_OUTER", "LRS_CAP_SCAN_DELTA",
+                 "LRS_CAP_ELEM_BACKWARD", "LRS_CAP_ELEM_STEP"):
         assert getattr(binding, name) == _header_int(name), name
     assert binding.LRS_ABI_VERSION_MAJOR == _header_int("LRS_ABI_VERSION_MAJOR")
 
 
 def test_version_and_check(lib):
     v = binding.lrs_abi_version()
-    assert v == (1 << 16) | (0 << 8) | 0
+    assert v == (1 << 16) | (1 << 8) | 0
+    assert binding.LRS_ABI_VERSION_MAJOR == 1
     assert binding.lrs_abi_check(1) == binding.LRS_OK
     assert binding.lrs_abi_check(2) == binding.LRS_E_UNSUPPORTED
     assert binding.lrs_abi_check(0) == binding.LRS_E_UNSUPPORTED
@@ -59,7 +65,8 @@ def test_version_and_check(lib):
 def test_caps_and_status_strings(lib):
     caps = binding.lrs_abi_caps()
     for bit in (binding.LRS_CAP_SCAN_FMA, binding.LRS_CAP_SCAN_GATED,
-                binding.LRS_CAP_SCAN_DIAG_OUTER, binding.LRS_CAP_SCAN_DELTA):
+                binding.LRS_CAP_SCAN_DIAG_OUTER, binding.LRS_CAP_SCAN_DELTA,
+                binding.LRS_CAP_ELEM_BACKWARD, binding.LRS_CAP_ELEM_STEP):
         assert caps & bit
     for st in (0, -1, -2, -3, -4, -5, -6, 17, -99):
         s = binding.lrs_status_string(st)
@@ -72,6 +79,12 @@ def test_null_context_and_null_out_are_rejected(lib):
     fake = P(0x1000)
     assert lib.lrs_scan_fma(None, fake, fake, None, fake, fake, 1, 1, 1, None) == binding.LRS_E_INVAL
     assert lib.lrs_scan_gated(None, fake, fake, None, fake, fake, 1, 1, 1, None) == binding.LRS_E_INVAL
+    assert lib.lrs_scan_fma_backward(None, fake, None, fake, fake, None, fake, fake, None,
+                                     1, 1, 1, None) == binding.LRS_E_INVAL
+    assert lib.lrs_scan_gated_backward(None, fake, fake, None, fake, fake, None, fake, fake, None,
+                                       1, 1, 1, None) == binding.LRS_E_INVAL
+    assert lib.lrs_step_fma(None, fake, fake, fake, 1, 1, None) == binding.LRS_E_INVAL
+    assert lib.lrs_step_gated(None, fake, fake, fake, 1, 1, None) == binding.LRS_E_INVAL
     assert lib.lrs_context_create(0, None) == binding.LRS_E_INVAL
     assert lib.lrs_context_set_param(None, 1, 0) == binding.LRS_E_INVAL
     assert lib.lrs_context_check(None) == binding.LRS_E_INVAL

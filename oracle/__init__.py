@@ -76,6 +76,10 @@ def _load():
             f = getattr(lib, name + sfx)
             f.argtypes = [P, P, P, P, R, P, P, P, I64, I64, I64, I64, I64, I]
             f.restype = None
+        for name in ("orc_scan_delta_decay", "orc_scan_delta_decay_explicit"):
+            f = getattr(lib, name + sfx)
+            f.argtypes = [P, P, P, P, P, R, P, P, P, I64, I64, I64, I64, I64, I]
+            f.restype = None
     lib.orc_version.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -250,3 +254,35 @@ def scan_delta_explicit(q, k, v, beta, scale=1.0, s0=None, dtype=np.float64, nth
     """Delta rule, explicit form S_t = (I - beta k k^T) S_{t-1} + beta k v^T
     [SunnyNet log §4.2], implemented separately from the rank-1 form."""
     return _delta("orc_scan_delta_explicit", q, k, v, beta, scale, s0, dtype, nthreads)
+
+
+def _delta_decay(name, q, k, v, g, beta, scale, s0, dtype, nthreads):
+    q, k, v, g, beta = (_arr(x, dtype) for x in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    V = v.shape[3]
+    _check_shape("k", k, (B, T, H, K))
+    _check_shape("g", g, (B, T, H, K))
+    _check_shape("v", v, (B, T, H, V))
+    _check_shape("beta", beta, (B, T, H))
+    s0 = _arr(s0, dtype)
+    _check_shape("s0", s0, (B, H, K, V))
+    o = np.empty((B, T, H, V), dtype=dtype)
+    fin = np.empty((B, H, K, V), dtype=dtype)
+    fn = getattr(_load(), name + _sfx(dtype))
+    fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(s0), _ptr(o), _ptr(fin),
+       B, T, H, K, V, nthreads or default_threads())
+    return o, fin
+
+
+def scan_delta_decay(q, k, v, g, beta, scale=1.0, s0=None, dtype=np.float64, nthreads=None):
+    """Delta rule with a per-key decay, rank-1 form [SunnyNet log §5.1, RWKV-7]:
+    delta_t = beta_t (v_t - S_{t-1}^T k_t), S_t = diag(exp(g_t)) S_{t-1} + k_t delta_t^T,
+    o_t = scale S_t^T q_t.  Shapes: q, k, g [B,T,H,K]; v [B,T,H,V]; beta [B,T,H].
+    """
+    return _delta_decay("orc_scan_delta_decay", q, k, v, g, beta, scale, s0, dtype, nthreads)
+
+
+def scan_delta_decay_explicit(q, k, v, g, beta, scale=1.0, s0=None, dtype=np.float64, nthreads=None):
+    """The same update as a dense transition S_t = (diag(exp(g_t)) - beta k k^T) S_{t-1}
+    + beta k v^T [SunnyNet log §5.1], implemented separately from the rank-1 form."""
+    return _delta_decay("orc_scan_delta_decay_explicit", q, k, v, g, beta, scale, s0, dtype, nthreads)

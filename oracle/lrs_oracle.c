@@ -1,8 +1,8 @@
 /*
  * lrs_oracle.c -- plain sequential CPU reference for the linear-recurrence
  * scans (first-order FMA and gated scans and their reverse (gradient) passes,
- * decay-separable outer-product state scan, delta-rule state scan, and an
- * explicit second form of the delta rule).
+ * decay-separable outer-product state scan, delta-rule state scan with and
+ * without a per-key decay, and an explicit second form of each delta rule).
  *
  * TEST INFRASTRUCTURE ONLY.  This file, its Python wrapper and everything
  * else under oracle/ exist to check the GPU library.  Only the test suite,
@@ -46,4 +46,4 @@
 #undef ORC_EXP
 
 /* Version of this oracle's arithmetic; bumped whenever a formula changes. */
-int orc_version(void) { return 2; }
+int orc_version(void) { return 3; }

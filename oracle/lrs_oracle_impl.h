@@ -284,6 +284,110 @@ void ORC_FN(orc_scan_delta_explicit)(const REAL* q, const REAL* k, const REAL* v
     }
 }
 
+/*
+ * Delta rule with a per-key decay (RWKV-7's state update), rank-1 form, per
+ * (b, h):
+ *     w_t[i]   = exp(g[b,t,h,i])                         (decay on the key axis)
+ *     p_j      = sum_i S_{t-1}[i][j] * k_t[i]             (read-back of the OLD state)
+ *     delta_j  = beta_t * (v_t[j] - p_j)
+ *     S_t[i][j]= w_t[i] * S_{t-1}[i][j] + k_t[i] * delta_j
+ *     o_t[j]   = scale * sum_i S_t[i][j] * q_t[i]
+ * [SunnyNet log §5.1]: the page writes S_t = S_{t-1} (.) w_t - (S_{t-1} k_t) k_t^T
+ * + v_t k_t^T for a state stored value-major; stored key-major ([K,V]) as
+ * here, with the in-context rate beta_t that the page's formula leaves out
+ * (beta = 1 gives the page's form), that is
+ * S_t = (diag(w_t) - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T: the removal
+ * reads the state before the decay.  With w = 1 it is orc_scan_delta.
+ * Layouts: q, k, g [B,T,H,K]; v, o [B,T,H,V]; beta [B,T,H]; s0, s_final [B,H,K,V].
+ */
+void ORC_FN(orc_scan_delta_decay)(const REAL* q, const REAL* k, const REAL* v, const REAL* g,
+                                  const REAL* beta, REAL scale, const REAL* s0, REAL* o,
+                                  REAL* s_final, int64_t B, int64_t T, int64_t H, int64_t K,
+                                  int64_t V, int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int64_t b = bh / H, h = bh % H;
+        REAL* S = (REAL*)malloc(sizeof(REAL) * (size_t)(K * V));
+        REAL* dl = (REAL*)malloc(sizeof(REAL) * (size_t)V);
+        for (int64_t e = 0; e < K * V; ++e) S[e] = s0 ? s0[bh * K * V + e] : (REAL)0;
+        for (int64_t t = 0; t < T; ++t) {
+            const REAL* qt = q + ((b * T + t) * H + h) * K;
+            const REAL* kt = k + ((b * T + t) * H + h) * K;
+            const REAL* gt = g + ((b * T + t) * H + h) * K;
+            const REAL* vt = v + ((b * T + t) * H + h) * V;
+            REAL bt = beta[(b * T + t) * H + h];
+            for (int64_t j = 0; j < V; ++j) {
+                REAL p = 0;
+                for (int64_t i = 0; i < K; ++i) p += S[i * V + j] * kt[i];
+                dl[j] = bt * (vt[j] - p);
+            }
+            for (int64_t i = 0; i < K; ++i) {
+                REAL wi = ORC_EXP(gt[i]);
+                for (int64_t j = 0; j < V; ++j) S[i * V + j] = wi * S[i * V + j] + kt[i] * dl[j];
+            }
+            REAL* ot = o + ((b * T + t) * H + h) * V;
+            for (int64_t j = 0; j < V; ++j) {
+                REAL acc = 0;
+                for (int64_t i = 0; i < K; ++i) acc += S[i * V + j] * qt[i];
+                ot[j] = scale * acc;
+            }
+        }
+        for (int64_t e = 0; e < K * V; ++e) s_final[bh * K * V + e] = S[e];
+        free(S);
+        free(dl);
+    }
+}
+
+/*
+ * The same update as orc_scan_delta_decay, written as a dense K x K
+ * transition [SunnyNet log §5.1, in the key-major reading above]:
+ *     M_t = diag(w_t) - beta_t * k_t k_t^T,   S_t = M_t S_{t-1} + beta_t * k_t v_t^T
+ * implemented separately from the rank-1 form.  Readout and layouts as there.
+ */
+void ORC_FN(orc_scan_delta_decay_explicit)(const REAL* q, const REAL* k, const REAL* v,
+                                           const REAL* g, const REAL* beta, REAL scale,
+                                           const REAL* s0, REAL* o, REAL* s_final, int64_t B,
+                                           int64_t T, int64_t H, int64_t K, int64_t V,
+                                           int nthreads) {
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t bh = 0; bh < B * H; ++bh) {
+        int64_t b = bh / H, h = bh % H;
+        REAL* S = (REAL*)malloc(sizeof(REAL) * (size_t)(K * V));
+        REAL* Sn = (REAL*)malloc(sizeof(REAL) * (size_t)(K * V));
+        REAL* M = (REAL*)malloc(sizeof(REAL) * (size_t)(K * K));
+        for (int64_t e = 0; e < K * V; ++e) S[e] = s0 ? s0[bh * K * V + e] : (REAL)0;
+        for (int64_t t = 0; t < T; ++t) {
+            const REAL* qt = q + ((b * T + t) * H + h) * K;
+            const REAL* kt = k + ((b * T + t) * H + h) * K;
+            const REAL* gt = g + ((b * T + t) * H + h) * K;
+            const REAL* vt = v + ((b * T + t) * H + h) * V;
+            REAL bt = beta[(b * T + t) * H + h];
+            for (int64_t r = 0; r < K; ++r)
+                for (int64_t c = 0; c < K; ++c)
+                    M[r * K + c] = (r == c ? ORC_EXP(gt[r]) : (REAL)0) - bt * kt[r] * kt[c];
+            for (int64_t r = 0; r < K; ++r)
+                for (int64_t j = 0; j < V; ++j) {
+                    REAL acc = 0;
+                    for (int64_t c = 0; c < K; ++c) acc += M[r * K + c] * S[c * V + j];
+                    Sn[r * V + j] = acc + bt * kt[r] * vt[j];
+                }
+            REAL* tmp = S;
+            S = Sn;
+            Sn = tmp;
+            REAL* ot = o + ((b * T + t) * H + h) * V;
+            for (int64_t j = 0; j < V; ++j) {
+                REAL acc = 0;
+                for (int64_t i = 0; i < K; ++i) acc += S[i * V + j] * qt[i];
+                ot[j] = scale * acc;
+            }
+        }
+        for (int64_t e = 0; e < K * V; ++e) s_final[bh * K * V + e] = S[e];
+        free(S);
+        free(Sn);
+        free(M);
+    }
+}
+
 #undef ORC_FN
 #undef ORC_CAT
 #undef ORC_CAT2

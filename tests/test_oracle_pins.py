@@ -590,6 +590,103 @@ def test_delta_chunked_ut_form():
 
 
 # ----------------------------------------------------------------------------
+# Delta rule with a per-key decay [SunnyNet log §5.1, RWKV-7's state update]
+# ----------------------------------------------------------------------------
+
+def _decay_inputs(r, B, T, H, K, V, with_s0=True, gmin=-0.6):
+    q, k, v, beta, s0 = _delta_inputs(r, B, T, H, K, V, with_s0=with_s0)
+    g = r.uniform(gmin, 0.0, (B, T, H, K))
+    return q, k, v, g, beta, s0
+
+
+@pytest.mark.parametrize("case", [0, 1])
+@pytest.mark.parametrize("form", ["rank1", "explicit"])
+def test_golden_delta_decay_hand(case, form):
+    d = _load("delta_decay_hand.json")["cases"][case]
+    fn = oracle.scan_delta_decay if form == "rank1" else oracle.scan_delta_decay_explicit
+    s0 = None if d["s0"] is None else np.array(d["s0"])
+    o, fin = fn(np.array(d["q"]), np.array(d["k"]), np.array(d["v"]), np.log(np.array(d["alpha"])),
+                np.array(d["beta"]), d["scale"], s0)
+    assert rel(o, d["o"]) < 1e-15
+    assert rel(fin, d["s_final"]) < 1e-15
+
+
+@pytest.mark.parametrize("K,V", [(6, 10), (10, 6), (8, 8)])
+def test_delta_decay_rank1_matches_explicit(K, V):
+    r = _rng(80 + K)
+    q, k, v, g, beta, s0 = _decay_inputs(r, 2, 40, 3, K, V)
+    g[0, 5] = 0.3            # a growing key now and then must not break the agreement
+    o1, f1 = oracle.scan_delta_decay(q, k, v, g, beta, 0.7, s0)
+    o2, f2 = oracle.scan_delta_decay_explicit(q, k, v, g, beta, 0.7, s0)
+    assert rel(o1, o2) < 1e-12
+    assert rel(f1, f2) < 1e-12
+
+
+def test_delta_decay_without_decay_is_the_delta_rule():
+    # w = 1 (g = 0) is DeltaNet's update, bit for bit
+    r = _rng(81)
+    q, k, v, g, beta, s0 = _decay_inputs(r, 2, 30, 2, 5, 7)
+    z = np.zeros_like(g)
+    o1, f1 = oracle.scan_delta_decay(q, k, v, z, beta, 0.8, s0)
+    o2, f2 = oracle.scan_delta(q, k, v, beta, 0.8, s0)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+    o1, f1 = oracle.scan_delta_decay_explicit(q, k, v, z, beta, 0.8, s0)
+    o2, f2 = oracle.scan_delta_explicit(q, k, v, beta, 0.8, s0)
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+
+
+def test_delta_decay_beta_zero_is_pure_decay():
+    # beta = 0: S_t = diag(exp(G_t)) S0 with G_t the running sum of g
+    r = _rng(82)
+    B, T, H, K, V = 2, 25, 2, 4, 6
+    q, k, v, g, _, s0 = _decay_inputs(r, B, T, H, K, V)
+    o, fin = oracle.scan_delta_decay(q, k, v, g, np.zeros((B, T, H)), 1.3, s0)
+    G = np.cumsum(g, axis=1)                                # [B,T,H,K]
+    ref = 1.3 * np.einsum("bthk,bhkv,bthk->bthv", np.exp(G), s0, q)
+    assert rel(o, ref) < 1e-13
+    assert rel(fin, np.exp(G[:, -1])[..., None] * s0) < 1e-13
+
+
+def test_delta_decay_k1_reduces_to_fma_scan():
+    # K = 1: each state column is s_t = (w_t - beta_t k_t^2) s_{t-1} + beta_t k_t v_t[j]
+    r = _rng(83)
+    B, T, H, V = 2, 60, 3, 5
+    q, k, v, g, beta, s0 = _decay_inputs(r, B, T, H, 1, V)
+    k = r.uniform(-1.0, 1.0, (B, T, H, 1))
+    o, fin = oracle.scan_delta_decay(q, k, v, g, beta, 1.0, s0)
+    a = np.exp(g[..., 0]) - beta * k[..., 0] ** 2                      # [B,T,H]
+    bb = (beta * k[..., 0])[..., None] * v                               # [B,T,H,V]
+    # channels (h, j) of the FMA scan, in its [B,T,N] layout
+    s, sf = oracle.scan_fma(np.repeat(a[..., None], V, axis=-1).reshape(B, T, H * V),
+                            bb.reshape(B, T, H * V), s0[:, :, 0, :].reshape(B, H * V))
+    assert rel(fin[:, :, 0, :], sf.reshape(B, H, V)) < 1e-13
+    assert rel(o, q[..., 0:1] * s.reshape(B, T, H, V)) < 1e-13
+
+
+def test_delta_decay_chunked_ut_form():
+    # The chunked form the GPU kernels use, solved with numpy.linalg: with G the
+    # within-chunk running sum of g (G_{-1} = 0) and, per key,
+    #   a_t = exp(G_{t-1}) k_t,   b_t = exp(-G_t) k_t,   qt_t = exp(G_t) q_t,
+    #   A = strict_lower(diag(beta) a b^T),  Delta = (I + A)^{-1} diag(beta) (V - a S0),
+    #   O = scale (qt S0 + tril(qt b^T) Delta),
+    #   S_L = diag(exp(G_L)) S0 + (exp(G_L - G_t) k_t)^T Delta.
+    r = _rng(84)
+    B, T, H, K, V = 1, 24, 2, 6, 5
+    q, k, v, g, beta, s0 = _decay_inputs(r, B, T, H, K, V)
+    o, fin = oracle.scan_delta_decay(q, k, v, g, beta, 0.9, s0)
+    for h in range(H):
+        Q, Km, Vm, bt, S0 = q[0, :, h], k[0, :, h], v[0, :, h], beta[0, :, h], s0[0, h]
+        G = np.cumsum(g[0, :, h], axis=0)
+        Gp = np.vstack([np.zeros((1, K)), G[:-1]])
+        a, bk, qt = np.exp(Gp) * Km, np.exp(-G) * Km, np.exp(G) * Q
+        A = np.tril(bt[:, None] * (a @ bk.T), -1)
+        Dl = np.linalg.solve(np.eye(T) + A, bt[:, None] * (Vm - a @ S0))
+        assert rel(o[0, :, h], 0.9 * (qt @ S0 + np.tril(qt @ bk.T) @ Dl)) < 1e-11
+        khat = np.exp(G[-1][None, :] - G) * Km
+        assert rel(fin[0, h], np.exp(G[-1])[:, None] * S0 + khat.T @ Dl) < 1e-11
+
+
+# ----------------------------------------------------------------------------
 # Segment continuation [SunnyNet log §4: two segments with the state carried
 # across reproduce the full run exactly] and thread-count invariance
 # ----------------------------------------------------------------------------
@@ -632,6 +729,13 @@ def test_continuation_bit_exact(dtype):
         return oracle.scan_delta(qd[:, lo:hi], kd[:, lo:hi], vd[:, lo:hi], bd[:, lo:hi], 1.0,
                                  Sd if lo == 0 else init, dtype=dtype)
     for full, first, second, t1 in _split_runs(run_l, T, splits):
+        assert np.array_equal(np.concatenate([first[0], second[0]], axis=1), full[0])
+        assert np.array_equal(second[1], full[1])
+    gd = r.uniform(-0.6, 0.0, (B, T, H, K)).astype(dtype)
+    def run_w(lo, hi, init):
+        return oracle.scan_delta_decay(qd[:, lo:hi], kd[:, lo:hi], vd[:, lo:hi], gd[:, lo:hi],
+                                       bd[:, lo:hi], 1.0, Sd if lo == 0 else init, dtype=dtype)
+    for full, first, second, t1 in _split_runs(run_w, T, splits):
         assert np.array_equal(np.concatenate([first[0], second[0]], axis=1), full[0])
         assert np.array_equal(second[1], full[1])
 

@@ -236,13 +236,16 @@ def profile_run(ctx, binding, inputs, dev, steps):
     for gen, kind in ((lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}), "diag"),
                       (lambda: inputs.gla(**inputs.GLA), "diag"),
                       (lambda: inputs.deltanet(**inputs.DELTANET), "delta"),
-                      (lambda: inputs.deltanet(**inputs.DELTANET_K64), "delta")):
+                      (lambda: inputs.deltanet(**inputs.DELTANET_K64), "delta"),
+                      (lambda: inputs.rwkv7(**inputs.RWKV7), "decay")):
         m = gen()
         q, k, v = (m[n].to(dev) for n in ("q", "k", "v"))
         for _ in range(steps):
             if kind == "diag":
                 binding.scan_diag_outer(ctx, q, k, v, m["g"].to(dev), m["decay_mode"],
                                         None if m["k_scale"] is None else m["k_scale"].to(dev), m["scale"])
+            elif kind == "decay":
+                binding.scan_delta_decay(ctx, q, k, v, m["g"].to(dev), m["beta"].to(dev), m["scale"])
             else:
                 binding.scan_delta(ctx, q, k, v, m["beta"].to(dev), m["scale"])
         torch.cuda.synchronize()
@@ -381,7 +384,8 @@ def delta_bytes(d):
     q, v, beta = d["q"], d["v"], d["beta"]
     B, T, H, K = q.shape
     V = v.shape[3]
-    return 2 * q.numel() * 2 + v.numel() * 2 + beta.numel() * 4 + B * T * H * V * 4 + B * H * K * V * 4
+    g = d["g"].numel() * 4 if "g" in d else 0   # the decayed form's per-key log-decay
+    return 2 * q.numel() * 2 + v.numel() * 2 + beta.numel() * 4 + g + B * T * H * V * 4 + B * H * K * V * 4
 
 
 def time_launches(fn, reps, warmup, flush):
@@ -443,6 +447,9 @@ def run_rows(ctx, args, binding, inputs, dev):
          ["delta_prep_deltanet_B4_T4096_H8_K128", "delta_scan_deltanet_B4_T4096_H8_K128_V128"]),
         ("scan_delta DeltaNet B=4 T=4096 H=8 K=64 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET_K64),
          ["delta_prep_deltanet_B4_T4096_H8_K64", "delta_scan_deltanet_B4_T4096_H8_K64_V128"]),
+        ("scan_delta_decay RWKV-7 B=4 T=4096 H=12 K=64 V=64 (per-key decay)", "decay",
+         lambda: inputs.rwkv7(**inputs.RWKV7),
+         ["delta_prep_rwkv7_B4_T4096_H12_K64", "delta_scan_rwkv7_B4_T4096_H12_K64_V64"]),
     ]
     for name, kind, gen, traffic_keys in specs:
         log(f"[bench] row {name}")
@@ -459,6 +466,11 @@ def run_rows(ctx, args, binding, inputs, dev):
                                                      None, o, fin)
             nbytes = diag_bytes(d)
             flops_per_unit = 5 * K * V
+        elif kind == "decay":
+            beta, g = d["beta"].to(dev), d["g"].to(dev)
+            fn = lambda: binding.lrs_scan_delta_decay(ctx, q, k, v, g, beta, d["scale"], None, o, fin)  # noqa: E731
+            nbytes = delta_bytes(d)
+            flops_per_unit = 6 * K * V
         else:
             beta = d["beta"].to(dev)
             fn = lambda: binding.lrs_scan_delta(ctx, q, k, v, beta, d["scale"], None, o, fin)  # noqa: E731
@@ -488,6 +500,10 @@ def run_rows(ctx, args, binding, inputs, dev):
                        None if d["k_scale"] is None else d["k_scale"][bb:bb + 1, :, hh:hh + 1], d["scale"])
                 t0 = time.perf_counter()
                 ro, rf = oracle.scan_diag_outer(*sub, nthreads=1)
+            elif kind == "decay":
+                sub = tuple(d[n][bb:bb + 1, :, hh:hh + 1] for n in ("q", "k", "v", "g", "beta"))
+                t0 = time.perf_counter()
+                ro, rf = oracle.scan_delta_decay(*sub, d["scale"], nthreads=1)
             else:
                 sub = tuple(d[n][bb:bb + 1, :, hh:hh + 1] for n in ("q", "k", "v", "beta"))
                 t0 = time.perf_counter()

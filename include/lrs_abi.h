@@ -10,6 +10,10 @@
  *   lrs_scan_delta       S_t = S_{t-1} + k_t [beta_t (v_t - S_{t-1}^T k_t)]^T,
  *                        o_t = scale S_t^T q_t                     (per head)
  *
+ *   lrs_scan_delta_decay S_t = diag(exp(g_t)) S_{t-1}
+ *                            + k_t [beta_t (v_t - S_{t-1}^T k_t)]^T,
+ *                        o_t = scale S_t^T q_t                     (per head)
+ *
  * plus, for the two elementwise forms, the reverse (gradient) pass
  * (lrs_scan_fma_backward, lrs_scan_gated_backward) and the in-place single
  * step (lrs_step_fma, lrs_step_gated).
@@ -94,6 +98,7 @@ enum {
 #define LRS_CAP_SCAN_DELTA      (1u << 3)
 #define LRS_CAP_ELEM_BACKWARD   (1u << 4)   /* since 1.1 */
 #define LRS_CAP_ELEM_STEP       (1u << 5)   /* since 1.1 */
+#define LRS_CAP_SCAN_DELTA_DECAY (1u << 6)  /* since 1.1 */
 
 /* Packed version of the library actually loaded. */
 uint32_t lrs_abi_version(void);
@@ -293,6 +298,37 @@ lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                           const lrs_bf16* v, const float* beta, float scale, const float* s0,
                           float* o, float* s_final, int32_t B, int32_t T, int32_t H, int32_t K,
                           int32_t V, void* stream);
+
+/* ---- delta rule with a per-key decay --------------------------------------
+ * RWKV-7's state update [SunnyNet log §5.1], which the page writes for a
+ * value-major state as S (.) w - (S k) k^T + v k^T.  Here the state is
+ * key-major ([K,V], as in lrs_scan_delta) and the write carries the in-context
+ * rate beta_t (beta = 1 is the page's form):
+ *
+ *   S_t = (diag(w_t) - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   w_t = exp(g_t)
+ *   o_t = scale S_t^T q_t
+ *
+ * The removal reads the state before the decay.  With g = 0 this is
+ * lrs_scan_delta.
+ *
+ *   q, k       bf16 [B,T,H,K]
+ *   v          bf16 [B,T,H,V]
+ *   g          fp32 [B,T,H,K]   log-decay per key (w = exp(g)), required
+ *   beta       fp32 [B,T,H]
+ *   s0         fp32 [B,H,K,V]   NULL means zeros
+ *   o          fp32 [B,T,H,V]   output
+ *   s_final    fp32 [B,H,K,V]   output
+ *
+ * Limits: 1 <= K <= 64 (LRS_E_UNSUPPORTED above), T <= 2796160.  The context
+ * workspace holds 48 KiB per (b,h,64-step chunk), grown on demand as for
+ * lrs_scan_delta.  Any finite g is accepted; chunks in which some key's
+ * running log-decay spans more than 60 nats take a slower exact path.
+ * Errors as lrs_scan_delta.
+ */
+lrs_status lrs_scan_delta_decay(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                const lrs_bf16* v, const float* g, const float* beta, float scale,
+                                const float* s0, float* o, float* s_final, int32_t B, int32_t T,
+                                int32_t H, int32_t K, int32_t V, void* stream);
 
 #ifdef __cplusplus
 }

@@ -277,7 +277,7 @@ LRS_API lrs_status lrs_abi_check(int32_t caller_major) {
 
 LRS_API uint32_t lrs_abi_caps(void) {
     return LRS_CAP_SCAN_FMA | LRS_CAP_SCAN_GATED | LRS_CAP_SCAN_DIAG_OUTER | LRS_CAP_SCAN_DELTA |
-           LRS_CAP_ELEM_BACKWARD | LRS_CAP_ELEM_STEP;
+           LRS_CAP_ELEM_BACKWARD | LRS_CAP_ELEM_STEP | LRS_CAP_SCAN_DELTA_DECAY;
 }
 
 LRS_API const char* lrs_status_string(lrs_status status) {
@@ -501,15 +501,19 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
     return LRS_OK;
 }
 
-LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
-                                  const lrs_bf16* v, const float* beta, float scale,
-                                  const float* s0, float* o, float* s_final, int32_t B, int32_t T,
-                                  int32_t H, int32_t K, int32_t V, void* stream) {
+namespace {
+
+// Shared by the plain and decayed delta-rule calls (g == NULL: plain).
+lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k, const lrs_bf16* v,
+                           const float* g, const float* beta, float scale, const float* s0, float* o,
+                           float* s_final, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                           void* stream) {
+    const bool decay = g != nullptr;
     if (!ctx || !q || !k || !v || !beta || !o || !s_final) return LRS_E_INVAL;
     if (B < 1 || T < 1 || H < 1 || K < 1 || V < 1) return LRS_E_INVAL;
-    if (K > 128) return LRS_E_UNSUPPORTED;
-    if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(beta, 4) || !aligned(s0, 4) ||
-        !aligned(o, 4) || !aligned(s_final, 4))
+    if (K > (decay ? lrs::delta_decay_max_k() : 128)) return LRS_E_UNSUPPORTED;
+    if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(g, 4) || !aligned(beta, 4) ||
+        !aligned(s0, 4) || !aligned(o, 4) || !aligned(s_final, 4))
         return LRS_E_INVAL;
     int64_t bth = B;
     if (!mul_ok(bth, T) || !mul_ok(bth, H)) return LRS_E_INVAL;
@@ -518,27 +522,29 @@ LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_
         return LRS_E_INVAL;
     const size_t bqk = static_cast<size_t>(nqk) * 2, bv = static_cast<size_t>(nv) * 2;
     const size_t bb = static_cast<size_t>(bth) * 4, bo = static_cast<size_t>(nv) * 4;
-    const size_t bst = static_cast<size_t>(nst) * 4;
-    const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {beta, bb}, {s0, bst}};
+    const size_t bst = static_cast<size_t>(nst) * 4, bg = decay ? static_cast<size_t>(nqk) * 4 : 0;
+    const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {beta, bb}, {s0, bst}, {g, bg}};
     const Span outs[] = {{o, bo}, {s_final, bst}};
-    if (!outputs_disjoint(outs, 2, ins, 5)) return LRS_E_INVAL;
+    if (!outputs_disjoint(outs, 2, ins, 6)) return LRS_E_INVAL;
 
     const int64_t nchunks = (static_cast<int64_t>(T) + 63) / 64;
     const int64_t vtiles = (V + lrs::delta_vtile() - 1) / lrs::delta_vtile();
     if (static_cast<int64_t>(B) * H * nchunks > 0x7fffffff || static_cast<int64_t>(B) * H * vtiles > 0x7fffffff)
         return LRS_E_UNSUPPORTED;
     // the scan kernel addresses one (batch, head) slice of the workspace with 32-bit offsets
-    if (lrs::delta_workspace_bytes(1, T, 1) >= (size_t{1} << 31)) return LRS_E_UNSUPPORTED;
+    if (lrs::delta_workspace_bytes(1, T, 1, decay) >= (size_t{1} << 31)) return LRS_E_UNSUPPORTED;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return LRS_E_DEVICE;
-    const lrs_status ws = grow_workspace(ctx->delta_ws, ctx->delta_ws_bytes, lrs::delta_workspace_bytes(B, T, H), st);
+    const lrs_status ws =
+        grow_workspace(ctx->delta_ws, ctx->delta_ws_bytes, lrs::delta_workspace_bytes(B, T, H, decay), st);
     if (ws != LRS_OK) return ws;
     lrs::DeltaParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
+    p.g = g;
     p.beta = beta;
     p.scale = scale;
     p.s0 = s0;
@@ -557,4 +563,22 @@ LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_
     ctx->last_stream = st;
     ctx->used = true;
     return LRS_OK;
+}
+
+}  // namespace
+
+LRS_API lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                  const lrs_bf16* v, const float* beta, float scale,
+                                  const float* s0, float* o, float* s_final, int32_t B, int32_t T,
+                                  int32_t H, int32_t K, int32_t V, void* stream) {
+    return scan_delta_impl(ctx, q, k, v, nullptr, beta, scale, s0, o, s_final, B, T, H, K, V, stream);
+}
+
+LRS_API lrs_status lrs_scan_delta_decay(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                        const lrs_bf16* v, const float* g, const float* beta,
+                                        float scale, const float* s0, float* o, float* s_final,
+                                        int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                        void* stream) {
+    if (!g) return LRS_E_INVAL;
+    return scan_delta_impl(ctx, q, k, v, g, beta, scale, s0, o, s_final, B, T, H, K, V, stream);
 }

@@ -112,6 +112,7 @@ struct DeltaParams {
     const uint16_t* k;
     const uint16_t* v;
     const float* beta;
+    const float* g;        // per-key log-decay [B,T,H,K]; NULL: the plain delta rule
     float scale;
     const float* s0;       // nullable
     float* o;
@@ -121,8 +122,11 @@ struct DeltaParams {
 };
 
 int delta_vtile();
-// Device workspace the delta scan needs (per-chunk UT-transform planes).
-size_t delta_workspace_bytes(int B, int T, int H);
+// Largest K of the decayed form.
+int delta_decay_max_k();
+// Device workspace the delta scan needs (per-chunk UT-transform planes, plus
+// the running log-decay with a decay).
+size_t delta_workspace_bytes(int B, int T, int H, bool decay);
 hipError_t launch_scan_delta(const DeltaParams& p, void* workspace, hipStream_t stream);
 
 // Fills `n` 64-bit words with zero (used to reset look-back status words).

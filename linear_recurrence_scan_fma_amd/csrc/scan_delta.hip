@@ -33,6 +33,21 @@
 //    (ds_read_b64_tr_b16).  Per chunk: Y = K S0 and Q S0, R = V - Y,
 //    Delta = Tb R and MTb R, S += K^T Delta.  fp32 operands are split into
 //    hi + lo bf16 terms.
+//
+// With a per-key decay (RWKV-7's update [SunnyNet log §5.1], read key-major):
+//   delta_t = beta_t (v_t - S_{t-1}^T k_t),  S_t = diag(w_t) S_{t-1} + k_t delta_t^T,
+// w_t = exp(g_t).  With G_t the running sum of g inside the chunk (G_{-1} = 0),
+// unrolling the chunk gives the same UT form on decayed operands:
+//   a_t = e^{G_{t-1}} k_t,  b_t = e^{-G_t} k_t,  qt_t = e^{G_t} q_t   (per key)
+//   A = strict_lower(diag(beta) a b^T),  MTb = tril(qt b^T) Tb,
+//   R = V - a S0,  Delta = Tb R,  O = scale (qt S0 + MTb R),
+//   S_L = diag(e^{G_L}) S0 + khat^T Delta,  khat_t = e^{G_L - G_t} k_t.
+// The prep kernel forms a b^T and qt b^T on the matrix cores from hi/lo
+// operands scaled about the chunk's middle step (every factor within e^{+-30}
+// while no key's running sum strays more than 30 nats from its middle value;
+// past that it takes the pairs one by one with exact exponentials), and
+// stores G for the scan kernel, which rebuilds a, qt and khat in registers
+// from the raw q and k and exp(G).  Decayed form: K <= 64.
 #include "lrs_internal.h"
 #include "mfma_util.h"
 
@@ -44,6 +59,15 @@ constexpr int NT = 256;
 constexpr int PLANE = L * L;   // elements of one 64 x 64 bf16 plane
 constexpr int NPLANES = 4;     // per chunk: Tb hi, Tb lo, MTb hi, MTb lo
 constexpr int VT = 16;         // V-tile width of the scan kernel
+constexpr int KD = 64;         // key width of the decayed form
+constexpr float kHalfSpan = 30.0f;   // decayed prep: factor exponents stay within +-30 nats
+
+// u16 elements of one chunk's workspace block: the four planes, then (decayed
+// form) the chunk's running log-decay G as fp32 [L][KD].
+template <bool DECAY>
+constexpr int chunk_u16() {
+    return NPLANES * PLANE + (DECAY ? 2 * L * KD : 0);
+}
 
 
 struct DeltaArgs {
@@ -51,10 +75,11 @@ struct DeltaArgs {
     const u16* k;
     const u16* v;
     const float* beta;
+    const float* g;   // per-key log-decay [B,T,H,K] (decayed form only)
     const float* s0;
     float* o;
     float* s_final;
-    u16* ws;          // per (b,h,chunk): NPLANES planes of 64 x 64 bf16
+    u16* ws;          // per (b,h,chunk): NPLANES planes of 64 x 64 bf16 (+ G, decayed form)
     int B, T, H, K, V;
     float scale;
     int vtiles;
@@ -138,18 +163,25 @@ __device__ __forceinline__ u32x4 load_piece(BufRes r, const u16* rowptr, int off
 // ---------------------------------------------------------------------------
 // prep: Tb = (I + strict_lower(diag(beta) K K^T))^{-1} diag(beta), MTb = tril(Q K^T) Tb
 // ---------------------------------------------------------------------------
-template <int KP, bool VEC>
+template <int KP, bool VEC, bool DECAY>
 __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
+    static_assert(!DECAY || KP == KD, "decayed form: K <= 64");
     constexpr int LDK = KP + 8;
     constexpr int LDA = L + 4;                     // fp32 rows of 272 bytes
-    constexpr int QK_BYTES = 2 * L * LDK * 2;      // sQ, sK (bf16)
+    constexpr int NTILE = DECAY ? 6 : 2;           // bf16 operand tiles
+    constexpr int QK_BYTES = NTILE * L * LDK * 2;  // sQ, sK (decayed: a, b, qt as hi/lo)
     constexpr int AT_BYTES = 2 * L * LDA * 4;      // sA, sT (fp32) reuse the same space
     constexpr int U_BYTES = QK_BYTES > AT_BYTES ? QK_BYTES : AT_BYTES;
     __shared__ __align__(16) unsigned char sU[U_BYTES];
-    __shared__ __align__(16) float sM[L * LDA];
+    __shared__ __align__(16) float sM[L * LDA];    // decayed form: G first, then M
     __shared__ float sBeta[L];
-    u16* sQ = reinterpret_cast<u16*>(sU);
-    u16* sK = sQ + L * LDK;
+    __shared__ float sTot[DECAY ? 4 : 1][DECAY ? KP : 1];
+    __shared__ float sRef[DECAY ? KP : 1];
+    // plain form: sQ, sK.  Decayed form: tiles a hi/lo, b hi/lo, qt hi/lo; the
+    // raw k and q are loaded into the a-hi and qt-hi tiles and transformed in place.
+    u16* tile = reinterpret_cast<u16*>(sU);
+    u16* sQ = DECAY ? tile + 4 * L * LDK : tile;
+    u16* sK = DECAY ? tile : tile + L * LDK;
     float* sA = reinterpret_cast<float*>(sU);
     float* sT = sA + L * LDA;
 
@@ -173,23 +205,127 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
         *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = load_piece<VEC>(rk, p.k + goff, off, c8, K, t < T);
     }
     if (tid < L) sBeta[tid] = (t0 + tid < T) ? p.beta[(b * T + t0 + tid) * H + h] : 0.0f;
+    float* sG = sM;
+    if constexpr (DECAY) {
+        // g rows of the chunk (zero past T and past K: no decay there)
+        for (int e = tid; e < L * KP; e += NT) {
+            const int row = e / KP, i = e % KP;
+            const int64_t t = t0 + row;
+            sG[row * LDA + i] = (t < T && i < K) ? p.g[((b * T + t) * H + h) * static_cast<int64_t>(K) + i] : 0.0f;
+        }
+    }
     __syncthreads();
 
     // A = K K^T and M = Q K^T lower-triangle blocks (20 jobs over 4 waves), kept in registers
     f32x4 acc[5];
+    if constexpr (DECAY) {
+        // running sum over the chunk per key: wave w sums rows 16w .. 16w+15 of key `lane`
+        float gl[16];
 #pragma unroll
-    for (int m = 0; m < 5; ++m) {
-        const int n = wave + 4 * m;
-        int bi, bj;
-        tri_block(n % 10, bi, bj);
-        const u16* left = n < 10 ? sK : sQ;
-        f32x4 a = zero4();
+        for (int r = 0; r < 16; ++r) gl[r] = sG[(16 * wave + r) * LDA + lane];
 #pragma unroll
-        for (int k0 = 0; k0 < KP; k0 += 32)
-            a = mfma16(frag<LDK>(left, 16 * bi, k0, lane), frag<LDK>(sK, 16 * bj, k0, lane), a);
-        acc[m] = a;
+        for (int r = 1; r < 16; ++r) gl[r] += gl[r - 1];
+        sTot[wave][lane] = gl[15];
+        __syncthreads();
+        float off = 0.0f;
+        for (int w2 = 0; w2 < wave; ++w2) off += sTot[w2][lane];
+        float* gws = reinterpret_cast<float*>(p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<true>() +
+                                              NPLANES * PLANE);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            gl[r] += off;
+            sG[(16 * wave + r) * LDA + lane] = gl[r];
+            gws[(16 * wave + r) * KP + lane] = gl[r];
+        }
+        if (wave == 1) sRef[lane] = gl[15];   // the middle step's running sum
+        __syncthreads();
+        const float ref = sRef[lane];
+        float dev = wave == 0 ? fabsf(ref) : 0.0f;   // G_{-1} = 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dev = fmaxf(dev, fabsf(gl[r] - ref));
+        const bool fast = !__syncthreads_or(dev > kHalfSpan);
+        u16* tAh = tile;
+        u16* tAl = tile + L * LDK;
+        u16* tBh = tile + 2 * L * LDK;
+        u16* tBl = tile + 3 * L * LDK;
+        u16* tQh = tile + 4 * L * LDK;
+        u16* tQl = tile + 5 * L * LDK;
+        if (fast) {
+            // a = e^{G_{t-1} - ref} k, b = e^{ref - G_t} k, qt = e^{G_t - ref} q, as hi/lo
+            for (int e = tid; e < L * KP; e += NT) {
+                const int t = e / KP, i = e % KP;
+                const float r0 = sRef[i];
+                const float gt = sG[t * LDA + i], gp = t > 0 ? sG[(t - 1) * LDA + i] : 0.0f;
+                const float kv = bf2f(tAh[t * LDK + i]), qv = bf2f(tQh[t * LDK + i]);
+                u16 hi, lo;
+                split_bf16(kv * __expf(gp - r0), hi, lo);
+                tAh[t * LDK + i] = hi;
+                tAl[t * LDK + i] = lo;
+                split_bf16(kv * __expf(r0 - gt), hi, lo);
+                tBh[t * LDK + i] = hi;
+                tBl[t * LDK + i] = lo;
+                split_bf16(qv * __expf(gt - r0), hi, lo);
+                tQh[t * LDK + i] = hi;
+                tQl[t * LDK + i] = lo;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < 5; ++m) {
+                const int n = wave + 4 * m;
+                int bi, bj;
+                tri_block(n % 10, bi, bj);
+                const u16* lh = n < 10 ? tAh : tQh;
+                const u16* ll = n < 10 ? tAl : tQl;
+                f32x4 a = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < KP; k0 += 32) {
+                    const bf16x8 xh = frag<LDK>(lh, 16 * bi, k0, lane), xl = frag<LDK>(ll, 16 * bi, k0, lane);
+                    const bf16x8 yh = frag<LDK>(tBh, 16 * bj, k0, lane), yl = frag<LDK>(tBl, 16 * bj, k0, lane);
+                    a = mfma16(xl, yh, a);
+                    a = mfma16(xh, yl, a);
+                    a = mfma16(xh, yh, a);
+                }
+                acc[m] = a;
+            }
+        } else {
+            // strong decay: each needed entry from its pairs, exact exponentials
+            // (tAh holds the raw k, tQh the raw q)
+#pragma unroll
+            for (int m = 0; m < 5; ++m) {
+                const int n = wave + 4 * m;
+                int bi, bj;
+                tri_block(n % 10, bi, bj);
+                const int tau = 16 * bj + c16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * bi + 4 * g + r;
+                    float sum = 0.0f;
+                    if (n < 10 ? tau < t : tau <= t) {
+                        const u16* lrow = (n < 10 ? tAh : tQh) + t * LDK;
+                        const u16* krow = tAh + tau * LDK;
+                        const float* gl_row = n < 10 ? sG + (t - 1) * LDA : sG + t * LDA;   // t >= 1 when n < 10
+                        for (int i = 0; i < KP; ++i)
+                            sum += bf2f(lrow[i]) * bf2f(krow[i]) * __expf(gl_row[i] - sG[tau * LDA + i]);
+                    }
+                    acc[m][r] = sum;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 5; ++m) {
+            const int n = wave + 4 * m;
+            int bi, bj;
+            tri_block(n % 10, bi, bj);
+            const u16* left = n < 10 ? sK : sQ;
+            f32x4 a = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < KP; k0 += 32)
+                a = mfma16(frag<LDK>(left, 16 * bi, k0, lane), frag<LDK>(sK, 16 * bj, k0, lane), a);
+            acc[m] = a;
+        }
     }
-    __syncthreads();   // sQ / sK are overwritten by sA / sT below
+    __syncthreads();   // sQ / sK (decayed form: the tiles and G) are overwritten by sA / sT / sM below
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
         const int n = wave + 4 * m;
@@ -244,7 +380,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     }
     __syncthreads();
 
-    u16* planes = p.ws + static_cast<int64_t>(blockIdx.x) * NPLANES * PLANE;
+    u16* planes = p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<DECAY>();
     // MTb lower blocks (i, j): (sum_{m=j}^{i} M_im T_mj) diag(beta); five block
     // products per wave
     {
@@ -327,14 +463,17 @@ __device__ __forceinline__ int swz(int r, int p) {
 //   2. Delta = Tb R, O = scale (O1 + MTb R) -> outputs; Delta -> LDS
 //   -- barrier --
 //   3. S += K^T Delta (tiles of this wave) -> LDS as the next chunk's operand
-template <int KP, bool VEC>
+template <int KP, bool VEC, bool DECAY>
 __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
+    static_assert(!DECAY || KP == KD, "decayed form: K <= 64");
     constexpr int PPR = KP / 8;          // 16-byte pieces per q / k row
     constexpr int QB = L * KP * 2;       // bytes of a q or k tile
     constexpr int PB = L * L * 2;        // bytes of a Tb / MTb plane
     constexpr int VB = L * VT * 2;       // bytes of the V tile
-    constexpr int STAGE = 2 * QB + 4 * PB + VB;
-    constexpr int OFF_K = QB, OFF_P = 2 * QB, OFF_V = 2 * QB + 4 * PB;
+    constexpr int GB = DECAY ? L * KP * 4 : 0;   // bytes of the G tile (fp32, 16 pieces per row)
+    constexpr int STAGE = 2 * QB + 4 * PB + VB + GB;
+    constexpr int OFF_K = QB, OFF_P = 2 * QB, OFF_V = 2 * QB + 4 * PB, OFF_G = 2 * QB + 4 * PB + VB;
+    constexpr int CHUNK_BYTES = chunk_u16<DECAY>() * 2;
     constexpr int LDK = KP + 8;
     constexpr int LDL = L + 8;
     constexpr int KS = KP / 32;          // k-steps over the key dimension
@@ -365,7 +504,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     const u16* qb = p.q + b * T * H * static_cast<int64_t>(K);
     const u16* kb = p.k + b * T * H * static_cast<int64_t>(K);
     const u16* vb = p.v + b * T * H * static_cast<int64_t>(V);
-    const u16* wsb = p.ws + static_cast<int64_t>(bh) * nchunks * NPLANES * PLANE;
+    const u16* wsb = p.ws + static_cast<int64_t>(bh) * nchunks * chunk_u16<DECAY>();
 
     // ---- fetch of one chunk's inputs into stage `buf` ----
     // Load run i (64 lanes x 16 bytes) fills bytes 1024 i .. of a tile: lane l
@@ -378,8 +517,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
             const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
             const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
-            const BufRes wp = make_rsrc_window(wsb, static_cast<int64_t>(nchunks) * NPLANES * PLANE * 2,
-                                               static_cast<int64_t>(c) * NPLANES * PLANE * 2);
+            const BufRes wp = make_rsrc_window(wsb, static_cast<int64_t>(nchunks) * CHUNK_BYTES,
+                                               static_cast<int64_t>(c) * CHUNK_BYTES);
 #pragma unroll
             for (int j = 0; j < QB / 1024 / 4; ++j) {
                 const int i = wave + 4 * j, sl = 64 * i + lane;
@@ -405,6 +544,17 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     wv, (__attribute__((address_space(3))) void*)(st + OFF_V + 1024 * wave), 16, off, 0, 0, 0);
             }
+            if constexpr (DECAY) {
+                // G rows of 16 pieces, piece p of row r stored at piece p ^ (r & 15)
+#pragma unroll
+                for (int j = 0; j < GB / 1024 / 4; ++j) {
+                    const int i = wave + 4 * j, sl = 64 * i + lane;
+                    const int row = sl / 16, pc = (sl % 16) ^ (row & 15);
+                    const int off = 4 * PB + row * KP * 4 + pc * 16;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        wp, (__attribute__((address_space(3))) void*)(st + OFF_G + 1024 * i), 16, off, 0, 0, 0);
+                }
+            }
         } else {
             // same slots, filled through registers (odd sizes or alignment)
             for (int sl = tid; sl < L * PPR; sl += NT) {
@@ -419,7 +569,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 *reinterpret_cast<u32x4*>(st + 16 * sl) = xq;
                 *reinterpret_cast<u32x4*>(st + OFF_K + 16 * sl) = xk;
             }
-            const u16* pw = wsb + static_cast<int64_t>(c) * NPLANES * PLANE;
+            const u16* pw = wsb + static_cast<int64_t>(c) * chunk_u16<DECAY>();
             for (int sl = tid; sl < 4 * L * 8; sl += NT) {
                 const int pl = sl / (L * 8), s2 = sl % (L * 8);
                 const int row = s2 / 8, col = ((s2 % 8) ^ (row & 7)) * 8;
@@ -433,7 +583,24 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 if (t < T) xv = load8_bf16(vb + (t * H + h) * static_cast<int64_t>(V) + v0, col, V - v0, false);
                 *reinterpret_cast<u32x4*>(st + OFF_V + 16 * tid) = xv;
             }
+            if constexpr (DECAY) {
+                const unsigned char* gw = reinterpret_cast<const unsigned char*>(pw + NPLANES * PLANE);
+                for (int sl = tid; sl < L * 16; sl += NT) {
+                    const int row = sl / 16, pc = (sl % 16) ^ (row & 15);
+                    *reinterpret_cast<u32x4*>(st + OFF_G + 16 * sl) =
+                        *reinterpret_cast<const u32x4*>(gw + row * KP * 4 + pc * 16);
+                }
+            }
         }
+    };
+    // G of step `row`, key `key` in the swizzled fp32 tile of a stage
+    auto g_at = [](const unsigned char* stg, int row, int key) -> float {
+        return *reinterpret_cast<const float*>(stg + OFF_G + row * (KP * 4) + (((key >> 2) ^ (row & 15)) << 4) +
+                                               (key & 3) * 4);
+    };
+    // G of step `row`, keys key0 .. key0+3 (key0 % 4 == 0)
+    auto g4_at = [](const unsigned char* stg, int row, int key0) -> f32x4 {
+        return *reinterpret_cast<const f32x4*>(stg + OFF_G + row * (KP * 4) + (((key0 >> 2) ^ (row & 15)) << 4));
     };
 
     // state: wave owns row tiles sr = STW * wave + st (keys 16 sr .. 16 sr + 15)
@@ -480,10 +647,39 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             const bf16x8 sl = frag<LDK>(sSl, 0, 32 * ks, lane);
             const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + OFF_K + swz<PPR>(arow, 4 * ks + g));
             const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st + swz<PPR>(arow, 4 * ks + g));
-            y = mfma16(ka, sl, y);
-            y = mfma16(ka, sh, y);
-            o1 = mfma16(qa, sl, o1);
-            o1 = mfma16(qa, sh, o1);
+            if constexpr (DECAY) {
+                // a = e^{G_{t-1}} k and qt = e^{G_t} q on keys 32 ks + 8 g .. +7, as hi/lo
+                const int key0 = 32 * ks + 8 * g;
+                const f32x4 gt0 = g4_at(st, arow, key0), gt1 = g4_at(st, arow, key0 + 4);
+                f32x4 gp0 = zero4(), gp1 = zero4();
+                if (arow > 0) {
+                    gp0 = g4_at(st, arow - 1, key0);
+                    gp1 = g4_at(st, arow - 1, key0 + 4);
+                }
+                const u32x4 kw = __builtin_bit_cast(u32x4, ka), qw = __builtin_bit_cast(u32x4, qa);
+                float av[8], qv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float gp = e < 4 ? gp0[e] : gp1[e - 4];
+                    const float gt = e < 4 ? gt0[e] : gt1[e - 4];
+                    av[e] = bf2f(piece_elem(kw, e)) * __expf(gp);
+                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(gt);
+                }
+                bf16x8 ah, al, qh, ql;
+                split8(av, ah, al);
+                split8(qv, qh, ql);
+                y = mfma16(al, sh, y);
+                y = mfma16(ah, sl, y);
+                y = mfma16(ah, sh, y);
+                o1 = mfma16(ql, sh, o1);
+                o1 = mfma16(qh, sl, o1);
+                o1 = mfma16(qh, sh, o1);
+            } else {
+                y = mfma16(ka, sl, y);
+                y = mfma16(ka, sh, y);
+                o1 = mfma16(qa, sl, o1);
+                o1 = mfma16(qa, sh, o1);
+            }
         }
         {
             // V rows 16 wave + 4g .. +3 at column c16, by the transposing read
@@ -544,6 +740,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             for (int s2 = 0; s2 < STW; ++s2) {
                 const int d0 = 16 * (STW * wave + s2);
                 const int col = d0 + 4 * (i16 & 3);
+                float gL = 0.0f;   // decayed form: G at the chunk's last step, key d0 + i16
+                if constexpr (DECAY) gL = g_at(st, L - 1, d0 + i16);
                 f32x4 ds = zero4();
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -556,11 +754,33 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                     const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
                     const bf16x8 ka =
                         __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                    ds = mfma16(ka, frag<LDL>(sDTl, 0, 32 * ks, lane), ds);
-                    ds = mfma16(ka, frag<LDL>(sDTh, 0, 32 * ks, lane), ds);
-                }
+                    if constexpr (DECAY) {
+                        // khat = e^{G_L - G_tau} k for tau = 32 ks + 8 g .. +7 at key d0 + i16
+                        const u32x4 kw = __builtin_bit_cast(u32x4, ka);
+                        float kv[8];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[s2][r] += ds[r];
+                        for (int e = 0; e < 8; ++e)
+                            kv[e] = bf2f(piece_elem(kw, e)) * __expf(gL - g_at(st, 32 * ks + 8 * g + e, d0 + i16));
+                        bf16x8 kh, kl;
+                        split8(kv, kh, kl);
+                        const bf16x8 dh = frag<LDL>(sDTh, 0, 32 * ks, lane), dlo = frag<LDL>(sDTl, 0, 32 * ks, lane);
+                        ds = mfma16(kl, dh, ds);
+                        ds = mfma16(kh, dlo, ds);
+                        ds = mfma16(kh, dh, ds);
+                    } else {
+                        ds = mfma16(ka, frag<LDL>(sDTl, 0, 32 * ks, lane), ds);
+                        ds = mfma16(ka, frag<LDL>(sDTh, 0, 32 * ks, lane), ds);
+                    }
+                }
+                if constexpr (DECAY) {
+                    // S <- diag(e^{G_L}) S + khat^T Delta on keys d0 + 4 g .. +3
+                    const f32x4 gl4 = g4_at(st, L - 1, d0 + 4 * g);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[s2][r] = __builtin_fmaf(S[s2][r], __expf(gl4[r]), ds[r]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[s2][r] += ds[r];
+                }
             }
         }
         write_state_lds();
@@ -578,19 +798,19 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     }
 }
 
-template <int KP>
+template <int KP, bool DECAY>
 hipError_t launch_t(const DeltaArgs& a, bool vec, hipStream_t stream) {
     const int64_t gprep = static_cast<int64_t>(a.B) * a.H * a.nchunks;
     const int64_t gscan = static_cast<int64_t>(a.B) * a.H * a.vtiles;
     if (vec) {
-        hipLaunchKernelGGL((delta_prep_kernel<KP, true>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
+        hipLaunchKernelGGL((delta_prep_kernel<KP, true, DECAY>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
                            stream, a);
-        hipLaunchKernelGGL((delta_scan_kernel<KP, true>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
+        hipLaunchKernelGGL((delta_scan_kernel<KP, true, DECAY>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
                            stream, a);
     } else {
-        hipLaunchKernelGGL((delta_prep_kernel<KP, false>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
+        hipLaunchKernelGGL((delta_prep_kernel<KP, false, DECAY>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
                            stream, a);
-        hipLaunchKernelGGL((delta_scan_kernel<KP, false>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
+        hipLaunchKernelGGL((delta_scan_kernel<KP, false, DECAY>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
                            stream, a);
     }
     return hipGetLastError();
@@ -600,10 +820,13 @@ hipError_t launch_t(const DeltaArgs& a, bool vec, hipStream_t stream) {
 
 int delta_vtile() { return VT; }
 
-size_t delta_workspace_bytes(int B, int T, int H) {
+size_t delta_workspace_bytes(int B, int T, int H, bool decay) {
     const int64_t nchunks = (static_cast<int64_t>(T) + L - 1) / L;
-    return static_cast<size_t>(B) * H * nchunks * NPLANES * PLANE * sizeof(u16);
+    const size_t per_chunk = decay ? chunk_u16<true>() : chunk_u16<false>();
+    return static_cast<size_t>(B) * H * nchunks * per_chunk * sizeof(u16);
 }
+
+int delta_decay_max_k() { return KD; }
 
 hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_t stream) {
     DeltaArgs a{};
@@ -611,6 +834,7 @@ hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_
     a.k = reinterpret_cast<const u16*>(prm.k);
     a.v = reinterpret_cast<const u16*>(prm.v);
     a.beta = prm.beta;
+    a.g = prm.g;
     a.s0 = prm.s0;
     a.o = prm.o;
     a.s_final = prm.s_final;
@@ -623,7 +847,11 @@ hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_
     a.scale = prm.scale;
     a.vtiles = (prm.V + VT - 1) / VT;
     a.nchunks = (prm.T + L - 1) / L;
-    return prm.K <= 64 ? launch_t<64>(a, prm.vec != 0, stream) : launch_t<128>(a, prm.vec != 0, stream);
+    if (prm.g) {
+        if (prm.K > KD) return hipErrorInvalidValue;
+        return launch_t<KD, true>(a, prm.vec != 0, stream);
+    }
+    return prm.K <= 64 ? launch_t<64, false>(a, prm.vec != 0, stream) : launch_t<128, false>(a, prm.vec != 0, stream);
 }
 
 }  // namespace lrs

@@ -20,10 +20,14 @@ float64 -> float32 -> bfloat16, each step round-to-nearest-even):
                        fp32 [B,T,H,K]; readout scale K**-0.5
 * DeltaNet shaped:     q, k = row-L2-normalised N(0,1), bf16 [B,T,H,K];
                        v ~ N(0,1) bf16 [B,T,H,V]; beta = sigmoid(N(0,1)) fp32 [B,T,H]
+* RWKV-7 shaped:       as DeltaNet, plus a per-key log-decay
+                       g = -exp(-softplus(-z) - 0.5), z ~ N(0,1), fp32 [B,T,H,K]
+                       (each step keeps a fraction in (0.545, 1) of every key row)
 
 Model shapes follow the models named on the pages: Mamba-2 130m (24 heads x 64,
 state 128) [SunnyNet log §4.1]; GLA 340M (4 heads x 128) [SunnyNet log §4.3];
-DeltaNet 340M (8 heads x 128) [SunnyNet log §4.2].  SunnyNet log =
+DeltaNet 340M (8 heads x 128) [SunnyNet log §4.2]; RWKV-7 191M (64 x 64 state per
+head, 12 heads) [SunnyNet log §5.1].  SunnyNet log =
 "SunnyNet 工程化实录：一个 O(N) 架构如何长出自己的 C 推理运行时" (developer.aliyun.com/article/1773847).
 """
 from __future__ import annotations
@@ -42,6 +46,7 @@ MAMBA2 = dict(B=8, T=4096, H=24, Hg=1, K=128, V=64)
 GLA = dict(B=4, T=4096, H=4, K=128, V=128)
 DELTANET = dict(B=4, T=4096, H=8, K=128, V=128)
 DELTANET_K64 = dict(B=4, T=4096, H=8, K=64, V=128)
+RWKV7 = dict(B=4, T=4096, H=12, K=64, V=64)
 
 
 def _f32(x64: np.ndarray) -> torch.Tensor:
@@ -138,6 +143,16 @@ def deltanet(B=4, T=4096, H=8, K=128, V=128, seed=SEED_BASE + 5):
     v = rng.standard_normal((B, T, H, V))
     beta = _sigmoid(rng.standard_normal((B, T, H)))
     return dict(q=_bf16(q), k=_bf16(k), v=_bf16(v), beta=_f32(beta), scale=1.0, s0=None)
+
+
+def rwkv7(B=4, T=4096, H=12, K=64, V=64, seed=SEED_BASE + 6):
+    """RWKV-7 shaped decayed delta rule: DeltaNet's q, k, v, beta plus a
+    per-key log-decay bounded in (-exp(-0.5), 0)."""
+    d = deltanet(B=B, T=T, H=H, K=K, V=V, seed=seed)
+    rng = np.random.default_rng(seed + 1000)
+    z = rng.standard_normal((B, T, H, K))
+    d["g"] = _f32(-np.exp(-_softplus(-z) - 0.5))
+    return d
 
 
 def random_state(shape, seed, std=1.0):

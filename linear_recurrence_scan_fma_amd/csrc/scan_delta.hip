@@ -196,22 +196,46 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     const int64_t row_elems = static_cast<int64_t>(H) * K;
     const BufRes rq = make_rsrc(p.q + b * T * row_elems, T * row_elems * 2);
     const BufRes rk = make_rsrc(p.k + b * T * row_elems, T * row_elems * 2);
-    for (int pi = tid; pi < L * KP / 8; pi += NT) {
+    // every load of the chunk is issued before the first LDS store, so the
+    // memory latency is paid once, not once per piece
+    constexpr int NPI = L * KP / 8 / NT;   // 16-byte q / k pieces per thread
+    constexpr int NGE = DECAY ? L * KP / NT : 1;   // g elements per thread
+    u32x4 xq[NPI], xk[NPI];
+#pragma unroll
+    for (int j = 0; j < NPI; ++j) {
+        const int pi = tid + j * NT;
         const int row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
         const int64_t t = t0 + row;
         const int off = ((static_cast<int>(t) * H + h) * K + c8) * 2;
         const int64_t goff = ((b * T + t) * H + h) * static_cast<int64_t>(K);
-        *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = load_piece<VEC>(rq, p.q + goff, off, c8, K, t < T);
-        *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = load_piece<VEC>(rk, p.k + goff, off, c8, K, t < T);
+        xq[j] = load_piece<VEC>(rq, p.q + goff, off, c8, K, t < T);
+        xk[j] = load_piece<VEC>(rk, p.k + goff, off, c8, K, t < T);
     }
-    if (tid < L) sBeta[tid] = (t0 + tid < T) ? p.beta[(b * T + t0 + tid) * H + h] : 0.0f;
-    float* sG = sM;
+    float xg[NGE];
     if constexpr (DECAY) {
         // g rows of the chunk (zero past T and past K: no decay there)
-        for (int e = tid; e < L * KP; e += NT) {
-            const int row = e / KP, i = e % KP;
+#pragma unroll
+        for (int j = 0; j < NGE; ++j) {
+            const int e = tid + j * NT, row = e / KP, i = e % KP;
             const int64_t t = t0 + row;
-            sG[row * LDA + i] = (t < T && i < K) ? p.g[((b * T + t) * H + h) * static_cast<int64_t>(K) + i] : 0.0f;
+            xg[j] = (t < T && i < K) ? p.g[((b * T + t) * H + h) * static_cast<int64_t>(K) + i] : 0.0f;
+        }
+    }
+    const float xb = (tid < L && t0 + tid < T) ? p.beta[(b * T + t0 + tid) * H + h] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NPI; ++j) {
+        const int pi = tid + j * NT;
+        const int row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
+        *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = xq[j];
+        *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = xk[j];
+    }
+    if (tid < L) sBeta[tid] = xb;
+    float* sG = sM;
+    if constexpr (DECAY) {
+#pragma unroll
+        for (int j = 0; j < NGE; ++j) {
+            const int e = tid + j * NT;
+            sG[(e / KP) * LDA + e % KP] = xg[j];
         }
     }
     __syncthreads();
@@ -251,22 +275,34 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
         u16* tQh = tile + 4 * L * LDK;
         u16* tQl = tile + 5 * L * LDK;
         if (fast) {
-            // a = e^{G_{t-1} - ref} k, b = e^{ref - G_t} k, qt = e^{G_t - ref} q, as hi/lo
-            for (int e = tid; e < L * KP; e += NT) {
-                const int t = e / KP, i = e % KP;
-                const float r0 = sRef[i];
-                const float gt = sG[t * LDA + i], gp = t > 0 ? sG[(t - 1) * LDA + i] : 0.0f;
-                const float kv = bf2f(tAh[t * LDK + i]), qv = bf2f(tQh[t * LDK + i]);
-                u16 hi, lo;
-                split_bf16(kv * __expf(gp - r0), hi, lo);
-                tAh[t * LDK + i] = hi;
-                tAl[t * LDK + i] = lo;
-                split_bf16(kv * __expf(r0 - gt), hi, lo);
-                tBh[t * LDK + i] = hi;
-                tBl[t * LDK + i] = lo;
-                split_bf16(qv * __expf(gt - r0), hi, lo);
-                tQh[t * LDK + i] = hi;
-                tQl[t * LDK + i] = lo;
+            // a = e^{G_{t-1} - ref} k, b = e^{ref - G_t} k, qt = e^{G_t - ref} q, as hi/lo;
+            // eight keys of one step per piece, transformed in place
+            constexpr int NPC = L * KP / 8 / NT;
+#pragma unroll
+            for (int j = 0; j < NPC; ++j) {
+                const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
+                const u32x4 kw = *reinterpret_cast<const u32x4*>(tAh + t * LDK + i0);
+                const u32x4 qw = *reinterpret_cast<const u32x4*>(tQh + t * LDK + i0);
+                float av[8], bv[8], qv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float r0 = sRef[i0 + e];
+                    const float gt = sG[t * LDA + i0 + e], gp = t > 0 ? sG[(t - 1) * LDA + i0 + e] : 0.0f;
+                    const float kv = bf2f(piece_elem(kw, e));
+                    av[e] = kv * __expf(gp - r0);
+                    bv[e] = kv * __expf(r0 - gt);
+                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(gt - r0);
+                }
+                bf16x8 hi, lo;
+                split8(av, hi, lo);
+                *reinterpret_cast<bf16x8*>(tAh + t * LDK + i0) = hi;
+                *reinterpret_cast<bf16x8*>(tAl + t * LDK + i0) = lo;
+                split8(bv, hi, lo);
+                *reinterpret_cast<bf16x8*>(tBh + t * LDK + i0) = hi;
+                *reinterpret_cast<bf16x8*>(tBl + t * LDK + i0) = lo;
+                split8(qv, hi, lo);
+                *reinterpret_cast<bf16x8*>(tQh + t * LDK + i0) = hi;
+                *reinterpret_cast<bf16x8*>(tQl + t * LDK + i0) = lo;
             }
             __syncthreads();
 #pragma unroll

@@ -70,7 +70,7 @@ def _load():
         f.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I]
         f.restype = None
         f = getattr(lib, "orc_scan_diag_outer" + sfx)
-        f.argtypes = [P, P, P, P, I, P, R, P, P, P, I64, I64, I64, I64, I64, I64, I]
+        f.argtypes = [P, P, P, P, I, P, P, R, P, P, P, I64, I64, I64, I64, I64, I64, I]
         f.restype = None
         for name in ("orc_scan_delta", "orc_scan_delta_explicit"):
             f = getattr(lib, name + sfx)
@@ -195,13 +195,15 @@ def scan_gated_backward(a, u, s, ds, s0=None, ds_final=None, dtype=np.float64, n
 
 
 def scan_diag_outer(q, k, v, g, decay_mode, k_scale=None, scale=1.0, s0=None,
-                    dtype=np.float64, nthreads=None):
+                    dtype=np.float64, nthreads=None, k_scale_key=None):
     """Decay-separable outer-product state scan with readout.
 
     S_t = diag(exp(g_t)) S_{t-1} + (kappa_t k_t) v_t^T,  o_t = scale S_t^T q_t
     [SunnyNet log §4.1 (Mamba-2), §4.3 (GLA)].  Shapes: q, k [B,T,Hg,K];
     v [B,T,H,V]; g [B,T,H] (mode 0) or [B,T,H,K] (mode 1); k_scale [B,T,H];
-    s0 [B,H,K,V].  Returns ``(o [B,T,H,V], s_final [B,H,K,V])``.
+    s0 [B,H,K,V].  ``k_scale_key`` [B,T,H,K] (instead of k_scale) scales each
+    key: the matrix associative memory [vs llama.cpp §8] with g = log p and
+    kappa = 1 - p.  Returns ``(o [B,T,H,V], s_final [B,H,K,V])``.
     """
     q, k, v, g = (_arr(x, dtype) for x in (q, k, v, g))
     B, T, Hg, K = q.shape
@@ -215,13 +217,17 @@ def scan_diag_outer(q, k, v, g, decay_mode, k_scale=None, scale=1.0, s0=None,
     _check_shape("g", g, (B, T, H) if decay_mode == 0 else (B, T, H, K))
     k_scale = _arr(k_scale, dtype)
     _check_shape("k_scale", k_scale, (B, T, H))
+    k_scale_key = _arr(k_scale_key, dtype)
+    _check_shape("k_scale_key", k_scale_key, (B, T, H, K))
+    if k_scale is not None and k_scale_key is not None:
+        raise ValueError("give k_scale or k_scale_key, not both")
     s0 = _arr(s0, dtype)
     _check_shape("s0", s0, (B, H, K, V))
     o = np.empty((B, T, H, V), dtype=dtype)
     fin = np.empty((B, H, K, V), dtype=dtype)
     fn = getattr(_load(), "orc_scan_diag_outer" + _sfx(dtype))
-    fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), int(decay_mode), _ptr(k_scale), float(scale),
-       _ptr(s0), _ptr(o), _ptr(fin), B, T, H, Hg, K, V, nthreads or default_threads())
+    fn(_ptr(q), _ptr(k), _ptr(v), _ptr(g), int(decay_mode), _ptr(k_scale), _ptr(k_scale_key),
+       float(scale), _ptr(s0), _ptr(o), _ptr(fin), B, T, H, Hg, K, V, nthreads or default_threads())
     return o, fin
 
 

@@ -145,14 +145,19 @@ void ORC_FN(orc_scan_gated_bwd)(const REAL* a, const REAL* u, const REAL* s0, co
  * Mamba-2: decay exp(dt*A) shared by the whole state, injection (dt*B) outer x
  * [SunnyNet log §4.1]; GLA: decay diag(exp(gk)) on the key axis, readout
  * scale * S^T q [SunnyNet log §4.3]; both restated in [vs llama.cpp §3].
- * kappa_t = k_scale[b,t,h] (1 when k_scale is NULL).
+ * kappa_t = k_scale[b,t,h] (1 when k_scale is NULL), or, with a per-key
+ * scale, kappa_t[i] = k_scale_key[b,t,h,i]: the matrix associative memory
+ * S_t = p (.) S_{t-1} + (1 - p) (.) (v_t (x) k_t) [vs llama.cpp §8] is this
+ * recurrence with a per-key p: g = log p, kappa = 1 - p.
  * Layouts: q, k [B,T,Hg,K]; v, o [B,T,H,V]; g [B,T,H] or [B,T,H,K];
- * k_scale [B,T,H]; s0, s_final [B,H,K,V].  Head h reads q/k group h/(H/Hg).
+ * k_scale [B,T,H]; k_scale_key [B,T,H,K]; s0, s_final [B,H,K,V].  Head h
+ * reads q/k group h/(H/Hg).  At most one of k_scale, k_scale_key is given.
  */
 void ORC_FN(orc_scan_diag_outer)(const REAL* q, const REAL* k, const REAL* v, const REAL* g,
-                                 int decay_mode, const REAL* k_scale, REAL scale,
-                                 const REAL* s0, REAL* o, REAL* s_final, int64_t B, int64_t T,
-                                 int64_t H, int64_t Hg, int64_t K, int64_t V, int nthreads) {
+                                 int decay_mode, const REAL* k_scale, const REAL* k_scale_key,
+                                 REAL scale, const REAL* s0, REAL* o, REAL* s_final, int64_t B,
+                                 int64_t T, int64_t H, int64_t Hg, int64_t K, int64_t V,
+                                 int nthreads) {
     int64_t heads_per_group = H / Hg;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
     for (int64_t bh = 0; bh < B * H; ++bh) {
@@ -170,7 +175,8 @@ void ORC_FN(orc_scan_diag_outer)(const REAL* q, const REAL* k, const REAL* v, co
                 alpha[i] = ORC_EXP(gi);
             }
             for (int64_t i = 0; i < K; ++i) {
-                REAL kk = kap * kt[i];
+                REAL kap_i = k_scale_key ? k_scale_key[((b * T + t) * H + h) * K + i] : kap;
+                REAL kk = kap_i * kt[i];
                 for (int64_t j = 0; j < V; ++j) {
                     REAL keep = alpha[i] * S[i * V + j];
                     REAL inject = kk * vt[j];

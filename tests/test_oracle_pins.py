@@ -398,10 +398,10 @@ def _diag_inputs(r, B, T, H, Hg, K, V, mode, with_kscale, with_s0, gscale=0.3):
     return q, k, v, g, ks, s0
 
 
-def _diag_quadratic(q, k, v, g, mode, ks, scale, s0, H):
+def _diag_quadratic(q, k, v, g, mode, ks, scale, s0, H, ksk=None):
     """O(T^2) closed form: o_t = scale sum_{i<=t} sum_d q_td k_id kappa_i e^{G_td - G_id} v_i
     + scale sum_d q_td e^{G_td} S0_d,  S_T = e^{G_T} S0 + sum_i e^{G_T - G_i} kappa_i k_i v_i^T,
-    with G_t = sum_{j<=t} g_j."""
+    with G_t = sum_{j<=t} g_j (kappa_i per key, kappa_id, when ksk is given)."""
     B, T, Hg, K = q.shape
     V = v.shape[-1]
     hpg = H // Hg
@@ -414,16 +414,18 @@ def _diag_quadratic(q, k, v, g, mode, ks, scale, s0, H):
             G = np.cumsum(gg, axis=0)                                   # [T, K]
             kap = ks[b, :, h] if ks is not None else np.ones(T)
             Q = q[b, :, grp]                                            # [T, K]
-            Km = k[b, :, grp]
+            Km = k[b, :, grp] * kap[:, None]
+            if ksk is not None:
+                Km = Km * ksk[b, :, h]                                  # per-key scale
             W = np.exp(G[:, None, :] - G[None, :, :])                   # [t, i, d]
-            Pm = np.einsum("td,id,tid->ti", Q, Km, W) * kap[None, :]
+            Pm = np.einsum("td,id,tid->ti", Q, Km, W)
             Pm = np.tril(Pm)
             o[b, :, h] = Pm @ v[b, :, h]
             S0 = s0[b, h] if s0 is not None else np.zeros((K, V))
             o[b, :, h] += (Q * np.exp(G)) @ S0
             o[b, :, h] *= scale
             fin[b, h] = np.exp(G[-1])[:, None] * S0 + (
-                (Km * np.exp(G[-1][None, :] - G) * kap[:, None]).T @ v[b, :, h])
+                (Km * np.exp(G[-1][None, :] - G)).T @ v[b, :, h])
     return o, fin
 
 
@@ -438,6 +440,49 @@ def test_diag_outer_quadratic_form(mode, with_s0):
     ro, rf = _diag_quadratic(q, k, v, g, mode, ks, scale, s0, H)
     assert rel(o, ro) < 1e-12
     assert rel(fin, rf) < 1e-12
+
+
+@pytest.mark.parametrize("with_s0", [False, True])
+def test_diag_outer_per_key_scale_quadratic_form(with_s0):
+    r = _rng(16 + with_s0)
+    B, T, H, Hg, K, V = 2, 21, 4, 2, 6, 5
+    q, k, v, g, _, s0 = _diag_inputs(r, B, T, H, Hg, K, V, 1, False, with_s0)
+    ksk = r.uniform(-0.5, 1.5, (B, T, H, K))
+    o, fin = oracle.scan_diag_outer(q, k, v, g, 1, None, 0.6, s0, k_scale_key=ksk)
+    ro, rf = _diag_quadratic(q, k, v, g, 1, None, 0.6, s0, H, ksk=ksk)
+    assert rel(o, ro) < 1e-12
+    assert rel(fin, rf) < 1e-12
+
+
+def test_diag_outer_per_key_scale_special_cases():
+    r = _rng(18)
+    B, T, H, Hg, K, V = 2, 30, 3, 3, 4, 6
+    q, k, v, g, ks, s0 = _diag_inputs(r, B, T, H, Hg, K, V, 1, True, True)
+    # a per-key scale equal on every key is the per-head scale, bit for bit
+    o1, f1 = oracle.scan_diag_outer(q, k, v, g, 1, ks, 0.8, s0)
+    o2, f2 = oracle.scan_diag_outer(q, k, v, g, 1, None, 0.8, s0,
+                                    k_scale_key=np.repeat(ks[..., None], K, axis=-1))
+    assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+    # the associative memory with one key: S_t = p S_{t-1} + (1 - p) k v_t, the
+    # gated elementwise scan with a = p and u = k v
+    p = r.uniform(0.3, 0.99, (B, T, H, 1))
+    k1 = r.uniform(-1.0, 1.0, (B, T, H, 1))
+    q1 = r.standard_normal((B, T, H, 1))
+    o, fin = oracle.scan_diag_outer(q1, k1, v, np.log(p), 1, None, 1.0, s0[:, :, :1],
+                                    k_scale_key=1.0 - p)
+    a = np.repeat(p, V, axis=-1).reshape(B, T, H * V)
+    u = (k1 * v).reshape(B, T, H * V)
+    s, sf = oracle.scan_gated(a, u, s0[:, :, 0, :].reshape(B, H * V))
+    assert rel(fin[:, :, 0, :], sf.reshape(B, H, V)) < 1e-13
+    assert rel(o, q1 * s.reshape(B, T, H, V)) < 1e-13
+    # the memory is a convex combination: it stays within the range of S0 and of every k v^T
+    K2 = 5
+    p = r.uniform(0.0, 1.0, (B, T, H, K2))
+    k2 = r.uniform(-1.0, 1.0, (B, T, H, K2))
+    _, fin = oracle.scan_diag_outer(r.standard_normal((B, T, H, K2)), k2, v, np.log(p), 1, None, 1.0,
+                                    np.zeros((B, H, K2, V)), k_scale_key=1.0 - p)
+    bound = np.max(np.abs(k2)) * np.max(np.abs(v))
+    assert np.all(np.abs(fin) <= bound * (1 + 1e-12))
 
 
 def test_diag_outer_zero_decay_is_causal_linear_attention():

@@ -235,6 +235,8 @@ def profile_run(ctx, binding, inputs, dev, steps):
     del sa, sx, st
     for gen, kind in ((lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}), "diag"),
                       (lambda: inputs.gla(**inputs.GLA), "diag"),
+                      (lambda: inputs.hgrn2(**inputs.HGRN2), "diag"),
+                      (lambda: inputs.assoc_memory(**inputs.ASSOC), "keyscale"),
                       (lambda: inputs.deltanet(**inputs.DELTANET), "delta"),
                       (lambda: inputs.deltanet(**inputs.DELTANET_K64), "delta"),
                       (lambda: inputs.rwkv7(**inputs.RWKV7), "decay")):
@@ -246,6 +248,8 @@ def profile_run(ctx, binding, inputs, dev, steps):
                                         None if m["k_scale"] is None else m["k_scale"].to(dev), m["scale"])
             elif kind == "decay":
                 binding.scan_delta_decay(ctx, q, k, v, m["g"].to(dev), m["beta"].to(dev), m["scale"])
+            elif kind == "keyscale":
+                binding.scan_diag_outer_keyscale(ctx, q, k, v, m["g"].to(dev), m["k_scale_key"].to(dev), m["scale"])
             else:
                 binding.scan_delta(ctx, q, k, v, m["beta"].to(dev), m["scale"])
         torch.cuda.synchronize()
@@ -377,6 +381,8 @@ def diag_bytes(d):
     B, T, Hg, K = q.shape
     H, V = v.shape[2], v.shape[3]
     n = 2 * q.numel() * 2 + v.numel() * 2 + g.numel() * 4 + (ks.numel() * 4 if ks is not None else 0)
+    if d.get("k_scale_key") is not None:
+        n += d["k_scale_key"].numel() * 4
     return n + B * T * H * V * 4 + B * H * K * V * 4
 
 
@@ -443,6 +449,12 @@ def run_rows(ctx, args, binding, inputs, dev):
         ("scan_diag_outer GLA B=4 T=4096 H=4 K=128 V=128 (per-key decay)", "diag",
          lambda: inputs.gla(**inputs.GLA),
          ["diag_outer_agg_gla_B4_T4096_H4_K128_V128", "diag_outer_out_gla_B4_T4096_H4_K128_V128"]),
+        ("scan_diag_outer HGRN2 B=4 T=4096 H=16 K=128 V=128 (per-key decay, key = 1 - forget gate)", "diag",
+         lambda: inputs.hgrn2(**inputs.HGRN2),
+         ["diag_outer_agg_hgrn2_B4_T4096_H16_K128_V128", "diag_outer_out_hgrn2_B4_T4096_H16_K128_V128"]),
+        ("scan_diag_outer_keyscale associative memory B=4 T=4096 H=8 K=64 V=64 (per-key decay and kappa)",
+         "keyscale", lambda: inputs.assoc_memory(**inputs.ASSOC),
+         ["diag_outer_agg_assoc_B4_T4096_H8_K64_V64", "diag_outer_out_assoc_B4_T4096_H8_K64_V64"]),
         ("scan_delta DeltaNet B=4 T=4096 H=8 K=128 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET),
          ["delta_prep_deltanet_B4_T4096_H8_K128", "delta_scan_deltanet_B4_T4096_H8_K128_V128"]),
         ("scan_delta DeltaNet B=4 T=4096 H=8 K=64 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET_K64),
@@ -466,6 +478,11 @@ def run_rows(ctx, args, binding, inputs, dev):
                                                      None, o, fin)
             nbytes = diag_bytes(d)
             flops_per_unit = 5 * K * V
+        elif kind == "keyscale":
+            g, kk = d["g"].to(dev), d["k_scale_key"].to(dev)
+            fn = lambda: binding.lrs_scan_diag_outer_keyscale(ctx, q, k, v, g, kk, d["scale"], None, o, fin)  # noqa: E731
+            nbytes = diag_bytes(d)
+            flops_per_unit = 5 * K * V
         elif kind == "decay":
             beta, g = d["beta"].to(dev), d["g"].to(dev)
             fn = lambda: binding.lrs_scan_delta_decay(ctx, q, k, v, g, beta, d["scale"], None, o, fin)  # noqa: E731
@@ -485,7 +502,7 @@ def run_rows(ctx, args, binding, inputs, dev):
                             "frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                             "bytes_per_call": nbytes},
                "algorithmic_TFLOP/s": round(units * flops_per_unit / (med * 1e-3) / 1e12, 3)}
-        src = "scan_diag_outer.hip" if kind == "diag" else "scan_delta.hip"
+        src = "scan_diag_outer.hip" if kind in ("diag", "keyscale") else "scan_delta.hip"
         tr = [measured_traffic(key, src) for key in traffic_keys]
         row["roofline"]["traffic"] = None if any(t is None for t in tr) else sum(tr)
         row["mfma_util"] = measured_mfma_util(traffic_keys, src)
@@ -500,6 +517,11 @@ def run_rows(ctx, args, binding, inputs, dev):
                        None if d["k_scale"] is None else d["k_scale"][bb:bb + 1, :, hh:hh + 1], d["scale"])
                 t0 = time.perf_counter()
                 ro, rf = oracle.scan_diag_outer(*sub, nthreads=1)
+            elif kind == "keyscale":
+                sub = tuple(d[n][bb:bb + 1, :, hh:hh + 1] for n in ("q", "k", "v", "g"))
+                t0 = time.perf_counter()
+                ro, rf = oracle.scan_diag_outer(*sub, 1, None, d["scale"], nthreads=1,
+                                                k_scale_key=d["k_scale_key"][bb:bb + 1, :, hh:hh + 1])
             elif kind == "decay":
                 sub = tuple(d[n][bb:bb + 1, :, hh:hh + 1] for n in ("q", "k", "v", "g", "beta"))
                 t0 = time.perf_counter()

@@ -10,6 +10,7 @@
  *   lrs_scan_delta       S_t = S_{t-1} + k_t [beta_t (v_t - S_{t-1}^T k_t)]^T,
  *                        o_t = scale S_t^T q_t                     (per head)
  *
+ *   lrs_scan_diag_outer_keyscale  as lrs_scan_diag_outer, kappa per key
  *   lrs_scan_delta_decay S_t = diag(exp(g_t)) S_{t-1}
  *                            + k_t [beta_t (v_t - S_{t-1}^T k_t)]^T,
  *                        o_t = scale S_t^T q_t                     (per head)
@@ -99,6 +100,7 @@ enum {
 #define LRS_CAP_ELEM_BACKWARD   (1u << 4)   /* since 1.1 */
 #define LRS_CAP_ELEM_STEP       (1u << 5)   /* since 1.1 */
 #define LRS_CAP_SCAN_DELTA_DECAY (1u << 6)  /* since 1.1 */
+#define LRS_CAP_SCAN_DIAG_KEYSCALE (1u << 7) /* since 1.1 */
 
 /* Packed version of the library actually loaded. */
 uint32_t lrs_abi_version(void);
@@ -298,6 +300,31 @@ lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                           const lrs_bf16* v, const float* beta, float scale, const float* s0,
                           float* o, float* s_final, int32_t B, int32_t T, int32_t H, int32_t K,
                           int32_t V, void* stream);
+
+/* ---- decay-separable scan with a per-key injection scale ------------------
+ * As lrs_scan_diag_outer with a per-key decay (decay mode 1), but kappa is a
+ * vector over the keys:
+ *
+ *   S_t[i][j] = exp(g_t[i]) S_{t-1}[i][j] + kappa_t[i] k_t[i] v_t[j],
+ *   o_t = scale S_t^T q_t
+ *
+ * The matrix associative memory [vs llama.cpp §8],
+ * S_t = p (.) S_{t-1} + (1 - p) (.) (v_t (x) k_t) with p on the key axis, is
+ * this call with g = log p and kappa = 1 - p (its output projection is a
+ * model layer and stays with the caller).
+ *
+ *   q, k     bf16 [B,T,Hg,K];  v bf16 [B,T,H,V]
+ *   g        fp32 [B,T,H,K]    log-decay per key
+ *   k_scale  fp32 [B,T,H,K]    kappa per key, required
+ *   s0, o, s_final as lrs_scan_diag_outer
+ *
+ * Limits, workspace and errors as lrs_scan_diag_outer (decay mode 1).
+ */
+lrs_status lrs_scan_diag_outer_keyscale(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                        const lrs_bf16* v, const float* g, const float* k_scale,
+                                        float scale, const float* s0, float* o, float* s_final,
+                                        int32_t B, int32_t T, int32_t H, int32_t Hg, int32_t K,
+                                        int32_t V, void* stream);
 
 /* ---- delta rule with a per-key decay --------------------------------------
  * RWKV-7's state update [SunnyNet log §5.1], which the page writes for a

@@ -25,6 +25,7 @@ LRS_OK, LRS_E_INVAL, LRS_E_NOMEM, LRS_E_IO, LRS_E_FORMAT, LRS_E_UNSUPPORTED, LRS
     0, -1, -2, -3, -4, -5, -6)
 LRS_CAP_SCAN_FMA, LRS_CAP_SCAN_GATED, LRS_CAP_SCAN_DIAG_OUTER, LRS_CAP_SCAN_DELTA = 1, 2, 4, 8
 LRS_CAP_ELEM_BACKWARD, LRS_CAP_ELEM_STEP, LRS_CAP_SCAN_DELTA_DECAY = 16, 32, 64
+LRS_CAP_SCAN_DIAG_KEYSCALE = 128
 LRS_PARAM_ELEM_SCHEDULE = 1
 LRS_PARAM_DIAG_SEGMENTS = 2
 LRS_ELEM_SCHEDULE_AUTO, LRS_ELEM_SCHEDULE_STREAM, LRS_ELEM_SCHEDULE_LOOKBACK = 0, 1, 2
@@ -52,6 +53,8 @@ SIGNATURES = {
     "lrs_step_gated": (_I32, [_P, _P, _P, _P, _I32, _I32, _P]),
     "lrs_scan_diag_outer": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _F, _P, _P, _P,
                                    _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "lrs_scan_diag_outer_keyscale": (_I32, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P,
+                                            _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_delta": (_I32, [_P, _P, _P, _P, _P, _F, _P, _P, _P,
                               _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_delta_decay": (_I32, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P,
@@ -290,6 +293,26 @@ def lrs_scan_diag_outer(ctx, q, k, v, g, decay_mode, k_scale, scale, s0, o, s_fi
     _check("lrs_scan_diag_outer", st)
 
 
+def lrs_scan_diag_outer_keyscale(ctx, q, k, v, g, k_scale, scale, s0, o, s_final, stream=None) -> None:
+    """As lrs_scan_diag_outer with per-key decay g [B,T,H,K] and per-key kappa
+    k_scale [B,T,H,K] fp32 (required)."""
+    import torch
+
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    d = ctx.device
+    bf, f32 = torch.bfloat16, torch.float32
+    args = (
+        _ptr(q, bf, (B, T, Hg, K), "q", d), _ptr(k, bf, (B, T, Hg, K), "k", d),
+        _ptr(v, bf, (B, T, H, V), "v", d), _ptr(g, f32, (B, T, H, K), "g", d),
+        _ptr(k_scale, f32, (B, T, H, K), "k_scale", d), float(scale),
+        _ptr(s0, f32, (B, H, K, V), "s0", d), _ptr(o, f32, (B, T, H, V), "o", d),
+        _ptr(s_final, f32, (B, H, K, V), "s_final", d),
+    )
+    st = lib().lrs_scan_diag_outer_keyscale(ctx.handle, *args, B, T, H, Hg, K, V, _stream(stream, d))
+    _check("lrs_scan_diag_outer_keyscale", st)
+
+
 def lrs_scan_delta(ctx, q, k, v, beta, scale, s0, o, s_final, stream=None) -> None:
     """delta_t = beta_t (v_t - S^T k_t), S += k_t delta_t^T, o_t = scale S_t^T q_t.
 
@@ -388,4 +411,15 @@ def scan_delta_decay(ctx, q, k, v, g, beta, scale=1.0, s0=None, stream=None):
     o = torch.empty((B, T, H, V), dtype=torch.float32, device=q.device)
     fin = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
     lrs_scan_delta_decay(ctx, q, k, v, g, beta, scale, s0, o, fin, stream)
+    return o, fin
+
+
+def scan_diag_outer_keyscale(ctx, q, k, v, g, k_scale, scale=1.0, s0=None, stream=None):
+    import torch
+
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    o = torch.empty((B, T, H, V), dtype=torch.float32, device=q.device)
+    fin = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
+    lrs_scan_diag_outer_keyscale(ctx, q, k, v, g, k_scale, scale, s0, o, fin, stream)
     return o, fin

@@ -277,7 +277,8 @@ LRS_API lrs_status lrs_abi_check(int32_t caller_major) {
 
 LRS_API uint32_t lrs_abi_caps(void) {
     return LRS_CAP_SCAN_FMA | LRS_CAP_SCAN_GATED | LRS_CAP_SCAN_DIAG_OUTER | LRS_CAP_SCAN_DELTA |
-           LRS_CAP_ELEM_BACKWARD | LRS_CAP_ELEM_STEP | LRS_CAP_SCAN_DELTA_DECAY;
+           LRS_CAP_ELEM_BACKWARD | LRS_CAP_ELEM_STEP | LRS_CAP_SCAN_DELTA_DECAY |
+           LRS_CAP_SCAN_DIAG_KEYSCALE;
 }
 
 LRS_API const char* lrs_status_string(lrs_status status) {
@@ -439,12 +440,15 @@ lrs_status grow_workspace(void*& ptr, size_t& cap, size_t need, hipStream_t stre
 
 }  // namespace
 
-LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
-                                       const lrs_bf16* v, const float* g, int32_t decay_mode,
-                                       const float* k_scale, float scale, const float* s0,
-                                       float* o, float* s_final, int32_t B, int32_t T, int32_t H,
-                                       int32_t Hg, int32_t K, int32_t V, void* stream) {
+namespace {
+
+// Shared by the per-head (or absent) and per-key kappa calls.
+lrs_status scan_diag_outer_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k, const lrs_bf16* v,
+                                const float* g, int32_t decay_mode, const float* k_scale, bool kscale_key,
+                                float scale, const float* s0, float* o, float* s_final, int32_t B,
+                                int32_t T, int32_t H, int32_t Hg, int32_t K, int32_t V, void* stream) {
     if (!ctx || !q || !k || !v || !g || !o || !s_final) return LRS_E_INVAL;
+    if (kscale_key && (!k_scale || decay_mode != 1)) return LRS_E_INVAL;
     if (B < 1 || T < 1 || H < 1 || Hg < 1 || K < 1 || V < 1) return LRS_E_INVAL;
     if (H % Hg != 0 || (decay_mode != 0 && decay_mode != 1)) return LRS_E_INVAL;
     if (K > 128) return LRS_E_UNSUPPORTED;
@@ -458,7 +462,8 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
         (decay_mode == 1 && !mul_ok(ng, K)) || !mul_ok(nst, H) || !mul_ok(nst, K) || !mul_ok(nst, V))
         return LRS_E_INVAL;
     const size_t bqk = static_cast<size_t>(nqk) * 2, bv = static_cast<size_t>(nv) * 2;
-    const size_t bg = static_cast<size_t>(ng) * 4, bks = static_cast<size_t>(bt) * H * 4;
+    const size_t bg = static_cast<size_t>(ng) * 4;
+    const size_t bks = static_cast<size_t>(bt) * H * (kscale_key ? K : 1) * 4;
     const size_t bo = static_cast<size_t>(nv) * 4, bst = static_cast<size_t>(nst) * 4;
     const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {g, bg}, {k_scale, bks}, {s0, bst}};
     const Span outs[] = {{o, bo}, {s_final, bst}};
@@ -473,6 +478,7 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
     p.g = g;
     p.decay_mode = decay_mode;
     p.k_scale = k_scale;
+    p.k_scale_key = kscale_key ? 1 : 0;
     p.scale = scale;
     p.s0 = s0;
     p.o = o;
@@ -486,9 +492,10 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
     // the vector path addresses one batch row of each tensor with 32-bit buffer offsets
     const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
-             aligned(g, 16) && aligned(o, 16) && row_bytes < (int64_t{1} << 31)) ? 1 : 0;
-    const lrs::DiagPlan plan =
-        lrs::diag_outer_plan(B, T, H, V, K, decay_mode, p.vec != 0, ctx->num_cus, ctx->diag_segments);
+             aligned(g, 16) && aligned(o, 16) && (!kscale_key || aligned(k_scale, 16)) &&
+             row_bytes < (int64_t{1} << 31)) ? 1 : 0;
+    const lrs::DiagPlan plan = lrs::diag_outer_plan(B, T, H, V, K, decay_mode, kscale_key, p.vec != 0,
+                                                    ctx->num_cus, ctx->diag_segments);
     const int64_t grid = static_cast<int64_t>(B) * H * plan.vtiles * plan.nseg;
     if (grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -499,6 +506,26 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
     ctx->last_stream = st;
     ctx->used = true;
     return LRS_OK;
+}
+
+}  // namespace
+
+LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                       const lrs_bf16* v, const float* g, int32_t decay_mode,
+                                       const float* k_scale, float scale, const float* s0,
+                                       float* o, float* s_final, int32_t B, int32_t T, int32_t H,
+                                       int32_t Hg, int32_t K, int32_t V, void* stream) {
+    return scan_diag_outer_impl(ctx, q, k, v, g, decay_mode, k_scale, false, scale, s0, o, s_final, B, T, H,
+                                Hg, K, V, stream);
+}
+
+LRS_API lrs_status lrs_scan_diag_outer_keyscale(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                                const lrs_bf16* v, const float* g, const float* k_scale,
+                                                float scale, const float* s0, float* o, float* s_final,
+                                                int32_t B, int32_t T, int32_t H, int32_t Hg, int32_t K,
+                                                int32_t V, void* stream) {
+    return scan_diag_outer_impl(ctx, q, k, v, g, 1, k_scale, true, scale, s0, o, s_final, B, T, H, Hg, K, V,
+                                stream);
 }
 
 namespace {

@@ -77,7 +77,8 @@ struct DiagParams {
     const uint16_t* v;
     const float* g;
     int decay_mode;        // 0: g [B,T,H]; 1: g [B,T,H,K]
-    const float* k_scale;  // nullable
+    const float* k_scale;  // nullable; [B,T,H], or [B,T,H,K] with k_scale_key
+    int k_scale_key;       // kappa per key (decay mode 1 only)
     float scale;
     const float* s0;       // nullable
     float* o;
@@ -98,8 +99,8 @@ struct DiagPlan {
 
 // requested_segments <= 0 picks as many segments as fill the chip's resident
 // workgroup slots once.
-DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool vec, int num_cus,
-                         int requested_segments);
+DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool kscale_key, bool vec,
+                         int num_cus, int requested_segments);
 size_t diag_outer_workspace_bytes(int B, int H, int K, int V, int nseg);
 hipError_t launch_scan_diag_outer(const DiagParams& p, const DiagPlan& plan, void* workspace,
                                   hipStream_t stream);

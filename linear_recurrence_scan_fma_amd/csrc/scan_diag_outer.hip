@@ -116,8 +116,10 @@ __device__ __forceinline__ bool score_job8(int wave, int n, int& kb, int& qb) {
 
 // AGG = true: segment reduction (a_seg, U_seg) from a zero state, no outputs.
 // AGG = false: outputs and the final state, starting from the folded segment state.
-template <int MODE, int KP, int WPB, bool VEC, bool AGG>
+// KK = true (per-key decay only): kappa per key, k_scale [B,T,H,K].
+template <int MODE, int KP, int WPB, bool VEC, bool AGG, bool KK = false>
 __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
+    static_assert(!KK || MODE == 1, "a per-key kappa needs the per-key decay path");
     constexpr bool OUT = !AGG;
     constexpr int NT = 64 * WPB;   // threads per workgroup
     constexpr int VT = 16 * WPB;   // V-tile width
@@ -148,6 +150,7 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     __shared__ __align__(16) float sTot[MODE == 1 ? RG * KP : 1];
     __shared__ float sGL[MODE == 1 ? KP : 1];    // G_L per key
     __shared__ __align__(16) float sEGL[MODE == 1 ? KP : 1];   // e^{G_L} per key
+    __shared__ __align__(16) float sKK[KK && OUT ? L * KP : 1];   // per-key kappa (exact-pairs path)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,13 +179,13 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     const int64_t qk_row = static_cast<int64_t>(Hg) * K * 2;        // bytes per step
     const int64_t v_row = static_cast<int64_t>(H) * V * 2;
     const int64_t g_row = static_cast<int64_t>(H) * (MODE == 1 ? K : 1) * 4;
-    const int64_t s_row = static_cast<int64_t>(H) * 4;               // k_scale
+    const int64_t s_row = static_cast<int64_t>(H) * (KK ? K : 1) * 4;   // k_scale
     const int64_t o_row = static_cast<int64_t>(H) * V * 4;
     const u16* qb = p.q + b * T * Hg * static_cast<int64_t>(K);
     const u16* kb_ = p.k + b * T * Hg * static_cast<int64_t>(K);
     const u16* vb = p.v + b * T * H * static_cast<int64_t>(V);
     const float* gb = p.g + b * T * H * static_cast<int64_t>(MODE == 1 ? K : 1);
-    const float* ksb = p.ks ? p.ks + b * T * H : nullptr;
+    const float* ksb = p.ks ? p.ks + b * T * H * static_cast<int64_t>(KK ? K : 1) : nullptr;
     float* ob = p.o + b * T * H * static_cast<int64_t>(V);
 
     // per-lane offsets within a chunk window
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     u32x2 cq2[MODE == 1 ? NQ : 1], ck2[MODE == 1 ? NQ : 1];
     u32x4 cgv[MODE == 1 ? NQ : 1];
     float ckp[MODE == 1 ? NQ : 1];
+    u32x4 ckk[KK ? NQ : 1];   // per-key kappa, 4 keys per row, as g
     u32x4 cv[PV];
     float cgs = 0.0f, ckap = 0.0f;
 
@@ -256,7 +260,8 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
 #pragma unroll
                     for (int r = 0; r < NQ; ++r) {
                         cgv[r] = buf_load16(wg, offg[r]);
-                        ckp[r] = buf_load_f32(ws, offs[r]);   // raw; NULL k_scale handled at use
+                        if constexpr (KK) ckk[r] = buf_load16(ws, offg[r]);
+                        else ckp[r] = buf_load_f32(ws, offs[r]);   // raw; NULL k_scale handled at use
                     }
                 }
 #pragma unroll
@@ -292,6 +297,7 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                     const int64_t t = t0 + rg * RPG + r;
                     u16 qe[4] = {0, 0, 0, 0}, ke[4] = {0, 0, 0, 0};
                     float ge[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    float kk4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                     float kp = 0.0f;
                     if (t < T) {
                         const int64_t oq = (t * Hg + grp) * static_cast<int64_t>(K);
@@ -302,10 +308,14 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                                 if constexpr (OUT) qe[e] = qb[oq + d0 + e];
                                 ke[e] = kb_[oq + d0 + e];
                                 ge[e] = gb[og + d0 + e];
+                                if constexpr (KK) kk4[e] = ksb[og + d0 + e];
                             }
                         }
-                        kp = ksb ? ksb[t * H + h] : 1.0f;
+                        if constexpr (!KK) kp = ksb ? ksb[t * H + h] : 1.0f;
                     }
+                    if constexpr (KK)
+                        ckk[r] = u32x4{__float_as_uint(kk4[0]), __float_as_uint(kk4[1]), __float_as_uint(kk4[2]),
+                                       __float_as_uint(kk4[3])};
                     cq2[r] = u32x2{qe[0] | (static_cast<uint32_t>(qe[1]) << 16),
                                    qe[2] | (static_cast<uint32_t>(qe[3]) << 16)};
                     ck2[r] = u32x2{ke[0] | (static_cast<uint32_t>(ke[1]) << 16),
@@ -457,7 +467,12 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
             float kapr[NQ];
 #pragma unroll
             for (int r = 0; r < NQ; ++r)
-                kapr[r] = (VEC && !p.ks) ? (t0 + rg * RPG + r < T ? 1.0f : 0.0f) : ckp[r];
+                kapr[r] = KK ? 1.0f : (VEC && !p.ks) ? (t0 + rg * RPG + r < T ? 1.0f : 0.0f) : ckp[r];
+            // kappa of row r, key d0 + e
+            auto kap_at = [&](int r, int e) -> float {
+                if constexpr (KK) return __uint_as_float(ckk[r][e]);
+                else return kapr[r];
+            };
             if (OUT && !fast) {
                 // exact scores pair by pair: raw q, k and G into the operand space
                 float* sGf = reinterpret_cast<float*>(sK);
@@ -468,6 +483,9 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                     *reinterpret_cast<u32x2*>(sQ + L * LDK + t * LDK + d0) = ck2[r];
                     *reinterpret_cast<f32x4*>(sGf + t * KP + d0) = f32x4{G[r][0], G[r][1], G[r][2], G[r][3]};
                     if (kg == 0) sKap[t] = scale * kapr[r];
+                    if constexpr (KK)
+                        *reinterpret_cast<f32x4*>(sKK + t * KP + d0) =
+                            f32x4{kap_at(r, 0), kap_at(r, 1), kap_at(r, 2), kap_at(r, 3)};
                 }
                 __syncthreads();
                 for (int idx = tid; idx < L * L; idx += NT) {
@@ -475,7 +493,8 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                     float a = 0.0f;
                     if (tau <= t) {
                         for (int d = 0; d < KP; ++d)
-                            a += bf2f(sQ[t * LDK + d]) * bf2f(sQ[L * LDK + tau * LDK + d]) *
+                            a += bf2f(sQ[t * LDK + d]) * (KK ? bf2f(sQ[L * LDK + tau * LDK + d]) * sKK[tau * KP + d]
+                                                             : bf2f(sQ[L * LDK + tau * LDK + d])) *
                                  __expf(sGf[t * KP + d] - sGf[tau * KP + d]);
                         a *= sKap[tau];
                     }
@@ -494,7 +513,7 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (OUT) qv[e] = bf2f(half_elem(cq2[r], e)) * (scale * __expf(fast ? G[r][e] - tot[e] : G[r][e]));
-                    kv[e] = bf2f(half_elem(ck2[r], e)) * (kapr[r] * __expf(tot[e] - G[r][e]));
+                    kv[e] = bf2f(half_elem(ck2[r], e)) * (kap_at(r, e) * __expf(tot[e] - G[r][e]));
                 }
                 uint32_t hq[2], lq[2], hk[2], lk[2];
                 if constexpr (OUT) {
@@ -701,30 +720,30 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     }
 }
 
-template <int MODE, int KP, int WPB>
+template <int MODE, int KP, int WPB, bool KK>
 hipError_t launch_t(const DiagArgs& a, bool vec, hipStream_t stream) {
     const int64_t units = static_cast<int64_t>(a.B) * a.H * a.vtiles;
     const dim3 block(64 * WPB);
     if (a.nseg > 1) {
         const dim3 grid(static_cast<unsigned>(units * (a.nseg - 1)));
-        if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, true>), grid, block, 0, stream, a);
+        if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, true, KK>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, true, KK>), grid, block, 0, stream, a);
     }
     const dim3 grid(static_cast<unsigned>(units * a.nseg));
-    if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, false>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, false>), grid, block, 0, stream, a);
+    if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, false, KK>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, false, KK>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 
 // Output-pass workgroups that fit on one compute unit at once (LDS and
 // registers), measured once per kernel variant.
-template <int MODE, int KP, int WPB, bool VEC>
+template <int MODE, int KP, int WPB, bool VEC, bool KK>
 int resident_blocks() {
     static int n = 0;
     if (n == 0) {
         int m = 1;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, diag_outer_kernel<MODE, KP, WPB, VEC, false>, 64 * WPB,
-                                                         0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, diag_outer_kernel<MODE, KP, WPB, VEC, false, KK>,
+                                                         64 * WPB, 0) != hipSuccess ||
             m < 1)
             m = 1;
         n = m;
@@ -732,26 +751,28 @@ int resident_blocks() {
     return n;
 }
 
-template <int MODE, int KP>
+template <int MODE, int KP, bool KK>
 int resident_blocks_w(int wpb, bool vec) {
-    if (wpb == 8) return vec ? resident_blocks<MODE, KP, 8, true>() : resident_blocks<MODE, KP, 8, false>();
-    return vec ? resident_blocks<MODE, KP, 4, true>() : resident_blocks<MODE, KP, 4, false>();
+    if (wpb == 8) return vec ? resident_blocks<MODE, KP, 8, true, KK>() : resident_blocks<MODE, KP, 8, false, KK>();
+    return vec ? resident_blocks<MODE, KP, 4, true, KK>() : resident_blocks<MODE, KP, 4, false, KK>();
 }
 
-int resident_blocks(int decay_mode, int K, int wpb, bool vec) {
-    if (decay_mode == 0) return K <= 64 ? resident_blocks_w<0, 64>(wpb, vec) : resident_blocks_w<0, 128>(wpb, vec);
-    return K <= 64 ? resident_blocks_w<1, 64>(wpb, vec) : resident_blocks_w<1, 128>(wpb, vec);
+int resident_blocks(int decay_mode, bool kk, int K, int wpb, bool vec) {
+    if (decay_mode == 0)
+        return K <= 64 ? resident_blocks_w<0, 64, false>(wpb, vec) : resident_blocks_w<0, 128, false>(wpb, vec);
+    if (kk) return K <= 64 ? resident_blocks_w<1, 64, true>(wpb, vec) : resident_blocks_w<1, 128, true>(wpb, vec);
+    return K <= 64 ? resident_blocks_w<1, 64, false>(wpb, vec) : resident_blocks_w<1, 128, false>(wpb, vec);
 }
 
-template <int MODE, int KP>
+template <int MODE, int KP, bool KK>
 hipError_t launch_w(const DiagArgs& a, int wpb, bool vec, hipStream_t stream) {
-    return wpb == 8 ? launch_t<MODE, KP, 8>(a, vec, stream) : launch_t<MODE, KP, 4>(a, vec, stream);
+    return wpb == 8 ? launch_t<MODE, KP, 8, KK>(a, vec, stream) : launch_t<MODE, KP, 4, KK>(a, vec, stream);
 }
 
 }  // namespace
 
-DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool vec, int num_cus,
-                         int requested_segments) {
+DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool kscale_key, bool vec,
+                         int num_cus, int requested_segments) {
     DiagPlan pl{};
     pl.waves = waves_for(V);
     const int vt = 16 * pl.waves;
@@ -764,7 +785,8 @@ DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool
         // second round covers the tail of the first), but at least
         // kMinChunksPerSegment chunks each: every extra segment costs a
         // reduction pass over its chunks and a longer fold
-        const int64_t slots = static_cast<int64_t>(num_cus) * resident_blocks(decay_mode, K, pl.waves, vec);
+        const int64_t slots =
+            static_cast<int64_t>(num_cus) * resident_blocks(decay_mode, kscale_key, K, pl.waves, vec);
         nseg = 2 * slots / units;
         if (nseg > pl.nchunks / kMinChunksPerSegment) nseg = pl.nchunks / kMinChunksPerSegment;
     }
@@ -811,8 +833,10 @@ hipError_t launch_scan_diag_outer(const DiagParams& prm, const DiagPlan& pl, voi
     const bool vec = prm.vec != 0;
     const bool k64 = prm.K <= 64;
     if (prm.decay_mode == 0)
-        return k64 ? launch_w<0, 64>(a, pl.waves, vec, stream) : launch_w<0, 128>(a, pl.waves, vec, stream);
-    return k64 ? launch_w<1, 64>(a, pl.waves, vec, stream) : launch_w<1, 128>(a, pl.waves, vec, stream);
+        return k64 ? launch_w<0, 64, false>(a, pl.waves, vec, stream) : launch_w<0, 128, false>(a, pl.waves, vec, stream);
+    if (prm.k_scale_key)
+        return k64 ? launch_w<1, 64, true>(a, pl.waves, vec, stream) : launch_w<1, 128, true>(a, pl.waves, vec, stream);
+    return k64 ? launch_w<1, 64, false>(a, pl.waves, vec, stream) : launch_w<1, 128, false>(a, pl.waves, vec, stream);
 }
 
 }  // namespace lrs

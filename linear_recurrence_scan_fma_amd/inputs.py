@@ -20,6 +20,12 @@ float64 -> float32 -> bfloat16, each step round-to-nearest-even):
                        fp32 [B,T,H,K]; readout scale K**-0.5
 * DeltaNet shaped:     q, k = row-L2-normalised N(0,1), bf16 [B,T,H,K];
                        v ~ N(0,1) bf16 [B,T,H,V]; beta = sigmoid(N(0,1)) fp32 [B,T,H]
+* associative memory:  q, k, v ~ N(0,1) bf16 [B,T,H,D]; p = sigmoid(N(2,1)) per
+                       key fp32 [B,T,H,K]; g = log p, kappa = 1 - p (each from p
+                       in float64); readout scale 1
+* HGRN2 shaped:        f = sigmoid(N(2,1)) per key; g = log f fp32; k = 1 - f
+                       bf16 (the key is tied to the forget gate); q, v ~ N(0,1)
+                       bf16; readout scale 1
 * RWKV-7 shaped:       as DeltaNet, plus a per-key log-decay
                        g = -exp(-softplus(-z) - 0.5), z ~ N(0,1), fp32 [B,T,H,K]
                        (each step keeps a fraction in (0.545, 1) of every key row)
@@ -27,7 +33,8 @@ float64 -> float32 -> bfloat16, each step round-to-nearest-even):
 Model shapes follow the models named on the pages: Mamba-2 130m (24 heads x 64,
 state 128) [SunnyNet log §4.1]; GLA 340M (4 heads x 128) [SunnyNet log §4.3];
 DeltaNet 340M (8 heads x 128) [SunnyNet log §4.2]; RWKV-7 191M (64 x 64 state per
-head, 12 heads) [SunnyNet log §5.1].  SunnyNet log =
+head, 12 heads) [SunnyNet log §5.1]; HGRN2 1.3B (dim 2048, 16 heads) ["我拿同一份权重和
+llama.cpp 正面比了一场" §4].  The associative memory's shape is not given on the pages.  SunnyNet log =
 "SunnyNet 工程化实录：一个 O(N) 架构如何长出自己的 C 推理运行时" (developer.aliyun.com/article/1773847).
 """
 from __future__ import annotations
@@ -47,6 +54,8 @@ GLA = dict(B=4, T=4096, H=4, K=128, V=128)
 DELTANET = dict(B=4, T=4096, H=8, K=128, V=128)
 DELTANET_K64 = dict(B=4, T=4096, H=8, K=64, V=128)
 RWKV7 = dict(B=4, T=4096, H=12, K=64, V=64)
+HGRN2 = dict(B=4, T=4096, H=16, K=128, V=128)
+ASSOC = dict(B=4, T=4096, H=8, K=64, V=64)
 
 
 def _f32(x64: np.ndarray) -> torch.Tensor:
@@ -153,6 +162,30 @@ def rwkv7(B=4, T=4096, H=12, K=64, V=64, seed=SEED_BASE + 6):
     z = rng.standard_normal((B, T, H, K))
     d["g"] = _f32(-np.exp(-_softplus(-z) - 0.5))
     return d
+
+
+def assoc_memory(B=4, T=4096, H=8, K=64, V=64, seed=SEED_BASE + 7):
+    """Matrix associative memory S_t = p (.) S_{t-1} + (1 - p) (.) (v_t (x) k_t),
+    p per key: returned as the per-key-scale decay-separable scan (g = log p,
+    kappa = 1 - p)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, K))
+    k = rng.standard_normal((B, T, H, K))
+    v = rng.standard_normal((B, T, H, V))
+    pk = _sigmoid(rng.standard_normal((B, T, H, K)) + 2.0)
+    return dict(q=_bf16(q), k=_bf16(k), v=_bf16(v), g=_f32(np.log(pk)), decay_mode=1,
+                k_scale=None, k_scale_key=_f32(1.0 - pk), scale=1.0, s0=None)
+
+
+def hgrn2(B=4, T=4096, H=16, K=128, V=128, seed=SEED_BASE + 8):
+    """HGRN2 shaped scan: GLA's recurrence with the key tied to the per-key
+    forget gate, k = 1 - f, decay f."""
+    rng = np.random.default_rng(seed)
+    f = _sigmoid(rng.standard_normal((B, T, H, K)) + 2.0)
+    q = rng.standard_normal((B, T, H, K))
+    v = rng.standard_normal((B, T, H, V))
+    return dict(q=_bf16(q), k=_bf16(1.0 - f), v=_bf16(v), g=_f32(np.log(f)), decay_mode=1,
+                k_scale=None, scale=1.0, s0=None)
 
 
 def random_state(shape, seed, std=1.0):

@@ -292,3 +292,25 @@ def scan_delta_decay_explicit(q, k, v, g, beta, scale=1.0, s0=None, dtype=np.flo
     """The same update as a dense transition S_t = (diag(exp(g_t)) - beta k k^T) S_{t-1}
     + beta k v^T [SunnyNet log §5.1], implemented separately from the rank-1 form."""
     return _delta_decay("orc_scan_delta_decay_explicit", q, k, v, g, beta, scale, s0, dtype, nthreads)
+
+
+# ---- output epilogues (plain numpy definitions, float64) -----------------------
+def epilogue_norm_gate(o, z, weight=None, eps=1e-6):
+    """GLA's output epilogue [SunnyNet log §4.3]: normalise first, then gate.
+
+    out[b,t,h,:] = o / sqrt(mean_j o[b,t,h,j]^2 + eps) * weight * silu(z[b,t,h,:]),
+    silu(x) = x / (1 + exp(-x)); RMSNorm over the value axis of each head;
+    ``weight`` [V] (None: ones).  o, z [B,T,H,V].
+    """
+    o = np.asarray(o, dtype=np.float64)
+    z = _arr(z, np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    w = np.ones(o.shape[-1]) if weight is None else _arr(weight, np.float64)
+    return o / np.sqrt(ms + eps) * w * (z / (1.0 + np.exp(-z)))
+
+
+def epilogue_skip(o, d_skip, x):
+    """Mamba-2's skip connection: out[b,t,h,:] = o[b,t,h,:] + D[h] x[b,t,h,:],
+    with x the scan's value input.  o, x [B,T,H,V]; D [H]."""
+    o = np.asarray(o, dtype=np.float64)
+    return o + _arr(d_skip, np.float64)[None, None, :, None] * _arr(x, np.float64)

@@ -635,6 +635,51 @@ def test_delta_chunked_ut_form():
 
 
 # ----------------------------------------------------------------------------
+# Output epilogues: GLA's RMSNorm(o) * silu(g) [SunnyNet log §4.3] and
+# Mamba-2's D x skip
+# ----------------------------------------------------------------------------
+
+def test_epilogue_norm_gate_hand_worked():
+    # o = [3, 4]: mean square 12.5, so o / rms = [3, 4] / sqrt(12.5) = [0.6 sqrt2, 0.8 sqrt2];
+    # weight [1, 2]; z = [0, ln 3]: silu(0) = 0, silu(ln 3) = (3/4) ln 3
+    o = np.array([3.0, 4.0]).reshape(1, 1, 1, 2)
+    z = np.array([0.0, math.log(3.0)]).reshape(1, 1, 1, 2)
+    out = oracle.epilogue_norm_gate(o, z, np.array([1.0, 2.0]), eps=0.0)
+    ref = np.array([0.0, 0.8 * math.sqrt(2.0) * 2.0 * 0.75 * math.log(3.0)])
+    assert rel(out.reshape(2), ref) < 1e-15
+
+
+def test_epilogue_norm_gate_invariants():
+    r = _rng(90)
+    B, T, H, V = 2, 7, 3, 16
+    o = r.standard_normal((B, T, H, V)) * 5.0
+    # z = 0 gates everything off
+    assert np.array_equal(oracle.epilogue_norm_gate(o, np.zeros_like(o)), np.zeros_like(o))
+    # constant gate c, unit weight: the mean square of a row is silu(c)^2 ms / (ms + eps)
+    c, eps = 1.7, 1e-3
+    out = oracle.epilogue_norm_gate(o, np.full_like(o, c), None, eps)
+    ms = np.mean(o * o, axis=-1)
+    sil = c / (1.0 + math.exp(-c))
+    assert rel(np.mean(out * out, axis=-1), sil * sil * ms / (ms + eps)) < 1e-13
+    # scale invariance: o and 10 o normalise to the same rows when eps = 0
+    assert rel(oracle.epilogue_norm_gate(10 * o, o, None, 0.0), oracle.epilogue_norm_gate(o, o, None, 0.0)) < 1e-14
+    # the weight multiplies each value column
+    w = r.uniform(0.5, 2.0, V)
+    assert rel(oracle.epilogue_norm_gate(o, o, w), oracle.epilogue_norm_gate(o, o) * w) < 1e-15
+
+
+def test_epilogue_skip():
+    r = _rng(91)
+    B, T, H, V = 2, 5, 3, 4
+    o = r.standard_normal((B, T, H, V))
+    x = r.standard_normal((B, T, H, V))
+    assert np.array_equal(oracle.epilogue_skip(o, np.zeros(H), x), o)
+    assert np.array_equal(oracle.epilogue_skip(np.zeros_like(o), np.ones(H), x), x)
+    dsk = np.array([0.5, -2.0, 3.0])
+    assert rel(oracle.epilogue_skip(o, dsk, x)[:, :, 1], o[:, :, 1] - 2.0 * x[:, :, 1]) < 1e-15
+
+
+# ----------------------------------------------------------------------------
 # Delta rule with a per-key decay [SunnyNet log §5.1, RWKV-7's state update]
 # ----------------------------------------------------------------------------
 

@@ -253,6 +253,14 @@ def profile_run(ctx, binding, inputs, dev, steps):
             else:
                 binding.scan_delta(ctx, q, k, v, m["beta"].to(dev), m["scale"])
         torch.cuda.synchronize()
+    for gen, epi in ((lambda: inputs.gla(**inputs.GLA), binding.LRS_EPILOGUE_NORM_GATE),
+                     (lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}),
+                      binding.LRS_EPILOGUE_SKIP)):
+        m = with_epilogue(inputs, gen(), epi)
+        fn, _ = epilogue_call(binding, ctx, m, dev)
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
     assert binding.lrs_context_check(ctx) == binding.LRS_OK
     log("[bench] profile run done")
 
@@ -372,6 +380,51 @@ def elem_rows(ctx, binding, inputs, dev, flush):
         rows.append(row)
         del sa, sx, st
     return rows
+
+
+def with_epilogue(inputs, d, epi):
+    """A diag-outer workload plus the inputs of one output epilogue."""
+    B, T, H, V = d["v"].shape
+    d = dict(d)
+    if epi == 2:   # LRS_EPILOGUE_NORM_GATE
+        d.update(inputs.norm_gate_epilogue(B, T, H, V))
+    else:
+        d.update(inputs.skip_epilogue(H))
+    d["epilogue"] = epi
+    return d
+
+
+def epilogue_call(binding, ctx, d, dev):
+    """A closure running the fused-epilogue scan with a bf16 output, and its
+    output tensors."""
+    import torch
+
+    q, k, v, g = (d[n].to(dev) for n in ("q", "k", "v", "g"))
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    ks = None if d["k_scale"] is None else d["k_scale"].to(dev)
+    z = d["gate"].to(dev) if "gate" in d else None
+    w = d["norm_weight"].to(dev) if "norm_weight" in d else None
+    dsk = d["d_skip"].to(dev) if "d_skip" in d else None
+    o = torch.empty((B, T, H, V), device=dev, dtype=torch.bfloat16)
+    fin = torch.empty((B, H, K, V), device=dev)
+
+    def fn():
+        binding.lrs_scan_diag_outer_epilogue(ctx, q, k, v, g, d["decay_mode"], ks, d["scale"], None, d["epilogue"],
+                                             dsk, z, w, d.get("eps", 0.0), binding.LRS_DTYPE_BF16, o, fin)
+    return fn, (o, fin)
+
+
+def epilogue_bytes(d):
+    """Algorithmic bytes of a fused-epilogue call with a bf16 output: the scan's
+    inputs, the epilogue's inputs, a bf16 o and the fp32 final state."""
+    B, T, H, V = d["v"].shape
+    n = diag_bytes(d) - B * T * H * V * 4 + B * T * H * V * 2
+    if "gate" in d:
+        n += d["gate"].numel() * 2 + d["norm_weight"].numel() * 4
+    if "d_skip" in d:
+        n += d["d_skip"].numel() * 4
+    return n
 
 
 def diag_bytes(d):
@@ -543,6 +596,60 @@ def run_rows(ctx, args, binding, inputs, dev):
                                          f"scaled by the {min(nth, B * H)} threads the oracle spreads heads over"}
         rows.append(row)
         del q, k, v, o, fin
+
+    # fused output epilogues with a bf16 output
+    epi_specs = [
+        ("scan_diag_outer_epilogue GLA B=4 T=4096 H=4 K=128 V=128 + RMSNorm(o)*silu(gate), bf16 out",
+         lambda: inputs.gla(**inputs.GLA), binding.LRS_EPILOGUE_NORM_GATE,
+         ["diag_outer_agg_gla_B4_T4096_H4_K128_V128", "diag_outer_out_epi_normgate_gla_B4_T4096_H4_K128_V128"]),
+        ("scan_diag_outer_epilogue Mamba-2 B=8 T=4096 H=24 P=64 N=128 + D x skip, bf16 out",
+         lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}), binding.LRS_EPILOGUE_SKIP,
+         ["diag_outer_agg_mamba2_B8_T4096_H24_P64_N128", "diag_outer_out_epi_skip_mamba2_B8_T4096_H24_P64_N128"]),
+    ]
+    for name, gen, epi, traffic_keys in epi_specs:
+        log(f"[bench] row {name}")
+        d = with_epilogue(inputs, gen(), epi)
+        fn, (o, fin) = epilogue_call(binding, ctx, d, dev)
+        B, T, H, V = d["v"].shape
+        K = d["q"].shape[3]
+        med, mn = time_launches(fn, 20, 3, flush)
+        nbytes = epilogue_bytes(d)
+        units = B * T * H
+        row = {"row": name, "us_median": round(med * 1e3, 2), "us_min": round(mn * 1e3, 2),
+               "tokens_heads_per_s": round(units / (med * 1e-3), 1),
+               "roofline": {"bound": "hbm", "achieved": round(nbytes / (med * 1e-3) / 1e9, 2),
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "bytes_per_call": nbytes},
+               "algorithmic_TFLOP/s": round(units * 5 * K * V / (med * 1e-3) / 1e12, 3)}
+        tr = [measured_traffic(key, "scan_diag_outer.hip") for key in traffic_keys]
+        row["roofline"]["traffic"] = None if any(t is None for t in tr) else sum(tr)
+        row["mfma_util"] = measured_mfma_util(traffic_keys, "scan_diag_outer.hip")
+        errs, t_cpu = [], 0.0
+        for (bb, hh) in heads:
+            grp = 0 if d["q"].shape[2] == 1 else hh
+            sl = lambda x, c: x[bb:bb + 1, :, c:c + 1]  # noqa: E731
+            t0 = time.perf_counter()
+            ro, rf = oracle.scan_diag_outer(sl(d["q"], grp), sl(d["k"], grp), sl(d["v"], hh), sl(d["g"], hh),
+                                            d["decay_mode"], None if d["k_scale"] is None else sl(d["k_scale"], hh),
+                                            d["scale"], nthreads=1)
+            if epi == binding.LRS_EPILOGUE_NORM_GATE:
+                ro = oracle.epilogue_norm_gate(ro, sl(d["gate"], hh), d["norm_weight"], d["eps"])
+            else:
+                ro = oracle.epilogue_skip(ro, d["d_skip"][hh:hh + 1], sl(d["v"], hh))
+            t_cpu += time.perf_counter() - t0
+            go = o[bb:bb + 1, :, hh:hh + 1].float().cpu().double().numpy()
+            gf = fin[bb:bb + 1, hh:hh + 1].cpu().double().numpy()
+            errs.append(max(float(np.max(np.abs(go - ro)) / np.max(np.abs(ro))),
+                            float(np.max(np.abs(gf - rf)) / np.max(np.abs(rf)))))
+        row["parity_max_rel_err_sampled_heads"] = max(errs)
+        row["parity_note"] = "bf16 output: tolerance 2e-3 + 2^-8 (the output's own rounding)"
+        row["cpu_baseline"] = {"value": round(len(heads) * T / t_cpu * min(nth, B * H), 1),
+                               "unit": "tokens*heads/s", "cores": min(nth, B * H), "kind": "oracle",
+                               "sample": f"{len(heads)} heads x full T, scan then epilogue, one thread each "
+                                         f"(fp64 oracle), scaled by {min(nth, B * H)} threads"}
+        rows.append(row)
+        del o, fin, d
     return rows
 
 

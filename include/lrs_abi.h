@@ -10,6 +10,8 @@
  *   lrs_scan_delta       S_t = S_{t-1} + k_t [beta_t (v_t - S_{t-1}^T k_t)]^T,
  *                        o_t = scale S_t^T q_t                     (per head)
  *
+ *   lrs_scan_diag_outer_epilogue  as lrs_scan_diag_outer, with a fused output
+ *                        epilogue (skip or norm-gate) and fp32 or bf16 output
  *   lrs_scan_diag_outer_keyscale  as lrs_scan_diag_outer, kappa per key
  *   lrs_scan_delta_decay S_t = diag(exp(g_t)) S_{t-1}
  *                            + k_t [beta_t (v_t - S_{t-1}^T k_t)]^T,
@@ -101,6 +103,11 @@ enum {
 #define LRS_CAP_ELEM_STEP       (1u << 5)   /* since 1.1 */
 #define LRS_CAP_SCAN_DELTA_DECAY (1u << 6)  /* since 1.1 */
 #define LRS_CAP_SCAN_DIAG_KEYSCALE (1u << 7) /* since 1.1 */
+#define LRS_CAP_SCAN_DIAG_EPILOGUE (1u << 8) /* since 1.1 */
+
+/* Output epilogues and dtypes of lrs_scan_diag_outer_epilogue (since 1.1). */
+enum { LRS_EPILOGUE_NONE = 0, LRS_EPILOGUE_SKIP = 1, LRS_EPILOGUE_NORM_GATE = 2 };
+enum { LRS_DTYPE_F32 = 0, LRS_DTYPE_BF16 = 1 };
 
 /* Packed version of the library actually loaded. */
 uint32_t lrs_abi_version(void);
@@ -300,6 +307,37 @@ lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                           const lrs_bf16* v, const float* beta, float scale, const float* s0,
                           float* o, float* s_final, int32_t B, int32_t T, int32_t H, int32_t K,
                           int32_t V, void* stream);
+
+/* ---- decay-separable scan with a fused output epilogue -------------------
+ * lrs_scan_diag_outer whose outputs go through an epilogue inside the kernel
+ * before they are written, in fp32 or bf16:
+ *
+ *   LRS_EPILOGUE_NONE       out = o
+ *   LRS_EPILOGUE_SKIP       out = o + d_skip[h] * v          (Mamba-2's D x skip)
+ *   LRS_EPILOGUE_NORM_GATE  out = o / sqrt(mean_j o_j^2 + eps) * norm_weight * silu(gate)
+ *                           (GLA's output norm and gate [SunnyNet log §4.3]:
+ *                           RMSNorm over the value axis of each head, then the gate)
+ *
+ * with o = scale S_t^T q_t as in lrs_scan_diag_outer and silu(x) = x / (1 + e^-x).
+ *
+ *   d_skip       fp32 [H]          SKIP only (else ignored)
+ *   gate         bf16 [B,T,H,V]    NORM_GATE only
+ *   norm_weight  fp32 [V]          NORM_GATE only; NULL means ones
+ *   eps          >= 0              NORM_GATE only
+ *   out_dtype    LRS_DTYPE_F32 or LRS_DTYPE_BF16 (rounded to nearest even)
+ *   o            [B,T,H,V] of out_dtype (device pointer, 4- or 2-byte aligned)
+ *
+ * Writing bf16 halves the output bytes, which are 28-61% of these scans'
+ * traffic.  NORM_GATE needs V <= 128 (LRS_E_UNSUPPORTED above).  Other
+ * arguments, limits and errors as lrs_scan_diag_outer.
+ */
+lrs_status lrs_scan_diag_outer_epilogue(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                        const lrs_bf16* v, const float* g, int32_t decay_mode,
+                                        const float* k_scale, float scale, const float* s0,
+                                        int32_t epilogue, const float* d_skip, const lrs_bf16* gate,
+                                        const float* norm_weight, float eps, int32_t out_dtype,
+                                        void* o, float* s_final, int32_t B, int32_t T, int32_t H,
+                                        int32_t Hg, int32_t K, int32_t V, void* stream);
 
 /* ---- decay-separable scan with a per-key injection scale ------------------
  * As lrs_scan_diag_outer with a per-key decay (decay mode 1), but kappa is a

@@ -25,7 +25,9 @@ LRS_OK, LRS_E_INVAL, LRS_E_NOMEM, LRS_E_IO, LRS_E_FORMAT, LRS_E_UNSUPPORTED, LRS
     0, -1, -2, -3, -4, -5, -6)
 LRS_CAP_SCAN_FMA, LRS_CAP_SCAN_GATED, LRS_CAP_SCAN_DIAG_OUTER, LRS_CAP_SCAN_DELTA = 1, 2, 4, 8
 LRS_CAP_ELEM_BACKWARD, LRS_CAP_ELEM_STEP, LRS_CAP_SCAN_DELTA_DECAY = 16, 32, 64
-LRS_CAP_SCAN_DIAG_KEYSCALE = 128
+LRS_CAP_SCAN_DIAG_KEYSCALE, LRS_CAP_SCAN_DIAG_EPILOGUE = 128, 256
+LRS_EPILOGUE_NONE, LRS_EPILOGUE_SKIP, LRS_EPILOGUE_NORM_GATE = 0, 1, 2
+LRS_DTYPE_F32, LRS_DTYPE_BF16 = 0, 1
 LRS_PARAM_ELEM_SCHEDULE = 1
 LRS_PARAM_DIAG_SEGMENTS = 2
 LRS_ELEM_SCHEDULE_AUTO, LRS_ELEM_SCHEDULE_STREAM, LRS_ELEM_SCHEDULE_LOOKBACK = 0, 1, 2
@@ -55,6 +57,8 @@ SIGNATURES = {
                                    _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_diag_outer_keyscale": (_I32, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P,
                                             _I32, _I32, _I32, _I32, _I32, _I32, _P]),
+    "lrs_scan_diag_outer_epilogue": (_I32, [_P, _P, _P, _P, _P, _I32, _P, _F, _P, _I32, _P, _P, _P, _F,
+                                            _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_delta": (_I32, [_P, _P, _P, _P, _P, _F, _P, _P, _P,
                               _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_delta_decay": (_I32, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P,
@@ -293,6 +297,32 @@ def lrs_scan_diag_outer(ctx, q, k, v, g, decay_mode, k_scale, scale, s0, o, s_fi
     _check("lrs_scan_diag_outer", st)
 
 
+def lrs_scan_diag_outer_epilogue(ctx, q, k, v, g, decay_mode, k_scale, scale, s0, epilogue, d_skip, gate,
+                                 norm_weight, eps, out_dtype, o, s_final, stream=None) -> None:
+    """lrs_scan_diag_outer with a fused output epilogue (LRS_EPILOGUE_*) and an
+    fp32 or bf16 output (LRS_DTYPE_*): d_skip [H] fp32; gate [B,T,H,V] bf16;
+    norm_weight [V] fp32 or None; o [B,T,H,V] of out_dtype."""
+    import torch
+
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    d = ctx.device
+    bf, f32 = torch.bfloat16, torch.float32
+    gshape = (B, T, H) if decay_mode == 0 else (B, T, H, K)
+    odt = bf if out_dtype == LRS_DTYPE_BF16 else f32
+    args = (
+        _ptr(q, bf, (B, T, Hg, K), "q", d), _ptr(k, bf, (B, T, Hg, K), "k", d),
+        _ptr(v, bf, (B, T, H, V), "v", d), _ptr(g, f32, gshape, "g", d), int(decay_mode),
+        _ptr(k_scale, f32, (B, T, H), "k_scale", d), float(scale),
+        _ptr(s0, f32, (B, H, K, V), "s0", d), int(epilogue), _ptr(d_skip, f32, (H,), "d_skip", d),
+        _ptr(gate, bf, (B, T, H, V), "gate", d), _ptr(norm_weight, f32, (V,), "norm_weight", d),
+        float(eps), int(out_dtype), _ptr(o, odt, (B, T, H, V), "o", d),
+        _ptr(s_final, f32, (B, H, K, V), "s_final", d),
+    )
+    st = lib().lrs_scan_diag_outer_epilogue(ctx.handle, *args, B, T, H, Hg, K, V, _stream(stream, d))
+    _check("lrs_scan_diag_outer_epilogue", st)
+
+
 def lrs_scan_diag_outer_keyscale(ctx, q, k, v, g, k_scale, scale, s0, o, s_final, stream=None) -> None:
     """As lrs_scan_diag_outer with per-key decay g [B,T,H,K] and per-key kappa
     k_scale [B,T,H,K] fp32 (required)."""
@@ -422,4 +452,19 @@ def scan_diag_outer_keyscale(ctx, q, k, v, g, k_scale, scale=1.0, s0=None, strea
     o = torch.empty((B, T, H, V), dtype=torch.float32, device=q.device)
     fin = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
     lrs_scan_diag_outer_keyscale(ctx, q, k, v, g, k_scale, scale, s0, o, fin, stream)
+    return o, fin
+
+
+def scan_diag_outer_epilogue(ctx, q, k, v, g, decay_mode, k_scale=None, scale=1.0, s0=None,
+                             epilogue=0, d_skip=None, gate=None, norm_weight=None, eps=1e-6,
+                             out_dtype=0, stream=None):
+    import torch
+
+    B, T, Hg, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    odt = torch.bfloat16 if out_dtype == LRS_DTYPE_BF16 else torch.float32
+    o = torch.empty((B, T, H, V), dtype=odt, device=q.device)
+    fin = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
+    lrs_scan_diag_outer_epilogue(ctx, q, k, v, g, decay_mode, k_scale, scale, s0, epilogue, d_skip, gate,
+                                 norm_weight, eps, out_dtype, o, fin, stream)
     return o, fin

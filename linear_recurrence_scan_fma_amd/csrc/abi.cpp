@@ -278,7 +278,7 @@ LRS_API lrs_status lrs_abi_check(int32_t caller_major) {
 LRS_API uint32_t lrs_abi_caps(void) {
     return LRS_CAP_SCAN_FMA | LRS_CAP_SCAN_GATED | LRS_CAP_SCAN_DIAG_OUTER | LRS_CAP_SCAN_DELTA |
            LRS_CAP_ELEM_BACKWARD | LRS_CAP_ELEM_STEP | LRS_CAP_SCAN_DELTA_DECAY |
-           LRS_CAP_SCAN_DIAG_KEYSCALE;
+           LRS_CAP_SCAN_DIAG_KEYSCALE | LRS_CAP_SCAN_DIAG_EPILOGUE;
 }
 
 LRS_API const char* lrs_status_string(lrs_status status) {
@@ -442,18 +442,41 @@ lrs_status grow_workspace(void*& ptr, size_t& cap, size_t need, hipStream_t stre
 
 namespace {
 
-// Shared by the per-head (or absent) and per-key kappa calls.
+// Output epilogue of a diag-outer call (all zero: none, fp32 output).
+struct DiagEpilogue {
+    int32_t kind = LRS_EPILOGUE_NONE;
+    int32_t out_dtype = LRS_DTYPE_F32;
+    const float* d_skip = nullptr;
+    const lrs_bf16* gate = nullptr;
+    const float* norm_weight = nullptr;
+    float eps = 0.0f;
+};
+
+// Shared by the per-head (or absent) kappa, per-key kappa and epilogue calls.
 lrs_status scan_diag_outer_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k, const lrs_bf16* v,
                                 const float* g, int32_t decay_mode, const float* k_scale, bool kscale_key,
-                                float scale, const float* s0, float* o, float* s_final, int32_t B,
-                                int32_t T, int32_t H, int32_t Hg, int32_t K, int32_t V, void* stream) {
+                                float scale, const float* s0, void* o, float* s_final, int32_t B,
+                                int32_t T, int32_t H, int32_t Hg, int32_t K, int32_t V, void* stream,
+                                const DiagEpilogue& epi = DiagEpilogue()) {
     if (!ctx || !q || !k || !v || !g || !o || !s_final) return LRS_E_INVAL;
     if (kscale_key && (!k_scale || decay_mode != 1)) return LRS_E_INVAL;
+    if (epi.kind != LRS_EPILOGUE_NONE && epi.kind != LRS_EPILOGUE_SKIP && epi.kind != LRS_EPILOGUE_NORM_GATE)
+        return LRS_E_INVAL;
+    if (epi.out_dtype != LRS_DTYPE_F32 && epi.out_dtype != LRS_DTYPE_BF16) return LRS_E_INVAL;
+    if ((epi.kind == LRS_EPILOGUE_SKIP && !epi.d_skip) || (epi.kind == LRS_EPILOGUE_NORM_GATE && !epi.gate))
+        return LRS_E_INVAL;
+    if (!(epi.eps >= 0.0f)) return LRS_E_INVAL;
+    // the norm needs a whole value row in one workgroup: at most 128 columns
+    if (epi.kind == LRS_EPILOGUE_NORM_GATE && V > 128) return LRS_E_UNSUPPORTED;
+    const bool use_epi = epi.kind != LRS_EPILOGUE_NONE || epi.out_dtype != LRS_DTYPE_F32;
+    if (use_epi && kscale_key) return LRS_E_UNSUPPORTED;
+    const size_t osz = epi.out_dtype == LRS_DTYPE_BF16 ? 2 : 4;
     if (B < 1 || T < 1 || H < 1 || Hg < 1 || K < 1 || V < 1) return LRS_E_INVAL;
     if (H % Hg != 0 || (decay_mode != 0 && decay_mode != 1)) return LRS_E_INVAL;
     if (K > 128) return LRS_E_UNSUPPORTED;
     if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(g, 4) || !aligned(k_scale, 4) ||
-        !aligned(s0, 4) || !aligned(o, 4) || !aligned(s_final, 4))
+        !aligned(s0, 4) || !aligned(o, osz) || !aligned(s_final, 4) || !aligned(epi.d_skip, 4) ||
+        !aligned(epi.gate, 2) || !aligned(epi.norm_weight, 4))
         return LRS_E_INVAL;
     int64_t bt = B;
     if (!mul_ok(bt, T)) return LRS_E_INVAL;
@@ -464,10 +487,12 @@ lrs_status scan_diag_outer_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf
     const size_t bqk = static_cast<size_t>(nqk) * 2, bv = static_cast<size_t>(nv) * 2;
     const size_t bg = static_cast<size_t>(ng) * 4;
     const size_t bks = static_cast<size_t>(bt) * H * (kscale_key ? K : 1) * 4;
-    const size_t bo = static_cast<size_t>(nv) * 4, bst = static_cast<size_t>(nst) * 4;
-    const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {g, bg}, {k_scale, bks}, {s0, bst}};
+    const size_t bo = static_cast<size_t>(nv) * osz, bst = static_cast<size_t>(nst) * 4;
+    const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {g, bg}, {k_scale, bks}, {s0, bst},
+                        {epi.d_skip, static_cast<size_t>(H) * 4}, {epi.gate, bv},
+                        {epi.norm_weight, static_cast<size_t>(V) * 4}};
     const Span outs[] = {{o, bo}, {s_final, bst}};
-    if (!outputs_disjoint(outs, 2, ins, 6)) return LRS_E_INVAL;
+    if (!outputs_disjoint(outs, 2, ins, 9)) return LRS_E_INVAL;
 
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return LRS_E_DEVICE;
@@ -481,8 +506,14 @@ lrs_status scan_diag_outer_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf
     p.k_scale_key = kscale_key ? 1 : 0;
     p.scale = scale;
     p.s0 = s0;
-    p.o = o;
+    p.o = static_cast<float*>(o);
     p.s_final = s_final;
+    p.epi_kind = epi.kind;
+    p.out_bf16 = epi.out_dtype == LRS_DTYPE_BF16 ? 1 : 0;
+    p.d_skip = epi.kind == LRS_EPILOGUE_SKIP ? epi.d_skip : nullptr;
+    p.gate = epi.kind == LRS_EPILOGUE_NORM_GATE ? epi.gate : nullptr;
+    p.norm_w = epi.kind == LRS_EPILOGUE_NORM_GATE ? epi.norm_weight : nullptr;
+    p.eps = epi.eps;
     p.B = B;
     p.T = T;
     p.H = H;
@@ -493,7 +524,7 @@ lrs_status scan_diag_outer_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf
     const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
              aligned(g, 16) && aligned(o, 16) && (!kscale_key || aligned(k_scale, 16)) &&
-             row_bytes < (int64_t{1} << 31)) ? 1 : 0;
+             (!epi.gate || aligned(epi.gate, 16)) && row_bytes < (int64_t{1} << 31)) ? 1 : 0;
     const lrs::DiagPlan plan = lrs::diag_outer_plan(B, T, H, V, K, decay_mode, kscale_key, p.vec != 0,
                                                     ctx->num_cus, ctx->diag_segments);
     const int64_t grid = static_cast<int64_t>(B) * H * plan.vtiles * plan.nseg;
@@ -517,6 +548,24 @@ LRS_API lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const
                                        int32_t Hg, int32_t K, int32_t V, void* stream) {
     return scan_diag_outer_impl(ctx, q, k, v, g, decay_mode, k_scale, false, scale, s0, o, s_final, B, T, H,
                                 Hg, K, V, stream);
+}
+
+LRS_API lrs_status lrs_scan_diag_outer_epilogue(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
+                                                const lrs_bf16* v, const float* g, int32_t decay_mode,
+                                                const float* k_scale, float scale, const float* s0,
+                                                int32_t epilogue, const float* d_skip, const lrs_bf16* gate,
+                                                const float* norm_weight, float eps, int32_t out_dtype, void* o,
+                                                float* s_final, int32_t B, int32_t T, int32_t H, int32_t Hg,
+                                                int32_t K, int32_t V, void* stream) {
+    DiagEpilogue epi;
+    epi.kind = epilogue;
+    epi.out_dtype = out_dtype;
+    epi.d_skip = d_skip;
+    epi.gate = gate;
+    epi.norm_weight = norm_weight;
+    epi.eps = eps;
+    return scan_diag_outer_impl(ctx, q, k, v, g, decay_mode, k_scale, false, scale, s0, o, s_final, B, T, H, Hg,
+                                K, V, stream, epi);
 }
 
 LRS_API lrs_status lrs_scan_diag_outer_keyscale(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,

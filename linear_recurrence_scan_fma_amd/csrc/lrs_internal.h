@@ -81,10 +81,17 @@ struct DiagParams {
     int k_scale_key;       // kappa per key (decay mode 1 only)
     float scale;
     const float* s0;       // nullable
-    float* o;
+    float* o;              // fp32, or bf16 when out_bf16
     float* s_final;
     int B, T, H, Hg, K, V;
     int vec;               // 16-byte vector loads and stores allowed
+    // output epilogue: 0 none, 1 o + D_h v, 2 RMSNorm(o) * norm_w * silu(gate) (needs V <= 128)
+    int epi_kind;
+    int out_bf16;
+    const float* d_skip;       // [H]
+    const uint16_t* gate;      // bf16 [B,T,H,V]
+    const float* norm_w;       // [V], nullable
+    float eps;
 };
 
 // Time-axis split of the diag-outer scan: chunks of 64 steps grouped into

@@ -73,6 +73,13 @@ struct DiagArgs {
     float scale;
     int vtiles;
     int nchunks, nseg, cps;   // chunks, segments, chunks per segment
+    // output epilogue (EPI variants): kind 0 none, 1 o + D_h v, 2 RMSNorm(o) w silu(z)
+    int epi_kind;
+    int out_bf16;             // o is bf16 (else fp32)
+    const float* d_skip;      // [H]
+    const u16* gate;          // z, bf16 [B,T,H,V]
+    const float* norm_w;      // [V], nullable (ones)
+    float eps;
 };
 
 __device__ __forceinline__ void store4(u16* dst, const u16 (&x)[4]) {
@@ -117,9 +124,11 @@ __device__ __forceinline__ bool score_job8(int wave, int n, int& kb, int& qb) {
 // AGG = true: segment reduction (a_seg, U_seg) from a zero state, no outputs.
 // AGG = false: outputs and the final state, starting from the folded segment state.
 // KK = true (per-key decay only): kappa per key, k_scale [B,T,H,K].
-template <int MODE, int KP, int WPB, bool VEC, bool AGG, bool KK = false>
+// EPI = true (output pass only): the output epilogue and dtype of DiagArgs.
+template <int MODE, int KP, int WPB, bool VEC, bool AGG, bool KK = false, bool EPI = false>
 __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     static_assert(!KK || MODE == 1, "a per-key kappa needs the per-key decay path");
+    static_assert(!(EPI && AGG), "the epilogue belongs to the output pass");
     constexpr bool OUT = !AGG;
     constexpr int NT = 64 * WPB;   // threads per workgroup
     constexpr int VT = 16 * WPB;   // V-tile width
@@ -151,6 +160,8 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     __shared__ float sGL[MODE == 1 ? KP : 1];    // G_L per key
     __shared__ __align__(16) float sEGL[MODE == 1 ? KP : 1];   // e^{G_L} per key
     __shared__ __align__(16) float sKK[KK && OUT ? L * KP : 1];   // per-key kappa (exact-pairs path)
+    __shared__ float sRS[EPI ? WPB * L : 1];   // epilogue: per-wave sums of squares of each step's row
+    __shared__ __align__(16) float sNW[EPI ? 16 * WPB : 1];   // epilogue: RMSNorm weight of the tile's columns
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -213,6 +224,17 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
         offv[i] = v0 + c8 < V ? ((row * H + h) * V + v0 + c8) * 2 : kBufOOB;
     }
     const int offo = jcol - c16 + 4 * g4 < V ? ((c16 * H + h) * V + v0 + 16 * wave + 4 * g4) * 4 : kBufOOB;
+    // epilogue: bf16 views of the gate and of the output (same [B,T,H,V] layout)
+    const int off2 = offo == kBufOOB ? kBufOOB : offo / 2;
+    const int64_t z_row = static_cast<int64_t>(H) * V * 2;
+    const u16* zb = EPI && p.gate ? p.gate + b * T * H * static_cast<int64_t>(V) : nullptr;
+    u16* ob16 = reinterpret_cast<u16*>(p.o) + b * T * H * static_cast<int64_t>(V);
+    float dsk = 0.0f;
+    if constexpr (EPI) {
+        // RMSNorm weight of the tile's columns (read after the first chunk's barriers)
+        if (tid < VT) sNW[tid] = (p.norm_w && v0 + tid < V) ? p.norm_w[v0 + tid] : 1.0f;
+        if (p.d_skip) dsk = p.d_skip[h];
+    }
 
     // ---- prefetch registers: raw inputs of one chunk ----
     // mode 0: q/k as 16-byte row pieces; mode 1: 4 keys x RPG rows per thread
@@ -598,6 +620,34 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                     }
                 }
             }
+            // epilogue gate of this lane's four columns at its four steps (issued before the
+            // readout's products, which hide its latency)
+            u32x2 zq[EPI ? 4 : 1];
+            if constexpr (EPI) {
+                if (p.epi_kind == 2) {
+                    if constexpr (VEC) {
+                        const BufRes wz = make_rsrc_window(zb, T * z_row, t0 * z_row);
+#pragma unroll
+                        for (int tb = 0; tb < 4; ++tb)
+                            zq[tb] = __builtin_amdgcn_raw_buffer_load_b64(
+                                wz, off2 == kBufOOB ? kBufOOB : off2 + tb * 16 * static_cast<int>(z_row), 0, 0);
+                    } else {
+#pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) {
+                            const int64_t t = t0 + 16 * tb + c16;
+                            const int col = v0 + 16 * wave + 4 * g4;
+                            u16 z4[4] = {0, 0, 0, 0};
+                            if (t < T) {
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (col + r < V) z4[r] = zb[(t * H + h) * static_cast<int64_t>(V) + col + r];
+                            }
+                            zq[tb] = u32x2{z4[0] | (static_cast<uint32_t>(z4[1]) << 16),
+                                           z4[2] | (static_cast<uint32_t>(z4[3]) << 16)};
+                        }
+                    }
+                }
+            }
             bf16x8 sh[KM], sl[KM];
 #pragma unroll
             for (int m = 0; m < KM; ++m) {
@@ -633,7 +683,76 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                 }
             }
             // acc[tb]: rows = columns v0 + 16 wave + 4 g4 + r, column = step t0 + 16 tb + c16
-            if constexpr (VEC) {
+            if constexpr (EPI) {
+                if (p.epi_kind == 1) {
+                    // skip connection: o + D_h v, v from the chunk's value tile
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        const u32x2 v4 = *reinterpret_cast<const u32x2*>(sV + (16 * tb + c16) * LDV + 16 * wave + 4 * g4);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[tb][r] = __builtin_fmaf(dsk, bf2f(half_elem(v4, r)), acc[tb][r]);
+                    }
+                } else if (p.epi_kind == 2) {
+                    // RMSNorm over the value axis (the whole row is in this workgroup), then the gate
+                    float ss[4];
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        float x = 0.0f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) x = __builtin_fmaf(acc[tb][r], acc[tb][r], x);
+                        x += __shfl_xor(x, 16);
+                        x += __shfl_xor(x, 32);
+                        ss[tb] = x;
+                    }
+                    if (g4 == 0) {
+#pragma unroll
+                        for (int tb = 0; tb < 4; ++tb) sRS[wave * L + 16 * tb + c16] = ss[tb];
+                    }
+                    __syncthreads();
+                    const float inv_v = 1.0f / static_cast<float>(V);
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        float tot = 0.0f;
+#pragma unroll
+                        for (int w = 0; w < WPB; ++w) tot += sRS[w * L + 16 * tb + c16];
+                        const float inv = 1.0f / sqrtf(__builtin_fmaf(tot, inv_v, p.eps));
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float z = bf2f(half_elem(zq[tb], r));
+                            const float silu = z / (1.0f + __expf(-z));
+                            acc[tb][r] = acc[tb][r] * inv * sNW[16 * wave + 4 * g4 + r] * silu;
+                        }
+                    }
+                }
+            }
+            if (EPI && p.out_bf16) {
+                // bf16 output, rounded to nearest even
+                u32x2 pk[4];
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    pk[tb].x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{acc[tb][0], acc[tb][1]}, bf16x2));
+                    pk[tb].y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{acc[tb][2], acc[tb][3]}, bf16x2));
+                }
+                if constexpr (VEC) {
+                    const BufRes wo = make_rsrc_window(ob16, T * z_row, t0 * z_row);
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            pk[tb], wo, off2 == kBufOOB ? kBufOOB : off2 + tb * 16 * static_cast<int>(z_row), 0, 0);
+                } else {
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) {
+                        const int64_t t = t0 + 16 * tb + c16;
+                        const int col = v0 + 16 * wave + 4 * g4;
+                        if (t < T) {
+                            u16* dst = ob16 + (t * H + h) * static_cast<int64_t>(V) + col;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (col + r < V) dst[r] = half_elem(pk[tb], r);
+                        }
+                    }
+                }
+            } else if constexpr (VEC) {
                 const BufRes wo = make_rsrc_window(ob, T * o_row, t0 * o_row);
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
@@ -730,6 +849,17 @@ hipError_t launch_t(const DiagArgs& a, bool vec, hipStream_t stream) {
         else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, true, KK>), grid, block, 0, stream, a);
     }
     const dim3 grid(static_cast<unsigned>(units * a.nseg));
+    if (a.epi_kind != 0 || a.out_bf16) {
+        if constexpr (!KK) {
+            if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, false, false, true>), grid, block, 0,
+                                        stream, a);
+            else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, false, false, true>), grid, block, 0,
+                                    stream, a);
+            return hipGetLastError();
+        } else {
+            return hipErrorInvalidValue;   // the epilogue is not built for the per-key kappa variant
+        }
+    }
     if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, false, KK>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, false, KK>), grid, block, 0, stream, a);
     return hipGetLastError();
@@ -825,6 +955,12 @@ hipError_t launch_scan_diag_outer(const DiagParams& prm, const DiagPlan& pl, voi
     a.nchunks = pl.nchunks;
     a.nseg = pl.nseg;
     a.cps = pl.cps;
+    a.epi_kind = prm.epi_kind;
+    a.out_bf16 = prm.out_bf16;
+    a.d_skip = prm.d_skip;
+    a.gate = reinterpret_cast<const u16*>(prm.gate);
+    a.norm_w = prm.norm_w;
+    a.eps = prm.eps;
     if (pl.nseg > 1) {
         const size_t kp = prm.K <= 64 ? 64 : 128;
         a.agg_u = static_cast<float*>(workspace);

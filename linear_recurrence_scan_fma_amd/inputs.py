@@ -26,6 +26,8 @@ float64 -> float32 -> bfloat16, each step round-to-nearest-even):
 * HGRN2 shaped:        f = sigmoid(N(2,1)) per key; g = log f fp32; k = 1 - f
                        bf16 (the key is tied to the forget gate); q, v ~ N(0,1)
                        bf16; readout scale 1
+* output epilogues:    GLA norm-gate: gate z ~ N(0,1) bf16 [B,T,H,V], norm weight
+                       ~ U(0.5,1.5) fp32 [V], eps 1e-6; Mamba-2 skip: D ~ U(0.5,1.5) [H]
 * RWKV-7 shaped:       as DeltaNet, plus a per-key log-decay
                        g = -exp(-softplus(-z) - 0.5), z ~ N(0,1), fp32 [B,T,H,K]
                        (each step keeps a fraction in (0.545, 1) of every key row)
@@ -186,6 +188,19 @@ def hgrn2(B=4, T=4096, H=16, K=128, V=128, seed=SEED_BASE + 8):
     v = rng.standard_normal((B, T, H, V))
     return dict(q=_bf16(q), k=_bf16(1.0 - f), v=_bf16(v), g=_f32(np.log(f)), decay_mode=1,
                 k_scale=None, scale=1.0, s0=None)
+
+
+def norm_gate_epilogue(B, T, H, V, seed=SEED_BASE + 9):
+    """Inputs of GLA's output norm-gate: gate z [B,T,H,V] bf16, RMSNorm weight [V]."""
+    rng = np.random.default_rng(seed)
+    return dict(gate=_bf16(rng.standard_normal((B, T, H, V))),
+                norm_weight=_f32(rng.uniform(0.5, 1.5, size=(V,))), eps=1e-6)
+
+
+def skip_epilogue(H, seed=SEED_BASE + 10):
+    """Mamba-2's per-head skip weight D [H]."""
+    rng = np.random.default_rng(seed)
+    return dict(d_skip=_f32(rng.uniform(0.5, 1.5, size=(H,))))
 
 
 def random_state(shape, seed, std=1.0):

@@ -608,13 +608,13 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     if (static_cast<int64_t>(B) * H * nchunks > 0x7fffffff || static_cast<int64_t>(B) * H * vtiles > 0x7fffffff)
         return LRS_E_UNSUPPORTED;
     // the scan kernel addresses one (batch, head) slice of the workspace with 32-bit offsets
-    if (lrs::delta_workspace_bytes(1, T, 1, decay) >= (size_t{1} << 31)) return LRS_E_UNSUPPORTED;
+    if (lrs::delta_workspace_bytes(1, T, 1, K, decay) >= (size_t{1} << 31)) return LRS_E_UNSUPPORTED;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return LRS_E_DEVICE;
     const lrs_status ws =
-        grow_workspace(ctx->delta_ws, ctx->delta_ws_bytes, lrs::delta_workspace_bytes(B, T, H, decay), st);
+        grow_workspace(ctx->delta_ws, ctx->delta_ws_bytes, lrs::delta_workspace_bytes(B, T, H, K, decay), st);
     if (ws != LRS_OK) return ws;
     lrs::DeltaParams p{};
     p.q = q;

@@ -134,7 +134,7 @@ int delta_vtile();
 int delta_decay_max_k();
 // Device workspace the delta scan needs (per-chunk UT-transform planes, plus
 // the running log-decay with a decay).
-size_t delta_workspace_bytes(int B, int T, int H, bool decay);
+size_t delta_workspace_bytes(int B, int T, int H, int K, bool decay);
 hipError_t launch_scan_delta(const DeltaParams& p, void* workspace, hipStream_t stream);
 
 // Fills `n` 64-bit words with zero (used to reset look-back status words).

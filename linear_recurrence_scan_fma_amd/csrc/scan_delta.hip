@@ -11,43 +11,38 @@
 // S0, the deltas Delta (L x V) satisfy (I + A) Delta = diag(beta)(V - K S0)
 // with A = strict_lower(diag(beta) K K^T), because step t subtracts the
 // read-back of the earlier deltas of the same chunk.  With
-// Tb = (I + A)^{-1} diag(beta) and MTb = tril(Q K^T) Tb:
-//   R = V - K S0,   Delta = Tb R,   O = scale (Q S0 + MTb R),   S_L = S0 + K^T Delta.
-// This is the sequential recurrence regrouped exactly (the pages call the
-// rank-1 form token-serial; the regrouping changes only the order of
-// additions).
-//
-// Two kernels:
-//  * delta_prep, one workgroup per (batch, head, chunk), all in parallel:
-//    A and tril(Q K^T) on the matrix cores (bf16 inputs enter exactly); the
-//    16x16 diagonal blocks of (I + A)^{-1} by forward substitution; the
-//    off-diagonal blocks column block by column block, each in one wave with
-//    no barrier, on 16x16x16 matrix-core products whose 16x16 result is laid
-//    out exactly as the next product's right operand.  Tb and MTb go to the
-//    context workspace as hi/lo bf16 planes (hi + lo ~ fp32).
-//  * delta_scan, one workgroup per (batch, head, 16-wide V-tile), walks the
-//    chunks in order with its K x 16 state in registers.  q, k, Tb and MTb of
-//    the next chunk are prefetched straight into matrix-core operand
-//    registers (no LDS round trip).  K also goes to LDS row-major once; the
-//    state update reads K^T operands from it with the transposing LDS read
-//    (ds_read_b64_tr_b16).  Per chunk: Y = K S0 and Q S0, R = V - Y,
-//    Delta = Tb R and MTb R, S += K^T Delta.  fp32 operands are split into
-//    hi + lo bf16 terms.
+// Tb = (I + A)^{-1} diag(beta), MTb = tril(Q K^T) Tb and W = K^T Tb:
+//   R = V - K S0,   O = scale (Q S0 + MTb R),   S_L = S0 + W R
+// (Delta = Tb R itself is never formed).  This is the sequential recurrence
+// regrouped exactly (the pages call the rank-1 form token-serial; the
+// regrouping changes only the order of additions).
 //
 // With a per-key decay (RWKV-7's update [SunnyNet log §5.1], read key-major):
 //   delta_t = beta_t (v_t - S_{t-1}^T k_t),  S_t = diag(w_t) S_{t-1} + k_t delta_t^T,
 // w_t = exp(g_t).  With G_t the running sum of g inside the chunk (G_{-1} = 0),
-// unrolling the chunk gives the same UT form on decayed operands:
-//   a_t = e^{G_{t-1}} k_t,  b_t = e^{-G_t} k_t,  qt_t = e^{G_t} q_t   (per key)
-//   A = strict_lower(diag(beta) a b^T),  MTb = tril(qt b^T) Tb,
-//   R = V - a S0,  Delta = Tb R,  O = scale (qt S0 + MTb R),
-//   S_L = diag(e^{G_L}) S0 + khat^T Delta,  khat_t = e^{G_L - G_t} k_t.
-// The prep kernel forms a b^T and qt b^T on the matrix cores from hi/lo
-// operands scaled about the chunk's middle step (every factor within e^{+-30}
-// while no key's running sum strays more than 30 nats from its middle value;
-// past that it takes the pairs one by one with exact exponentials), and
-// stores G for the scan kernel, which rebuilds a, qt and khat in registers
-// from the raw q and k and exp(G).  Decayed form: K <= 64.
+// unrolling the chunk gives the same form on decayed operands (per key):
+//   a_t = e^{G_{t-1}} k_t,  b_t = e^{-G_t} k_t,  qt_t = e^{G_t} q_t,  khat_t = e^{G_L - G_t} k_t,
+//   A = strict_lower(diag(beta) a b^T),  MTb = tril(qt b^T) Tb,  W = khat^T Tb,
+//   R = V - a S0,  O = scale (qt S0 + MTb R),  S_L = diag(e^{G_L}) S0 + W R.
+//
+// Two kernels:
+//  * delta_prep, one workgroup per (batch, head, chunk), all in parallel:
+//    A and tril(Q K^T) on the matrix cores; the 16x16 diagonal blocks of
+//    (I + A)^{-1} by forward substitution, the off-diagonal blocks column
+//    block by column block, each in one wave with no barrier, on 16x16x16
+//    matrix-core products whose 16x16 result is laid out exactly as the next
+//    product's right operand; then MTb and W, stored as hi/lo bf16 planes
+//    (hi + lo ~ fp32).  The decayed form takes the running log-decay per key,
+//    forms a b^T and qt b^T from hi/lo operands scaled about the chunk's
+//    middle step (every factor within e^{+-30} while no key's running sum
+//    strays more than 30 nats from its middle value; past that it takes the
+//    pairs one by one with exact exponentials), and also stores a and qt as
+//    hi/lo planes and e^{G_L}, so the scan does no transcendental work.
+//  * delta_scan, one workgroup per (batch, head, 16-wide V-tile), walks the
+//    chunks in order with its K x 16 state in registers.  Per chunk, two
+//    phases and two barriers: Y = K S0 (a S0) and Q S0 (qt S0), R = V - Y;
+//    then MTb R for the outputs and S = S0 + W R (diag(e^{G_L}) S0 + W R).
+//    fp32 operands are split into hi + lo bf16 terms.  Decayed form: K <= 64.
 #include "lrs_internal.h"
 #include "mfma_util.h"
 
@@ -57,16 +52,25 @@ namespace {
 constexpr int L = 64;
 constexpr int NT = 256;
 constexpr int PLANE = L * L;   // elements of one 64 x 64 bf16 plane
-constexpr int NPLANES = 4;     // per chunk: Tb hi, Tb lo, MTb hi, MTb lo
 constexpr int VT = 16;         // V-tile width of the scan kernel
 constexpr int KD = 64;         // key width of the decayed form
 constexpr float kHalfSpan = 30.0f;   // decayed prep: factor exponents stay within +-30 nats
 
-// u16 elements of one chunk's workspace block: the four planes, then (decayed
-// form) the chunk's running log-decay G as fp32 [L][KD].
-template <bool DECAY>
+// One chunk's workspace block, in u16 elements:
+//   MTb hi, MTb lo          2 x [L][L]
+//   W hi, W lo              2 x [KP][L]   (key-major: row = key, 64 steps)
+//   decayed form only:
+//   a hi, a lo, qt hi, qt lo   4 x [L][KP]
+//   e^{G_L}                    [KP] fp32
+template <int KP>
+constexpr int off_w() { return 2 * PLANE; }
+template <int KP>
+constexpr int off_aq() { return 2 * PLANE + 2 * KP * L; }
+template <int KP>
+constexpr int off_el() { return off_aq<KP>() + 4 * L * KP; }
+template <int KP, bool DECAY>
 constexpr int chunk_u16() {
-    return NPLANES * PLANE + (DECAY ? 2 * L * KD : 0);
+    return DECAY ? off_el<KP>() + 2 * KP : off_aq<KP>();
 }
 
 
@@ -79,7 +83,7 @@ struct DeltaArgs {
     const float* s0;
     float* o;
     float* s_final;
-    u16* ws;          // per (b,h,chunk): NPLANES planes of 64 x 64 bf16 (+ G, decayed form)
+    u16* ws;          // per (b,h,chunk): one chunk_u16() block
     int B, T, H, K, V;
     float scale;
     int vtiles;
@@ -138,6 +142,15 @@ __device__ __forceinline__ f32x4 mm16(f32x4 xa, f32x4 yb, f32x4 acc) {
     s16x4 ah, al, bh, bl;
     split4(xa, ah, al);
     split4(yb, bh, bl);
+    acc = mfma16k16(al, bh, acc);
+    acc = mfma16k16(ah, bl, acc);
+    return mfma16k16(ah, bh, acc);
+}
+
+// As mm16 with the right operand already split into hi/lo.
+__device__ __forceinline__ f32x4 mm16_rb(f32x4 xa, s16x4 bh, s16x4 bl, f32x4 acc) {
+    s16x4 ah, al;
+    split4(xa, ah, al);
     acc = mfma16k16(al, bh, acc);
     acc = mfma16k16(ah, bl, acc);
     return mfma16k16(ah, bh, acc);
@@ -242,6 +255,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
 
     // A = K K^T and M = Q K^T lower-triangle blocks (20 jobs over 4 waves), kept in registers
     f32x4 acc[5];
+    bf16x8 khh[DECAY ? NPI : 1], khl[DECAY ? NPI : 1];   // decayed form: khat pieces, hi/lo
     if constexpr (DECAY) {
         // running sum over the chunk per key: wave w sums rows 16w .. 16w+15 of key `lane`
         float gl[16];
@@ -253,13 +267,10 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
         __syncthreads();
         float off = 0.0f;
         for (int w2 = 0; w2 < wave; ++w2) off += sTot[w2][lane];
-        float* gws = reinterpret_cast<float*>(p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<true>() +
-                                              NPLANES * PLANE);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             gl[r] += off;
             sG[(16 * wave + r) * LDA + lane] = gl[r];
-            gws[(16 * wave + r) * KP + lane] = gl[r];
         }
         if (wave == 1) sRef[lane] = gl[15];   // the middle step's running sum
         __syncthreads();
@@ -274,6 +285,38 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
         u16* tBl = tile + 3 * L * LDK;
         u16* tQh = tile + 4 * L * LDK;
         u16* tQl = tile + 5 * L * LDK;
+        {
+            // the scan's operands, relative to the chunk start: a = e^{G_{t-1}} k and
+            // qt = e^{G_t} q as hi/lo planes, e^{G_L}, and khat = e^{G_L - G_t} k (kept
+            // in registers for W); every exponent is <= 0 while g <= 0
+            u16* blk = p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<KP, true>();
+            u16* aq = blk + off_aq<KP>();
+#pragma unroll
+            for (int j = 0; j < NPI; ++j) {
+                const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
+                const u32x4 kw = *reinterpret_cast<const u32x4*>(tAh + t * LDK + i0);
+                const u32x4 qw = *reinterpret_cast<const u32x4*>(tQh + t * LDK + i0);
+                float av[8], qv[8], kv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float gt = sG[t * LDA + i0 + e], gp = t > 0 ? sG[(t - 1) * LDA + i0 + e] : 0.0f;
+                    const float gL = sG[(L - 1) * LDA + i0 + e];
+                    const float kx = bf2f(piece_elem(kw, e));
+                    av[e] = kx * __expf(gp);
+                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(gt);
+                    kv[e] = kx * __expf(gL - gt);
+                }
+                bf16x8 hi, lo;
+                split8(av, hi, lo);
+                *reinterpret_cast<bf16x8*>(aq + t * KP + i0) = hi;
+                *reinterpret_cast<bf16x8*>(aq + L * KP + t * KP + i0) = lo;
+                split8(qv, hi, lo);
+                *reinterpret_cast<bf16x8*>(aq + 2 * L * KP + t * KP + i0) = hi;
+                *reinterpret_cast<bf16x8*>(aq + 3 * L * KP + t * KP + i0) = lo;
+                split8(kv, khh[j], khl[j]);
+            }
+            if (tid < KP) reinterpret_cast<float*>(blk + off_el<KP>())[tid] = __expf(sG[(L - 1) * LDA + tid]);
+        }
         if (fast) {
             // a = e^{G_{t-1} - ref} k, b = e^{ref - G_t} k, qt = e^{G_t - ref} q, as hi/lo;
             // eight keys of one step per piece, transformed in place
@@ -416,7 +459,24 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     }
     __syncthreads();
 
-    u16* planes = p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<DECAY>();
+    // Tb = T diag(beta), transposed ([step'][step], zero above the diagonal of T)
+    // and split hi/lo into A's space: the right operand of the MTb and W
+    // products, read four steps at a time
+    constexpr int LDT = L + 4;   // u16 row stride: 8-byte aligned rows
+    static_assert(2 * L * LDT * 2 <= L * LDA * 4, "Tb^T tiles fit in A's space");
+    u16* tTh = reinterpret_cast<u16*>(sA);
+    u16* tTl = tTh + L * LDT;
+    for (int e = tid; e < L * L; e += NT) {
+        const int tau = e / L, tp = e % L;
+        const float x = tau >= tp ? sT[tau * LDA + tp] * sBeta[tp] : 0.0f;
+        u16 hi, lo;
+        split_bf16(x, hi, lo);
+        tTh[tp * LDT + tau] = hi;
+        tTl[tp * LDT + tau] = lo;
+    }
+    __syncthreads();
+
+    u16* blk = p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<KP, DECAY>();
     // MTb lower blocks (i, j): (sum_{m=j}^{i} M_im T_mj) diag(beta); five block
     // products per wave
     {
@@ -427,51 +487,75 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             f32x4 X = zero4();
             for (int m = bj; m <= bi; ++m) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(sM + (16 * bi + c16) * LDA + 16 * m + 4 * g);
-                f32x4 bcol;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) bcol[r] = sT[(16 * m + 4 * g + r) * LDA + 16 * bj + c16];
-                X = mm16(a, bcol, X);
+                const int to = (16 * bj + c16) * LDT + 16 * m + 4 * g;
+                X = mm16_rb(a, *reinterpret_cast<const s16x4*>(tTh + to), *reinterpret_cast<const s16x4*>(tTl + to), X);
             }
-            const float beta_col = sBeta[16 * bj + c16];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 u16 hi, lo;
-                split_bf16(X[r] * beta_col, hi, lo);
+                split_bf16(X[r], hi, lo);
                 const int idx = (16 * bi + 4 * g + r) * L + 16 * bj + c16;
-                planes[2 * PLANE + idx] = hi;
-                planes[3 * PLANE + idx] = lo;
+                blk[idx] = hi;
+                blk[PLANE + idx] = lo;
             }
         }
-    }
-    // Tb = T diag(beta) (zero above the diagonal) and zeros for the upper blocks of MTb
-    {
+        // zeros for the blocks right of the diagonal
         const int row = tid / 4, c0 = (tid % 4) * 16;
-        u16 hi[16], lo[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int col = c0 + e;
-            split_bf16(col <= row ? sT[row * LDA + col] * sBeta[col] : 0.0f, hi[e], lo[e]);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            u32x4 wh, wl;
-            wh.x = hi[8 * half + 0] | (static_cast<uint32_t>(hi[8 * half + 1]) << 16);
-            wh.y = hi[8 * half + 2] | (static_cast<uint32_t>(hi[8 * half + 3]) << 16);
-            wh.z = hi[8 * half + 4] | (static_cast<uint32_t>(hi[8 * half + 5]) << 16);
-            wh.w = hi[8 * half + 6] | (static_cast<uint32_t>(hi[8 * half + 7]) << 16);
-            wl.x = lo[8 * half + 0] | (static_cast<uint32_t>(lo[8 * half + 1]) << 16);
-            wl.y = lo[8 * half + 2] | (static_cast<uint32_t>(lo[8 * half + 3]) << 16);
-            wl.z = lo[8 * half + 4] | (static_cast<uint32_t>(lo[8 * half + 5]) << 16);
-            wl.w = lo[8 * half + 6] | (static_cast<uint32_t>(lo[8 * half + 7]) << 16);
-            *reinterpret_cast<u32x4*>(planes + row * L + c0 + 8 * half) = wh;
-            *reinterpret_cast<u32x4*>(planes + PLANE + row * L + c0 + 8 * half) = wl;
-        }
-        if (c0 >= 16 * (row / 16 + 1)) {   // a 16-column group right of the diagonal block
+        if (c0 >= 16 * (row / 16 + 1)) {
             const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(planes + 2 * PLANE + row * L + c0) = z;
-            *reinterpret_cast<u32x4*>(planes + 2 * PLANE + row * L + c0 + 8) = z;
-            *reinterpret_cast<u32x4*>(planes + 3 * PLANE + row * L + c0) = z;
-            *reinterpret_cast<u32x4*>(planes + 3 * PLANE + row * L + c0 + 8) = z;
+            *reinterpret_cast<u32x4*>(blk + row * L + c0) = z;
+            *reinterpret_cast<u32x4*>(blk + row * L + c0 + 8) = z;
+            *reinterpret_cast<u32x4*>(blk + PLANE + row * L + c0) = z;
+            *reinterpret_cast<u32x4*>(blk + PLANE + row * L + c0 + 8) = z;
+        }
+    }
+    __syncthreads();   // M is read: its space takes khat
+    // W = khat^T Tb (key-major, [KP][L]); khat = k (plain form, exact in
+    // bf16) or e^{G_L - G_t} k (decayed form, hi/lo), staged [step][key] in M's space
+    {
+        u16* sKh = reinterpret_cast<u16*>(sM);
+        u16* sKl = sKh + L * KP;
+#pragma unroll
+        for (int j = 0; j < NPI; ++j) {
+            const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
+            if constexpr (DECAY) {
+                *reinterpret_cast<bf16x8*>(sKh + t * KP + i0) = khh[j];
+                *reinterpret_cast<bf16x8*>(sKl + t * KP + i0) = khl[j];
+            } else {
+                *reinterpret_cast<u32x4*>(sKh + t * KP + i0) = xk[j];
+            }
+        }
+        __syncthreads();
+        u16* wh = blk + off_w<KP>();
+        u16* wl = wh + KP * L;
+        for (int n = wave; n < KP / 16 * 4; n += 4) {
+            const int ib = n / 4, jb = n % 4;   // key block, step block
+            f32x4 acc2 = zero4();
+            for (int m = jb; m < 4; ++m) {
+                // left: khat^T (row = key 16 ib + c16, k = step 16 m + 4 g + e);
+                // right: Tb (column = step 16 jb + c16, same k), lower blocks only
+                // the transposing LDS read: lane i of a 16-lane group supplies step
+                // 16 m + 4 g + i / 4, keys 16 ib + 4 (i % 4) .. +3; lane j receives
+                // khat[16 m + 4 g .. +3][16 ib + j]
+                const int xoff = (16 * m + 4 * g + (c16 >> 2)) * KP + 16 * ib + 4 * (c16 & 3);
+                const s16x4 xh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sKh + xoff));
+                s16x4 xl;
+                if constexpr (DECAY) xl = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(sKl + xoff));
+                const int to = (16 * jb + c16) * LDT + 16 * m + 4 * g;
+                const s16x4 yh = *reinterpret_cast<const s16x4*>(tTh + to);
+                const s16x4 yl = *reinterpret_cast<const s16x4*>(tTl + to);
+                if constexpr (DECAY) acc2 = mfma16k16(xl, yh, acc2);
+                acc2 = mfma16k16(xh, yl, acc2);
+                acc2 = mfma16k16(xh, yh, acc2);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u16 hi, lo;
+                split_bf16(acc2[r], hi, lo);
+                const int idx = (16 * ib + 4 * g + r) * L + 16 * jb + c16;
+                wh[idx] = hi;
+                wl[idx] = lo;
+            }
         }
     }
 }
@@ -487,29 +571,32 @@ __device__ __forceinline__ int swz(int r, int p) {
     return r * (PPR * 16) + ((p ^ (r & (PPR - 1))) << 4);
 }
 
-// Wave w owns chunk rows 16w .. 16w+15 (Y, R, Delta, outputs) and state keys
-// 16 STW w .. (row tiles of S).  The chunk's q, k, Tb / MTb planes and V tile
-// are fetched one chunk ahead straight into LDS (buffer loads with an LDS
-// destination: whole 1 KB runs per instruction, no registers held), double
-// buffered by chunk parity, into swizzled tiles read as matrix-core operands.
-// Per chunk, three barriers:
+// Wave w owns chunk rows 16w .. 16w+15 (Y, R, outputs) and state keys
+// 16 STW w .. (row tiles of S).  The chunk's operand tiles (q and k; decayed
+// form: a and qt as hi/lo), the MTb planes and the V tile are fetched one
+// chunk ahead straight into LDS (buffer loads with an LDS destination: whole
+// 1 KB runs per instruction, no registers held), double buffered by chunk
+// parity, into swizzled tiles read as matrix-core operands.  W (and e^{G_L})
+// of the next chunk are prefetched into registers: each wave reads only the
+// rows of its own state keys.  Per chunk, two barriers:
 //   -- inputs of chunk c visible --
 //   1. Y = K S0, O1 = Q S0 (rows of this wave); R = V - Y -> LDS
 //   -- barrier --
-//   2. Delta = Tb R, O = scale (O1 + MTb R) -> outputs; Delta -> LDS
-//   -- barrier --
-//   3. S += K^T Delta (tiles of this wave) -> LDS as the next chunk's operand
+//   2. O = scale (O1 + MTb R) -> outputs; S = D S0 + W R (tiles of this wave)
+//      -> LDS as the next chunk's operand
 template <int KP, bool VEC, bool DECAY>
 __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     static_assert(!DECAY || KP == KD, "decayed form: K <= 64");
-    constexpr int PPR = KP / 8;          // 16-byte pieces per q / k row
-    constexpr int QB = L * KP * 2;       // bytes of a q or k tile
-    constexpr int PB = L * L * 2;        // bytes of a Tb / MTb plane
+    constexpr int PPR = KP / 8;          // 16-byte pieces per operand row
+    constexpr int QB = L * KP * 2;       // bytes of one [L][KP] bf16 operand tile
+    constexpr int PB = L * L * 2;        // bytes of an MTb plane
     constexpr int VB = L * VT * 2;       // bytes of the V tile
-    constexpr int GB = DECAY ? L * KP * 4 : 0;   // bytes of the G tile (fp32, 16 pieces per row)
-    constexpr int STAGE = 2 * QB + 4 * PB + VB + GB;
-    constexpr int OFF_K = QB, OFF_P = 2 * QB, OFF_V = 2 * QB + 4 * PB, OFF_G = 2 * QB + 4 * PB + VB;
-    constexpr int CHUNK_BYTES = chunk_u16<DECAY>() * 2;
+    constexpr int NOPS = DECAY ? 4 : 2;  // operand tiles: q, k; or a hi, a lo, qt hi, qt lo
+    constexpr int OFF_AH = DECAY ? 0 : QB, OFF_AL = QB;        // k (a hi, a lo)
+    constexpr int OFF_QH = DECAY ? 2 * QB : 0, OFF_QL = 3 * QB;   // q (qt hi, qt lo)
+    constexpr int OFF_P = NOPS * QB, OFF_V = OFF_P + 2 * PB;
+    constexpr int STAGE = OFF_V + VB;
+    constexpr int CHUNK_BYTES = chunk_u16<KP, DECAY>() * 2;
     constexpr int LDK = KP + 8;
     constexpr int LDL = L + 8;
     constexpr int KS = KP / 32;          // k-steps over the key dimension
@@ -520,8 +607,6 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     __shared__ __align__(16) unsigned char sIn[2 * STAGE];
     __shared__ __align__(16) u16 sRTh[VT * LDL];     // R^T hi/lo
     __shared__ __align__(16) u16 sRTl[VT * LDL];
-    __shared__ __align__(16) u16 sDTh[VT * LDL];     // Delta^T hi/lo
-    __shared__ __align__(16) u16 sDTl[VT * LDL];
     __shared__ __align__(16) u16 sSh[VT * LDK];      // S^T hi/lo entering the chunk
     __shared__ __align__(16) u16 sSl[VT * LDK];
 
@@ -540,9 +625,10 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     const u16* qb = p.q + b * T * H * static_cast<int64_t>(K);
     const u16* kb = p.k + b * T * H * static_cast<int64_t>(K);
     const u16* vb = p.v + b * T * H * static_cast<int64_t>(V);
-    const u16* wsb = p.ws + static_cast<int64_t>(bh) * nchunks * chunk_u16<DECAY>();
+    const u16* wsb = p.ws + static_cast<int64_t>(bh) * nchunks * chunk_u16<KP, DECAY>();
+    const int64_t ws_bytes = static_cast<int64_t>(nchunks) * CHUNK_BYTES;
 
-    // ---- fetch of one chunk's inputs into stage `buf` ----
+    // ---- fetch of one chunk's LDS operands into stage `buf` ----
     // Load run i (64 lanes x 16 bytes) fills bytes 1024 i .. of a tile: lane l
     // takes slot s = 64 i + l, i.e. row s / PPR, stored piece s % PPR, which
     // holds the row's piece (s % PPR) ^ (row & (PPR - 1)).
@@ -550,24 +636,35 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         unsigned char* st = sIn + buf * STAGE;
         const int64_t t0 = static_cast<int64_t>(c) * L;
         if constexpr (VEC) {
-            const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
-            const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
             const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
-            const BufRes wp = make_rsrc_window(wsb, static_cast<int64_t>(nchunks) * CHUNK_BYTES,
-                                               static_cast<int64_t>(c) * CHUNK_BYTES);
+            const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
+            if constexpr (DECAY) {
+                // a hi, a lo, qt hi, qt lo: four [L][KP] tiles, back to back in the workspace
 #pragma unroll
-            for (int j = 0; j < QB / 1024 / 4; ++j) {
-                const int i = wave + 4 * j, sl = 64 * i + lane;
-                const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
-                const int off = col < K ? ((row * H + h) * K + col) * 2 : kBufOOB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wq, (__attribute__((address_space(3))) void*)(st + 1024 * i),
-                                                         16, off, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    wk, (__attribute__((address_space(3))) void*)(st + OFF_K + 1024 * i), 16, off, 0, 0, 0);
+                for (int j = 0; j < 4 * QB / 1024 / 4; ++j) {
+                    const int i = wave + 4 * j, tl = i / (QB / 1024), sl = 64 * (i % (QB / 1024)) + lane;
+                    const int row = sl / PPR, pc = (sl % PPR) ^ (row & (PPR - 1));
+                    const int off = off_aq<KP>() * 2 + tl * QB + row * KP * 2 + pc * 16;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        wp, (__attribute__((address_space(3))) void*)(st + 1024 * i), 16, off, 0, 0, 0);
+                }
+            } else {
+                const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
+                const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
+#pragma unroll
+                for (int j = 0; j < QB / 1024 / 4; ++j) {
+                    const int i = wave + 4 * j, sl = 64 * i + lane;
+                    const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
+                    const int off = col < K ? ((row * H + h) * K + col) * 2 : kBufOOB;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        wq, (__attribute__((address_space(3))) void*)(st + OFF_QH + 1024 * i), 16, off, 0, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        wk, (__attribute__((address_space(3))) void*)(st + OFF_AH + 1024 * i), 16, off, 0, 0, 0);
+                }
             }
 #pragma unroll
-            for (int j = 0; j < 4 * PB / 1024 / 4; ++j) {
-                const int i = wave + 4 * j;                 // run over the four planes
+            for (int j = 0; j < 2 * PB / 1024 / 4; ++j) {
+                const int i = wave + 4 * j;                 // run over the two MTb planes
                 const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
                 const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
                 const int off = (pl * PLANE + row * L + col) * 2;
@@ -580,33 +677,32 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     wv, (__attribute__((address_space(3))) void*)(st + OFF_V + 1024 * wave), 16, off, 0, 0, 0);
             }
-            if constexpr (DECAY) {
-                // G rows of 16 pieces, piece p of row r stored at piece p ^ (r & 15)
-#pragma unroll
-                for (int j = 0; j < GB / 1024 / 4; ++j) {
-                    const int i = wave + 4 * j, sl = 64 * i + lane;
-                    const int row = sl / 16, pc = (sl % 16) ^ (row & 15);
-                    const int off = 4 * PB + row * KP * 4 + pc * 16;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        wp, (__attribute__((address_space(3))) void*)(st + OFF_G + 1024 * i), 16, off, 0, 0, 0);
-                }
-            }
         } else {
             // same slots, filled through registers (odd sizes or alignment)
-            for (int sl = tid; sl < L * PPR; sl += NT) {
-                const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
-                const int64_t t = t0 + row;
-                u32x4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
-                if (t < T) {
-                    const int64_t o = (t * H + h) * static_cast<int64_t>(K);
-                    xq = load8_bf16(qb + o, col, K, false);
-                    xk = load8_bf16(kb + o, col, K, false);
+            const u16* pw = wsb + static_cast<int64_t>(c) * chunk_u16<KP, DECAY>();
+            if constexpr (DECAY) {
+                const unsigned char* aw = reinterpret_cast<const unsigned char*>(pw + off_aq<KP>());
+                for (int s2 = tid; s2 < 4 * L * PPR; s2 += NT) {
+                    const int tl = s2 / (L * PPR), sl = s2 % (L * PPR);
+                    const int row = sl / PPR, pc = (sl % PPR) ^ (row & (PPR - 1));
+                    *reinterpret_cast<u32x4*>(st + tl * QB + 16 * sl) =
+                        *reinterpret_cast<const u32x4*>(aw + tl * QB + row * KP * 2 + pc * 16);
                 }
-                *reinterpret_cast<u32x4*>(st + 16 * sl) = xq;
-                *reinterpret_cast<u32x4*>(st + OFF_K + 16 * sl) = xk;
+            } else {
+                for (int sl = tid; sl < L * PPR; sl += NT) {
+                    const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
+                    const int64_t t = t0 + row;
+                    u32x4 xq = {0u, 0u, 0u, 0u}, xk = {0u, 0u, 0u, 0u};
+                    if (t < T) {
+                        const int64_t o = (t * H + h) * static_cast<int64_t>(K);
+                        xq = load8_bf16(qb + o, col, K, false);
+                        xk = load8_bf16(kb + o, col, K, false);
+                    }
+                    *reinterpret_cast<u32x4*>(st + OFF_QH + 16 * sl) = xq;
+                    *reinterpret_cast<u32x4*>(st + OFF_AH + 16 * sl) = xk;
+                }
             }
-            const u16* pw = wsb + static_cast<int64_t>(c) * chunk_u16<DECAY>();
-            for (int sl = tid; sl < 4 * L * 8; sl += NT) {
+            for (int sl = tid; sl < 2 * L * 8; sl += NT) {
                 const int pl = sl / (L * 8), s2 = sl % (L * 8);
                 const int row = s2 / 8, col = ((s2 % 8) ^ (row & 7)) * 8;
                 *reinterpret_cast<u32x4*>(st + OFF_P + 16 * sl) =
@@ -619,24 +715,43 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 if (t < T) xv = load8_bf16(vb + (t * H + h) * static_cast<int64_t>(V) + v0, col, V - v0, false);
                 *reinterpret_cast<u32x4*>(st + OFF_V + 16 * tid) = xv;
             }
-            if constexpr (DECAY) {
-                const unsigned char* gw = reinterpret_cast<const unsigned char*>(pw + NPLANES * PLANE);
-                for (int sl = tid; sl < L * 16; sl += NT) {
-                    const int row = sl / 16, pc = (sl % 16) ^ (row & 15);
-                    *reinterpret_cast<u32x4*>(st + OFF_G + 16 * sl) =
-                        *reinterpret_cast<const u32x4*>(gw + row * KP * 4 + pc * 16);
-                }
-            }
         }
     };
-    // G of step `row`, key `key` in the swizzled fp32 tile of a stage
-    auto g_at = [](const unsigned char* stg, int row, int key) -> float {
-        return *reinterpret_cast<const float*>(stg + OFF_G + row * (KP * 4) + (((key >> 2) ^ (row & 15)) << 4) +
-                                               (key & 3) * 4);
-    };
-    // G of step `row`, keys key0 .. key0+3 (key0 % 4 == 0)
-    auto g4_at = [](const unsigned char* stg, int row, int key0) -> f32x4 {
-        return *reinterpret_cast<const f32x4*>(stg + OFF_G + row * (KP * 4) + (((key0 >> 2) ^ (row & 15)) << 4));
+
+    // ---- W rows of this wave's state keys (and e^{G_L}), into registers ----
+    // W frag (st, ks): key 16 sr + c16, steps 32 ks + 8 g .. +7; hi then lo
+    u32x4 wcur[STW][2][2], wnxt[STW][2][2];
+    f32x4 ecur[DECAY ? STW : 1], enxt[DECAY ? STW : 1];
+    auto load_w = [&](int c, u32x4 (&w)[STW][2][2], f32x4 (&e)[DECAY ? STW : 1]) {
+        const int64_t cb = static_cast<int64_t>(c) * CHUNK_BYTES;
+        if constexpr (VEC) {
+            const BufRes wp = make_rsrc_window(wsb, ws_bytes, cb);
+#pragma unroll
+            for (int st2 = 0; st2 < STW; ++st2) {
+                const int key = 16 * (STW * wave + st2) + c16;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+                        w[st2][ks][hl] = buf_load16(wp, off_w<KP>() * 2 + hl * KP * L * 2 + (key * L + 32 * ks + 8 * g) * 2);
+                if constexpr (DECAY)
+                    e[st2] = __builtin_bit_cast(f32x4, buf_load16(wp, off_el<KP>() * 2 + (16 * (STW * wave + st2) + 4 * g) * 4));
+            }
+        } else {
+            const unsigned char* pw = reinterpret_cast<const unsigned char*>(wsb) + cb;
+#pragma unroll
+            for (int st2 = 0; st2 < STW; ++st2) {
+                const int key = 16 * (STW * wave + st2) + c16;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+                        w[st2][ks][hl] = *reinterpret_cast<const u32x4*>(
+                            pw + off_w<KP>() * 2 + hl * KP * L * 2 + (key * L + 32 * ks + 8 * g) * 2);
+                if constexpr (DECAY)
+                    e[st2] = *reinterpret_cast<const f32x4*>(pw + off_el<KP>() * 2 + (16 * (STW * wave + st2) + 4 * g) * 4);
+            }
+        }
     };
 
     // state: wave owns row tiles sr = STW * wave + st (keys 16 sr .. 16 sr + 15)
@@ -666,14 +781,18 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     };
     write_state_lds();
     fetch(0, 0);
+    load_w(0, wcur, ecur);
 
     const int arow = 16 * wave + c16;    // operand row of this wave
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
         const unsigned char* st = sIn + (c & 1) * STAGE;
-        if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads into LDS are done
+        if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads are done
         __syncthreads();                                         // ... and every wave's
-        if (c + 1 < nchunks) fetch(c + 1, (c + 1) & 1);
+        if (c + 1 < nchunks) {
+            fetch(c + 1, (c + 1) & 1);
+            load_w(c + 1, wnxt, enxt);
+        }
 
         // ---- 1: Y = K S0, O1 = Q S0 (row block = wave), R = V - Y ----
         f32x4 y = zero4(), o1 = zero4();
@@ -681,41 +800,19 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 sh = frag<LDK>(sSh, 0, 32 * ks, lane);
             const bf16x8 sl = frag<LDK>(sSl, 0, 32 * ks, lane);
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(st + OFF_K + swz<PPR>(arow, 4 * ks + g));
-            const bf16x8 qa = *reinterpret_cast<const bf16x8*>(st + swz<PPR>(arow, 4 * ks + g));
+            const int po = swz<PPR>(arow, 4 * ks + g);
+            const bf16x8 ah = *reinterpret_cast<const bf16x8*>(st + OFF_AH + po);
+            const bf16x8 qh = *reinterpret_cast<const bf16x8*>(st + OFF_QH + po);
             if constexpr (DECAY) {
-                // a = e^{G_{t-1}} k and qt = e^{G_t} q on keys 32 ks + 8 g .. +7, as hi/lo
-                const int key0 = 32 * ks + 8 * g;
-                const f32x4 gt0 = g4_at(st, arow, key0), gt1 = g4_at(st, arow, key0 + 4);
-                f32x4 gp0 = zero4(), gp1 = zero4();
-                if (arow > 0) {
-                    gp0 = g4_at(st, arow - 1, key0);
-                    gp1 = g4_at(st, arow - 1, key0 + 4);
-                }
-                const u32x4 kw = __builtin_bit_cast(u32x4, ka), qw = __builtin_bit_cast(u32x4, qa);
-                float av[8], qv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float gp = e < 4 ? gp0[e] : gp1[e - 4];
-                    const float gt = e < 4 ? gt0[e] : gt1[e - 4];
-                    av[e] = bf2f(piece_elem(kw, e)) * __expf(gp);
-                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(gt);
-                }
-                bf16x8 ah, al, qh, ql;
-                split8(av, ah, al);
-                split8(qv, qh, ql);
+                const bf16x8 al = *reinterpret_cast<const bf16x8*>(st + OFF_AL + po);
+                const bf16x8 ql = *reinterpret_cast<const bf16x8*>(st + OFF_QL + po);
                 y = mfma16(al, sh, y);
-                y = mfma16(ah, sl, y);
-                y = mfma16(ah, sh, y);
                 o1 = mfma16(ql, sh, o1);
-                o1 = mfma16(qh, sl, o1);
-                o1 = mfma16(qh, sh, o1);
-            } else {
-                y = mfma16(ka, sl, y);
-                y = mfma16(ka, sh, y);
-                o1 = mfma16(qa, sl, o1);
-                o1 = mfma16(qa, sh, o1);
             }
+            y = mfma16(ah, sl, y);
+            y = mfma16(ah, sh, y);
+            o1 = mfma16(qh, sl, o1);
+            o1 = mfma16(qh, sh, o1);
         }
         {
             // V rows 16 wave + 4g .. +3 at column c16, by the transposing read
@@ -734,24 +831,23 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
         __syncthreads();
 
-        // ---- 2: Delta = Tb R, O = scale (O1 + MTb R) ----
-        f32x4 dl = zero4(), o2 = zero4();
+        // ---- 2: O = scale (O1 + MTb R); S = D S0 + W R ----
+        bf16x8 rh[2], rl[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            if (ks <= wave / 2) {   // Tb and MTb are lower triangular
-                const bf16x8 rh = frag<LDL>(sRTh, 0, 32 * ks, lane);
-                const bf16x8 rl = frag<LDL>(sRTl, 0, 32 * ks, lane);
+            rh[ks] = frag<LDL>(sRTh, 0, 32 * ks, lane);
+            rl[ks] = frag<LDL>(sRTl, 0, 32 * ks, lane);
+        }
+        f32x4 o2 = zero4();
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks <= wave / 2) {   // MTb is lower triangular
                 const int po = swz<8>(arow, 4 * ks + g);
-                const bf16x8 th = *reinterpret_cast<const bf16x8*>(st + OFF_P + po);
-                const bf16x8 tl = *reinterpret_cast<const bf16x8*>(st + OFF_P + PB + po);
-                const bf16x8 mh = *reinterpret_cast<const bf16x8*>(st + OFF_P + 2 * PB + po);
-                const bf16x8 ml = *reinterpret_cast<const bf16x8*>(st + OFF_P + 3 * PB + po);
-                dl = mfma16(tl, rh, dl);
-                dl = mfma16(th, rl, dl);
-                dl = mfma16(th, rh, dl);
-                o2 = mfma16(ml, rh, o2);
-                o2 = mfma16(mh, rl, o2);
-                o2 = mfma16(mh, rh, o2);
+                const bf16x8 mh = *reinterpret_cast<const bf16x8*>(st + OFF_P + po);
+                const bf16x8 ml = *reinterpret_cast<const bf16x8*>(st + OFF_P + PB + po);
+                o2 = mfma16(ml, rh[ks], o2);
+                o2 = mfma16(mh, rl[ks], o2);
+                o2 = mfma16(mh, rh[ks], o2);
             }
         }
         {
@@ -761,65 +857,37 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             for (int r = 0; r < 4; ++r)
                 if (t0 + t + r < T && j < V)
                     p.o[((b * T + t0 + t + r) * H + h) * static_cast<int64_t>(V) + j] = p.scale * (o1[r] + o2[r]);
-            uint32_t hi[2], lo[2];
-            split2(dl[0], dl[1], hi[0], lo[0]);
-            split2(dl[2], dl[3], hi[1], lo[1]);
-            *reinterpret_cast<u32x2*>(sDTh + c16 * LDL + t) = u32x2{hi[0], hi[1]};
-            *reinterpret_cast<u32x2*>(sDTl + c16 * LDL + t) = u32x2{lo[0], lo[1]};
         }
-        __syncthreads();
-
-        // ---- 3: S += K^T Delta (K^T operands by transposing LDS reads) ----
-        {
-            const int i16 = lane & 15;
 #pragma unroll
-            for (int s2 = 0; s2 < STW; ++s2) {
-                const int d0 = 16 * (STW * wave + s2);
-                const int col = d0 + 4 * (i16 & 3);
-                float gL = 0.0f;   // decayed form: G at the chunk's last step, key d0 + i16
-                if constexpr (DECAY) gL = g_at(st, L - 1, d0 + i16);
-                f32x4 ds = zero4();
+        for (int s2 = 0; s2 < STW; ++s2) {
+            f32x4 ds = zero4();
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    // lane i of a 16-lane group supplies row tau0 + i/4, columns d0 + 4(i%4)..+3;
-                    // lane j then holds K[tau0 .. tau0+3][d0 + j]
-                    const int tau0 = 32 * ks + 8 * g + (i16 >> 2);
-                    const unsigned char* a0 = st + OFF_K + swz<PPR>(tau0, col >> 3) + (col & 4) * 2;
-                    const unsigned char* a1 = st + OFF_K + swz<PPR>(tau0 + 4, col >> 3) + (col & 4) * 2;
-                    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-                    const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
-                    const bf16x8 ka =
-                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                    if constexpr (DECAY) {
-                        // khat = e^{G_L - G_tau} k for tau = 32 ks + 8 g .. +7 at key d0 + i16
-                        const u32x4 kw = __builtin_bit_cast(u32x4, ka);
-                        float kv[8];
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8 wh = as_bf16x8(wcur[s2][ks][0]), wl = as_bf16x8(wcur[s2][ks][1]);
+                ds = mfma16(wl, rh[ks], ds);
+                ds = mfma16(wh, rl[ks], ds);
+                ds = mfma16(wh, rh[ks], ds);
+            }
+            if constexpr (DECAY) {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            kv[e] = bf2f(piece_elem(kw, e)) * __expf(gL - g_at(st, 32 * ks + 8 * g + e, d0 + i16));
-                        bf16x8 kh, kl;
-                        split8(kv, kh, kl);
-                        const bf16x8 dh = frag<LDL>(sDTh, 0, 32 * ks, lane), dlo = frag<LDL>(sDTl, 0, 32 * ks, lane);
-                        ds = mfma16(kl, dh, ds);
-                        ds = mfma16(kh, dlo, ds);
-                        ds = mfma16(kh, dh, ds);
-                    } else {
-                        ds = mfma16(ka, frag<LDL>(sDTl, 0, 32 * ks, lane), ds);
-                        ds = mfma16(ka, frag<LDL>(sDTh, 0, 32 * ks, lane), ds);
-                    }
-                }
-                if constexpr (DECAY) {
-                    // S <- diag(e^{G_L}) S + khat^T Delta on keys d0 + 4 g .. +3
-                    const f32x4 gl4 = g4_at(st, L - 1, d0 + 4 * g);
+                for (int r = 0; r < 4; ++r) S[s2][r] = __builtin_fmaf(S[s2][r], ecur[s2][r], ds[r]);
+            } else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[s2][r] = __builtin_fmaf(S[s2][r], __expf(gl4[r]), ds[r]);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) S[s2][r] += ds[r];
-                }
+                for (int r = 0; r < 4; ++r) S[s2][r] += ds[r];
             }
         }
         write_state_lds();
+        if (c + 1 < nchunks) {
+#pragma unroll
+            for (int s2 = 0; s2 < STW; ++s2) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    wcur[s2][ks][0] = wnxt[s2][ks][0];
+                    wcur[s2][ks][1] = wnxt[s2][ks][1];
+                }
+                if constexpr (DECAY) ecur[s2] = enxt[s2];
+            }
+        }
     }
 
 #pragma unroll
@@ -856,9 +924,9 @@ hipError_t launch_t(const DeltaArgs& a, bool vec, hipStream_t stream) {
 
 int delta_vtile() { return VT; }
 
-size_t delta_workspace_bytes(int B, int T, int H, bool decay) {
+size_t delta_workspace_bytes(int B, int T, int H, int K, bool decay) {
     const int64_t nchunks = (static_cast<int64_t>(T) + L - 1) / L;
-    const size_t per_chunk = decay ? chunk_u16<true>() : chunk_u16<false>();
+    const size_t per_chunk = decay ? chunk_u16<KD, true>() : (K <= 64 ? chunk_u16<64, false>() : chunk_u16<128, false>());
     return static_cast<size_t>(B) * H * nchunks * per_chunk * sizeof(u16);
 }
 
@@ -891,3 +959,4 @@ hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_
 }
 
 }  // namespace lrs
+

@@ -298,10 +298,12 @@ lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf1
  *   o         fp32 [B,T,H,V]     output
  *   s_final   fp32 [B,H,K,V]     output
  *
- * Limits: 1 <= K <= 128 and T <= 4194304 (LRS_E_UNSUPPORTED beyond).  The
- * context keeps a workspace of 32 KiB per (batch, head, 64-step chunk),
- * grown on demand (LRS_E_NOMEM if that allocation fails); growing it waits
- * for the stream of the call.
+ * Limits: 1 <= K <= 128; T <= 4194240 for K <= 64 and T <= 2796160 for
+ * K > 64 (LRS_E_UNSUPPORTED beyond: one (batch, head) slice of the workspace
+ * must stay under 2 GiB).  The context keeps a workspace per (batch, head,
+ * 64-step chunk) of 32 KiB (K <= 64) or 48 KiB (K > 64), holding the chunk's
+ * output and state-update factors, grown on demand (LRS_E_NOMEM if that
+ * allocation fails); growing it waits for the stream of the call.
  */
 lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                           const lrs_bf16* v, const float* beta, float scale, const float* s0,
@@ -384,9 +386,10 @@ lrs_status lrs_scan_diag_outer_keyscale(LrsContext* ctx, const lrs_bf16* q, cons
  *   o          fp32 [B,T,H,V]   output
  *   s_final    fp32 [B,H,K,V]   output
  *
- * Limits: 1 <= K <= 64 (LRS_E_UNSUPPORTED above), T <= 2796160.  The context
- * workspace holds 48 KiB per (b,h,64-step chunk), grown on demand as for
- * lrs_scan_delta.  Any finite g is accepted; chunks in which some key's
+ * Limits: 1 <= K <= 64 and T <= 2088960 (LRS_E_UNSUPPORTED beyond).  The
+ * context workspace holds 64.25 KiB per (b,h,64-step chunk): the factors of
+ * lrs_scan_delta plus the chunk's decayed keys and queries and its total
+ * decay, grown on demand as for lrs_scan_delta.  Any finite g is accepted; chunks in which some key's
  * running log-decay spans more than 60 nats take a slower exact path.
  * Errors as lrs_scan_delta.
  */

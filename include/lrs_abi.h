@@ -153,9 +153,11 @@ void lrs_context_destroy(LrsContext* ctx);
  * LRS_PARAM_DIAG_SEGMENTS sets how many segments lrs_scan_diag_outer splits
  * the time axis into (each a run of 64-step chunks processed by its own
  * workgroups; a first pass reduces every segment but the last to a decay
- * product and a state contribution, kept in the context's workspace):
- *   0 (default)  about two workgroups per resident workgroup slot of the
- *                device, but at least 5 chunks (320 steps) per segment;
+ * product and a state contribution, kept in the context's workspace, and a
+ * prefix over them gives each segment its starting state):
+ *   0 (default)  one workgroup per resident workgroup slot of the device
+ *                where a compute unit holds one of them, about two where it
+ *                holds more, but at least 4 chunks (256 steps) per segment;
  *   n >= 1       n segments (capped at the number of chunks).
  * Any value gives results within the documented tolerance.
  * Errors: LRS_E_INVAL for a NULL context, unknown parameter or value. */

@@ -54,7 +54,7 @@ constexpr int L = 64;     // chunk length
 // workgroup covers a V-tile of 16 WPB columns.  Heads wider than 64 columns use
 // 8 waves, so that the per-chunk staging and scores are shared by all columns.
 inline int waves_for(int V) { return V > 64 ? 8 : 4; }
-constexpr int kMinChunksPerSegment = 5;
+constexpr int kMinChunksPerSegment = 4;
 constexpr float kFastPathMaxDecay = 60.0f;
 
 struct DiagArgs {
@@ -66,8 +66,9 @@ struct DiagArgs {
     const float* s0;
     float* o;
     float* s_final;
-    float* agg_u;    // [nseg-1][unit][wave][KP/16][lane][4]: segment state contributions,
-                     // in the accumulator-tile order of the lanes that own them
+    float* agg_u;    // [nseg-1][unit][wave][KP/16][lane][4]: per segment, its state from zero
+                     // (from s0 for the first), then in place the state after it; in the
+                     // accumulator-tile order of the lanes that own them
     float* agg_a;    // [nseg-1][B*H][KP]: segment decay products (1 past K)
     int B, T, H, Hg, K, V;
     float scale;
@@ -357,45 +358,27 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
         }
     };
 
-    // ---- state: S0 folded through the earlier segments (output pass) or zero ----
+    // ---- state entering the segment: s0 for the first, else the prefix state
+    // that the segment pass and the prefix kernel left for the segment before ----
+    const int units = p.B * H * p.vtiles;
     f32x4 S[KB];
+    if (OUT && seg > 0) {
+        const float* ub = p.agg_u + ((static_cast<int64_t>(seg - 1) * units + rest) * WPB + wave) * (KB * 256);
 #pragma unroll
-    for (int db = 0; db < KB; ++db) {
+        for (int db = 0; db < KB; ++db) S[db] = *reinterpret_cast<const f32x4*>(ub + (db * 64 + lane) * 4);
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d = 16 * db + 4 * g4 + r;
-            float x = 0.0f;
-            if (OUT && p.s0 && d < K && jcol < V) x = p.s0[((static_cast<int64_t>(b) * H + h) * K + d) * V + jcol];
-            S[db][r] = x;
+        for (int db = 0; db < KB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * db + 4 * g4 + r;
+                float x = 0.0f;
+                if (seg == 0 && p.s0 && d < K && jcol < V) x = p.s0[((static_cast<int64_t>(b) * H + h) * K + d) * V + jcol];
+                S[db][r] = x;
+            }
         }
     }
     if constexpr (OUT) {
-        if (seg > 0) {
-            // S = (prod_s a_s) o S0 + sum_s (prod_{s' > s} a_s') o U_s over the earlier
-            // segments, newest first: every segment's loads are independent of the
-            // running result, so they overlap
-            const int units = p.B * H * p.vtiles;
-            f32x4 acc[KB], pr[KB];
-#pragma unroll
-            for (int db = 0; db < KB; ++db) {
-                acc[db] = zero4();
-                pr[db] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-            }
-#pragma unroll 2
-            for (int s2 = seg - 1; s2 >= 0; --s2) {
-                const float* ub = p.agg_u + ((static_cast<int64_t>(s2) * units + rest) * WPB + wave) * (KB * 256);
-                const float* ab = p.agg_a + (static_cast<int64_t>(s2) * p.B * H + bh) * KP;
-#pragma unroll
-                for (int db = 0; db < KB; ++db) {
-                    const f32x4 u = *reinterpret_cast<const f32x4*>(ub + (db * 64 + lane) * 4);
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(ab + 16 * db + 4 * g4);
-                    acc[db] += pr[db] * u;
-                    pr[db] *= a;
-                }
-            }
-#pragma unroll
-            for (int db = 0; db < KB; ++db) S[db] = pr[db] * S[db] + acc[db];
-        }
         // score blocks right of the diagonal that the readout reads: always zero
         if (tid < 256) {
             const int blk = tid >> 7, plane = (tid >> 6) & 1, row = (tid >> 2) & 15, quad = tid & 3;
@@ -819,7 +802,6 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
 
     // ---- epilogue ----
     if constexpr (AGG) {
-        const int units = p.B * H * p.vtiles;
         float* ub = p.agg_u + ((static_cast<int64_t>(seg) * units + rest) * WPB + wave) * (KB * 256);
 #pragma unroll
         for (int db = 0; db < KB; ++db) *reinterpret_cast<f32x4*>(ub + (db * 64 + lane) * 4) = S[db];
@@ -839,6 +821,50 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     }
 }
 
+// Prefix over the segment states, in place, between the two passes: the
+// segment pass leaves P_0 (segment 0 starts from s0) and, for s >= 1, the
+// state U_s that segment s builds from zero with its decay product a_s; this
+// makes P_s = a_s o P_{s-1} + U_s, the state after segment s, so each
+// workgroup of the output pass loads one state.  One thread per (unit, wave,
+// key tile, lane) owns 4 keys of one column; the loads of a batch of
+// segments are issued before any of them is combined.
+template <int KP, int WPB>
+__global__ __launch_bounds__(256) void diag_segment_prefix_kernel(DiagArgs p) {
+    constexpr int KB = KP / 16;
+    constexpr int PER_UNIT = WPB * KB * 64;   // f32x4 per unit and segment
+    constexpr int BATCH = 8;
+    const int units = p.B * p.H * p.vtiles;
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (gid >= static_cast<int64_t>(units) * PER_UNIT) return;
+    const int unit = static_cast<int>(gid / PER_UNIT);
+    const int rem = static_cast<int>(gid - static_cast<int64_t>(unit) * PER_UNIT);   // (wave, key tile, lane)
+    const int db = (rem >> 6) % KB;
+    const int g4 = (rem & 63) >> 4;
+    const int bh = unit / p.vtiles;
+    const int64_t ustride = static_cast<int64_t>(units) * PER_UNIT * 4;   // floats per segment
+    const int64_t astride = static_cast<int64_t>(p.B) * p.H * KP;
+    float* u = p.agg_u + (static_cast<int64_t>(unit) * PER_UNIT + rem) * 4;
+    const float* a = p.agg_a + static_cast<int64_t>(bh) * KP + 16 * db + 4 * g4;
+    f32x4 x = *reinterpret_cast<const f32x4*>(u);
+    for (int s0 = 1; s0 < p.nseg - 1; s0 += BATCH) {
+        f32x4 us[BATCH], as[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            if (s0 + j < p.nseg - 1) {
+                us[j] = *reinterpret_cast<const f32x4*>(u + (s0 + j) * ustride);
+                as[j] = *reinterpret_cast<const f32x4*>(a + (s0 + j) * astride);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            if (s0 + j < p.nseg - 1) {
+                x = as[j] * x + us[j];
+                *reinterpret_cast<f32x4*>(u + (s0 + j) * ustride) = x;
+            }
+        }
+    }
+}
+
 template <int MODE, int KP, int WPB, bool KK>
 hipError_t launch_t(const DiagArgs& a, bool vec, hipStream_t stream) {
     const int64_t units = static_cast<int64_t>(a.B) * a.H * a.vtiles;
@@ -847,6 +873,11 @@ hipError_t launch_t(const DiagArgs& a, bool vec, hipStream_t stream) {
         const dim3 grid(static_cast<unsigned>(units * (a.nseg - 1)));
         if (vec) hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, true, true, KK>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((diag_outer_kernel<MODE, KP, WPB, false, true, KK>), grid, block, 0, stream, a);
+        if (a.nseg > 2) {
+            const int64_t threads = units * WPB * (KP / 16) * 64;
+            hipLaunchKernelGGL((diag_segment_prefix_kernel<KP, WPB>), dim3(static_cast<unsigned>((threads + 255) / 256)),
+                               dim3(256), 0, stream, a);
+        }
     }
     const dim3 grid(static_cast<unsigned>(units * a.nseg));
     if (a.epi_kind != 0 || a.out_bf16) {
@@ -911,13 +942,15 @@ DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool
     const int64_t units = static_cast<int64_t>(B) * H * pl.vtiles;
     int64_t nseg = requested_segments;
     if (nseg <= 0) {
-        // enough segments for two workgroups per resident slot of the chip (a
-        // second round covers the tail of the first), but at least
-        // kMinChunksPerSegment chunks each: every extra segment costs a
-        // reduction pass over its chunks and a longer fold
-        const int64_t slots =
-            static_cast<int64_t>(num_cus) * resident_blocks(decay_mode, kscale_key, K, pl.waves, vec);
-        nseg = 2 * slots / units;
+        // Segments to fill the chip's resident workgroup slots: once where a
+        // compute unit holds one workgroup (wide per-key heads), twice where it
+        // holds two or more (the second round covers the tail of the first);
+        // at least kMinChunksPerSegment chunks each, since every extra
+        // segment adds a reduction pass over its chunks.  Measured on the
+        // Mamba-2, GLA, HGRN2 and associative-memory shapes.
+        const int res = resident_blocks(decay_mode, kscale_key, K, pl.waves, vec);
+        const int64_t slots = static_cast<int64_t>(num_cus) * res;
+        nseg = (res >= 2 ? 2 * slots : slots) / units;
         if (nseg > pl.nchunks / kMinChunksPerSegment) nseg = pl.nchunks / kMinChunksPerSegment;
     }
     if (nseg > pl.nchunks) nseg = pl.nchunks;

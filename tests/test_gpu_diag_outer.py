@@ -134,12 +134,14 @@ def test_key_decay_strong_gates_exact_fallback(ctx, gval, segments):
         _check(ctx, d, inputs.random_state((B, H, K, V), 4))
 
 
-@pytest.mark.parametrize("segments", [1, 2, 3, 7, 0])
+@pytest.mark.parametrize("segments", [1, 2, 3, 7, 11, 0])
 @pytest.mark.parametrize("mode,V", [(0, 64), (1, 64), (0, 128), (1, 128)])
 def test_time_segments(ctx, mode, V, segments):
-    # each segment starts from s0 folded through the (decay product, state
-    # contribution) pairs of the segments before it; any count must agree
-    # with the sequential oracle, including segments of unequal length
+    # each segment starts from the state after the segments before it (s0
+    # carried through their decay products and contributions by the prefix
+    # over segments); any count must agree with the sequential oracle,
+    # including segments of unequal length and more segments than one batch
+    # of the prefix
     B, T, H, K = 2, 650, 2, 128
     if mode == 0:
         d = _mamba(B, T, H, K, V, seed=61)

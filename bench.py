@@ -111,8 +111,9 @@ def main():
                          "device copy that calibrates the HBM byte counters; prints no JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the scans run on a single MI355X and this "
-              "build has no multi-GPU path (see DESIGN.md for how it would shard).", flush=True)
+        print("bench.py measures one GPU only: the scans run on a single MI355X; the library "
+              "has no multi-GPU path (batch and head slices are independent, so each GPU would "
+              "run its own share).", flush=True)
         sys.exit(2)
 
     import numpy as np

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     float* sA = reinterpret_cast<float*>(sU);
     float* sT = sA + L * LDA;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int c = blockIdx.x % p.nchunks;
     const int bh = blockIdx.x / p.nchunks;
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     __shared__ __align__(16) u16 sSh[VT * LDK];      // S^T hi/lo entering the chunk
     __shared__ __align__(16) u16 sSl[VT * LDK];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
     const int vt = lid % p.vtiles;

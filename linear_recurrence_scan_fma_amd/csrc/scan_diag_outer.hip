@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int g4 = lane >> 4;
     const int c16 = lane & 15;
     const int nsegk = AGG ? p.nseg - 1 : p.nseg;

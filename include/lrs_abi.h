@@ -275,9 +275,11 @@ lrs_status lrs_step_gated(LrsContext* ctx, const float* a, const float* u, float
  * finite value is accepted.  Limits: 1 <= K <= 128 (LRS_E_UNSUPPORTED above),
  * H % Hg == 0 (LRS_E_INVAL otherwise), decay_mode in {0,1}.  With more than
  * one time segment (LRS_PARAM_DIAG_SEGMENTS) the context keeps a workspace of
- * (segments - 1) * B * H * (ceil(V/64)*64*KP + KP) * 4 bytes, KP = 64 for
- * K <= 64 and 128 otherwise, grown on demand (LRS_E_NOMEM if that allocation
- * fails); growing it waits for the stream of the call.
+ * (segments - 1) * B * H * (ceil(V/VT)*VT*KP + KP) * 4 bytes, KP = 64 for
+ * K <= 64 and 128 otherwise, VT = 64 for V <= 64 and 128 otherwise, grown on
+ * demand (LRS_E_NOMEM if that allocation fails); growing it waits for the
+ * stream of the call.  LRS_E_UNSUPPORTED also when B * H * ceil(V/VT) is
+ * 2^27 or more (launch grid limits).
  */
 lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                                const lrs_bf16* v, const float* g, int32_t decay_mode,

@@ -528,7 +528,8 @@ lrs_status scan_diag_outer_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf
     const lrs::DiagPlan plan = lrs::diag_outer_plan(B, T, H, V, K, decay_mode, kscale_key, p.vec != 0,
                                                     ctx->num_cus, ctx->diag_segments);
     const int64_t grid = static_cast<int64_t>(B) * H * plan.vtiles * plan.nseg;
-    if (grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
+    // (the prefix over segments launches up to 16 workgroups per (batch, head, V-tile))
+    if (grid > 0x7fffffff || static_cast<int64_t>(B) * H * plan.vtiles * 16 > 0x7fffffff) return LRS_E_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const lrs_status ws = grow_workspace(ctx->diag_ws, ctx->diag_ws_bytes,
                                          lrs::diag_outer_workspace_bytes(B, H, K, V, plan.nseg), st);

@@ -499,16 +499,20 @@ def run_rows(ctx, args, binding, inputs, dev):
     specs = [
         ("scan_diag_outer Mamba-2 B=8 T=4096 H=24 P=64 N=128 (scalar decay, 1 group)", "diag",
          lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}),
-         ["diag_outer_agg_mamba2_B8_T4096_H24_P64_N128", "diag_outer_out_mamba2_B8_T4096_H24_P64_N128"]),
+         ["diag_outer_agg_mamba2_B8_T4096_H24_P64_N128", "diag_prefix_mamba2_B8_T4096_H24_P64_N128",
+          "diag_outer_out_mamba2_B8_T4096_H24_P64_N128"]),
         ("scan_diag_outer GLA B=4 T=4096 H=4 K=128 V=128 (per-key decay)", "diag",
          lambda: inputs.gla(**inputs.GLA),
-         ["diag_outer_agg_gla_B4_T4096_H4_K128_V128", "diag_outer_out_gla_B4_T4096_H4_K128_V128"]),
+         ["diag_outer_agg_gla_B4_T4096_H4_K128_V128", "diag_prefix_gla_B4_T4096_H4_K128_V128",
+          "diag_outer_out_gla_B4_T4096_H4_K128_V128"]),
         ("scan_diag_outer HGRN2 B=4 T=4096 H=16 K=128 V=128 (per-key decay, key = 1 - forget gate)", "diag",
          lambda: inputs.hgrn2(**inputs.HGRN2),
-         ["diag_outer_agg_hgrn2_B4_T4096_H16_K128_V128", "diag_outer_out_hgrn2_B4_T4096_H16_K128_V128"]),
+         ["diag_outer_agg_hgrn2_B4_T4096_H16_K128_V128", "diag_prefix_hgrn2_B4_T4096_H16_K128_V128",
+          "diag_outer_out_hgrn2_B4_T4096_H16_K128_V128"]),
         ("scan_diag_outer_keyscale associative memory B=4 T=4096 H=8 K=64 V=64 (per-key decay and kappa)",
          "keyscale", lambda: inputs.assoc_memory(**inputs.ASSOC),
-         ["diag_outer_agg_assoc_B4_T4096_H8_K64_V64", "diag_outer_out_assoc_B4_T4096_H8_K64_V64"]),
+         ["diag_outer_agg_assoc_B4_T4096_H8_K64_V64", "diag_prefix_assoc_B4_T4096_H8_K64_V64",
+          "diag_outer_out_assoc_B4_T4096_H8_K64_V64"]),
         ("scan_delta DeltaNet B=4 T=4096 H=8 K=128 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET),
          ["delta_prep_deltanet_B4_T4096_H8_K128", "delta_scan_deltanet_B4_T4096_H8_K128_V128"]),
         ("scan_delta DeltaNet B=4 T=4096 H=8 K=64 V=128", "delta", lambda: inputs.deltanet(**inputs.DELTANET_K64),
@@ -602,10 +606,12 @@ def run_rows(ctx, args, binding, inputs, dev):
     epi_specs = [
         ("scan_diag_outer_epilogue GLA B=4 T=4096 H=4 K=128 V=128 + RMSNorm(o)*silu(gate), bf16 out",
          lambda: inputs.gla(**inputs.GLA), binding.LRS_EPILOGUE_NORM_GATE,
-         ["diag_outer_agg_gla_B4_T4096_H4_K128_V128", "diag_outer_out_epi_normgate_gla_B4_T4096_H4_K128_V128"]),
+         ["diag_outer_agg_gla_B4_T4096_H4_K128_V128", "diag_prefix_gla_B4_T4096_H4_K128_V128",
+          "diag_outer_out_epi_normgate_gla_B4_T4096_H4_K128_V128"]),
         ("scan_diag_outer_epilogue Mamba-2 B=8 T=4096 H=24 P=64 N=128 + D x skip, bf16 out",
          lambda: inputs.mamba2(**{k: v for k, v in inputs.MAMBA2.items() if k != "Hg"}), binding.LRS_EPILOGUE_SKIP,
-         ["diag_outer_agg_mamba2_B8_T4096_H24_P64_N128", "diag_outer_out_epi_skip_mamba2_B8_T4096_H24_P64_N128"]),
+         ["diag_outer_agg_mamba2_B8_T4096_H24_P64_N128", "diag_prefix_mamba2_B8_T4096_H24_P64_N128",
+          "diag_outer_out_epi_skip_mamba2_B8_T4096_H24_P64_N128"]),
     ]
     for name, gen, epi, traffic_keys in epi_specs:
         log(f"[bench] row {name}")

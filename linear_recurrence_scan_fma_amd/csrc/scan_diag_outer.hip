@@ -17,8 +17,9 @@
 // which is the sequential recurrence regrouped (no approximation).  Across
 // chunks the state obeys S <- a (.) S + U with a diagonal `a`, so the time
 // axis also splits into segments: a first kernel reduces each segment to its
-// pair (a_seg, U_seg) from a zero state, and the output kernel starts each
-// segment from S0 folded through the pairs of the segments before it.
+// pair (a_seg, U_seg) from a zero state (the first segment from S0), a prefix
+// kernel turns the pairs into the state after each segment, and the output
+// kernel starts each segment from the state after the one before it.
 //
 // Work split: a workgroup owns (batch, head, 64-column V-tile, segment); wave w
 // owns state columns 16w..16w+15 for all keys, as 16x16 fp32 accumulator tiles

@@ -156,6 +156,15 @@ __device__ __forceinline__ f32x4 mm16_rb(f32x4 xa, s16x4 bh, s16x4 bl, f32x4 acc
     return mfma16k16(ah, bh, acc);
 }
 
+// As mm16 with the left operand already split into hi/lo.
+__device__ __forceinline__ f32x4 mm16_la(s16x4 ah, s16x4 al, f32x4 yb, f32x4 acc) {
+    s16x4 bh, bl;
+    split4(yb, bh, bl);
+    acc = mfma16k16(al, bh, acc);
+    acc = mfma16k16(ah, bl, acc);
+    return mfma16k16(ah, bh, acc);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
 // 8 consecutive bf16 (columns c0..c0+7 of a row of n columns); zero past the
@@ -187,7 +196,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     constexpr int U_BYTES = QK_BYTES > AT_BYTES ? QK_BYTES : AT_BYTES;
     __shared__ __align__(16) unsigned char sU[U_BYTES];
     __shared__ __align__(16) float sM[L * LDA];    // decayed form: G first, then M
-    __shared__ float sBeta[L];
+    __shared__ __align__(16) float sBeta[L];
     __shared__ float sTot[DECAY ? 4 : 1][DECAY ? KP : 1];
     __shared__ float sRef[DECAY ? KP : 1];
     // plain form: sQ, sK.  Decayed form: tiles a hi/lo, b hi/lo, qt hi/lo; the
@@ -466,19 +475,33 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     static_assert(2 * L * LDT * 2 <= L * LDA * 4, "Tb^T tiles fit in A's space");
     u16* tTh = reinterpret_cast<u16*>(sA);
     u16* tTl = tTh + L * LDT;
-    for (int e = tid; e < L * L; e += NT) {
-        const int tau = e / L, tp = e % L;
-        const float x = tau >= tp ? sT[tau * LDA + tp] * sBeta[tp] : 0.0f;
-        u16 hi, lo;
-        split_bf16(x, hi, lo);
-        tTh[tp * LDT + tau] = hi;
-        tTl[tp * LDT + tau] = lo;
+    {
+        // one 4x4 block per thread: rows tau = 4 a4 .., columns tp = 4 b4 .. of T,
+        // transposed in registers and written four steps at a time
+        static_assert(NT == (L / 4) * (L / 4), "one 4x4 block of T per thread");
+        const int a4 = tid / (L / 4), b4 = tid % (L / 4);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(sBeta + 4 * b4);
+        f32x4 rows[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rows[i] = *reinterpret_cast<const f32x4*>(sT + (4 * a4 + i) * LDA + 4 * b4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u16 hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = 4 * a4 + i >= 4 * b4 + j ? rows[i][j] * bt[j] : 0.0f;
+                split_bf16(x, hi[i], lo[i]);
+            }
+            store4(tTh + (4 * b4 + j) * LDT + 4 * a4, hi[0], hi[1], hi[2], hi[3]);
+            store4(tTl + (4 * b4 + j) * LDT + 4 * a4, lo[0], lo[1], lo[2], lo[3]);
+        }
     }
     __syncthreads();
 
     u16* blk = p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<KP, DECAY>();
     // MTb lower blocks (i, j): (sum_{m=j}^{i} M_im T_mj) diag(beta); five block
-    // products per wave
+    // products per wave, formed transposed (Tb^T M^T) so that each lane holds
+    // four consecutive columns of one row: one 8-byte store per plane
     {
         for (int qj = 0; qj < 4; ++qj) {
             int bi, bj;
@@ -488,16 +511,15 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             for (int m = bj; m <= bi; ++m) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(sM + (16 * bi + c16) * LDA + 16 * m + 4 * g);
                 const int to = (16 * bj + c16) * LDT + 16 * m + 4 * g;
-                X = mm16_rb(a, *reinterpret_cast<const s16x4*>(tTh + to), *reinterpret_cast<const s16x4*>(tTl + to), X);
+                X = mm16_la(*reinterpret_cast<const s16x4*>(tTh + to), *reinterpret_cast<const s16x4*>(tTl + to), a, X);
             }
+            // X[r]: row 16 bi + c16, column 16 bj + 4 g + r
+            u16 hi[4], lo[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u16 hi, lo;
-                split_bf16(X[r], hi, lo);
-                const int idx = (16 * bi + 4 * g + r) * L + 16 * bj + c16;
-                blk[idx] = hi;
-                blk[PLANE + idx] = lo;
-            }
+            for (int r = 0; r < 4; ++r) split_bf16(X[r], hi[r], lo[r]);
+            const int idx = (16 * bi + c16) * L + 16 * bj + 4 * g;
+            store4(blk + idx, hi[0], hi[1], hi[2], hi[3]);
+            store4(blk + PLANE + idx, lo[0], lo[1], lo[2], lo[3]);
         }
         // zeros for the blocks right of the diagonal
         const int row = tid / 4, c0 = (tid % 4) * 16;
@@ -532,8 +554,8 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             const int ib = n / 4, jb = n % 4;   // key block, step block
             f32x4 acc2 = zero4();
             for (int m = jb; m < 4; ++m) {
-                // left: khat^T (row = key 16 ib + c16, k = step 16 m + 4 g + e);
-                // right: Tb (column = step 16 jb + c16, same k), lower blocks only
+                // right: khat (column = key 16 ib + c16, k = step 16 m + 4 g + e);
+                // left: Tb^T (row = step 16 jb + c16, same k), lower blocks only;
                 // the transposing LDS read: lane i of a 16-lane group supplies step
                 // 16 m + 4 g + i / 4, keys 16 ib + 4 (i % 4) .. +3; lane j receives
                 // khat[16 m + 4 g .. +3][16 ib + j]
@@ -544,18 +566,18 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                 const int to = (16 * jb + c16) * LDT + 16 * m + 4 * g;
                 const s16x4 yh = *reinterpret_cast<const s16x4*>(tTh + to);
                 const s16x4 yl = *reinterpret_cast<const s16x4*>(tTl + to);
-                if constexpr (DECAY) acc2 = mfma16k16(xl, yh, acc2);
-                acc2 = mfma16k16(xh, yl, acc2);
-                acc2 = mfma16k16(xh, yh, acc2);
+                // formed transposed (Tb^T khat): the left operand is Tb^T, the right khat
+                if constexpr (DECAY) acc2 = mfma16k16(yh, xl, acc2);
+                acc2 = mfma16k16(yl, xh, acc2);
+                acc2 = mfma16k16(yh, xh, acc2);
             }
+            // acc2[r]: key 16 ib + c16, step 16 jb + 4 g + r
+            u16 hi[4], lo[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                u16 hi, lo;
-                split_bf16(acc2[r], hi, lo);
-                const int idx = (16 * ib + 4 * g + r) * L + 16 * jb + c16;
-                wh[idx] = hi;
-                wl[idx] = lo;
-            }
+            for (int r = 0; r < 4; ++r) split_bf16(acc2[r], hi[r], lo[r]);
+            const int idx = (16 * ib + c16) * L + 16 * jb + 4 * g;
+            store4(wh + idx, hi[0], hi[1], hi[2], hi[3]);
+            store4(wl + idx, lo[0], lo[1], lo[2], lo[3]);
         }
     }
 }

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     constexpr int AT_BYTES = 2 * L * LDA * 4;      // sA, sT (fp32) reuse the same space
     constexpr int U_BYTES = QK_BYTES > AT_BYTES ? QK_BYTES : AT_BYTES;
     __shared__ __align__(16) unsigned char sU[U_BYTES];
-    __shared__ __align__(16) float sM[L * LDA];    // decayed form: G first, then M
+    __shared__ __align__(16) float sG_[DECAY ? L * LDA : 4];   // decayed form: the running log-decay G
     __shared__ __align__(16) float sBeta[L];
     __shared__ float sTot[DECAY ? 4 : 1][DECAY ? KP : 1];
     __shared__ float sRef[DECAY ? KP : 1];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
         *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = xk[j];
     }
     if (tid < L) sBeta[tid] = xb;
-    float* sG = sM;
+    float* sG = sG_;
     if constexpr (DECAY) {
 #pragma unroll
         for (int j = 0; j < NGE; ++j) {
@@ -413,18 +413,19 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             acc[m] = a;
         }
     }
-    __syncthreads();   // sQ / sK (decayed form: the tiles and G) are overwritten by sA / sT / sM below
+    __syncthreads();   // sQ / sK (decayed form: the tiles) are overwritten by sA / sT below
+    // A into LDS now; the blocks of M stay in registers until T's space is free
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
         const int n = wave + 4 * m;
+        if (n >= 10) continue;
         int bi, bj;
-        tri_block(n % 10, bi, bj);
+        tri_block(n, bi, bj);
         const int tau = 16 * bj + c16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 16 * bi + 4 * g + r;
-            if (n < 10) sA[t * LDA + tau] = tau < t ? sBeta[t] * acc[m][r] : 0.0f;
-            else sM[t * LDA + tau] = tau <= t ? acc[m][r] : 0.0f;
+            sA[t * LDA + tau] = tau < t ? sBeta[t] * acc[m][r] : 0.0f;
         }
     }
     __syncthreads();
@@ -498,6 +499,24 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     }
     __syncthreads();
 
+    // M into T's space, which the staging above has consumed (so the kernel
+    // needs no separate M buffer: a smaller LDS footprint, more workgroups per CU)
+    float* sM = sT;
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+        const int n = wave + 4 * m;
+        if (n < 10) continue;
+        int bi, bj;
+        tri_block(n - 10, bi, bj);
+        const int tau = 16 * bj + c16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * bi + 4 * g + r;
+            sM[t * LDA + tau] = tau <= t ? acc[m][r] : 0.0f;
+        }
+    }
+    __syncthreads();
+
     u16* blk = p.ws + static_cast<int64_t>(blockIdx.x) * chunk_u16<KP, DECAY>();
     // MTb lower blocks (i, j): (sum_{m=j}^{i} M_im T_mj) diag(beta); five block
     // products per wave, formed transposed (Tb^T M^T) so that each lane holds
@@ -535,6 +554,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     // W = khat^T Tb (key-major, [KP][L]); khat = k (plain form, exact in
     // bf16) or e^{G_L - G_t} k (decayed form, hi/lo), staged [step][key] in M's space
     {
+        static_assert((DECAY ? 2 : 1) * L * KP * 2 <= L * LDA * 4, "khat fits in M's space");
         u16* sKh = reinterpret_cast<u16*>(sM);
         u16* sKl = sKh + L * KP;
 #pragma unroll

@@ -124,7 +124,7 @@ __device__ __forceinline__ bool score_job8(int wave, int n, int& kb, int& qb) {
 }
 
 // AGG = true: segment reduction (a_seg, U_seg) from a zero state, no outputs.
-// AGG = false: outputs and the final state, starting from the folded segment state.
+// AGG = false: outputs and the final state, starting from the state entering the segment.
 // KK = true (per-key decay only): kappa per key, k_scale [B,T,H,K].
 // EPI = true (output pass only): the output epilogue and dtype of DiagArgs.
 template <int MODE, int KP, int WPB, bool VEC, bool AGG, bool KK = false, bool EPI = false>

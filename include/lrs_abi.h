@@ -51,6 +51,16 @@
  *   outputs are valid once the stream reaches that point.  A context serves
  *   one stream at a time: its workspace is reused by every call, so calls on
  *   one context must not run concurrently on different streams.
+ * Graph capture.  A call may be captured into a HIP graph once the context's
+ *   workspace is large enough for it (make one uncaptured call of the same or
+ *   a larger size first: growing the workspace allocates and synchronizes).
+ *   Every call keeps no per-call state on the host once captured, so a
+ *   replay recomputes it on the captured buffers' current contents.  The
+ *   elementwise look-back schedule takes a fresh tile-counter base and
+ *   status epoch on the host for every call, which a replay would reuse: an
+ *   elementwise call made while its stream is being captured therefore uses
+ *   the stream schedule when the schedule is automatic, and returns
+ *   LRS_E_UNSUPPORTED (nothing captured) when the look-back is forced.
  * Errors.  Arguments are validated on the host before anything is enqueued.
  *   On a non-zero status nothing was enqueued and the outputs are untouched.
  *   LRS_E_INVAL       NULL context or required pointer, a dimension < 1,

@@ -123,14 +123,25 @@ lrs_status next_epoch(LrsContext* ctx, hipStream_t stream, unsigned int* out) {
     return LRS_OK;
 }
 
+// True while `stream` is being captured into a graph.
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
+
 // Resolves the schedule and plan of an elementwise pass over [B,T,N] and, for
 // the look-back schedule, sizes the status words and takes a fresh epoch.
-// Fills p.B/T/N, p.gated, p.schedule and the look-back fields.
+// Fills p.B/T/N, p.gated, p.schedule and the look-back fields.  A look-back
+// launch carries its tile-counter base and status epoch from the host, which
+// a graph replay would reuse, so a call captured into a graph uses the stream
+// schedule (automatic choice) or is refused (look-back forced).
 lrs_status elem_prepare(LrsContext* ctx, bool gated, int32_t B, int32_t T, int32_t N, bool al16,
                         hipStream_t stream, lrs::ElemPlan& plan, lrs::ElemParams& p) {
     int schedule = ctx->elem_schedule;
+    const bool captured = capturing(stream);
+    if (captured && schedule == LRS_ELEM_SCHEDULE_LOOKBACK) return LRS_E_UNSUPPORTED;
     if (schedule == LRS_ELEM_SCHEDULE_AUTO)
-        schedule = lrs::elem_auto_schedule(B, T, N, al16, ctx->num_cus);
+        schedule = captured ? LRS_ELEM_SCHEDULE_STREAM : lrs::elem_auto_schedule(B, T, N, al16, ctx->num_cus);
     const int ksched = schedule == LRS_ELEM_SCHEDULE_LOOKBACK ? lrs::kElemLookback : lrs::kElemStream;
     plan = lrs::elem_plan(B, T, N, al16, ksched);
     if (plan.grid > 0x7fffffff) return LRS_E_UNSUPPORTED;

@@ -1,0 +1,180 @@
+"""Calls captured into a HIP graph and replayed (torch.cuda.graph on the
+caller's stream).  The library keeps no per-call host state in a captured
+call, so a replay recomputes the call on whatever the captured buffers then
+hold.  Each replay follows new inputs copied into those buffers and eager
+work with synchronizations, and must equal an eager call on the same inputs.
+
+The elementwise look-back schedule carries a tile-counter base and epoch
+from the host, which a replay would reuse: under capture the automatic
+schedule takes the stream schedule, and a forced look-back is refused
+without capturing anything or disturbing later eager calls.
+"""
+import pytest
+import torch
+
+from linear_recurrence_scan_fma_amd import binding, inputs
+from _helpers import rel, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = binding.Context(0)
+    yield c
+    c.close()
+
+
+def _replay_matches(run, bufs, fresh, outs, n=3):
+    """Capture run() once, then n times: copy fresh(i) into bufs, replay, and
+    compare outs with an eager run() on the same inputs."""
+    torch.cuda.synchronize()
+    run()                                   # warm-up: sizes the context's workspaces
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for i in range(n):
+        for dst, src in zip(bufs, fresh(i)):
+            dst.copy_(src)
+        junk = torch.randn(1 << 20, device="cuda:0").sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        run()
+        torch.cuda.synchronize()
+        for a, b in zip(got, outs):
+            assert torch.equal(a, b), f"replay {i}"
+        del junk
+
+
+def test_graph_diag_outer(ctx):
+    B, T, H, K, V = 1, 300, 2, 128, 128
+    d = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=1201)
+    q, k, v, g = (d[n].to("cuda:0") for n in ("q", "k", "v", "g"))
+    o = torch.empty((B, T, H, V), device="cuda:0")
+    fin = torch.empty((B, H, K, V), device="cuda:0")
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_DIAG_SEGMENTS, 3)
+    try:
+        say("graph: diag outer, 3 segments")
+        run = lambda: binding.lrs_scan_diag_outer(ctx, q, k, v, g, 1, None, d["scale"], None, o, fin)  # noqa: E731
+        fresh = lambda i: [inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=1300 + i)[n].to("cuda:0")  # noqa: E731
+                           for n in ("q", "k", "v", "g")]
+        _replay_matches(run, [q, k, v, g], fresh, [o, fin])
+    finally:
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_DIAG_SEGMENTS, 0)
+
+
+@pytest.mark.parametrize("decay", [False, True])
+def test_graph_delta(ctx, decay):
+    B, T, H, K, V = 1, 200, 2, 64, 64
+    gen = inputs.rwkv7 if decay else inputs.deltanet
+    d = gen(B=B, T=T, H=H, K=K, V=V, seed=1401)
+    names = ("q", "k", "v", "g", "beta") if decay else ("q", "k", "v", "beta")
+    x = [d[n].to("cuda:0") for n in names]
+    o = torch.empty((B, T, H, V), device="cuda:0")
+    fin = torch.empty((B, H, K, V), device="cuda:0")
+    say(f"graph: delta decay={decay}")
+    if decay:
+        run = lambda: binding.lrs_scan_delta_decay(ctx, *x, 1.0, None, o, fin)  # noqa: E731
+    else:
+        run = lambda: binding.lrs_scan_delta(ctx, *x, 1.0, None, o, fin)  # noqa: E731
+    fresh = lambda i: [gen(B=B, T=T, H=H, K=K, V=V, seed=1500 + i)[n].to("cuda:0") for n in names]  # noqa: E731
+    _replay_matches(run, x, fresh, [o, fin])
+
+
+def test_graph_elementwise_stream_schedule(ctx):
+    B, T, N = 2, 500, 256
+    d = inputs.elementwise_small(B, T, N, seed=1601)
+    a, u = d["a"].to("cuda:0"), d["u"].to("cuda:0")
+    s = torch.empty_like(a)
+    fin = torch.empty((B, N), device="cuda:0")
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_STREAM)
+    try:
+        say("graph: gated scan, stream schedule")
+        run = lambda: binding.lrs_scan_gated(ctx, a, u, None, s, fin)  # noqa: E731
+        fresh = lambda i: [inputs.elementwise_small(B, T, N, seed=1700 + i)[n].to("cuda:0")  # noqa: E731
+                           for n in ("a", "u")]
+        _replay_matches(run, [a, u], fresh, [s, fin])
+    finally:
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_AUTO)
+
+
+def test_graph_elementwise_automatic_schedule_under_capture(ctx):
+    # a shape whose eager automatic schedule is the look-back: captured, the
+    # call takes the (deterministic) stream schedule, so replays equal an
+    # eager stream-schedule call bit for bit
+    B, T, N = 2, 500, 256
+    d = inputs.elementwise_small(B, T, N, seed=1801)
+    a, u = d["a"].to("cuda:0"), d["u"].to("cuda:0")
+    s = torch.empty_like(a)
+    fin = torch.empty((B, N), device="cuda:0")
+    s_ref = torch.empty_like(a)
+    f_ref = torch.empty_like(fin)
+    say("graph: gated scan, automatic schedule")
+    run = lambda: binding.lrs_scan_gated(ctx, a, u, None, s, fin)  # noqa: E731
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        fresh = inputs.elementwise_small(B, T, N, seed=1900 + i)
+        a.copy_(fresh["a"].to("cuda:0"))
+        u.copy_(fresh["u"].to("cuda:0"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_STREAM)
+        try:
+            binding.lrs_scan_gated(ctx, a, u, None, s_ref, f_ref)
+            torch.cuda.synchronize()
+        finally:
+            binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_AUTO)
+        assert torch.equal(s, s_ref) and torch.equal(fin, f_ref), i
+    assert binding.lib().lrs_context_check(ctx.handle) == binding.LRS_OK
+
+
+def test_graph_forced_lookback_is_refused(ctx):
+    B, T, N = 2, 500, 256
+    d = inputs.elementwise_small(B, T, N, seed=2001)
+    a, u = d["a"].to("cuda:0"), d["u"].to("cuda:0")
+    s = torch.empty_like(a)
+    fin = torch.empty((B, N), device="cuda:0")
+    L = binding.lib()
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_LOOKBACK)
+    try:
+        say("graph: forced look-back under capture")
+        binding.lrs_scan_gated(ctx, a, u, None, s, fin)
+        torch.cuda.synchronize()
+        want_s, want_f = s.clone(), fin.clone()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                rc = L.lrs_scan_gated(ctx.handle, a.data_ptr(), u.data_ptr(), None, s.data_ptr(),
+                                      fin.data_ptr(), B, T, N, st.cuda_stream)
+                fin.add_(0.0)                   # the graph captures something
+        assert rc == binding.LRS_E_UNSUPPORTED
+        torch.cuda.synchronize()
+        # later eager look-back calls are unaffected
+        s.fill_(-7.0)
+        fin.fill_(-7.0)
+        binding.lrs_scan_gated(ctx, a, u, None, s, fin)
+        torch.cuda.synchronize()
+        assert rel(s, want_s) <= 1e-6 and rel(fin, want_f) <= 1e-6
+        assert L.lrs_context_check(ctx.handle) == binding.LRS_OK
+    finally:
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_AUTO)

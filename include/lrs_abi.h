@@ -50,7 +50,10 @@
  *   stream).  Calls only enqueue work and return without synchronizing;
  *   outputs are valid once the stream reaches that point.  A context serves
  *   one stream at a time: its workspace is reused by every call, so calls on
- *   one context must not run concurrently on different streams.
+ *   one context must not run concurrently on different streams.  A context is
+ *   not thread-safe: calls on one context (lrs_context_set_param included)
+ *   must come from one host thread at a time; separate contexts are
+ *   independent.
  * Graph capture.  A call may be captured into a HIP graph once the context's
  *   workspace is large enough for it (make one uncaptured call of the same or
  *   a larger size first: growing the workspace allocates and synchronizes).

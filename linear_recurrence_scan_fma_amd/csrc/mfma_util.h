@@ -63,6 +63,16 @@ __device__ __forceinline__ bf16x8 frag(const u16* base, int r0, int k0, int lane
     return *reinterpret_cast<const bf16x8*>(base + (r0 + (lane & 15)) * LD + k0 + 8 * (lane >> 4));
 }
 
+// The same fragment from an array whose rows are only 8-byte aligned: two
+// 8-byte LDS reads per lane.
+template <int LD>
+__device__ __forceinline__ bf16x8 frag_b64(const u16* base, int r0, int k0, int lane) {
+    const u16* p = base + (r0 + (lane & 15)) * LD + k0 + 8 * (lane >> 4);
+    const u32x2 a = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 b = *reinterpret_cast<const u32x2*>(p + 4);
+    return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
+}
+
 // The contraction index of a 16x16x32 product may be permuted as long as both
 // operands agree.  "Slot" operands give lane group g the contraction indices
 // {k0 + 4g .. k0 + 4g + 3} u {k0 + 16 + 4g .. k0 + 16 + 4g + 3}: exactly what

@@ -134,9 +134,20 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     constexpr bool OUT = !AGG;
     constexpr int NT = 64 * WPB;   // threads per workgroup
     constexpr int VT = 16 * WPB;   // V-tile width
-    constexpr int LDK = KP + 8;   // row stride of the [L][KP] bf16 operands
-    constexpr int LDV = VT + 8;
-    constexpr int LDP = L + 8;
+    // LDS row strides (bf16 elements), chosen by the reads each array serves
+    // (LDS: 32 four-byte banks; an 8-byte read serves 16 lanes per pass, a
+    // transposing read 16 lanes from 4 rows):
+    //  * K and V feed the transposing reads of the update and the readout:
+    //    rows 2 KP + 32 (2 VT + 32) bytes apart put 4 consecutive rows on
+    //    disjoint 8-bank groups;
+    //  * Q and P feed 8-byte reads of 16 consecutive rows at one column
+    //    (readout operands, and the scores' Q operand): rows 8 bytes off a
+    //    multiple of 128 put those 16 reads on disjoint bank pairs.  Q rows are
+    //    then 8-byte aligned only, so Q is written and read in 8-byte pieces.
+    constexpr int LDK = KP + 16;
+    constexpr int LDV = VT + 16;
+    constexpr int LDQ = KP + 4;
+    constexpr int LDP = L + 4;
     constexpr int KB = KP / 16;   // 16-row state tiles per wave
     constexpr int KM = KP / 32;   // 32-wide steps over the key axis
     constexpr int NPL = MODE == 1 ? 2 : 1;   // hi/lo planes of the q/k operands
@@ -148,8 +159,9 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     constexpr int NQ = MODE == 0 ? PQ : RPG;
     static_assert(PQ >= 1 && PV >= 1 && RPG >= 1, "tile shape");
     static_assert(MODE == 0 || NPL * L * LDK * 2 >= L * KP * 4, "fallback scores reuse the key operand space");
+    static_assert((2 * LDK) % 16 == 0 && (2 * LDV) % 16 == 0 && (2 * LDQ) % 8 == 0 && (2 * LDP) % 8 == 0, "row alignment");
 
-    __shared__ __align__(16) u16 sQ[OUT ? NPL * L * LDK : 8];
+    __shared__ __align__(16) u16 sQ[OUT ? NPL * L * LDQ : 8];
     __shared__ __align__(16) u16 sK[NPL * L * LDK];
     __shared__ __align__(16) u16 sV[L * LDV];
     __shared__ __align__(16) u16 sP[OUT ? 2 * L * LDP : 8];
@@ -411,7 +423,15 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                 const int pi = tid + NT * i;
                 const int row = pi / (KP / 8);
                 const int c8 = (pi % (KP / 8)) * 8;
-                if constexpr (OUT) *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = cq[i];
+                if constexpr (OUT) {
+                    // two 8-byte halves; pieces 8..15 of a row write their upper half first,
+                    // so the 16 lanes of a pass cover all banks
+                    const u32x2 lo2 = {cq[i].x, cq[i].y}, hi2 = {cq[i].z, cq[i].w};
+                    const bool swap = ((pi % (KP / 8)) >> 3) & 1;
+                    u16* dq = sQ + row * LDQ + c8;
+                    *reinterpret_cast<u32x2*>(dq + (swap ? 4 : 0)) = swap ? hi2 : lo2;
+                    *reinterpret_cast<u32x2*>(dq + (swap ? 0 : 4)) = swap ? lo2 : hi2;
+                }
                 *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = ck[i];
             }
             if (wave == 0) {
@@ -485,8 +505,8 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
                     const int t = rg * RPG + r;
-                    *reinterpret_cast<u32x2*>(sQ + t * LDK + d0) = cq2[r];
-                    *reinterpret_cast<u32x2*>(sQ + L * LDK + t * LDK + d0) = ck2[r];
+                    *reinterpret_cast<u32x2*>(sQ + t * LDQ + d0) = cq2[r];
+                    *reinterpret_cast<u32x2*>(sQ + L * LDQ + t * LDQ + d0) = ck2[r];
                     *reinterpret_cast<f32x4*>(sGf + t * KP + d0) = f32x4{G[r][0], G[r][1], G[r][2], G[r][3]};
                     if (kg == 0) sKap[t] = scale * kapr[r];
                     if constexpr (KK)
@@ -499,8 +519,8 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                     float a = 0.0f;
                     if (tau <= t) {
                         for (int d = 0; d < KP; ++d)
-                            a += bf2f(sQ[t * LDK + d]) * (KK ? bf2f(sQ[L * LDK + tau * LDK + d]) * sKK[tau * KP + d]
-                                                             : bf2f(sQ[L * LDK + tau * LDK + d])) *
+                            a += bf2f(sQ[t * LDQ + d]) * (KK ? bf2f(sQ[L * LDQ + tau * LDQ + d]) * sKK[tau * KP + d]
+                                                             : bf2f(sQ[L * LDQ + tau * LDQ + d])) *
                                  __expf(sGf[t * KP + d] - sGf[tau * KP + d]);
                         a *= sKap[tau];
                     }
@@ -525,8 +545,8 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                 if constexpr (OUT) {
                     split2(qv[0], qv[1], hq[0], lq[0]);
                     split2(qv[2], qv[3], hq[1], lq[1]);
-                    *reinterpret_cast<u32x2*>(sQ + t * LDK + d0) = u32x2{hq[0], hq[1]};
-                    *reinterpret_cast<u32x2*>(sQ + L * LDK + t * LDK + d0) = u32x2{lq[0], lq[1]};
+                    *reinterpret_cast<u32x2*>(sQ + t * LDQ + d0) = u32x2{hq[0], hq[1]};
+                    *reinterpret_cast<u32x2*>(sQ + L * LDQ + t * LDQ + d0) = u32x2{lq[0], lq[1]};
                 }
                 split2(kv[0], kv[1], hk[0], lk[0]);
                 split2(kv[2], kv[3], hk[1], lk[1]);
@@ -553,10 +573,10 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
 #pragma unroll
                 for (int ks = 0; ks < KM; ++ks) {
                     const bf16x8 ah = frag<LDK>(sK, 16 * kb, 32 * ks, lane);
-                    const bf16x8 bh_ = frag<LDK>(sQ, 16 * qbk, 32 * ks, lane);
+                    const bf16x8 bh_ = frag_b64<LDQ>(sQ, 16 * qbk, 32 * ks, lane);
                     if constexpr (MODE == 1) {
                         const bf16x8 al = frag<LDK>(sK + L * LDK, 16 * kb, 32 * ks, lane);
-                        const bf16x8 bl = frag<LDK>(sQ + L * LDK, 16 * qbk, 32 * ks, lane);
+                        const bf16x8 bl = frag_b64<LDQ>(sQ + L * LDQ, 16 * qbk, 32 * ks, lane);
                         acc = mfma16(al, bh_, acc);
                         acc = mfma16(ah, bl, acc);
                     }
@@ -646,11 +666,11 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
             for (int m = 0; m < KM; ++m) {
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
-                    const u16* qrow = sQ + (16 * tb + c16) * LDK + 4 * g4 + 32 * m;
+                    const u16* qrow = sQ + (16 * tb + c16) * LDQ + 4 * g4 + 32 * m;
                     const bf16x8 qh = slot_frag(qrow);
                     acc[tb] = mfma16(sl[m], qh, acc[tb]);
                     acc[tb] = mfma16(sh[m], qh, acc[tb]);
-                    if constexpr (MODE == 1) acc[tb] = mfma16(sh[m], slot_frag(qrow + L * LDK), acc[tb]);
+                    if constexpr (MODE == 1) acc[tb] = mfma16(sh[m], slot_frag(qrow + L * LDQ), acc[tb]);
                 }
             }
             if constexpr (MODE == 0) {

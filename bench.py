@@ -10,8 +10,8 @@ once) over the wall-clock of K steps; `roofline.achieved` uses the average
 kernel duration from HIP events recorded on the launch stream.
 
 `rows` reports the other scans at their workload shapes (each timed with
-per-launch events; the 256 MB last-level cache is flushed between launches of
-the matrix scans), each with its own roofline figure.
+per-launch events; before each launch a 512 MB read evicts the call's inputs
+from the 256 MB last-level cache), each with its own roofline figure.
 
 `cpu_baseline` is the sequential CPU oracle (fp64) timed on this host.
 """
@@ -450,13 +450,19 @@ def delta_bytes(d):
 
 def time_launches(fn, reps, warmup, flush):
     """Median and min of per-launch HIP-event times on the current stream, with
-    the 256 MB last-level cache flushed (a 512 MB write) before each launch."""
+    the 256 MB last-level cache emptied of the call's data before each launch.
+
+    The eviction reads a 512 MB buffer (a reduction), so the cache is left
+    holding clean lines only: a write-based flush would leave up to 256 MB of
+    its own dirty lines, whose write-back the timed call would then pay for.
+    The reduction is queued ahead of the timed call without a host wait, as the
+    call would be queued behind other work in a pipeline."""
     import torch
 
     stream = torch.cuda.current_stream()
     ts = []
     for i in range(warmup + reps):
-        flush.add_(1.0)
+        flush.sum()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -492,7 +498,7 @@ def run_rows(ctx, args, binding, inputs, dev):
                      "GB/s": round(nbytes / (ms_kernel * 1e-3) / 1e9, 2),
                      "note": "launch-latency bound (394 KB per call); no roofline claim"})
 
-    flush = torch.empty(512 * 1024 * 1024 // 4, device=dev)
+    flush = torch.ones(512 * 1024 * 1024 // 4, device=dev)
     rows += elem_rows(ctx, binding, inputs, dev, flush)
     nth = oracle.default_threads()
     heads = [(0, 0), (1, 1)]

@@ -57,6 +57,8 @@
  * Graph capture.  A call may be captured into a HIP graph once the context's
  *   workspace is large enough for it (make one uncaptured call of the same or
  *   a larger size first: growing the workspace allocates and synchronizes).
+ *   A captured diag-outer or delta call that would need a larger workspace
+ *   returns LRS_E_UNSUPPORTED and captures nothing.
  *   Every call keeps no per-call state on the host once captured, so a
  *   replay recomputes it on the captured buffers' current contents.  The
  *   elementwise look-back schedule takes a fresh tile-counter base and
@@ -290,8 +292,9 @@ lrs_status lrs_step_gated(LrsContext* ctx, const float* a, const float* u, float
  * one time segment (LRS_PARAM_DIAG_SEGMENTS) the context keeps a workspace of
  * (segments - 1) * B * H * (ceil(V/VT)*VT*KP + KP) * 4 bytes, KP = 64 for
  * K <= 64 and 128 otherwise, VT = 64 for V <= 64 and 128 otherwise, grown on
- * demand (LRS_E_NOMEM if that allocation fails); growing it waits for the
- * stream of the call.  LRS_E_UNSUPPORTED also when B * H * ceil(V/VT) is
+ * demand (LRS_E_NOMEM if that allocation fails); growing it first waits for
+ * the whole device, since an earlier call on another stream may still use
+ * the old workspace.  LRS_E_UNSUPPORTED also when B * H * ceil(V/VT) is
  * 2^27 or more (launch grid limits).
  */
 lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
@@ -320,7 +323,8 @@ lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf1
  * must stay under 2 GiB).  The context keeps a workspace per (batch, head,
  * 64-step chunk) of 32 KiB (K <= 64) or 48 KiB (K > 64), holding the chunk's
  * output and state-update factors, grown on demand (LRS_E_NOMEM if that
- * allocation fails); growing it waits for the stream of the call.
+ * allocation fails); growing it first waits for the whole device, since an
+ * earlier call on another stream may still use the old workspace.
  */
 lrs_status lrs_scan_delta(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k,
                           const lrs_bf16* v, const float* beta, float scale, const float* s0,

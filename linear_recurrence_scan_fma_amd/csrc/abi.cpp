@@ -89,12 +89,22 @@ bool mul_ok(int64_t& acc, int64_t v) {
     return true;
 }
 
+// True while `stream` is being captured into a graph.
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
+}
+
+// Growing a context buffer frees the old one: every stream may still hold work
+// of an earlier call that uses it (a context serves one stream at a time, but
+// successive calls may use different streams), so the whole device is waited
+// for first.  Growth is rare: a context keeps its largest size.
 lrs_status grow_words(LrsContext* ctx, size_t need, hipStream_t stream) {
     if (need <= ctx->words_cap) return LRS_OK;
     size_t cap = ctx->words_cap ? ctx->words_cap : 4096;
     while (cap < need) cap *= 2;
     if (ctx->words) {
-        if (hipStreamSynchronize(stream) != hipSuccess) return LRS_E_DEVICE;
+        if (hipDeviceSynchronize() != hipSuccess) return LRS_E_DEVICE;
         (void)hipFree(ctx->words);
         ctx->words = nullptr;
         ctx->words_cap = 0;
@@ -121,12 +131,6 @@ lrs_status next_epoch(LrsContext* ctx, hipStream_t stream, unsigned int* out) {
     }
     *out = ++ctx->epoch;
     return LRS_OK;
-}
-
-// True while `stream` is being captured into a graph.
-bool capturing(hipStream_t stream) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    return hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive;
 }
 
 // Resolves the schedule and plan of an elementwise pass over [B,T,N] and, for
@@ -429,12 +433,15 @@ LRS_API lrs_status lrs_step_gated(LrsContext* ctx, const float* a, const float* 
 
 namespace {
 
-// Grows a context-owned device buffer to `need` bytes.  A buffer in use by
-// earlier work on `stream` is released only after that work finishes.
+// Grows a context-owned device buffer to `need` bytes.  The old buffer is
+// released only after the device has finished all earlier work (see
+// grow_words).  Under graph capture nothing may allocate or wait: growth is
+// refused there (the caller enqueues nothing and returns the status).
 lrs_status grow_workspace(void*& ptr, size_t& cap, size_t need, hipStream_t stream) {
     if (need <= cap) return LRS_OK;
+    if (capturing(stream)) return LRS_E_UNSUPPORTED;
     if (ptr) {
-        if (hipStreamSynchronize(stream) != hipSuccess) return LRS_E_DEVICE;
+        if (hipDeviceSynchronize() != hipSuccess) return LRS_E_DEVICE;
         (void)hipFree(ptr);
         ptr = nullptr;
         cap = 0;

@@ -178,3 +178,34 @@ def test_graph_forced_lookback_is_refused(ctx):
         assert L.lrs_context_check(ctx.handle) == binding.LRS_OK
     finally:
         binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_AUTO)
+
+
+def test_graph_capture_refuses_workspace_growth():
+    """A captured matrix-scan call that would have to grow the context's
+    workspace (allocate and wait) is refused with nothing captured; the same
+    call made eagerly afterwards sizes the workspace and matches the oracle's
+    shape of result (the eager path is unaffected)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B, T, H, K, V = 1, 200, 2, 64, 64
+    d = inputs.deltanet(B=B, T=T, H=H, K=K, V=V, seed=1207)
+    q, k, v, beta = (d[n].to("cuda:0") for n in ("q", "k", "v", "beta"))
+    o = torch.empty((B, T, H, V), device="cuda:0")
+    fin = torch.empty((B, H, K, V), device="cuda:0")
+    L = binding.lib()
+    with binding.Context(0) as fresh:   # empty workspace
+        say("graph: capture on a context whose workspace must grow")
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                rc = L.lrs_scan_delta(fresh.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(),
+                                      1.0, None, o.data_ptr(), fin.data_ptr(), B, T, H, K, V, st.cuda_stream)
+                fin.add_(0.0)                   # the graph captures something
+        assert rc == binding.LRS_E_UNSUPPORTED
+        torch.cuda.synchronize()
+        o2, fin2 = binding.scan_delta(fresh, q, k, v, beta, 1.0)
+        o3, fin3 = binding.scan_delta(fresh, q, k, v, beta, 1.0)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o2).all() and torch.equal(o2, o3) and torch.equal(fin2, fin3)

@@ -662,15 +662,24 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
             f32x4 acc[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) acc[tb] = zero4();
+            // per key step: all four step blocks' operands first, then the products
+            // term by term, so that no product waits on the one just issued
 #pragma unroll
             for (int m = 0; m < KM; ++m) {
+                bf16x8 qh[4], ql[MODE == 1 ? 4 : 1];
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb) {
                     const u16* qrow = sQ + (16 * tb + c16) * LDQ + 4 * g4 + 32 * m;
-                    const bf16x8 qh = slot_frag(qrow);
-                    acc[tb] = mfma16(sl[m], qh, acc[tb]);
-                    acc[tb] = mfma16(sh[m], qh, acc[tb]);
-                    if constexpr (MODE == 1) acc[tb] = mfma16(sh[m], slot_frag(qrow + L * LDQ), acc[tb]);
+                    qh[tb] = slot_frag(qrow);
+                    if constexpr (MODE == 1) ql[tb] = slot_frag(qrow + L * LDQ);
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma16(sl[m], qh[tb], acc[tb]);
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma16(sh[m], qh[tb], acc[tb]);
+                if constexpr (MODE == 1) {
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma16(sh[m], ql[tb], acc[tb]);
                 }
             }
             if constexpr (MODE == 0) {
@@ -805,17 +814,23 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
         }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+            // all key tiles' operands first, then the products term by term
+            bf16x8 kh[KB];
 #pragma unroll
-            for (int db = 0; db < KB; ++db) {
-                const bf16x8 kh = tr_frag<LDK>(sK, 32 * ks, 16 * db, lane);
-                if constexpr (MODE == 0) {
-                    S[db] = mfma16(kh, wBl[ks], S[db]);
-                    S[db] = mfma16(kh, wBh[ks], S[db]);
-                } else {
-                    const bf16x8 kl = tr_frag<LDK>(sK + L * LDK, 32 * ks, 16 * db, lane);
-                    S[db] = mfma16(kl, vA[ks], S[db]);
-                    S[db] = mfma16(kh, vA[ks], S[db]);
-                }
+            for (int db = 0; db < KB; ++db) kh[db] = tr_frag<LDK>(sK, 32 * ks, 16 * db, lane);
+            if constexpr (MODE == 0) {
+#pragma unroll
+                for (int db = 0; db < KB; ++db) S[db] = mfma16(kh[db], wBl[ks], S[db]);
+#pragma unroll
+                for (int db = 0; db < KB; ++db) S[db] = mfma16(kh[db], wBh[ks], S[db]);
+            } else {
+                bf16x8 kl[KB];
+#pragma unroll
+                for (int db = 0; db < KB; ++db) kl[db] = tr_frag<LDK>(sK + L * LDK, 32 * ks, 16 * db, lane);
+#pragma unroll
+                for (int db = 0; db < KB; ++db) S[db] = mfma16(kl[db], vA[ks], S[db]);
+#pragma unroll
+                for (int db = 0; db < KB; ++db) S[db] = mfma16(kh[db], vA[ks], S[db]);
             }
         }
         __syncthreads();   // LDS operands are restaged by the next chunk

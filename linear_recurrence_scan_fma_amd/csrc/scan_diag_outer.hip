@@ -173,7 +173,6 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
     __shared__ __align__(16) float sTot[MODE == 1 ? RG * KP : 1];
     __shared__ float sGL[MODE == 1 ? KP : 1];    // G_L per key
     __shared__ __align__(16) float sEGL[MODE == 1 ? KP : 1];   // e^{G_L} per key
-    __shared__ __align__(16) float sKK[KK && OUT ? L * KP : 1];   // per-key kappa (exact-pairs path)
     __shared__ float sRS[EPI ? WPB * L : 1];   // epilogue: per-wave sums of squares of each step's row
     __shared__ __align__(16) float sNW[EPI ? 16 * WPB : 1];   // epilogue: RMSNorm weight of the tile's columns
 
@@ -509,19 +508,21 @@ __global__ __launch_bounds__(64 * WPB) void diag_outer_kernel(DiagArgs p) {
                     *reinterpret_cast<u32x2*>(sQ + L * LDQ + t * LDQ + d0) = ck2[r];
                     *reinterpret_cast<f32x4*>(sGf + t * KP + d0) = f32x4{G[r][0], G[r][1], G[r][2], G[r][3]};
                     if (kg == 0) sKap[t] = scale * kapr[r];
-                    if constexpr (KK)
-                        *reinterpret_cast<f32x4*>(sKK + t * KP + d0) =
-                            f32x4{kap_at(r, 0), kap_at(r, 1), kap_at(r, 2), kap_at(r, 3)};
                 }
                 __syncthreads();
+                // (the per-key kappa of this rare path is read from memory, so the
+                // variant needs no LDS buffer for it)
                 for (int idx = tid; idx < L * L; idx += NT) {
                     const int t = idx / L, tau = idx % L;
                     float a = 0.0f;
                     if (tau <= t) {
-                        for (int d = 0; d < KP; ++d)
-                            a += bf2f(sQ[t * LDQ + d]) * (KK ? bf2f(sQ[L * LDQ + tau * LDQ + d]) * sKK[tau * KP + d]
-                                                             : bf2f(sQ[L * LDQ + tau * LDQ + d])) *
-                                 __expf(sGf[t * KP + d] - sGf[tau * KP + d]);
+                        const bool row_ok = t0 + tau < T;
+                        const float* kk_row = KK ? ksb + ((t0 + tau) * H + h) * static_cast<int64_t>(K) : nullptr;
+                        for (int d = 0; d < KP; ++d) {
+                            float kd = bf2f(sQ[L * LDQ + tau * LDQ + d]);
+                            if constexpr (KK) kd *= (row_ok && d < K) ? kk_row[d] : 0.0f;
+                            a += bf2f(sQ[t * LDQ + d]) * kd * __expf(sGf[t * KP + d] - sGf[tau * KP + d]);
+                        }
                         a *= sKap[tau];
                     }
                     u16 hi, lo;

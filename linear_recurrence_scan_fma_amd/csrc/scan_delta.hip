@@ -185,25 +185,38 @@ __device__ __forceinline__ u32x4 load_piece(BufRes r, const u16* rowptr, int off
 // ---------------------------------------------------------------------------
 // prep: Tb = (I + strict_lower(diag(beta) K K^T))^{-1} diag(beta), MTb = tril(Q K^T) Tb
 // ---------------------------------------------------------------------------
+// Decayed-form prep tiles: [L][KD] bf16, unpadded, 16-byte piece p of row r
+// stored at piece p ^ (r & 7), so the 8 rows of a 16-byte fragment read fall
+// on distinct banks.  Element offset of (row, column):
+__device__ __forceinline__ int tswz(int r, int i) { return r * KD + ((((i >> 3) ^ (r & 7))) << 3) + (i & 7); }
+
+// 16x16x32 operand fragment (rows r0.., columns k0 + 8 (lane / 16) ..) of such a tile
+__device__ __forceinline__ bf16x8 tfrag(const u16* t, int r0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(t + tswz(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
+}
+
 template <int KP, bool VEC, bool DECAY>
 __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     static_assert(!DECAY || KP == KD, "decayed form: K <= 64");
     constexpr int LDK = KP + 8;
     constexpr int LDA = L + 4;                     // fp32 rows of 272 bytes
-    constexpr int NTILE = DECAY ? 6 : 2;           // bf16 operand tiles
-    constexpr int QK_BYTES = NTILE * L * LDK * 2;  // sQ, sK (decayed: a, b, qt as hi/lo)
+    // plain form: sQ, sK as padded rows.  Decayed form: four unpadded tiles
+    // whose 16-byte pieces are rotated by an XOR of the row (a hi/lo, later
+    // overwritten by qt hi/lo, and b hi/lo), then the running log-decay G; the
+    // whole block is dead once A and M are formed, so sA and sT reuse it.  The
+    // decayed form thus fits three workgroups per compute unit.
+    constexpr int TILE_D = L * KP * 2;
+    constexpr int G_OFF = 4 * TILE_D;
+    constexpr int QK_BYTES = DECAY ? G_OFF + L * LDA * 4 : 2 * L * LDK * 2;
     constexpr int AT_BYTES = 2 * L * LDA * 4;      // sA, sT (fp32) reuse the same space
     constexpr int U_BYTES = QK_BYTES > AT_BYTES ? QK_BYTES : AT_BYTES;
     __shared__ __align__(16) unsigned char sU[U_BYTES];
-    __shared__ __align__(16) float sG_[DECAY ? L * LDA : 4];   // decayed form: the running log-decay G
     __shared__ __align__(16) float sBeta[L];
     __shared__ float sTot[DECAY ? 4 : 1][DECAY ? KP : 1];
     __shared__ float sRef[DECAY ? KP : 1];
-    // plain form: sQ, sK.  Decayed form: tiles a hi/lo, b hi/lo, qt hi/lo; the
-    // raw k and q are loaded into the a-hi and qt-hi tiles and transformed in place.
     u16* tile = reinterpret_cast<u16*>(sU);
-    u16* sQ = DECAY ? tile + 4 * L * LDK : tile;
-    u16* sK = DECAY ? tile : tile + L * LDK;
+    u16* sQ = tile;                 // plain form
+    u16* sK = tile + L * LDK;       // plain form
     float* sA = reinterpret_cast<float*>(sU);
     float* sT = sA + L * LDA;
 
@@ -244,15 +257,18 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
         }
     }
     const float xb = (tid < L && t0 + tid < T) ? p.beta[(b * T + t0 + tid) * H + h] : 0.0f;
+    if constexpr (!DECAY) {
 #pragma unroll
-    for (int j = 0; j < NPI; ++j) {
-        const int pi = tid + j * NT;
-        const int row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
-        *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = xq[j];
-        *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = xk[j];
+        for (int j = 0; j < NPI; ++j) {
+            const int pi = tid + j * NT;
+            const int row = pi / (KP / 8), c8 = (pi % (KP / 8)) * 8;
+            *reinterpret_cast<u32x4*>(sQ + row * LDK + c8) = xq[j];
+            *reinterpret_cast<u32x4*>(sK + row * LDK + c8) = xk[j];
+        }
     }
     if (tid < L) sBeta[tid] = xb;
-    float* sG = sG_;
+    // decayed form: the raw q and k stay in the registers they were loaded into
+    float* sG = reinterpret_cast<float*>(sU + G_OFF);
     if constexpr (DECAY) {
 #pragma unroll
         for (int j = 0; j < NGE; ++j) {
@@ -288,12 +304,10 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dev = fmaxf(dev, fabsf(gl[r] - ref));
         const bool fast = !__syncthreads_or(dev > kHalfSpan);
-        u16* tAh = tile;
-        u16* tAl = tile + L * LDK;
-        u16* tBh = tile + 2 * L * LDK;
-        u16* tBl = tile + 3 * L * LDK;
-        u16* tQh = tile + 4 * L * LDK;
-        u16* tQl = tile + 5 * L * LDK;
+        u16* tAh = tile;                 // a hi, later qt hi
+        u16* tAl = tile + L * KP;        // a lo, later qt lo
+        u16* tBh = tile + 2 * L * KP;
+        u16* tBl = tile + 3 * L * KP;
         {
             // the scan's operands, relative to the chunk start: a = e^{G_{t-1}} k and
             // qt = e^{G_t} q as hi/lo planes, e^{G_L}, and khat = e^{G_L - G_t} k (kept
@@ -303,8 +317,8 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
 #pragma unroll
             for (int j = 0; j < NPI; ++j) {
                 const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
-                const u32x4 kw = *reinterpret_cast<const u32x4*>(tAh + t * LDK + i0);
-                const u32x4 qw = *reinterpret_cast<const u32x4*>(tQh + t * LDK + i0);
+                const u32x4 kw = xk[j];
+                const u32x4 qw = xq[j];
                 float av[8], qv[8], kv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -327,15 +341,15 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             if (tid < KP) reinterpret_cast<float*>(blk + off_el<KP>())[tid] = __expf(sG[(L - 1) * LDA + tid]);
         }
         if (fast) {
-            // a = e^{G_{t-1} - ref} k, b = e^{ref - G_t} k, qt = e^{G_t - ref} q, as hi/lo;
-            // eight keys of one step per piece, transformed in place
+            // a = e^{G_{t-1} - ref} k and b = e^{ref - G_t} k as hi/lo, eight keys of
+            // one step per piece (the raw k in registers); A = a b^T; then
+            // qt = e^{G_t - ref} q into a's tiles and M = qt b^T
             constexpr int NPC = L * KP / 8 / NT;
 #pragma unroll
             for (int j = 0; j < NPC; ++j) {
                 const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
-                const u32x4 kw = *reinterpret_cast<const u32x4*>(tAh + t * LDK + i0);
-                const u32x4 qw = *reinterpret_cast<const u32x4*>(tQh + t * LDK + i0);
-                float av[8], bv[8], qv[8];
+                const u32x4 kw = xk[j];
+                float av[8], bv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float r0 = sRef[i0 + e];
@@ -343,41 +357,64 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                     const float kv = bf2f(piece_elem(kw, e));
                     av[e] = kv * __expf(gp - r0);
                     bv[e] = kv * __expf(r0 - gt);
-                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(gt - r0);
                 }
                 bf16x8 hi, lo;
+                const int o = tswz(t, i0);
                 split8(av, hi, lo);
-                *reinterpret_cast<bf16x8*>(tAh + t * LDK + i0) = hi;
-                *reinterpret_cast<bf16x8*>(tAl + t * LDK + i0) = lo;
+                *reinterpret_cast<bf16x8*>(tAh + o) = hi;
+                *reinterpret_cast<bf16x8*>(tAl + o) = lo;
                 split8(bv, hi, lo);
-                *reinterpret_cast<bf16x8*>(tBh + t * LDK + i0) = hi;
-                *reinterpret_cast<bf16x8*>(tBl + t * LDK + i0) = lo;
-                split8(qv, hi, lo);
-                *reinterpret_cast<bf16x8*>(tQh + t * LDK + i0) = hi;
-                *reinterpret_cast<bf16x8*>(tQl + t * LDK + i0) = lo;
+                *reinterpret_cast<bf16x8*>(tBh + o) = hi;
+                *reinterpret_cast<bf16x8*>(tBl + o) = lo;
             }
             __syncthreads();
+            auto blocks = [&](bool want_m) {
 #pragma unroll
-            for (int m = 0; m < 5; ++m) {
-                const int n = wave + 4 * m;
-                int bi, bj;
-                tri_block(n % 10, bi, bj);
-                const u16* lh = n < 10 ? tAh : tQh;
-                const u16* ll = n < 10 ? tAl : tQl;
-                f32x4 a = zero4();
+                for (int m = 0; m < 5; ++m) {
+                    const int n = wave + 4 * m;
+                    if ((n >= 10) != want_m) continue;
+                    int bi, bj;
+                    tri_block(n % 10, bi, bj);
+                    f32x4 a = zero4();
 #pragma unroll
-                for (int k0 = 0; k0 < KP; k0 += 32) {
-                    const bf16x8 xh = frag<LDK>(lh, 16 * bi, k0, lane), xl = frag<LDK>(ll, 16 * bi, k0, lane);
-                    const bf16x8 yh = frag<LDK>(tBh, 16 * bj, k0, lane), yl = frag<LDK>(tBl, 16 * bj, k0, lane);
-                    a = mfma16(xl, yh, a);
-                    a = mfma16(xh, yl, a);
-                    a = mfma16(xh, yh, a);
+                    for (int k0 = 0; k0 < KP; k0 += 32) {
+                        const bf16x8 xh = tfrag(tAh, 16 * bi, k0, lane), xl = tfrag(tAl, 16 * bi, k0, lane);
+                        const bf16x8 yh = tfrag(tBh, 16 * bj, k0, lane), yl = tfrag(tBl, 16 * bj, k0, lane);
+                        a = mfma16(xl, yh, a);
+                        a = mfma16(xh, yl, a);
+                        a = mfma16(xh, yh, a);
+                    }
+                    acc[m] = a;
                 }
-                acc[m] = a;
+            };
+            blocks(false);
+            __syncthreads();   // a is read: its tiles take qt
+#pragma unroll
+            for (int j = 0; j < NPC; ++j) {
+                const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
+                const u32x4 qw = xq[j];
+                float qv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(sG[t * LDA + i0 + e] - sRef[i0 + e]);
+                bf16x8 hi, lo;
+                const int o = tswz(t, i0);
+                split8(qv, hi, lo);
+                *reinterpret_cast<bf16x8*>(tAh + o) = hi;
+                *reinterpret_cast<bf16x8*>(tAl + o) = lo;
             }
+            __syncthreads();
+            blocks(true);
         } else {
             // strong decay: each needed entry from its pairs, exact exponentials
-            // (tAh holds the raw k, tQh the raw q)
+            // (the raw k into tAh, the raw q into tBh)
+#pragma unroll
+            for (int j = 0; j < NPI; ++j) {
+                const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
+                *reinterpret_cast<u32x4*>(tAh + tswz(t, i0)) = xk[j];
+                *reinterpret_cast<u32x4*>(tBh + tswz(t, i0)) = xq[j];
+            }
+            __syncthreads();
 #pragma unroll
             for (int m = 0; m < 5; ++m) {
                 const int n = wave + 4 * m;
@@ -389,11 +426,11 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                     const int t = 16 * bi + 4 * g + r;
                     float sum = 0.0f;
                     if (n < 10 ? tau < t : tau <= t) {
-                        const u16* lrow = (n < 10 ? tAh : tQh) + t * LDK;
-                        const u16* krow = tAh + tau * LDK;
+                        const u16* ltile = n < 10 ? tAh : tBh;
                         const float* gl_row = n < 10 ? sG + (t - 1) * LDA : sG + t * LDA;   // t >= 1 when n < 10
                         for (int i = 0; i < KP; ++i)
-                            sum += bf2f(lrow[i]) * bf2f(krow[i]) * __expf(gl_row[i] - sG[tau * LDA + i]);
+                            sum += bf2f(ltile[tswz(t, i)]) * bf2f(tAh[tswz(tau, i)]) *
+                                   __expf(gl_row[i] - sG[tau * LDA + i]);
                     }
                     acc[m][r] = sum;
                 }

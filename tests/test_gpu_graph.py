@@ -209,3 +209,100 @@ def test_graph_capture_refuses_workspace_growth():
         o3, fin3 = binding.scan_delta(fresh, q, k, v, beta, 1.0)
         torch.cuda.synchronize()
         assert torch.isfinite(o2).all() and torch.equal(o2, o3) and torch.equal(fin2, fin3)
+
+
+def test_graph_diag_outer_keyscale(ctx):
+    B, T, H, K, V = 1, 300, 2, 64, 64
+    names = ("q", "k", "v", "g", "k_scale_key")
+    d = inputs.assoc_memory(B=B, T=T, H=H, K=K, V=V, seed=1211)
+    x = [d[n].to("cuda:0") for n in names]
+    o = torch.empty((B, T, H, V), device="cuda:0")
+    fin = torch.empty((B, H, K, V), device="cuda:0")
+    say("graph: diag outer with a per-key kappa")
+    run = lambda: binding.lrs_scan_diag_outer_keyscale(ctx, *x, d["scale"], None, o, fin)  # noqa: E731
+    fresh = lambda i: [inputs.assoc_memory(B=B, T=T, H=H, K=K, V=V, seed=1311 + i)[n].to("cuda:0")  # noqa: E731
+                       for n in names]
+    _replay_matches(run, x, fresh, [o, fin])
+
+
+def test_graph_diag_outer_epilogue(ctx):
+    B, T, H, K, V = 1, 300, 2, 128, 128
+    d = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=1221)
+    e = inputs.norm_gate_epilogue(B, T, H, V, seed=1222)
+    x = [d[n].to("cuda:0") for n in ("q", "k", "v", "g")] + [e["gate"].to("cuda:0")]
+    w = e["norm_weight"].to("cuda:0")
+    o = torch.empty((B, T, H, V), dtype=torch.bfloat16, device="cuda:0")
+    fin = torch.empty((B, H, K, V), device="cuda:0")
+    say("graph: diag outer with the norm-gate epilogue, bf16 output")
+    run = lambda: binding.lrs_scan_diag_outer_epilogue(  # noqa: E731
+        ctx, x[0], x[1], x[2], x[3], 1, None, d["scale"], None, binding.LRS_EPILOGUE_NORM_GATE, None, x[4], w,
+        e["eps"], binding.LRS_DTYPE_BF16, o, fin)
+
+    def fresh(i):
+        f = inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=1321 + i)
+        z = inputs.norm_gate_epilogue(B, T, H, V, seed=1421 + i)["gate"]
+        return [f[n].to("cuda:0") for n in ("q", "k", "v", "g")] + [z.to("cuda:0")]
+
+    _replay_matches(run, x, fresh, [o, fin])
+
+
+def test_graph_elementwise_backward(ctx):
+    B, T, N = 2, 500, 256
+    d = inputs.elementwise_small(B, T, N, seed=2101)
+    a, u = d["a"].to("cuda:0"), d["u"].to("cuda:0")
+    s = inputs.random_normal((B, T, N), 2102).to("cuda:0")
+    ds = inputs.random_normal((B, T, N), 2103).to("cuda:0")
+    s0 = inputs.random_state((B, N), 2104).to("cuda:0")
+    dsf = inputs.random_state((B, N), 2105).to("cuda:0")
+    da, du = torch.empty_like(a), torch.empty_like(a)
+    ds0 = torch.empty((B, N), device="cuda:0")
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_STREAM)
+    try:
+        say("graph: gated gradient pass, stream schedule")
+        run = lambda: binding.lrs_scan_gated_backward(ctx, a, u, s0, s, ds, dsf, da, du, ds0)  # noqa: E731
+
+        def fresh(i):
+            f = inputs.elementwise_small(B, T, N, seed=2200 + i)
+            return [f["a"].to("cuda:0"), f["u"].to("cuda:0"),
+                    inputs.random_normal((B, T, N), 2300 + i).to("cuda:0"),
+                    inputs.random_normal((B, T, N), 2400 + i).to("cuda:0")]
+
+        _replay_matches(run, [a, u, s, ds], fresh, [da, du, ds0])
+    finally:
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, binding.LRS_ELEM_SCHEDULE_AUTO)
+
+
+def test_graph_step(ctx):
+    # the step updates s in place: each replay and the eager call it is
+    # compared with start from the same fresh state
+    B, N = 4, 4096
+    d = inputs.elementwise_small(B, 1, N, seed=2501)
+    a, u = d["a"][:, 0].contiguous().to("cuda:0"), d["u"][:, 0].contiguous().to("cuda:0")
+    s = inputs.random_state((B, N), 2502).to("cuda:0")
+    say("graph: gated single step")
+    run = lambda: binding.lrs_step_gated(ctx, a, u, s)  # noqa: E731
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            run()
+    torch.cuda.synchronize()
+    for i in range(3):
+        f = inputs.elementwise_small(B, 1, N, seed=2600 + i)
+        fs = inputs.random_state((B, N), 2700 + i).to("cuda:0")
+        a.copy_(f["a"][:, 0].to("cuda:0"))
+        u.copy_(f["u"][:, 0].to("cuda:0"))
+        s.copy_(fs)
+        junk = torch.randn(1 << 20, device="cuda:0").sum()   # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = s.clone()
+        s.copy_(fs)
+        run()
+        torch.cuda.synchronize()
+        assert torch.equal(got, s), f"replay {i}"
+        del junk

@@ -58,7 +58,12 @@
  *   workspace is large enough for it (make one uncaptured call of the same or
  *   a larger size first: growing the workspace allocates and synchronizes).
  *   A captured diag-outer or delta call that would need a larger workspace
- *   returns LRS_E_UNSUPPORTED and captures nothing.
+ *   returns LRS_E_UNSUPPORTED and captures nothing.  A graph keeps the
+ *   workspace it was captured with: once a context has served a captured
+ *   call, a later uncaptured call that grows a workspace keeps the old buffer
+ *   alive (until lrs_context_destroy) rather than freeing it, so earlier
+ *   graphs stay valid.  Destroying the context invalidates every graph that
+ *   captured its calls.
  *   Every call keeps no per-call state on the host once captured, so a
  *   replay recomputes it on the captured buffers' current contents.  The
  *   elementwise look-back schedule takes a fresh tile-counter base and

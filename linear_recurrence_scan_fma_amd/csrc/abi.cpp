@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "lrs_abi.h"
 #include "lrs_internal.h"
@@ -35,6 +36,12 @@ struct LrsContext {
     size_t diag_ws_bytes = 0;
     hipStream_t last_stream = nullptr;
     bool used = false;
+    // Set once a diag-outer or delta call has been captured into a HIP graph:
+    // such a graph keeps the workspace pointer it was captured with, so from
+    // then on a grown workspace's old buffer is retired (kept until
+    // lrs_context_destroy) instead of freed.
+    bool captured = false;
+    std::vector<void*> retired;
 };
 
 namespace {
@@ -355,6 +362,7 @@ LRS_API void lrs_context_destroy(LrsContext* ctx) {
         if (ctx->delta_ws) (void)hipFree(ctx->delta_ws);
         if (ctx->diag_ws) (void)hipFree(ctx->diag_ws);
         if (ctx->fixed) (void)hipFree(ctx->fixed);
+        for (void* r : ctx->retired) (void)hipFree(r);
     }
     delete ctx;
 }
@@ -436,13 +444,19 @@ namespace {
 // Grows a context-owned device buffer to `need` bytes.  The old buffer is
 // released only after the device has finished all earlier work (see
 // grow_words).  Under graph capture nothing may allocate or wait: growth is
-// refused there (the caller enqueues nothing and returns the status).
-lrs_status grow_workspace(void*& ptr, size_t& cap, size_t need, hipStream_t stream) {
+// refused there (the caller enqueues nothing and returns the status).  Once a
+// call of this context has been captured, a graph may still hold the old
+// buffer, so it is retired instead of freed (lrs_context_destroy frees it).
+lrs_status grow_workspace(LrsContext* ctx, void*& ptr, size_t& cap, size_t need, hipStream_t stream) {
     if (need <= cap) return LRS_OK;
     if (capturing(stream)) return LRS_E_UNSUPPORTED;
     if (ptr) {
-        if (hipDeviceSynchronize() != hipSuccess) return LRS_E_DEVICE;
-        (void)hipFree(ptr);
+        if (ctx->captured) {
+            ctx->retired.push_back(ptr);
+        } else {
+            if (hipDeviceSynchronize() != hipSuccess) return LRS_E_DEVICE;
+            (void)hipFree(ptr);
+        }
         ptr = nullptr;
         cap = 0;
     }
@@ -549,10 +563,11 @@ lrs_status scan_diag_outer_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf
     // (the prefix over segments launches up to 16 workgroups per (batch, head, V-tile))
     if (grid > 0x7fffffff || static_cast<int64_t>(B) * H * plan.vtiles * 16 > 0x7fffffff) return LRS_E_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const lrs_status ws = grow_workspace(ctx->diag_ws, ctx->diag_ws_bytes,
+    const lrs_status ws = grow_workspace(ctx, ctx->diag_ws, ctx->diag_ws_bytes,
                                          lrs::diag_outer_workspace_bytes(B, H, K, V, plan.nseg), st);
     if (ws != LRS_OK) return ws;
     if (lrs::launch_scan_diag_outer(p, plan, ctx->diag_ws, st) != hipSuccess) return LRS_E_DEVICE;
+    if (capturing(st)) ctx->captured = true;
     ctx->last_stream = st;
     ctx->used = true;
     return LRS_OK;
@@ -632,8 +647,8 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     hipStream_t st = static_cast<hipStream_t>(stream);
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return LRS_E_DEVICE;
-    const lrs_status ws =
-        grow_workspace(ctx->delta_ws, ctx->delta_ws_bytes, lrs::delta_workspace_bytes(B, T, H, K, decay), st);
+    const lrs_status ws = grow_workspace(ctx, ctx->delta_ws, ctx->delta_ws_bytes,
+                                         lrs::delta_workspace_bytes(B, T, H, K, decay), st);
     if (ws != LRS_OK) return ws;
     lrs::DeltaParams p{};
     p.q = q;
@@ -655,6 +670,7 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
              row_bytes < (int64_t{1} << 31)) ? 1 : 0;
     if (lrs::launch_scan_delta(p, ctx->delta_ws, st) != hipSuccess) return LRS_E_DEVICE;
+    if (capturing(st)) ctx->captured = true;
     ctx->last_stream = st;
     ctx->used = true;
     return LRS_OK;

@@ -44,6 +44,8 @@
 //    inside the fp32/bf16 range while the chunk's decay is below 60 nats on every
 //    key (GLA-shaped gates use a few nats); otherwise the chunk evaluates P pair
 //    by pair with exact exponentials and reads out with q o e^{G_t} and S0.
+#include <atomic>
+
 #include "lrs_internal.h"
 #include "mfma_util.h"
 
@@ -934,10 +936,13 @@ hipError_t launch_t(const DiagArgs& a, bool vec, hipStream_t stream) {
 }
 
 // Output-pass workgroups that fit on one compute unit at once (LDS and
-// registers), measured once per kernel variant.
+// registers), measured once per kernel variant.  Host threads driving separate
+// contexts may ask at the same time: the cache is a relaxed atomic, and a
+// race only repeats the (idempotent) query.
 template <int MODE, int KP, int WPB, bool VEC, bool KK>
 int resident_blocks() {
-    static int n = 0;
+    static std::atomic<int> cached{0};
+    int n = cached.load(std::memory_order_relaxed);
     if (n == 0) {
         int m = 1;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, diag_outer_kernel<MODE, KP, WPB, VEC, false, KK>,
@@ -945,6 +950,7 @@ int resident_blocks() {
             m < 1)
             m = 1;
         n = m;
+        cached.store(n, std::memory_order_relaxed);
     }
     return n;
 }

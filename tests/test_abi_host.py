@@ -110,3 +110,4 @@ def test_context_create_without_gpu_is_unsupported(lib):
     h = ctypes.c_void_p()
     assert lib.lrs_context_create(0, ctypes.byref(h)) == binding.LRS_E_UNSUPPORTED
     assert not h.value
+

@@ -211,6 +211,64 @@ def test_graph_capture_refuses_workspace_growth():
         assert torch.isfinite(o2).all() and torch.equal(o2, o3) and torch.equal(fin2, fin3)
 
 
+@pytest.mark.parametrize("kind", ["delta", "diag"])
+def test_graph_replay_after_eager_workspace_growth(kind):
+    """A graph captured on a context keeps the workspace it was captured with.
+    An eager call that then grows the context's workspace must not free it:
+    replaying the graph afterwards still equals an eager call on the captured
+    shape (and the grown, eager path is unaffected)."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    with binding.Context(0) as c:
+        small = dict(B=1, T=200, H=2, K=64, V=64)
+        large = dict(B=2, T=900, H=4, K=64, V=64)
+        if kind == "delta":
+            gen, names = inputs.deltanet, ("q", "k", "v", "beta")
+        else:
+            gen, names = inputs.gla, ("q", "k", "v", "g")
+            binding.lrs_context_set_param(c, binding.LRS_PARAM_DIAG_SEGMENTS, 3)
+        d = gen(**small, seed=1901)
+        x = [d[n].to("cuda:0") for n in names]
+        B, T, H, K, V = (small[n] for n in ("B", "T", "H", "K", "V"))
+        o = torch.empty((B, T, H, V), device="cuda:0")
+        fin = torch.empty((B, H, K, V), device="cuda:0")
+        if kind == "delta":
+            run = lambda: binding.lrs_scan_delta(c, *x, 1.0, None, o, fin)  # noqa: E731
+        else:
+            run = lambda: binding.lrs_scan_diag_outer(c, *x, 1, None, d["scale"], None, o, fin)  # noqa: E731
+        say(f"graph: {kind}, capture then grow the workspace eagerly, then replay")
+        run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(g, stream=st):
+                run()
+        torch.cuda.synchronize()
+        # an eager call on a larger shape grows the workspace
+        dl = gen(**large, seed=1902)
+        xl = [dl[n].to("cuda:0") for n in names]
+        if kind == "delta":
+            ol, fl = binding.scan_delta(c, *xl, 1.0)
+        else:
+            ol, fl = binding.scan_diag_outer(c, *xl, 1, None, dl["scale"])
+        torch.cuda.synchronize()
+        assert torch.isfinite(ol).all() and torch.isfinite(fl).all()
+        for i in range(3):
+            for dst, n in zip(x, names):
+                dst.copy_(gen(**small, seed=1910 + i)[n])
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got = (o.clone(), fin.clone())
+            run()
+            torch.cuda.synchronize()
+            assert torch.equal(got[0], o) and torch.equal(got[1], fin), f"replay {i}"
+        del g
+        torch.cuda.synchronize()
+
+
 def test_graph_diag_outer_keyscale(ctx):
     B, T, H, K, V = 1, 300, 2, 64, 64
     names = ("q", "k", "v", "g", "k_scale_key")

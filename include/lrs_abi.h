@@ -99,7 +99,7 @@ extern "C" {
 
 /* ---- version and capabilities [SunnyNet log §6] ------------------------ */
 #define LRS_ABI_VERSION_MAJOR 1
-#define LRS_ABI_VERSION_MINOR 1
+#define LRS_ABI_VERSION_MINOR 2
 #define LRS_ABI_VERSION_PATCH 0
 #define LRS_ABI_VERSION \
     ((LRS_ABI_VERSION_MAJOR << 16) | (LRS_ABI_VERSION_MINOR << 8) | LRS_ABI_VERSION_PATCH)
@@ -423,6 +423,36 @@ lrs_status lrs_scan_delta_decay(LrsContext* ctx, const lrs_bf16* q, const lrs_bf
                                 const lrs_bf16* v, const float* g, const float* beta, float scale,
                                 const float* s0, float* o, float* s_final, int32_t B, int32_t T,
                                 int32_t H, int32_t K, int32_t V, void* stream);
+
+/* ---- allocation-free gated scan (since 1.2) --------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * scan as lrs_scan_gated ([SunnyNet log §2.1]), without a context: it runs on
+ * the calling thread's current HIP device and calls no hipMalloc, hipFree or
+ * other allocating routine.  Its look-back scratch (tile counter, error flag
+ * and status words) is a static device array of 64 MiB that the library holds
+ * on each GPU it runs on until the process ends.
+ *
+ *   a, u, s0, s, s_final   as lrs_scan_gated (s0 may be NULL)
+ *
+ * Limit: the look-back needs 24 bytes per channel and 128-step chunk (32-step
+ * chunks below T = 512); when the time axis spans two or more chunks those
+ * words must fit in the scratch, 64 MiB - 256 B (e.g. B=16, T=8192, N=2048
+ * needs 48 MiB).  Larger shapes return LRS_E_UNSUPPORTED before anything is
+ * enqueued or any HIP call is made.  Under graph capture the call takes the
+ * stream schedule, which uses no scratch.
+ * Every call on one GPU shares that GPU's scratch (the status words carry a
+ * per-call tag, so nothing needs clearing between calls; the library zeroes
+ * the array with a fill kernel on its first use on a device).  Calls that
+ * overlap on one GPU -- on different streams, or from threads that do not
+ * order their streams -- race on it and give wrong results; calls issued one
+ * after another on one stream are safe from any thread.  A look-back wait
+ * that expires (it should never) leaves NaN outputs; there is no context to
+ * report it.  Errors as lrs_scan_gated, plus LRS_E_DEVICE when no HIP device
+ * is current.
+ */
+lrs_status lrs_scan_gated_noalloc(const float* a, const float* u, const float* s0, float* s,
+                                  float* s_final, int32_t B, int32_t T, int32_t N, void* stream);
 
 #ifdef __cplusplus
 }

@@ -63,6 +63,7 @@ SIGNATURES = {
                               _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_delta_decay": (_I32, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P,
                                     _I32, _I32, _I32, _I32, _I32, _P]),
+    "lrs_scan_gated_noalloc": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
 }
 
 _lib = None
@@ -211,6 +212,25 @@ def lrs_scan_fma(ctx, a, b, s0, s, s_final, stream=None) -> None:
 def lrs_scan_gated(ctx, a, u, s0, s, s_final, stream=None) -> None:
     """s_t = a_t s_{t-1} + (1 - a_t) u_t; shapes as lrs_scan_fma."""
     _elem("lrs_scan_gated", ctx, a, u, s0, s, s_final, stream)
+
+
+def lrs_scan_gated_noalloc(a, u, s0, s, s_final, stream=None) -> None:
+    """lrs_scan_gated without a context or any allocation, on the tensors'
+    device (which must be the current device); shapes as lrs_scan_gated."""
+    import torch
+
+    B, T, N = a.shape
+    d = a.device.index if a.device.type == "cuda" else -1
+    if d != torch.cuda.current_device():
+        raise ValueError("lrs_scan_gated_noalloc runs on the current device: the tensors must live there")
+    f32 = torch.float32
+    args = (
+        _ptr(a, f32, (B, T, N), "a", d), _ptr(u, f32, (B, T, N), "u", d),
+        _ptr(s0, f32, (B, N), "s0", d), _ptr(s, f32, (B, T, N), "s", d),
+        _ptr(s_final, f32, (B, N), "s_final", d),
+    )
+    st = lib().lrs_scan_gated_noalloc(*args, B, T, N, _stream(stream, d))
+    _check("lrs_scan_gated_noalloc", st)
 
 
 def lrs_scan_fma_backward(ctx, a, s0, s, ds, ds_final, da, db, ds0, stream=None) -> None:

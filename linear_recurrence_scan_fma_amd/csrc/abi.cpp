@@ -415,6 +415,52 @@ LRS_API lrs_status lrs_scan_gated(LrsContext* ctx, const float* a, const float* 
     return scan_elem(ctx, true, a, u, s0, s, s_final, B, T, N, stream);
 }
 
+LRS_API lrs_status lrs_scan_gated_noalloc(const float* a, const float* u, const float* s0, float* s,
+                                          float* s_final, int32_t B, int32_t T, int32_t N, void* stream_ptr) {
+    if (!a || !u || !s || !s_final) return LRS_E_INVAL;
+    int64_t seq = 0;
+    if (!elem_dims_ok(B, T, N, seq)) return LRS_E_INVAL;
+    if (!aligned(a, 4) || !aligned(u, 4) || !aligned(s0, 4) || !aligned(s, 4) || !aligned(s_final, 4))
+        return LRS_E_INVAL;
+    const size_t seq_bytes = static_cast<size_t>(seq) * sizeof(float);
+    const size_t st_bytes = static_cast<size_t>(B) * N * sizeof(float);
+    const Span ins[] = {{a, seq_bytes}, {u, seq_bytes}, {s0, st_bytes}};
+    const Span outs[] = {{s, seq_bytes}, {s_final, st_bytes}};
+    if (!outputs_disjoint(outs, 2, ins, 3)) return LRS_E_INVAL;
+    // the size limit is a property of the shape alone, checked before any HIP call
+    const bool al16 = aligned(a, 16) && aligned(u, 16) && aligned(s, 16);
+    const lrs::ElemPlan lb = lrs::elem_plan(B, T, N, al16, lrs::kElemLookback);
+    const bool multi_chunk = lb.chunks > 1;
+    if (multi_chunk && lb.words > lrs::noalloc_words_capacity()) return LRS_E_UNSUPPORTED;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    int device = -1;
+    if (hipGetDevice(&device) != hipSuccess) {
+        (void)hipGetLastError();
+        return LRS_E_DEVICE;
+    }
+    // look-back whenever the time axis spans two chunks, as the automatic
+    // schedule does; under graph capture the stream schedule (no scratch, and
+    // no host-side epoch or counter base for a replay to reuse)
+    const int ksched = multi_chunk && !capturing(stream) ? lrs::kElemLookback : lrs::kElemStream;
+    const lrs::ElemPlan plan = ksched == lrs::kElemLookback ? lb : lrs::elem_plan(B, T, N, al16, ksched);
+    if (plan.grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
+    lrs::ElemParams p{};
+    p.a = a;
+    p.x = u;
+    p.s0 = s0;
+    p.s = s;
+    p.s_final = s_final;
+    p.B = B;
+    p.T = T;
+    p.N = N;
+    p.gated = true;
+    p.schedule = ksched;
+    const int rc = lrs::launch_scan_elem_noalloc(p, plan, device, stream);
+    if (rc == lrs::kNoallocUnsupported) return LRS_E_UNSUPPORTED;
+    return rc == lrs::kNoallocOk ? LRS_OK : LRS_E_DEVICE;
+}
+
 LRS_API lrs_status lrs_scan_fma_backward(LrsContext* ctx, const float* a, const float* s0,
                                          const float* s, const float* ds, const float* ds_final,
                                          float* da, float* db, float* ds0, int32_t B, int32_t T,

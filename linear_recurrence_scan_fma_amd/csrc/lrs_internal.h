@@ -64,6 +64,19 @@ struct ElemBwdParams {
 };
 hipError_t launch_scan_elem_bwd(const ElemBwdParams& p, const ElemPlan& plan, hipStream_t stream);
 
+// Allocation-free variant of launch_scan_elem: the look-back scratch (tile
+// counter, error flag, status words) is a static device array of
+// kNoallocScratchBytes per GPU.  Resolves this device's copy on its first use
+// (hipGetSymbolAddress with the device current), takes the look-back epoch
+// and counter base from per-device host state, launches, and advances that
+// state, all under one lock.  `p` carries the shape, form and resolved
+// schedule; its look-back fields are filled here.  Returns a kNoalloc* code.
+constexpr size_t kNoallocScratchBytes = size_t{64} << 20;
+enum NoallocStatus : int { kNoallocOk = 0, kNoallocUnsupported = 1, kNoallocDevice = 2 };
+// Status words the scratch holds (the look-back limit of the variant).
+size_t noalloc_words_capacity();
+int launch_scan_elem_noalloc(ElemParams p, const ElemPlan& plan, int device, hipStream_t stream);
+
 // One in-place step s = a s + x (or the gated form) over n channels.
 hipError_t launch_step_elem(bool gated, const float* a, const float* x, float* s, int64_t n, bool aligned16,
                             int num_cus, hipStream_t stream);

@@ -36,6 +36,8 @@
 //                running tile has already been taken by a running or finished
 //                workgroup, and aggregates never wait on anything: the walk
 //                always terminates.  It is additionally bounded in wall time.
+#include <mutex>
+
 #include "lrs_internal.h"
 
 namespace lrs {
@@ -732,6 +734,77 @@ hipError_t launch_step_elem(bool gated, const float* a, const float* x, float* s
         else hipLaunchKernelGGL((step_elem_kernel<false, false>), grid, block, 0, stream, a, x, s, n);
     }
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the look-back scratch in a static device array
+// ---------------------------------------------------------------------------
+// The tile counter, the error flag and the status words of the look-back live
+// in `scratch`, one copy per GPU that loads the library, held until the
+// process ends.  In host code `scratch` names a host-side stand-in: its device
+// address (per device) comes from hipGetSymbolAddress and is the only form
+// ever handed to a kernel or a fill.
+namespace {
+
+constexpr size_t kScratchHeaderWords = 32;   // [0] tile counter, [1] error flag, rest unused
+constexpr int kMaxNoallocDevices = 64;
+
+static __device__ __align__(256) unsigned long long scratch[kNoallocScratchBytes / sizeof(unsigned long long)];
+
+struct NoallocDevice {
+    unsigned long long* ptr = nullptr;       // this device's copy of `scratch`
+    bool cleared = false;                    // every word zeroed (epoch tag 0) once
+    unsigned int epoch = 0;                  // last epoch tag used
+    unsigned long long counter_base = 0;     // tiles taken from the counter so far
+};
+
+std::mutex g_noalloc_mu;
+NoallocDevice g_noalloc[kMaxNoallocDevices];
+
+}  // namespace
+
+size_t noalloc_words_capacity() { return kNoallocScratchBytes / sizeof(unsigned long long) - kScratchHeaderWords; }
+
+int launch_scan_elem_noalloc(ElemParams p, const ElemPlan& plan, int device, hipStream_t stream) {
+    const bool lookback = p.schedule == kElemLookback;
+    if (device < 0 || device >= kMaxNoallocDevices) return kNoallocUnsupported;
+    if (lookback && plan.words > noalloc_words_capacity()) return kNoallocUnsupported;
+    // one lock over set-up, launch and bookkeeping: the counter base of a
+    // launch must be the sum of the grids launched before it on this device
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    NoallocDevice& d = g_noalloc[device];
+    if (!d.ptr) {
+        // set-up, once per device, with that device current (the caller's)
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return kNoallocDevice;
+        }
+        d.ptr = static_cast<unsigned long long*>(ptr);
+    }
+    if (lookback) {
+        if (!d.cleared || d.epoch == 0xffffffffu) {
+            // tags must never repeat without a clear: zero every word (and the
+            // counter, whose base restarts at 0) with a fill kernel on the stream
+            if (launch_fill_zero_u64(d.ptr, kNoallocScratchBytes / sizeof(unsigned long long), stream) !=
+                hipSuccess)
+                return kNoallocDevice;
+            d.cleared = true;
+            d.epoch = 0;
+            d.counter_base = 0;
+        }
+        p.epoch = d.epoch + 1;
+        p.counter = d.ptr;
+        p.error_flag = reinterpret_cast<unsigned int*>(d.ptr + 1);
+        p.words = d.ptr + kScratchHeaderWords;
+        p.counter_base = d.counter_base;
+    }
+    if (launch_scan_elem(p, plan, stream) != hipSuccess) return kNoallocDevice;
+    if (lookback) {
+        d.epoch = p.epoch;
+        d.counter_base += static_cast<unsigned long long>(plan.grid);
+    }
+    return kNoallocOk;
 }
 
 hipError_t launch_fill_zero_u64(unsigned long long* p, size_t n, hipStream_t stream) {

@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     for n in names:
         assert hasattr(lib, n), f"{n} declared in lrs_abi.h but not exported"
     assert set(names) == set(binding.SIGNATURES), "binding and header disagree"
@@ -57,7 +57,7 @@ def test_python_mirrors_header_constants():
 
 def test_version_and_check(lib):
     v = binding.lrs_abi_version()
-    assert v == (1 << 16) | (1 << 8) | 0
+    assert v == (1 << 16) | (2 << 8) | 0
     assert binding.LRS_ABI_VERSION_MAJOR == 1
     assert binding.lrs_abi_check(1) == binding.LRS_OK
     assert binding.lrs_abi_check(2) == binding.LRS_E_UNSUPPORTED
@@ -111,3 +111,22 @@ def test_context_create_without_gpu_is_unsupported(lib):
     assert lib.lrs_context_create(0, ctypes.byref(h)) == binding.LRS_E_UNSUPPORTED
     assert not h.value
 
+
+def test_noalloc_entry_validates_before_any_hip_call(lib):
+    """The allocation-free gated scan rejects bad arguments (LRS_E_INVAL) and
+    shapes whose look-back words exceed its static scratch
+    (LRS_E_UNSUPPORTED) on the host, before any HIP call: both paths run here
+    without a GPU.  The pointers are never dereferenced."""
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    f = lib.lrs_scan_gated_noalloc
+    assert f(None, fake, None, fake, fake, 1, 1, 1, None) == binding.LRS_E_INVAL
+    assert f(fake, fake, None, fake, fake, 0, 1, 1, None) == binding.LRS_E_INVAL
+    gib = 1 << 36   # 64 GiB apart: the fake tensors below do not overlap
+    a, u, s, fin = (P(gib * (i + 1)) for i in range(4))
+    assert f(a, u, None, a, fin, 1, 64, 64, None) == binding.LRS_E_INVAL          # output aliases input
+    assert f(a, P(gib + 2), None, s, fin, 1, 64, 64, None) == binding.LRS_E_INVAL  # misaligned u
+    # 2^20 steps x 4096 channels: 8192 chunks x 64 channel tiles x 192 words
+    # = 768 MiB of status words, beyond the 64 MiB scratch
+    assert f(a, u, None, s, fin, 1, 1 << 20, 4096, None) == binding.LRS_E_UNSUPPORTED
+    # the headline shape fits (48 MiB of words); not called here: it would launch

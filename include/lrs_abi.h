@@ -124,6 +124,7 @@ enum {
 #define LRS_CAP_SCAN_DELTA_DECAY (1u << 6)  /* since 1.1 */
 #define LRS_CAP_SCAN_DIAG_KEYSCALE (1u << 7) /* since 1.1 */
 #define LRS_CAP_SCAN_DIAG_EPILOGUE (1u << 8) /* since 1.1 */
+#define LRS_CAP_SCAN_DELTA_OUT  (1u << 9)   /* since 1.2 */
 
 /* Output epilogues and dtypes of lrs_scan_diag_outer_epilogue (since 1.1). */
 enum { LRS_EPILOGUE_NONE = 0, LRS_EPILOGUE_SKIP = 1, LRS_EPILOGUE_NORM_GATE = 2 };
@@ -423,6 +424,26 @@ lrs_status lrs_scan_delta_decay(LrsContext* ctx, const lrs_bf16* q, const lrs_bf
                                 const lrs_bf16* v, const float* g, const float* beta, float scale,
                                 const float* s0, float* o, float* s_final, int32_t B, int32_t T,
                                 int32_t H, int32_t K, int32_t V, void* stream);
+
+/* ---- delta rule with an fp32 or bf16 output (since 1.2) --------------------
+ * lrs_scan_delta (g == NULL) or lrs_scan_delta_decay (g != NULL) with the
+ * output written as out_dtype: LRS_DTYPE_F32, or LRS_DTYPE_BF16 rounded to
+ * nearest even from the fp32 result.  DeltaNet's update and readout
+ * [SunnyNet log §4.2]; the per-key decay of RWKV-7 [SunnyNet log §5.1].
+ *
+ *   g          fp32 [B,T,H,K] per-key log-decay, or NULL for the plain delta rule
+ *   out_dtype  LRS_DTYPE_F32 or LRS_DTYPE_BF16
+ *   o          [B,T,H,V] of out_dtype (device pointer, 4- or 2-byte aligned)
+ *
+ * The state stays fp32 (s0, s_final).  A bf16 o halves the output bytes, the
+ * largest single term of these scans' traffic (39% of the DeltaNet
+ * workload's at fp32).  Other arguments, limits, workspace and errors as
+ * lrs_scan_delta (g == NULL) or lrs_scan_delta_decay.
+ */
+lrs_status lrs_scan_delta_out(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k, const lrs_bf16* v,
+                              const float* g, const float* beta, float scale, const float* s0,
+                              int32_t out_dtype, void* o, float* s_final, int32_t B, int32_t T, int32_t H,
+                              int32_t K, int32_t V, void* stream);
 
 /* ---- allocation-free gated scan (since 1.2) --------------------------------
  * For callers that cannot allocate device memory: code under HIP graph

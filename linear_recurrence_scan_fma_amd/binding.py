@@ -25,7 +25,7 @@ LRS_OK, LRS_E_INVAL, LRS_E_NOMEM, LRS_E_IO, LRS_E_FORMAT, LRS_E_UNSUPPORTED, LRS
     0, -1, -2, -3, -4, -5, -6)
 LRS_CAP_SCAN_FMA, LRS_CAP_SCAN_GATED, LRS_CAP_SCAN_DIAG_OUTER, LRS_CAP_SCAN_DELTA = 1, 2, 4, 8
 LRS_CAP_ELEM_BACKWARD, LRS_CAP_ELEM_STEP, LRS_CAP_SCAN_DELTA_DECAY = 16, 32, 64
-LRS_CAP_SCAN_DIAG_KEYSCALE, LRS_CAP_SCAN_DIAG_EPILOGUE = 128, 256
+LRS_CAP_SCAN_DIAG_KEYSCALE, LRS_CAP_SCAN_DIAG_EPILOGUE, LRS_CAP_SCAN_DELTA_OUT = 128, 256, 512
 LRS_EPILOGUE_NONE, LRS_EPILOGUE_SKIP, LRS_EPILOGUE_NORM_GATE = 0, 1, 2
 LRS_DTYPE_F32, LRS_DTYPE_BF16 = 0, 1
 LRS_PARAM_ELEM_SCHEDULE = 1
@@ -63,6 +63,8 @@ SIGNATURES = {
                               _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_delta_decay": (_I32, [_P, _P, _P, _P, _P, _P, _F, _P, _P, _P,
                                     _I32, _I32, _I32, _I32, _I32, _P]),
+    "lrs_scan_delta_out": (_I32, [_P, _P, _P, _P, _P, _P, _F, _P, _I32, _P, _P,
+                                  _I32, _I32, _I32, _I32, _I32, _P]),
     "lrs_scan_gated_noalloc": (_I32, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _P]),
 }
 
@@ -404,6 +406,27 @@ def lrs_scan_delta_decay(ctx, q, k, v, g, beta, scale, s0, o, s_final, stream=No
     _check("lrs_scan_delta_decay", st)
 
 
+def lrs_scan_delta_out(ctx, q, k, v, g, beta, scale, s0, out_dtype, o, s_final, stream=None) -> None:
+    """lrs_scan_delta (g None) or lrs_scan_delta_decay (g [B,T,H,K] fp32) with the
+    output o [B,T,H,V] written as out_dtype (LRS_DTYPE_F32: fp32 tensor,
+    LRS_DTYPE_BF16: bf16 tensor)."""
+    import torch
+
+    B, T, H, K = q.shape
+    V = v.shape[3]
+    d = ctx.device
+    bf, f32 = torch.bfloat16, torch.float32
+    odt = bf if out_dtype == LRS_DTYPE_BF16 else f32
+    args = (
+        _ptr(q, bf, (B, T, H, K), "q", d), _ptr(k, bf, (B, T, H, K), "k", d),
+        _ptr(v, bf, (B, T, H, V), "v", d), _ptr(g, f32, (B, T, H, K), "g", d),
+        _ptr(beta, f32, (B, T, H), "beta", d), float(scale), _ptr(s0, f32, (B, H, K, V), "s0", d),
+        int(out_dtype), _ptr(o, odt, (B, T, H, V), "o", d), _ptr(s_final, f32, (B, H, K, V), "s_final", d),
+    )
+    st = lib().lrs_scan_delta_out(ctx.handle, *args, B, T, H, K, V, _stream(stream, d))
+    _check("lrs_scan_delta_out", st)
+
+
 # ---- allocating conveniences (still marshalling only) -------------------------
 def scan_elementwise(ctx, kind, a, x, s0=None, stream=None):
     """Allocates s and s_final and runs lrs_scan_fma (kind 'fma') or lrs_scan_gated."""
@@ -487,4 +510,16 @@ def scan_diag_outer_epilogue(ctx, q, k, v, g, decay_mode, k_scale=None, scale=1.
     fin = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
     lrs_scan_diag_outer_epilogue(ctx, q, k, v, g, decay_mode, k_scale, scale, s0, epilogue, d_skip, gate,
                                  norm_weight, eps, out_dtype, o, fin, stream)
+    return o, fin
+
+
+def scan_delta_out(ctx, q, k, v, beta, g=None, scale=1.0, s0=None, out_dtype=LRS_DTYPE_BF16, stream=None):
+    import torch
+
+    B, T, H, K = q.shape
+    V = v.shape[3]
+    odt = torch.bfloat16 if out_dtype == LRS_DTYPE_BF16 else torch.float32
+    o = torch.empty((B, T, H, V), dtype=odt, device=q.device)
+    fin = torch.empty((B, H, K, V), dtype=torch.float32, device=q.device)
+    lrs_scan_delta_out(ctx, q, k, v, g, beta, scale, s0, out_dtype, o, fin, stream)
     return o, fin

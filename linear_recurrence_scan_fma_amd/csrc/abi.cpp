@@ -300,7 +300,7 @@ LRS_API lrs_status lrs_abi_check(int32_t caller_major) {
 LRS_API uint32_t lrs_abi_caps(void) {
     return LRS_CAP_SCAN_FMA | LRS_CAP_SCAN_GATED | LRS_CAP_SCAN_DIAG_OUTER | LRS_CAP_SCAN_DELTA |
            LRS_CAP_ELEM_BACKWARD | LRS_CAP_ELEM_STEP | LRS_CAP_SCAN_DELTA_DECAY |
-           LRS_CAP_SCAN_DIAG_KEYSCALE | LRS_CAP_SCAN_DIAG_EPILOGUE;
+           LRS_CAP_SCAN_DIAG_KEYSCALE | LRS_CAP_SCAN_DIAG_EPILOGUE | LRS_CAP_SCAN_DELTA_OUT;
 }
 
 LRS_API const char* lrs_status_string(lrs_status status) {
@@ -659,17 +659,20 @@ LRS_API lrs_status lrs_scan_diag_outer_keyscale(LrsContext* ctx, const lrs_bf16*
 
 namespace {
 
-// Shared by the plain and decayed delta-rule calls (g == NULL: plain).
+// Shared by the plain and decayed delta-rule calls (g == NULL: plain), with an
+// fp32 or bf16 output.
 lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k, const lrs_bf16* v,
-                           const float* g, const float* beta, float scale, const float* s0, float* o,
+                           const float* g, const float* beta, float scale, const float* s0, void* o,
                            float* s_final, int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
-                           void* stream) {
+                           void* stream, int32_t out_dtype = LRS_DTYPE_F32) {
     const bool decay = g != nullptr;
     if (!ctx || !q || !k || !v || !beta || !o || !s_final) return LRS_E_INVAL;
+    if (out_dtype != LRS_DTYPE_F32 && out_dtype != LRS_DTYPE_BF16) return LRS_E_INVAL;
+    const size_t osz = out_dtype == LRS_DTYPE_BF16 ? 2 : 4;
     if (B < 1 || T < 1 || H < 1 || K < 1 || V < 1) return LRS_E_INVAL;
     if (K > (decay ? lrs::delta_decay_max_k() : 128)) return LRS_E_UNSUPPORTED;
     if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(g, 4) || !aligned(beta, 4) ||
-        !aligned(s0, 4) || !aligned(o, 4) || !aligned(s_final, 4))
+        !aligned(s0, 4) || !aligned(o, osz) || !aligned(s_final, 4))
         return LRS_E_INVAL;
     int64_t bth = B;
     if (!mul_ok(bth, T) || !mul_ok(bth, H)) return LRS_E_INVAL;
@@ -677,7 +680,7 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     if (!mul_ok(nqk, K) || !mul_ok(nv, V) || !mul_ok(nst, H) || !mul_ok(nst, K) || !mul_ok(nst, V))
         return LRS_E_INVAL;
     const size_t bqk = static_cast<size_t>(nqk) * 2, bv = static_cast<size_t>(nv) * 2;
-    const size_t bb = static_cast<size_t>(bth) * 4, bo = static_cast<size_t>(nv) * 4;
+    const size_t bb = static_cast<size_t>(bth) * 4, bo = static_cast<size_t>(nv) * osz;
     const size_t bst = static_cast<size_t>(nst) * 4, bg = decay ? static_cast<size_t>(nqk) * 4 : 0;
     const Span ins[] = {{q, bqk}, {k, bqk}, {v, bv}, {beta, bb}, {s0, bst}, {g, bg}};
     const Span outs[] = {{o, bo}, {s_final, bst}};
@@ -704,13 +707,14 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     p.beta = beta;
     p.scale = scale;
     p.s0 = s0;
-    p.o = o;
+    p.o = static_cast<float*>(o);
     p.s_final = s_final;
     p.B = B;
     p.T = T;
     p.H = H;
     p.K = K;
     p.V = V;
+    p.out_bf16 = out_dtype == LRS_DTYPE_BF16 ? 1 : 0;
     // the vector path addresses one batch row of each tensor with 32-bit buffer offsets
     const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
@@ -738,4 +742,11 @@ LRS_API lrs_status lrs_scan_delta_decay(LrsContext* ctx, const lrs_bf16* q, cons
                                         void* stream) {
     if (!g) return LRS_E_INVAL;
     return scan_delta_impl(ctx, q, k, v, g, beta, scale, s0, o, s_final, B, T, H, K, V, stream);
+}
+
+LRS_API lrs_status lrs_scan_delta_out(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k, const lrs_bf16* v,
+                                      const float* g, const float* beta, float scale, const float* s0,
+                                      int32_t out_dtype, void* o, float* s_final, int32_t B, int32_t T, int32_t H,
+                                      int32_t K, int32_t V, void* stream) {
+    return scan_delta_impl(ctx, q, k, v, g, beta, scale, s0, o, s_final, B, T, H, K, V, stream, out_dtype);
 }

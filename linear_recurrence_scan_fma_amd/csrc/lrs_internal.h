@@ -140,6 +140,7 @@ struct DeltaParams {
     float* s_final;
     int B, T, H, K, V;
     int vec;               // 16-byte vector loads allowed
+    int out_bf16;          // o is bf16 (round to nearest even) instead of fp32
 };
 
 int delta_vtile();

@@ -88,6 +88,7 @@ struct DeltaArgs {
     float scale;
     int vtiles;
     int nchunks;
+    int out_bf16;     // o is bf16 (round to nearest even) instead of fp32
 };
 
 __device__ __forceinline__ void tri_block(int n, int& i, int& j) {
@@ -688,6 +689,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     __shared__ __align__(16) u16 sRTl[VT * LDL];
     __shared__ __align__(16) u16 sSh[VT * LDK];      // S^T hi/lo entering the chunk
     __shared__ __align__(16) u16 sSl[VT * LDK];
+    constexpr int LDO = 20;                          // fp32 row stride of the output tiles
+    __shared__ __align__(16) float sO[4][16 * LDO];  // each wave's 16 x 16 output tile
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
@@ -863,6 +866,39 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     load_w(0, wcur, ecur);
 
     const int arow = 16 * wave + c16;    // operand row of this wave
+    // A chunk's outputs wait in this wave's LDS tile (rows 16 wave .., the 16
+    // columns) and are stored during the next chunk, 16 bytes per lane (one
+    // store instruction per wave instead of four of 4-byte pieces), so the wait
+    // for this wave's loads at the top of a chunk does not wait on them.
+    float* so = sO[wave];
+    auto store_outputs = [&](int64_t tc) {
+        const int row = lane >> 2, cc = 4 * (lane & 3), col = v0 + cc;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(so + row * LDO + cc);
+        const int64_t t = tc + 16 * wave + row;
+        if (t < T) {
+            const int64_t oi = ((b * T + t) * H + h) * static_cast<int64_t>(V) + col;
+            if (p.out_bf16) {
+                u16* dst = reinterpret_cast<u16*>(p.o) + oi;
+                if (VEC && col + 4 <= V) {
+                    const uint32_t w0 = f2bf(x[0]) | (static_cast<uint32_t>(f2bf(x[1])) << 16);
+                    const uint32_t w1 = f2bf(x[2]) | (static_cast<uint32_t>(f2bf(x[3])) << 16);
+                    *reinterpret_cast<u32x2*>(dst) = u32x2{w0, w1};
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < V) dst[e] = f2bf(x[e]);
+                }
+            } else {
+                if (VEC && col + 4 <= V) {
+                    *reinterpret_cast<f32x4*>(p.o + oi) = x;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (col + e < V) p.o[oi + e] = x[e];
+                }
+            }
+        }
+    };
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
         const unsigned char* st = sIn + (c & 1) * STAGE;
@@ -872,6 +908,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             fetch(c + 1, (c + 1) & 1);
             load_w(c + 1, wnxt, enxt);
         }
+        if (c > 0) store_outputs(t0 - L);
 
         // ---- 1: Y = K S0, O1 = Q S0 (row block = wave), R = V - Y ----
         f32x4 y = zero4(), o1 = zero4();
@@ -929,14 +966,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 o2 = mfma16(mh, rh[ks], o2);
             }
         }
-        {
-            const int t = 16 * wave + 4 * g;
-            const int j = v0 + c16;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (t0 + t + r < T && j < V)
-                    p.o[((b * T + t0 + t + r) * H + h) * static_cast<int64_t>(V) + j] = p.scale * (o1[r] + o2[r]);
-        }
+        for (int r = 0; r < 4; ++r) so[(4 * g + r) * LDO + c16] = p.scale * (o1[r] + o2[r]);
 #pragma unroll
         for (int s2 = 0; s2 < STW; ++s2) {
             f32x4 ds = zero4();
@@ -969,6 +1000,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
     }
 
+    store_outputs(static_cast<int64_t>(nchunks - 1) * L);
 #pragma unroll
     for (int s2 = 0; s2 < STW; ++s2) {
         const int sr = STW * wave + s2;
@@ -1030,6 +1062,7 @@ hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_
     a.scale = prm.scale;
     a.vtiles = (prm.V + VT - 1) / VT;
     a.nchunks = (prm.T + L - 1) / L;
+    a.out_bf16 = prm.out_bf16;
     if (prm.g) {
         if (prm.K > KD) return hipErrorInvalidValue;
         return launch_t<KD, true>(a, prm.vec != 0, stream);

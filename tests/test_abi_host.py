@@ -37,7 +37,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     for n in names:
         assert hasattr(lib, n), f"{n} declared in lrs_abi.h but not exported"
     assert set(names) == set(binding.SIGNATURES), "binding and header disagree"
@@ -49,7 +49,8 @@ def test_python_mirrors_header_constants():
                  "LRS_ELEM_SCHEDULE_LOOKBACK", "LRS_PARAM_DIAG_SEGMENTS", "LRS_CAP_SCAN_FMA",
                  "LRS_CAP_SCAN_GATED", "LRS_CAP_SCAN_DIAG_OUTER", "LRS_CAP_SCAN_DELTA",
                  "LRS_CAP_ELEM_BACKWARD", "LRS_CAP_ELEM_STEP", "LRS_CAP_SCAN_DELTA_DECAY",
-                 "LRS_CAP_SCAN_DIAG_KEYSCALE", "LRS_CAP_SCAN_DIAG_EPILOGUE", "LRS_EPILOGUE_NONE",
+                 "LRS_CAP_SCAN_DIAG_KEYSCALE", "LRS_CAP_SCAN_DIAG_EPILOGUE", "LRS_CAP_SCAN_DELTA_OUT",
+                 "LRS_EPILOGUE_NONE",
                  "LRS_EPILOGUE_SKIP", "LRS_EPILOGUE_NORM_GATE", "LRS_DTYPE_F32", "LRS_DTYPE_BF16"):
         assert getattr(binding, name) == _header_int(name), name
     assert binding.LRS_ABI_VERSION_MAJOR == _header_int("LRS_ABI_VERSION_MAJOR")
@@ -70,7 +71,7 @@ def test_caps_and_status_strings(lib):
                 binding.LRS_CAP_SCAN_DIAG_OUTER, binding.LRS_CAP_SCAN_DELTA,
                 binding.LRS_CAP_ELEM_BACKWARD, binding.LRS_CAP_ELEM_STEP,
                 binding.LRS_CAP_SCAN_DELTA_DECAY, binding.LRS_CAP_SCAN_DIAG_KEYSCALE,
-                binding.LRS_CAP_SCAN_DIAG_EPILOGUE):
+                binding.LRS_CAP_SCAN_DIAG_EPILOGUE, binding.LRS_CAP_SCAN_DELTA_OUT):
         assert caps & bit
     for st in (0, -1, -2, -3, -4, -5, -6, 17, -99):
         s = binding.lrs_status_string(st)
@@ -96,6 +97,8 @@ def test_null_context_and_null_out_are_rejected(lib):
                                             None, 0.0, 0, fake, fake, 1, 1, 1, 1, 1, 1,
                                             None) == binding.LRS_E_INVAL
     assert lib.lrs_step_gated(None, fake, fake, fake, 1, 1, None) == binding.LRS_E_INVAL
+    assert lib.lrs_scan_delta_out(None, fake, fake, fake, None, fake, 1.0, None, 1, fake, fake,
+                                  1, 1, 1, 1, 1, None) == binding.LRS_E_INVAL
     assert lib.lrs_context_create(0, None) == binding.LRS_E_INVAL
     assert lib.lrs_context_set_param(None, 1, 0) == binding.LRS_E_INVAL
     assert lib.lrs_context_check(None) == binding.LRS_E_INVAL

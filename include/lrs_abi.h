@@ -181,8 +181,18 @@ void lrs_context_destroy(LrsContext* ctx);
  *                holds more, but at least 4 chunks (256 steps) per segment;
  *   n >= 1       n segments (capped at the number of chunks).
  * Any value gives results within the documented tolerance.
+ *
+ * LRS_PARAM_LOOKBACK_DELAY_SEED (since 1.2) is a verification knob for the
+ * elementwise look-back schedule (forward scans and gradient passes):
+ *   0 (default)  off;
+ *   n >= 1       every look-back tile sleeps a pseudo-random time seeded by n
+ *                (0 to about 4 us, per tile) before it publishes its aggregate,
+ *                before it walks back over its predecessors and before it
+ *                publishes its inclusive prefix, so tiles reach the status
+ *                words in an order unrelated to normal timing.  Results stay
+ *                within the documented tolerance; calls are much slower.
  * Errors: LRS_E_INVAL for a NULL context, unknown parameter or value. */
-enum { LRS_PARAM_ELEM_SCHEDULE = 1, LRS_PARAM_DIAG_SEGMENTS = 2 };
+enum { LRS_PARAM_ELEM_SCHEDULE = 1, LRS_PARAM_DIAG_SEGMENTS = 2, LRS_PARAM_LOOKBACK_DELAY_SEED = 3 };
 enum {
     LRS_ELEM_SCHEDULE_AUTO = 0,
     LRS_ELEM_SCHEDULE_STREAM = 1,

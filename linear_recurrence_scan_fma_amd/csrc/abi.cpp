@@ -20,6 +20,7 @@ struct LrsContext {
     int device = 0;
     int num_cus = 256;
     int elem_schedule = LRS_ELEM_SCHEDULE_AUTO;
+    unsigned int lookback_delay_seed = 0;   // LRS_PARAM_LOOKBACK_DELAY_SEED
     // small fixed block: [0] tile counter (u64), [1] error flag (u32 in a u64 slot)
     unsigned long long* fixed = nullptr;
     // look-back status words, grown on demand
@@ -148,11 +149,15 @@ lrs_status next_epoch(LrsContext* ctx, hipStream_t stream, unsigned int* out) {
 // schedule (automatic choice) or is refused (look-back forced).
 lrs_status elem_prepare(LrsContext* ctx, bool gated, int32_t B, int32_t T, int32_t N, bool al16,
                         hipStream_t stream, lrs::ElemPlan& plan, lrs::ElemParams& p) {
+    // The capture query runs only where a look-back could be chosen: a short
+    // call (one chunk) or a forced stream schedule pays no runtime query.
     int schedule = ctx->elem_schedule;
-    const bool captured = capturing(stream);
-    if (captured && schedule == LRS_ELEM_SCHEDULE_LOOKBACK) return LRS_E_UNSUPPORTED;
-    if (schedule == LRS_ELEM_SCHEDULE_AUTO)
-        schedule = captured ? LRS_ELEM_SCHEDULE_STREAM : lrs::elem_auto_schedule(B, T, N, al16, ctx->num_cus);
+    if (schedule == LRS_ELEM_SCHEDULE_LOOKBACK && capturing(stream)) return LRS_E_UNSUPPORTED;
+    if (schedule == LRS_ELEM_SCHEDULE_AUTO) {
+        schedule = lrs::elem_auto_schedule(B, T, N, al16, ctx->num_cus) == lrs::kElemLookback
+                       ? LRS_ELEM_SCHEDULE_LOOKBACK : LRS_ELEM_SCHEDULE_STREAM;
+        if (schedule == LRS_ELEM_SCHEDULE_LOOKBACK && capturing(stream)) schedule = LRS_ELEM_SCHEDULE_STREAM;
+    }
     const int ksched = schedule == LRS_ELEM_SCHEDULE_LOOKBACK ? lrs::kElemLookback : lrs::kElemStream;
     plan = lrs::elem_plan(B, T, N, al16, ksched);
     if (plan.grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
@@ -170,6 +175,7 @@ lrs_status elem_prepare(LrsContext* ctx, bool gated, int32_t B, int32_t T, int32
         p.counter = ctx->fixed;
         p.counter_base = ctx->counter_base;
         p.error_flag = reinterpret_cast<unsigned int*>(ctx->fixed + 1);
+        p.delay_seed = ctx->lookback_delay_seed;
     }
     return LRS_OK;
 }
@@ -379,6 +385,11 @@ LRS_API lrs_status lrs_context_set_param(LrsContext* ctx, int32_t param, int32_t
     if (param == LRS_PARAM_DIAG_SEGMENTS) {
         if (value < 0) return LRS_E_INVAL;
         ctx->diag_segments = value;
+        return LRS_OK;
+    }
+    if (param == LRS_PARAM_LOOKBACK_DELAY_SEED) {
+        if (value < 0) return LRS_E_INVAL;
+        ctx->lookback_delay_seed = static_cast<unsigned int>(value);
         return LRS_OK;
     }
     return LRS_E_INVAL;

@@ -29,6 +29,7 @@ struct ElemParams {
     unsigned long long counter_base;
     unsigned int epoch;           // tag of this call's status words, never 0
     unsigned int* error_flag;     // set to 1 when a bounded wait expires
+    unsigned int delay_seed;      // nonzero: the scrambled-arrival look-back variant
 };
 
 struct ElemPlan {

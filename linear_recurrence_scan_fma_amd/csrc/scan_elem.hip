@@ -67,7 +67,24 @@ struct ElemArgs {
     unsigned long long counter_base;
     unsigned int epoch;
     unsigned int* error_flag;
+    unsigned int delay_seed;   // scrambled-arrival variant only: seeds its delays
 };
+
+// Scrambled-arrival variant of the look-back (a verification tool): before a
+// tile publishes its aggregate, before it walks back and before it publishes
+// its inclusive prefix, its look-back wave sleeps a pseudo-random time (0 to
+// about 4 us, from a hash of the seed, the tile and the point), so tiles
+// arrive at the status words in an order unrelated to the normal timing.
+__device__ __forceinline__ void scramble_delay(unsigned int seed, int64_t tile, unsigned int point) {
+    unsigned int x = seed ^ (static_cast<unsigned int>(tile) * 0x9e3779b9u) ^ (point * 0x85ebca6bu);
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    const unsigned int n = x & 63u;   // 0 .. 63 sleeps of 64 x 2 cycles
+    for (unsigned int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(2);
+}
 
 template <bool GATED>
 __device__ __forceinline__ float step(float a, float x, float s) {
@@ -181,7 +198,7 @@ __device__ __forceinline__ bool take_tile(const ElemArgs& p, int tid, long long&
 // chunk here; the look-back schedule fetches it through the status words,
 // starting from p.s0 at chunk 0.  One barrier per chunk (two with look-back):
 // `tot` alternates between two buffers on consecutive chunks.
-template <int VEC, bool LOOKBACK>
+template <int VEC, bool LOOKBACK, bool SCR>
 __device__ __forceinline__ void lane_carry_in(const ElemArgs& p, int64_t chunk, int64_t tile, int64_t b,
                                               int64_t jt, int lane, int wave, int cl, int tlw,
                                               float (&A)[VEC], float (&Bv)[VEC], float (&carry)[VEC],
@@ -236,10 +253,13 @@ __device__ __forceinline__ void lane_carry_in(const ElemArgs& p, int64_t chunk, 
                 const int64_t ch = jt * NC + c;
                 cin = (p.s0 && ch < p.N) ? p.s0[b * p.N + ch] : 0.0f;
             } else {
+                if constexpr (SCR) scramble_delay(p.delay_seed, tile, 0u);
                 publish(p.words + (tile * 3 + 0) * NC + c, p.epoch, TA);
                 publish(p.words + (tile * 3 + 1) * NC + c, p.epoch, TB);
+                if constexpr (SCR) scramble_delay(p.delay_seed, tile, 1u);
                 cin = look_back(p, tile - p.ncols, c, NC);
             }
+            if constexpr (SCR) scramble_delay(p.delay_seed, tile, 2u);
             publish(p.words + (tile * 3 + 2) * NC + c, p.epoch, __builtin_fmaf(TA, cin, TB));
             sh_carry[c] = cin;
         }
@@ -275,7 +295,7 @@ __device__ __forceinline__ void lane_carry_in(const ElemArgs& p, int64_t chunk, 
     }
 }
 
-template <bool GATED, int VEC, int R, bool LOOKBACK>
+template <bool GATED, int VEC, int R, bool LOOKBACK, bool SCR = false>
 __global__ __launch_bounds__(kThreads) void scan_elem_kernel(ElemArgs p) {
     constexpr int NC = kChanLanes * VEC;   // channels per tile
     constexpr int CH = kTimeLanes * R;     // rows per chunk
@@ -346,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void scan_elem_kernel(ElemArgs p) {
             }
         }
         float st[VEC];
-        lane_carry_in<VEC, LOOKBACK>(p, chunk, tile, b, jt, lane, wave, cl, tlw, A, Bv, carry, st,
+        lane_carry_in<VEC, LOOKBACK, SCR>(p, chunk, tile, b, jt, lane, wave, cl, tlw, A, Bv, carry, st,
                                      sh_tot[chunk & 1], sh_carry);
 
         // 5. replay this lane's rows from the exact carry-in and stream states out
@@ -396,7 +416,7 @@ struct ElemBwdArgs {
     float* ds0;           // [B,N], nullable
 };
 
-template <bool GATED, int VEC, int R, bool LOOKBACK>
+template <bool GATED, int VEC, int R, bool LOOKBACK, bool SCR = false>
 __global__ __launch_bounds__(kThreads) void scan_elem_bwd_kernel(ElemBwdArgs q) {
     constexpr int NC = kChanLanes * VEC;
     constexpr int CH = kTimeLanes * R;
@@ -507,7 +527,7 @@ __global__ __launch_bounds__(kThreads) void scan_elem_bwd_kernel(ElemBwdArgs q) 
             }
         }
         float g[VEC];
-        lane_carry_in<VEC, LOOKBACK>(p, chunk, tile, b, jt, lane, wave, cl, tlw, A, Bv, carry, g,
+        lane_carry_in<VEC, LOOKBACK, SCR>(p, chunk, tile, b, jt, lane, wave, cl, tlw, A, Bv, carry, g,
                                      sh_tot[chunk & 1], sh_carry);
 
         // replay from the exact carry-in; gradients of this lane's rows
@@ -585,7 +605,10 @@ __global__ void fill_zero_u64_kernel(unsigned long long* p, size_t n) {
 
 template <bool GATED, int VEC, int R>
 hipError_t launch_variant(const ElemArgs& a, bool lookback, int64_t grid, hipStream_t stream) {
-    if (lookback) {
+    if (lookback && a.delay_seed) {
+        hipLaunchKernelGGL((scan_elem_kernel<GATED, VEC, R, true, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kThreads), 0, stream, a);
+    } else if (lookback) {
         hipLaunchKernelGGL((scan_elem_kernel<GATED, VEC, R, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(kThreads), 0, stream, a);
     } else {
@@ -612,7 +635,10 @@ hipError_t launch_gated(const ElemArgs& a, const ElemPlan& plan, bool lookback, 
 
 template <bool GATED, int VEC, int R>
 hipError_t launch_bwd_variant(const ElemBwdArgs& a, bool lookback, int64_t grid, hipStream_t stream) {
-    if (lookback) {
+    if (lookback && a.sc.delay_seed) {
+        hipLaunchKernelGGL((scan_elem_bwd_kernel<GATED, VEC, R, true, true>), dim3(static_cast<unsigned>(grid)),
+                           dim3(kThreads), 0, stream, a);
+    } else if (lookback) {
         hipLaunchKernelGGL((scan_elem_bwd_kernel<GATED, VEC, R, true>), dim3(static_cast<unsigned>(grid)),
                            dim3(kThreads), 0, stream, a);
     } else {
@@ -654,6 +680,7 @@ ElemArgs scan_args(const ElemParams& p, const ElemPlan& plan) {
     a.counter_base = p.counter_base;
     a.epoch = p.epoch;
     a.error_flag = p.error_flag;
+    a.delay_seed = p.delay_seed;
     return a;
 }
 

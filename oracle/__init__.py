@@ -43,8 +43,15 @@ def build() -> str:
 
 
 def default_threads() -> int:
-    """Host threads the oracle may use: the affinity set, at most 16."""
-    return max(1, min(16, len(os.sched_getaffinity(0))))
+    """Host threads the oracle may use: the threads this process is granted.
+    That is OMP_NUM_THREADS when the environment sets it (a host's share of
+    its cores for one job, which can be far below what the machine shows),
+    else the whole affinity set; never more than the affinity set."""
+    aff = max(1, len(os.sched_getaffinity(0)))
+    env = os.environ.get("OMP_NUM_THREADS", "").strip()
+    if env.isdigit() and int(env) > 0:
+        return min(aff, int(env))
+    return aff
 
 
 def _load():

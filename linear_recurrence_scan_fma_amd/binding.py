@@ -163,29 +163,46 @@ def lrs_context_check(ctx: Context) -> int:
 
 
 # ---- marshalling helpers -----------------------------------------------------
-def _ptr(t, dtype, shape, name, device):
-    import torch
+_Tensor = None
 
+
+def _ptr(t, dtype, shape, name, device):
+    # The checks use the cheapest tensor attributes (get_device() rather than
+    # t.device): this runs for every tensor of every call, and small calls
+    # (a decode step) are bounded by host time.
+    global _Tensor
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor):
+    if _Tensor is None:
+        import torch
+
+        _Tensor = torch.Tensor
+    if not isinstance(t, _Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda" or t.device.index != device:
+    if t.get_device() != device:
         raise ValueError(f"{name} must live on cuda:{device}, got {t.device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if tuple(t.shape) != tuple(shape):
+    if t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
 
 
-def _stream(stream, device):
-    import torch
+_raw_stream = None
 
+
+def _stream(stream, device):
+    global _raw_stream
     if stream is None:
-        return torch.cuda.current_stream(device).cuda_stream
+        if _raw_stream is None:
+            import torch
+
+            # the current stream's raw handle without building a Stream object
+            _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None) or (
+                lambda dev: torch.cuda.current_stream(dev).cuda_stream)
+        return _raw_stream(device)
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream

@@ -423,8 +423,9 @@ lrs_status lrs_scan_diag_outer_keyscale(LrsContext* ctx, const lrs_bf16* q, cons
  *   o          fp32 [B,T,H,V]   output
  *   s_final    fp32 [B,H,K,V]   output
  *
- * Limits: 1 <= K <= 64 and T <= 2088960 (LRS_E_UNSUPPORTED beyond).  The
- * context workspace holds 64.25 KiB per (b,h,64-step chunk): the factors of
+ * Limits: 1 <= K <= 128; T <= 2088960 for K <= 64 and T <= 1193024 for
+ * K > 64 (LRS_E_UNSUPPORTED beyond).  The context workspace holds 64.25 KiB
+ * (K <= 64) or 112.5 KiB (K > 64) per (b,h,64-step chunk): the factors of
  * lrs_scan_delta plus the chunk's decayed keys and queries and its total
  * decay, grown on demand as for lrs_scan_delta.  Any finite g is accepted; chunks in which some key's
  * running log-decay spans more than 60 nats take a slower exact path.

@@ -42,7 +42,7 @@
 //    chunks in order with its K x 16 state in registers.  Per chunk, two
 //    phases and two barriers: Y = K S0 (a S0) and Q S0 (qt S0), R = V - Y;
 //    then MTb R for the outputs and S = S0 + W R (diag(e^{G_L}) S0 + W R).
-//    fp32 operands are split into hi + lo bf16 terms.  Decayed form: K <= 64.
+//    fp32 operands are split into hi + lo bf16 terms.  K <= 128 in both forms.
 #include "lrs_internal.h"
 #include "mfma_util.h"
 
@@ -53,17 +53,23 @@ constexpr int L = 64;
 constexpr int NT = 256;
 constexpr int PLANE = L * L;   // elements of one 64 x 64 bf16 plane
 constexpr int VT = 16;         // V-tile width of the scan kernel
-constexpr int KD = 64;         // key width of the decayed form
+constexpr int KD = 128;        // largest key width of the decayed form
 constexpr float kHalfSpan = 30.0f;   // decayed prep: factor exponents stay within +-30 nats
 
 // One chunk's workspace block, in u16 elements:
 //   MTb hi, MTb lo          2 x [L][L]
-//   W hi, W lo              2 x [KP][L]   (key-major: row = key, 64 steps)
+//   W hi, W lo              KP / 16 x 2 x 2 blocks of 512: W in the scan's
+//                           operand order (below)
 //   decayed form only:
 //   a hi, a lo, qt hi, qt lo   4 x [L][KP]
 //   e^{G_L}                    [KP] fp32
 template <int KP>
 constexpr int off_w() { return 2 * PLANE; }
+// W (KP keys x 64 steps) is stored as the scan's 16x16x32 operand fragments:
+// block (key tile kt, step half ks, hi/lo hl) of 512 elements holds, for
+// lane l, keys 16 kt + l % 16 and steps 32 ks + 8 (l / 16) .. +7, so that each
+// of the scan's loads reads one contiguous kilobyte (whole cache lines).
+__device__ __forceinline__ int wfrag_off(int kt, int ks, int hl) { return ((kt * 2 + ks) * 2 + hl) * 512; }
 template <int KP>
 constexpr int off_aq() { return 2 * PLANE + 2 * KP * L; }
 template <int KP>
@@ -186,29 +192,34 @@ __device__ __forceinline__ u32x4 load_piece(BufRes r, const u16* rowptr, int off
 // ---------------------------------------------------------------------------
 // prep: Tb = (I + strict_lower(diag(beta) K K^T))^{-1} diag(beta), MTb = tril(Q K^T) Tb
 // ---------------------------------------------------------------------------
-// Decayed-form prep tiles: [L][KD] bf16, unpadded, 16-byte piece p of row r
-// stored at piece p ^ (r & 7), so the 8 rows of a 16-byte fragment read fall
-// on distinct banks.  Element offset of (row, column):
-__device__ __forceinline__ int tswz(int r, int i) { return r * KD + ((((i >> 3) ^ (r & 7))) << 3) + (i & 7); }
+// Decayed-form prep tiles: [L][KP] bf16, unpadded, 16-byte piece p of row r
+// stored at piece p ^ (r mod KP / 8), so the rows of a 16-byte fragment read
+// fall on distinct banks.  Element offset of (row, column):
+template <int KP>
+__device__ __forceinline__ int tswz(int r, int i) {
+    return r * KP + ((((i >> 3) ^ (r & (KP / 8 - 1)))) << 3) + (i & 7);
+}
 
 // 16x16x32 operand fragment (rows r0.., columns k0 + 8 (lane / 16) ..) of such a tile
+template <int KP>
 __device__ __forceinline__ bf16x8 tfrag(const u16* t, int r0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8*>(t + tswz(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
+    return *reinterpret_cast<const bf16x8*>(t + tswz<KP>(r0 + (lane & 15), k0 + 8 * (lane >> 4)));
 }
 
 template <int KP, bool VEC, bool DECAY>
 __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
-    static_assert(!DECAY || KP == KD, "decayed form: K <= 64");
+    static_assert(!DECAY || KP == 64 || KP == KD, "decayed form: K <= 128");
     constexpr int LDK = KP + 8;
     constexpr int LDA = L + 4;                     // fp32 rows of 272 bytes
+    constexpr int LDG = KP + 4;                    // fp32 rows of the running log-decay G
     // plain form: sQ, sK as padded rows.  Decayed form: four unpadded tiles
     // whose 16-byte pieces are rotated by an XOR of the row (a hi/lo, later
     // overwritten by qt hi/lo, and b hi/lo), then the running log-decay G; the
     // whole block is dead once A and M are formed, so sA and sT reuse it.  The
-    // decayed form thus fits three workgroups per compute unit.
+    // decayed form thus fits three workgroups per compute unit at K = 64.
     constexpr int TILE_D = L * KP * 2;
     constexpr int G_OFF = 4 * TILE_D;
-    constexpr int QK_BYTES = DECAY ? G_OFF + L * LDA * 4 : 2 * L * LDK * 2;
+    constexpr int QK_BYTES = DECAY ? G_OFF + L * LDG * 4 : 2 * L * LDK * 2;
     constexpr int AT_BYTES = 2 * L * LDA * 4;      // sA, sT (fp32) reuse the same space
     constexpr int U_BYTES = QK_BYTES > AT_BYTES ? QK_BYTES : AT_BYTES;
     __shared__ __align__(16) unsigned char sU[U_BYTES];
@@ -274,7 +285,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
 #pragma unroll
         for (int j = 0; j < NGE; ++j) {
             const int e = tid + j * NT;
-            sG[(e / KP) * LDA + e % KP] = xg[j];
+            sG[(e / KP) * LDG + e % KP] = xg[j];
         }
     }
     __syncthreads();
@@ -283,27 +294,41 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     f32x4 acc[5];
     bf16x8 khh[DECAY ? NPI : 1], khl[DECAY ? NPI : 1];   // decayed form: khat pieces, hi/lo
     if constexpr (DECAY) {
-        // running sum over the chunk per key: wave w sums rows 16w .. 16w+15 of key `lane`
-        float gl[16];
+        // running sum over the chunk per key: wave w sums rows 16w .. 16w+15 of
+        // keys lane, lane + 64, ...
+        constexpr int KPL = KP / 64;   // keys per lane
+        float gl[KPL][16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) gl[r] = sG[(16 * wave + r) * LDA + lane];
+        for (int kk = 0; kk < KPL; ++kk) {
+            const int key = lane + 64 * kk;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) gl[r] += gl[r - 1];
-        sTot[wave][lane] = gl[15];
-        __syncthreads();
-        float off = 0.0f;
-        for (int w2 = 0; w2 < wave; ++w2) off += sTot[w2][lane];
+            for (int r = 0; r < 16; ++r) gl[kk][r] = sG[(16 * wave + r) * LDG + key];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            gl[r] += off;
-            sG[(16 * wave + r) * LDA + lane] = gl[r];
+            for (int r = 1; r < 16; ++r) gl[kk][r] += gl[kk][r - 1];
+            sTot[wave][key] = gl[kk][15];
         }
-        if (wave == 1) sRef[lane] = gl[15];   // the middle step's running sum
         __syncthreads();
-        const float ref = sRef[lane];
-        float dev = wave == 0 ? fabsf(ref) : 0.0f;   // G_{-1} = 0
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dev = fmaxf(dev, fabsf(gl[r] - ref));
+        for (int kk = 0; kk < KPL; ++kk) {
+            const int key = lane + 64 * kk;
+            float off = 0.0f;
+            for (int w2 = 0; w2 < wave; ++w2) off += sTot[w2][key];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                gl[kk][r] += off;
+                sG[(16 * wave + r) * LDG + key] = gl[kk][r];
+            }
+            if (wave == 1) sRef[key] = gl[kk][15];   // the middle step's running sum
+        }
+        __syncthreads();
+        float dev = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < KPL; ++kk) {
+            const float ref = sRef[lane + 64 * kk];
+            if (wave == 0) dev = fmaxf(dev, fabsf(ref));   // G_{-1} = 0
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dev = fmaxf(dev, fabsf(gl[kk][r] - ref));
+        }
         const bool fast = !__syncthreads_or(dev > kHalfSpan);
         u16* tAh = tile;                 // a hi, later qt hi
         u16* tAl = tile + L * KP;        // a lo, later qt lo
@@ -323,8 +348,8 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                 float av[8], qv[8], kv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float gt = sG[t * LDA + i0 + e], gp = t > 0 ? sG[(t - 1) * LDA + i0 + e] : 0.0f;
-                    const float gL = sG[(L - 1) * LDA + i0 + e];
+                    const float gt = sG[t * LDG + i0 + e], gp = t > 0 ? sG[(t - 1) * LDG + i0 + e] : 0.0f;
+                    const float gL = sG[(L - 1) * LDG + i0 + e];
                     const float kx = bf2f(piece_elem(kw, e));
                     av[e] = kx * __expf(gp);
                     qv[e] = bf2f(piece_elem(qw, e)) * __expf(gt);
@@ -339,7 +364,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                 *reinterpret_cast<bf16x8*>(aq + 3 * L * KP + t * KP + i0) = lo;
                 split8(kv, khh[j], khl[j]);
             }
-            if (tid < KP) reinterpret_cast<float*>(blk + off_el<KP>())[tid] = __expf(sG[(L - 1) * LDA + tid]);
+            if (tid < KP) reinterpret_cast<float*>(blk + off_el<KP>())[tid] = __expf(sG[(L - 1) * LDG + tid]);
         }
         if (fast) {
             // a = e^{G_{t-1} - ref} k and b = e^{ref - G_t} k as hi/lo, eight keys of
@@ -354,13 +379,13 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float r0 = sRef[i0 + e];
-                    const float gt = sG[t * LDA + i0 + e], gp = t > 0 ? sG[(t - 1) * LDA + i0 + e] : 0.0f;
+                    const float gt = sG[t * LDG + i0 + e], gp = t > 0 ? sG[(t - 1) * LDG + i0 + e] : 0.0f;
                     const float kv = bf2f(piece_elem(kw, e));
                     av[e] = kv * __expf(gp - r0);
                     bv[e] = kv * __expf(r0 - gt);
                 }
                 bf16x8 hi, lo;
-                const int o = tswz(t, i0);
+                const int o = tswz<KP>(t, i0);
                 split8(av, hi, lo);
                 *reinterpret_cast<bf16x8*>(tAh + o) = hi;
                 *reinterpret_cast<bf16x8*>(tAl + o) = lo;
@@ -379,8 +404,8 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                     f32x4 a = zero4();
 #pragma unroll
                     for (int k0 = 0; k0 < KP; k0 += 32) {
-                        const bf16x8 xh = tfrag(tAh, 16 * bi, k0, lane), xl = tfrag(tAl, 16 * bi, k0, lane);
-                        const bf16x8 yh = tfrag(tBh, 16 * bj, k0, lane), yl = tfrag(tBl, 16 * bj, k0, lane);
+                        const bf16x8 xh = tfrag<KP>(tAh, 16 * bi, k0, lane), xl = tfrag<KP>(tAl, 16 * bi, k0, lane);
+                        const bf16x8 yh = tfrag<KP>(tBh, 16 * bj, k0, lane), yl = tfrag<KP>(tBl, 16 * bj, k0, lane);
                         a = mfma16(xl, yh, a);
                         a = mfma16(xh, yl, a);
                         a = mfma16(xh, yh, a);
@@ -397,9 +422,9 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                 float qv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(sG[t * LDA + i0 + e] - sRef[i0 + e]);
+                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(sG[t * LDG + i0 + e] - sRef[i0 + e]);
                 bf16x8 hi, lo;
-                const int o = tswz(t, i0);
+                const int o = tswz<KP>(t, i0);
                 split8(qv, hi, lo);
                 *reinterpret_cast<bf16x8*>(tAh + o) = hi;
                 *reinterpret_cast<bf16x8*>(tAl + o) = lo;
@@ -412,8 +437,8 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
 #pragma unroll
             for (int j = 0; j < NPI; ++j) {
                 const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
-                *reinterpret_cast<u32x4*>(tAh + tswz(t, i0)) = xk[j];
-                *reinterpret_cast<u32x4*>(tBh + tswz(t, i0)) = xq[j];
+                *reinterpret_cast<u32x4*>(tAh + tswz<KP>(t, i0)) = xk[j];
+                *reinterpret_cast<u32x4*>(tBh + tswz<KP>(t, i0)) = xq[j];
             }
             __syncthreads();
 #pragma unroll
@@ -428,10 +453,10 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                     float sum = 0.0f;
                     if (n < 10 ? tau < t : tau <= t) {
                         const u16* ltile = n < 10 ? tAh : tBh;
-                        const float* gl_row = n < 10 ? sG + (t - 1) * LDA : sG + t * LDA;   // t >= 1 when n < 10
+                        const float* gl_row = n < 10 ? sG + (t - 1) * LDG : sG + t * LDG;   // t >= 1 when n < 10
                         for (int i = 0; i < KP; ++i)
-                            sum += bf2f(ltile[tswz(t, i)]) * bf2f(tAh[tswz(tau, i)]) *
-                                   __expf(gl_row[i] - sG[tau * LDA + i]);
+                            sum += bf2f(ltile[tswz<KP>(t, i)]) * bf2f(tAh[tswz<KP>(tau, i)]) *
+                                   __expf(gl_row[i] - sG[tau * LDG + i]);
                     }
                     acc[m][r] = sum;
                 }
@@ -590,10 +615,12 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     }
     __syncthreads();   // M is read: its space takes khat
     // W = khat^T Tb (key-major, [KP][L]); khat = k (plain form, exact in
-    // bf16) or e^{G_L - G_t} k (decayed form, hi/lo), staged [step][key] in M's space
+    // bf16) or e^{G_L - G_t} k (decayed form, hi/lo), staged [step][key] in M's
+    // space, or past sA and sT where it does not fit there (decayed, K = 128)
     {
-        static_assert((DECAY ? 2 : 1) * L * KP * 2 <= L * LDA * 4, "khat fits in M's space");
-        u16* sKh = reinterpret_cast<u16*>(sM);
+        constexpr bool KH_PAST = (DECAY ? 2 : 1) * L * KP * 2 > L * LDA * 4;
+        static_assert(!KH_PAST || U_BYTES - AT_BYTES >= 2 * L * KP * 2, "khat fits past sA and sT");
+        u16* sKh = KH_PAST ? reinterpret_cast<u16*>(sU + AT_BYTES) : reinterpret_cast<u16*>(sM);
         u16* sKl = sKh + L * KP;
 #pragma unroll
         for (int j = 0; j < NPI; ++j) {
@@ -607,7 +634,6 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
         }
         __syncthreads();
         u16* wh = blk + off_w<KP>();
-        u16* wl = wh + KP * L;
         for (int n = wave; n < KP / 16 * 4; n += 4) {
             const int ib = n / 4, jb = n % 4;   // key block, step block
             f32x4 acc2 = zero4();
@@ -633,9 +659,11 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             u16 hi[4], lo[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) split_bf16(acc2[r], hi[r], lo[r]);
-            const int idx = (16 * ib + c16) * L + 16 * jb + 4 * g;
+            // steps 16 jb + 4 g + r: fragment lane c16 + 16 (2 (jb % 2) + g / 2),
+            // elements 4 (g % 2) + r of block (ib, jb / 2)
+            const int idx = wfrag_off(ib, jb >> 1, 0) + (c16 + 16 * (2 * (jb & 1) + (g >> 1))) * 8 + 4 * (g & 1);
             store4(wh + idx, hi[0], hi[1], hi[2], hi[3]);
-            store4(wl + idx, lo[0], lo[1], lo[2], lo[3]);
+            store4(wh + idx + 512, lo[0], lo[1], lo[2], lo[3]);
         }
     }
 }
@@ -664,9 +692,14 @@ __device__ __forceinline__ int swz(int r, int p) {
 //   -- barrier --
 //   2. O = scale (O1 + MTb R) -> outputs; S = D S0 + W R (tiles of this wave)
 //      -> LDS as the next chunk's operand
+// The decayed form at K = 128 has 64 KB of operand tiles per chunk, too much
+// to double buffer beside the rest: there they are single buffered, and each
+// wave loads the next chunk's rows of its own (the only rows it reads) as
+// soon as its step 1 is done with them, so they load during step 2.
 template <int KP, bool VEC, bool DECAY>
 __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
-    static_assert(!DECAY || KP == KD, "decayed form: K <= 64");
+    static_assert(!DECAY || KP == 64 || KP == KD, "decayed form: K <= 128");
+    constexpr bool SPLIT = DECAY && KP > 64;   // operand tiles single buffered
     constexpr int PPR = KP / 8;          // 16-byte pieces per operand row
     constexpr int QB = L * KP * 2;       // bytes of one [L][KP] bf16 operand tile
     constexpr int PB = L * L * 2;        // bytes of an MTb plane
@@ -674,8 +707,12 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     constexpr int NOPS = DECAY ? 4 : 2;  // operand tiles: q, k; or a hi, a lo, qt hi, qt lo
     constexpr int OFF_AH = DECAY ? 0 : QB, OFF_AL = QB;        // k (a hi, a lo)
     constexpr int OFF_QH = DECAY ? 2 * QB : 0, OFF_QL = 3 * QB;   // q (qt hi, qt lo)
-    constexpr int OFF_P = NOPS * QB, OFF_V = OFF_P + 2 * PB;
-    constexpr int STAGE = OFF_V + VB;
+    constexpr int OPS = NOPS * QB;       // operand stage
+    constexpr int OFF_P = 0, OFF_V = 2 * PB;
+    constexpr int PVS = OFF_V + VB;      // MTb + V stage
+    // load runs per wave and chunk (vector loads): operand tiles, MTb planes
+    constexpr int NJ_OPS = SPLIT ? 4 * 16 * PPR / 64 : (DECAY ? 4 : 1) * QB / 4096;
+    constexpr int NJ_P = 2 * PB / 4096;
     constexpr int CHUNK_BYTES = chunk_u16<KP, DECAY>() * 2;
     constexpr int LDK = KP + 8;
     constexpr int LDL = L + 8;
@@ -684,7 +721,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     static_assert(STW >= 1, "state tiles");
     static_assert(QB % 1024 == 0 && PB % 1024 == 0 && VB == 2048, "1 KB load runs");
 
-    __shared__ __align__(16) unsigned char sIn[2 * STAGE];
+    __shared__ __align__(16) unsigned char sOps[(SPLIT ? 1 : 2) * OPS];
+    __shared__ __align__(16) unsigned char sPV[2 * PVS];
     __shared__ __align__(16) u16 sRTh[VT * LDL];     // R^T hi/lo
     __shared__ __align__(16) u16 sRTl[VT * LDL];
     __shared__ __align__(16) u16 sSh[VT * LDK];      // S^T hi/lo entering the chunk
@@ -710,64 +748,67 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     const u16* wsb = p.ws + static_cast<int64_t>(bh) * nchunks * chunk_u16<KP, DECAY>();
     const int64_t ws_bytes = static_cast<int64_t>(nchunks) * CHUNK_BYTES;
 
-    // ---- fetch of one chunk's LDS operands into stage `buf` ----
+    // ---- fetch of one chunk's LDS operands ----
     // Load run i (64 lanes x 16 bytes) fills bytes 1024 i .. of a tile: lane l
     // takes slot s = 64 i + l, i.e. row s / PPR, stored piece s % PPR, which
     // holds the row's piece (s % PPR) ^ (row & (PPR - 1)).
-    auto fetch = [&](int c, int buf) {
-        unsigned char* st = sIn + buf * STAGE;
+    // Operand tiles into `so_`; all rows, or (SPLIT) this wave's 16.  With
+    // vector loads a wave issues its runs j0 .. j1 - 1 of NJ_OPS (a run: one
+    // load instruction per operand tile of the plain form, one in all of the
+    // decayed form), so that the loads can be spread over a chunk's work.
+    auto fetch_ops = [&](int c, unsigned char* so_, int j0 = 0, int j1 = -1) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
+        if (j1 < 0) j1 = NJ_OPS;
         if constexpr (VEC) {
-            const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
-            const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
             if constexpr (DECAY) {
                 // a hi, a lo, qt hi, qt lo: four [L][KP] tiles, back to back in the workspace
+                const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
+                if constexpr (SPLIT) {
+                    constexpr int RPR = 64 / PPR;   // rows per run
 #pragma unroll
-                for (int j = 0; j < 4 * QB / 1024 / 4; ++j) {
-                    const int i = wave + 4 * j, tl = i / (QB / 1024), sl = 64 * (i % (QB / 1024)) + lane;
-                    const int row = sl / PPR, pc = (sl % PPR) ^ (row & (PPR - 1));
-                    const int off = off_aq<KP>() * 2 + tl * QB + row * KP * 2 + pc * 16;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        wp, (__attribute__((address_space(3))) void*)(st + 1024 * i), 16, off, 0, 0, 0);
+                    for (int j = j0; j < j1; ++j) {
+                        const int tl = j / (16 / RPR), row0 = 16 * wave + RPR * (j % (16 / RPR));
+                        const int row = row0 + lane / PPR, pc = (lane % PPR) ^ (row & (PPR - 1));
+                        const int off = off_aq<KP>() * 2 + tl * QB + row * KP * 2 + pc * 16;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            wp, (__attribute__((address_space(3))) void*)(so_ + tl * QB + row0 * KP * 2), 16, off,
+                            0, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = j0; j < j1; ++j) {
+                        const int i = wave + 4 * j, tl = i / (QB / 1024), sl = 64 * (i % (QB / 1024)) + lane;
+                        const int row = sl / PPR, pc = (sl % PPR) ^ (row & (PPR - 1));
+                        const int off = off_aq<KP>() * 2 + tl * QB + row * KP * 2 + pc * 16;
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            wp, (__attribute__((address_space(3))) void*)(so_ + 1024 * i), 16, off, 0, 0, 0);
+                    }
                 }
             } else {
                 const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
                 const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
 #pragma unroll
-                for (int j = 0; j < QB / 1024 / 4; ++j) {
+                for (int j = j0; j < j1; ++j) {
                     const int i = wave + 4 * j, sl = 64 * i + lane;
                     const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
                     const int off = col < K ? ((row * H + h) * K + col) * 2 : kBufOOB;
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        wq, (__attribute__((address_space(3))) void*)(st + OFF_QH + 1024 * i), 16, off, 0, 0, 0);
+                        wq, (__attribute__((address_space(3))) void*)(so_ + OFF_QH + 1024 * i), 16, off, 0, 0, 0);
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        wk, (__attribute__((address_space(3))) void*)(st + OFF_AH + 1024 * i), 16, off, 0, 0, 0);
+                        wk, (__attribute__((address_space(3))) void*)(so_ + OFF_AH + 1024 * i), 16, off, 0, 0, 0);
                 }
-            }
-#pragma unroll
-            for (int j = 0; j < 2 * PB / 1024 / 4; ++j) {
-                const int i = wave + 4 * j;                 // run over the two MTb planes
-                const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
-                const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
-                const int off = (pl * PLANE + row * L + col) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    wp, (__attribute__((address_space(3))) void*)(st + OFF_P + 1024 * i), 16, off, 0, 0, 0);
-            }
-            if (wave < 2) {
-                const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
-                const int off = v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    wv, (__attribute__((address_space(3))) void*)(st + OFF_V + 1024 * wave), 16, off, 0, 0, 0);
             }
         } else {
             // same slots, filled through registers (odd sizes or alignment)
-            const u16* pw = wsb + static_cast<int64_t>(c) * chunk_u16<KP, DECAY>();
             if constexpr (DECAY) {
-                const unsigned char* aw = reinterpret_cast<const unsigned char*>(pw + off_aq<KP>());
-                for (int s2 = tid; s2 < 4 * L * PPR; s2 += NT) {
-                    const int tl = s2 / (L * PPR), sl = s2 % (L * PPR);
+                const unsigned char* aw = reinterpret_cast<const unsigned char*>(
+                    wsb + static_cast<int64_t>(c) * chunk_u16<KP, DECAY>() + off_aq<KP>());
+                const int first = SPLIT ? lane : tid, step = SPLIT ? 64 : NT;
+                for (int s2 = first; s2 < (SPLIT ? 4 * 16 * PPR : 4 * L * PPR); s2 += step) {
+                    const int per = SPLIT ? 16 * PPR : L * PPR;
+                    const int tl = s2 / per, sl = (SPLIT ? 16 * PPR * wave : 0) + s2 % per;
                     const int row = sl / PPR, pc = (sl % PPR) ^ (row & (PPR - 1));
-                    *reinterpret_cast<u32x4*>(st + tl * QB + 16 * sl) =
+                    *reinterpret_cast<u32x4*>(so_ + tl * QB + 16 * sl) =
                         *reinterpret_cast<const u32x4*>(aw + tl * QB + row * KP * 2 + pc * 16);
                 }
             } else {
@@ -780,14 +821,41 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                         xq = load8_bf16(qb + o, col, K, false);
                         xk = load8_bf16(kb + o, col, K, false);
                     }
-                    *reinterpret_cast<u32x4*>(st + OFF_QH + 16 * sl) = xq;
-                    *reinterpret_cast<u32x4*>(st + OFF_AH + 16 * sl) = xk;
+                    *reinterpret_cast<u32x4*>(so_ + OFF_QH + 16 * sl) = xq;
+                    *reinterpret_cast<u32x4*>(so_ + OFF_AH + 16 * sl) = xk;
                 }
             }
+        }
+    };
+    // MTb planes (runs j0 .. j1 - 1 of NJ_P with vector loads) and, with
+    // `with_v`, the V tile into `sp_`
+    auto fetch_pv = [&](int c, unsigned char* sp_, int j0 = 0, int j1 = -1, bool with_v = true) {
+        const int64_t t0 = static_cast<int64_t>(c) * L;
+        if (j1 < 0) j1 = NJ_P;
+        if constexpr (VEC) {
+            const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
+            const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
+#pragma unroll
+            for (int j = j0; j < j1; ++j) {
+                const int i = wave + 4 * j;                 // run over the two MTb planes
+                const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
+                const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
+                const int off = (pl * PLANE + row * L + col) * 2;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wp, (__attribute__((address_space(3))) void*)(sp_ + OFF_P + 1024 * i), 16, off, 0, 0, 0);
+            }
+            if (with_v && wave < 2) {
+                const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
+                const int off = v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    wv, (__attribute__((address_space(3))) void*)(sp_ + OFF_V + 1024 * wave), 16, off, 0, 0, 0);
+            }
+        } else {
+            const u16* pw = wsb + static_cast<int64_t>(c) * chunk_u16<KP, DECAY>();
             for (int sl = tid; sl < 2 * L * 8; sl += NT) {
                 const int pl = sl / (L * 8), s2 = sl % (L * 8);
                 const int row = s2 / 8, col = ((s2 % 8) ^ (row & 7)) * 8;
-                *reinterpret_cast<u32x4*>(st + OFF_P + 16 * sl) =
+                *reinterpret_cast<u32x4*>(sp_ + OFF_P + 16 * sl) =
                     *reinterpret_cast<const u32x4*>(pw + pl * PLANE + row * L + col);
             }
             if (tid < L * 2) {
@@ -795,8 +863,121 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 const int64_t t = t0 + row;
                 u32x4 xv = {0u, 0u, 0u, 0u};
                 if (t < T) xv = load8_bf16(vb + (t * H + h) * static_cast<int64_t>(V) + v0, col, V - v0, false);
-                *reinterpret_cast<u32x4*>(st + OFF_V + 16 * tid) = xv;
+                *reinterpret_cast<u32x4*>(sp_ + OFF_V + 16 * tid) = xv;
             }
+        }
+    };
+
+    // ---- register-staged prefetch of the next chunk (vector loads) ----
+    // The same 16-byte slots as the LDS-direct loads above, loaded into
+    // registers during a chunk and written to the other stage at its end.
+    // (An LDS-direct load in flight makes the compiler wait for it before any
+    // later LDS read it cannot tell apart, which would expose the prefetch.)
+    // Plain form: q and k pieces of runs 0 .. QB/4096 - 1; decayed form (not
+    // SPLIT): the four operand tiles' runs; then the MTb planes and the V tile.
+    constexpr int NPO = SPLIT ? 1 : (DECAY ? 4 : 2) * QB / 4096;
+    u32x4 pre_o[NPO], pre_p[NJ_P], pre_v;
+    auto preload_ops = [&](int c, int j0, int j1) {
+        if constexpr (DECAY) {
+            const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
+#pragma unroll
+            for (int j = j0; j < j1; ++j) {
+                const int i = wave + 4 * j, tl = i / (QB / 1024), sl = 64 * (i % (QB / 1024)) + lane;
+                const int row = sl / PPR, pc = (sl % PPR) ^ (row & (PPR - 1));
+                pre_o[j] = buf_load16(wp, off_aq<KP>() * 2 + tl * QB + row * KP * 2 + pc * 16);
+            }
+        } else {
+            const int64_t t0 = static_cast<int64_t>(c) * L;
+            const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
+            const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
+#pragma unroll
+            for (int j = j0; j < j1; ++j) {
+                const int i = wave + 4 * j, sl = 64 * i + lane;
+                const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
+                const int off = col < K ? ((row * H + h) * K + col) * 2 : kBufOOB;
+                pre_o[2 * j] = buf_load16(wq, off);
+                pre_o[2 * j + 1] = buf_load16(wk, off);
+            }
+        }
+    };
+    auto preload_p = [&](int c) {
+        const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
+#pragma unroll
+        for (int j = 0; j < NJ_P; ++j) {
+            const int i = wave + 4 * j;
+            const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
+            const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
+            pre_p[j] = buf_load16(wp, (pl * PLANE + row * L + col) * 2);
+        }
+    };
+    auto preload_v = [&](int c) {
+        if (wave < 2) {
+            const int64_t t0 = static_cast<int64_t>(c) * L;
+            const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
+            const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
+            pre_v = buf_load16(wv, v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB);
+        }
+    };
+    auto prestore = [&](unsigned char* so_, unsigned char* sp_) {
+        if constexpr (!SPLIT) {
+#pragma unroll
+            for (int j = 0; j < (DECAY ? NPO : NPO / 2); ++j) {
+                const int i = wave + 4 * j;
+                if constexpr (DECAY) {
+                    *reinterpret_cast<u32x4*>(so_ + 1024 * i + 16 * lane) = pre_o[j];
+                } else {
+                    *reinterpret_cast<u32x4*>(so_ + OFF_QH + 1024 * i + 16 * lane) = pre_o[2 * j];
+                    *reinterpret_cast<u32x4*>(so_ + OFF_AH + 1024 * i + 16 * lane) = pre_o[2 * j + 1];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ_P; ++j)
+            *reinterpret_cast<u32x4*>(sp_ + OFF_P + 1024 * (wave + 4 * j) + 16 * lane) = pre_p[j];
+        if (wave < 2) *reinterpret_cast<u32x4*>(sp_ + OFF_V + 1024 * wave + 16 * lane) = pre_v;
+    };
+
+    // ---- L2 touch of the (batch, head)'s shared lines, two chunks ahead ----
+    // The vtiles workgroups of one (batch, head) read the same workspace
+    // block and q / k rows, and each reads a slice of the same V rows: with
+    // no one ahead, all of them wait on the same misses.  Each touches one
+    // dword per 128-byte line of its 1/vtiles share of those lines two chunks
+    // ahead, so that the register loads one chunk later hit in L2.  The
+    // touched dwords are folded into a sink one chunk later (by then they
+    // have arrived, so the fold does not wait) and kept live at the end.
+    constexpr int LINE = 128;
+    constexpr int NTOUCH = 2;   // touches per thread and chunk (a share of up to 512 lines)
+    unsigned l2x[NTOUCH] = {0u, 0u}, l2sink = 0u;
+    auto l2_touch = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < NTOUCH; ++i) l2sink |= l2x[i];
+        const int64_t t0 = static_cast<int64_t>(c) * L;
+        const int lq = (K * 2 + LINE - 1) / LINE, lv = (V * 2 + LINE - 1) / LINE;   // lines per row
+        const int n_ws = CHUNK_BYTES / LINE, n_qk = DECAY ? 0 : 2 * L * lq;
+        const int n = n_ws + n_qk + L * lv;
+        const int beg = vt * n / p.vtiles, end = (vt + 1) * n / p.vtiles;
+        const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
+        const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
+        const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
+        const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
+#pragma unroll
+        for (int i = 0; i < NTOUCH; ++i) {
+            const int x = beg + tid + NT * i;
+            unsigned val = 0u;
+            if (x < end) {
+                if (x < n_ws) {
+                    val = __builtin_amdgcn_raw_buffer_load_b32(wp, x * LINE, 0, 0);
+                } else if (x < n_ws + n_qk) {
+                    const int j = x - n_ws, r = (j % (L * lq)) / lq, li = j % lq;
+                    const int off = r * static_cast<int>(qk_row) + h * K * 2 + min(li * LINE, K * 2 - 4);
+                    val = __builtin_amdgcn_raw_buffer_load_b32(j < L * lq ? wq : wk, off, 0, 0);
+                } else {
+                    const int j = x - n_ws - n_qk, r = j / lv, li = j % lv;
+                    const int off = r * static_cast<int>(v_row) + h * V * 2 + min(li * LINE, V * 2 - 4);
+                    val = __builtin_amdgcn_raw_buffer_load_b32(wv, off, 0, 0);
+                }
+            }
+            l2x[i] = val;
         }
     };
 
@@ -810,12 +991,12 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             const BufRes wp = make_rsrc_window(wsb, ws_bytes, cb);
 #pragma unroll
             for (int st2 = 0; st2 < STW; ++st2) {
-                const int key = 16 * (STW * wave + st2) + c16;
+                const int kt = STW * wave + st2;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int hl = 0; hl < 2; ++hl)
-                        w[st2][ks][hl] = buf_load16(wp, off_w<KP>() * 2 + hl * KP * L * 2 + (key * L + 32 * ks + 8 * g) * 2);
+                        w[st2][ks][hl] = buf_load16(wp, (off_w<KP>() + wfrag_off(kt, ks, hl) + 8 * lane) * 2);
                 if constexpr (DECAY)
                     e[st2] = __builtin_bit_cast(f32x4, buf_load16(wp, off_el<KP>() * 2 + (16 * (STW * wave + st2) + 4 * g) * 4));
             }
@@ -823,13 +1004,13 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             const unsigned char* pw = reinterpret_cast<const unsigned char*>(wsb) + cb;
 #pragma unroll
             for (int st2 = 0; st2 < STW; ++st2) {
-                const int key = 16 * (STW * wave + st2) + c16;
+                const int kt = STW * wave + st2;
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                     for (int hl = 0; hl < 2; ++hl)
                         w[st2][ks][hl] = *reinterpret_cast<const u32x4*>(
-                            pw + off_w<KP>() * 2 + hl * KP * L * 2 + (key * L + 32 * ks + 8 * g) * 2);
+                            pw + (off_w<KP>() + wfrag_off(kt, ks, hl) + 8 * lane) * 2);
                 if constexpr (DECAY)
                     e[st2] = *reinterpret_cast<const f32x4*>(pw + off_el<KP>() * 2 + (16 * (STW * wave + st2) + 4 * g) * 4);
             }
@@ -862,8 +1043,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
     };
     write_state_lds();
-    fetch(0, 0);
+    fetch_ops(0, sOps);
+    fetch_pv(0, sPV);
     load_w(0, wcur, ecur);
+    if constexpr (VEC && DECAY)
+        if (nchunks > 1) l2_touch(1);
 
     const int arow = 16 * wave + c16;    // operand row of this wave
     // A chunk's outputs wait in this wave's LDS tile (rows 16 wave .., the 16
@@ -901,12 +1085,24 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     };
     for (int c = 0; c < nchunks; ++c) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
-        const unsigned char* st = sIn + (c & 1) * STAGE;
-        if constexpr (VEC) __builtin_amdgcn_s_waitcnt(0x0F70);   // this wave's loads are done
-        __syncthreads();                                         // ... and every wave's
-        if (c + 1 < nchunks) {
-            fetch(c + 1, (c + 1) & 1);
+        const unsigned char* st = sOps + (SPLIT ? 0 : (c & 1) * OPS);
+        const unsigned char* sp = sPV + (c & 1) * PVS;
+        const bool more = c + 1 < nchunks;
+        unsigned char* so_n = sOps + (SPLIT ? 0 : ((c + 1) & 1) * OPS);
+        unsigned char* sp_n = sPV + ((c + 1) & 1) * PVS;
+        // LDS-direct loads in flight (the first chunk's; SPLIT: every chunk's
+        // operand rows) are waited for here; register-staged loads by their use
+        if constexpr (VEC)
+            if (SPLIT || c == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (more) {
             load_w(c + 1, wnxt, enxt);
+            if constexpr (VEC) {
+                preload_v(c + 1);
+            } else {
+                if constexpr (!SPLIT) fetch_ops(c + 1, so_n);
+                fetch_pv(c + 1, sp_n);
+            }
         }
         if (c > 0) store_outputs(t0 - L);
 
@@ -929,12 +1125,16 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             y = mfma16(ah, sh, y);
             o1 = mfma16(qh, sl, o1);
             o1 = mfma16(qh, sh, o1);
+            // the next chunk's operand pieces, a share per k-step
+            constexpr int NJO = DECAY ? NPO : NPO / 2;
+            if constexpr (VEC && !SPLIT)
+                if (more) preload_ops(c + 1, ks * NJO / KS, (ks + 1) * NJO / KS);
         }
         {
             // V rows 16 wave + 4g .. +3 at column c16, by the transposing read
             const int vr = 16 * wave + 4 * g + (c16 >> 2), vc = 4 * (c16 & 3);
             const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_s16x4*)(st + OFF_V + swz<2>(vr, vc >> 3) + (vc & 4) * 2));
+                (lds_s16x4*)(sp + OFF_V + swz<2>(vr, vc >> 3) + (vc & 4) * 2));
             float rr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) rr[r] = bf2f(static_cast<u16>(v4[r])) - y[r];
@@ -944,6 +1144,19 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             const int t = 16 * wave + 4 * g;
             *reinterpret_cast<u32x2*>(sRTh + c16 * LDL + t) = u32x2{hi[0], hi[1]};
             *reinterpret_cast<u32x2*>(sRTl + c16 * LDL + t) = u32x2{lo[0], lo[1]};
+        }
+        if constexpr (VEC) {
+            if (more) preload_p(c + 1);
+            if constexpr (DECAY)   // (the plain form's shared lines already hit in L2)
+                if (c + 2 < nchunks) l2_touch(c + 2);
+        }
+        if constexpr (SPLIT) {
+            // this wave's operand rows are read (y and o1 hold them): the next
+            // chunk's may overwrite them
+            if (more) {
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
+                fetch_ops(c + 1, sOps);
+            }
         }
         __syncthreads();
 
@@ -959,8 +1172,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         for (int ks = 0; ks < 2; ++ks) {
             if (ks <= wave / 2) {   // MTb is lower triangular
                 const int po = swz<8>(arow, 4 * ks + g);
-                const bf16x8 mh = *reinterpret_cast<const bf16x8*>(st + OFF_P + po);
-                const bf16x8 ml = *reinterpret_cast<const bf16x8*>(st + OFF_P + PB + po);
+                const bf16x8 mh = *reinterpret_cast<const bf16x8*>(sp + OFF_P + po);
+                const bf16x8 ml = *reinterpret_cast<const bf16x8*>(sp + OFF_P + PB + po);
                 o2 = mfma16(ml, rh[ks], o2);
                 o2 = mfma16(mh, rl[ks], o2);
                 o2 = mfma16(mh, rh[ks], o2);
@@ -987,7 +1200,9 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             }
         }
         write_state_lds();
-        if (c + 1 < nchunks) {
+        if constexpr (VEC)
+            if (more) prestore(so_n, sp_n);   // the other stage (SPLIT: this wave's rows only)
+        if (more) {
 #pragma unroll
             for (int s2 = 0; s2 < STW; ++s2) {
 #pragma unroll
@@ -1001,6 +1216,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     }
 
     store_outputs(static_cast<int64_t>(nchunks - 1) * L);
+    if constexpr (VEC && DECAY) {
+#pragma unroll
+        for (int i = 0; i < NTOUCH; ++i) l2sink |= l2x[i];
+        asm volatile("" ::"v"(l2sink));   // the touches stay
+    }
 #pragma unroll
     for (int s2 = 0; s2 < STW; ++s2) {
         const int sr = STW * wave + s2;
@@ -1037,7 +1257,8 @@ int delta_vtile() { return VT; }
 
 size_t delta_workspace_bytes(int B, int T, int H, int K, bool decay) {
     const int64_t nchunks = (static_cast<int64_t>(T) + L - 1) / L;
-    const size_t per_chunk = decay ? chunk_u16<KD, true>() : (K <= 64 ? chunk_u16<64, false>() : chunk_u16<128, false>());
+    const size_t per_chunk = decay ? (K <= 64 ? chunk_u16<64, true>() : chunk_u16<128, true>())
+                                   : (K <= 64 ? chunk_u16<64, false>() : chunk_u16<128, false>());
     return static_cast<size_t>(B) * H * nchunks * per_chunk * sizeof(u16);
 }
 
@@ -1065,7 +1286,7 @@ hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_
     a.out_bf16 = prm.out_bf16;
     if (prm.g) {
         if (prm.K > KD) return hipErrorInvalidValue;
-        return launch_t<KD, true>(a, prm.vec != 0, stream);
+        return prm.K <= 64 ? launch_t<64, true>(a, prm.vec != 0, stream) : launch_t<128, true>(a, prm.vec != 0, stream);
     }
     return prm.K <= 64 ? launch_t<64, false>(a, prm.vec != 0, stream) : launch_t<128, false>(a, prm.vec != 0, stream);
 }

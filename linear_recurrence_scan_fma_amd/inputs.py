@@ -56,6 +56,7 @@ GLA = dict(B=4, T=4096, H=4, K=128, V=128)
 DELTANET = dict(B=4, T=4096, H=8, K=128, V=128)
 DELTANET_K64 = dict(B=4, T=4096, H=8, K=64, V=128)
 RWKV7 = dict(B=4, T=4096, H=12, K=64, V=64)
+DELTA_DECAY_K128 = dict(B=4, T=4096, H=8, K=128, V=128)   # RWKV-7's decay law at DeltaNet's head shape
 HGRN2 = dict(B=4, T=4096, H=16, K=128, V=128)
 ASSOC = dict(B=4, T=4096, H=8, K=64, V=64)
 

@@ -3,10 +3,11 @@
 sequential fp64 oracle, through the C ABI.
 
 Tolerance: normwise relative error <= 2e-3 per (batch, head) slice of o and of
-s_final, as for the other matrix scans.  Cases cover K != V both ways, ragged
-chunks and V tiles, the scalar-load path, T = 1, K = V = 1, decays strong
-enough to take the kernel's exact-exponential path, growth (g > 0) and the
-no-decay limit.
+s_final, as for the other matrix scans.  Cases cover both key widths of the
+kernel (K <= 64 and 64 < K <= 128), K != V both ways, ragged chunks and V
+tiles, the scalar-load path, T = 1, K = V = 1, decays strong enough to take
+the kernel's exact-exponential path, growth (g > 0), the no-decay limit, and
+the full-size workload at K = V = 128 on every head with both paths present.
 """
 import pytest
 import torch
@@ -58,6 +59,11 @@ def _check(ctx, d, s0=None, tol=TOL):
     (1, 77, 2, 36, 20),      # K, V not multiples of 8 (scalar loads)
     (1, 1, 1, 64, 64),       # T = 1
     (2, 50, 2, 1, 1),        # K = V = 1
+    (2, 200, 3, 128, 128),   # K = 128: DeltaNet's head shape, ragged T
+    (1, 150, 2, 128, 64),    # K = 128 > V
+    (1, 130, 2, 100, 40),    # 64 < K < 128 (zero-padded keys), ragged V tile
+    (1, 77, 2, 90, 20),      # 64 < K, not a multiple of 8 (scalar loads)
+    (1, 1, 1, 128, 128),     # K = 128, T = 1
 ], ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("with_s0", [False, True])
 def test_delta_decay_parity(ctx, shape, with_s0):
@@ -68,12 +74,13 @@ def test_delta_decay_parity(ctx, shape, with_s0):
     _check(ctx, d, s0)
 
 
+@pytest.mark.parametrize("K", [64, 128])
 @pytest.mark.parametrize("gval", [-2.0, -0.9], ids=["all_exact_path", "mixed"])
-def test_delta_decay_strong_decay(ctx, gval):
+def test_delta_decay_strong_decay(ctx, gval, K):
     # -2 nats per step: every chunk's running sum spans 126 nats (exact-exponential
     # path); -0.9 on every other step: spans near the switch, both paths
-    B, T, H, K, V = 1, 260, 2, 64, 64
-    say(f"delta decay strong g={gval}")
+    B, T, H, V = 1, 260, 2, 64
+    say(f"delta decay strong g={gval} K={K}")
     d = inputs.rwkv7(B=B, T=T, H=H, K=K, V=V, seed=81)
     g = d["g"].clone()
     if gval == -2.0:
@@ -147,7 +154,7 @@ def test_delta_decay_rejects_bad_arguments(ctx):
     assert L.lrs_scan_delta_decay(h, P(q), P(k), P(v), None, P(beta), 1.0, None, P(o), P(f),
                                   1, 8, 2, 16, 16, None) == binding.LRS_E_INVAL        # g missing
     assert L.lrs_scan_delta_decay(h, P(q), P(k), P(v), P(g), P(beta), 1.0, None, P(o), P(f),
-                                  1, 8, 2, 65, 16, None) == binding.LRS_E_UNSUPPORTED  # K > 64
+                                  1, 8, 2, 129, 16, None) == binding.LRS_E_UNSUPPORTED  # K > 128
     assert L.lrs_scan_delta_decay(h, P(q), P(k), P(v), P(g), P(beta), 1.0, None, P(o), P(o),
                                   1, 8, 2, 16, 16, None) == binding.LRS_E_INVAL        # outputs alias
     assert L.lrs_scan_delta_decay(h, P(q), P(k), P(v), P(g), P(beta), 1.0, None, P(g), P(f),
@@ -169,3 +176,21 @@ def test_rwkv7_full_size_sampled(ctx):
         say(f"   head ({b},{h}): rel err o={eo:.2e} s_final={ef:.2e}")
         assert eo <= TOL and ef <= TOL
     assert torch.isfinite(o).all() and torch.isfinite(fin).all()
+
+
+def test_delta_decay_k128_full_size_all_heads(ctx):
+    # the decayed delta rule at DeltaNet's full size (B=4, T=4096, H=8, K=V=128),
+    # RWKV-7's decay law; on heads 0 and 5 of batch row 1 a stretch of steps
+    # decays by 2 nats per step, so those chunks take the exact-exponential path
+    shape = inputs.DELTA_DECAY_K128
+    say(f"delta decay K=128 full size {shape}, all heads")
+    d = inputs.rwkv7(**shape)
+    g = d["g"].clone()
+    g[1, 1000:1400, 0] = -2.0
+    g[1, 3000:3100, 5, :64] = -2.0
+    d["g"] = g
+    o, fin = _gpu(ctx, d)
+    ro, rf = _ref(d)
+    eo, ef = rel_heads(o, ro, "bthv"), rel_heads(fin, rf, "bhkv")
+    say(f"   worst slice rel err o={eo:.2e} s_final={ef:.2e}")
+    assert eo <= TOL and ef <= TOL, (eo, ef)

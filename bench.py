@@ -494,6 +494,12 @@ MATRIX_ROWS = {
               ["delta_prep_rwkv7_B4_T4096_H12_K64", "delta_scan_rwkv7_B4_T4096_H12_K64_V64"], "f32"),
     "rwkv7_bf16": ("scan_delta_out RWKV-7 B=4 T=4096 H=12 K=64 V=64 (per-key decay), bf16 out", "decay", "rwkv7",
                    ["delta_prep_rwkv7_B4_T4096_H12_K64", "delta_scan_rwkv7_B4_T4096_H12_K64_V64_bf16"], "bf16"),
+    "decay_k128": ("scan_delta_decay B=4 T=4096 H=8 K=128 V=128 (per-key decay, RWKV-7's decay law)", "decay",
+                   "decay_k128", ["delta_prep_decay_B4_T4096_H8_K128", "delta_scan_decay_B4_T4096_H8_K128_V128"],
+                   "f32"),
+    "decay_k128_bf16": ("scan_delta_out B=4 T=4096 H=8 K=128 V=128 (per-key decay), bf16 out", "decay",
+                        "decay_k128", ["delta_prep_decay_B4_T4096_H8_K128",
+                                       "delta_scan_decay_B4_T4096_H8_K128_V128_bf16"], "bf16"),
 }
 
 
@@ -504,7 +510,8 @@ def gen_workload(inputs, which):
             "assoc": lambda: inputs.assoc_memory(**inputs.ASSOC),
             "deltanet": lambda: inputs.deltanet(**inputs.DELTANET),
             "deltanet_k64": lambda: inputs.deltanet(**inputs.DELTANET_K64),
-            "rwkv7": lambda: inputs.rwkv7(**inputs.RWKV7)}[which]()
+            "rwkv7": lambda: inputs.rwkv7(**inputs.RWKV7),
+            "decay_k128": lambda: inputs.rwkv7(**inputs.DELTA_DECAY_K128)}[which]()
 
 
 def oracle_matrix(kind, d, nthreads, heads=None):
@@ -721,11 +728,22 @@ def run_rows_in_subprocesses():
     return rows
 
 
-def profile_run(ctx, binding, inputs, dev, steps):
+def profile_run(ctx, binding, inputs, dev, steps, manifest_path=None):
     """Each kernel at its workload shape, `steps` launches, for rocprofv3
     (kernel trace or counters).  The copy of a 1 GiB tensor reads and writes
-    exactly 2^30 bytes each way and calibrates FETCH_SIZE / WRITE_SIZE."""
+    exactly 2^30 bytes each way and calibrates FETCH_SIZE / WRITE_SIZE.
+
+    With `manifest_path`, writes the launch order as JSON: a list of groups
+    {"keys": [...], "calls": n, "alg_bytes": {...}, "title": ...}; each call
+    of a group dispatches one kernel per key, in order (the library's
+    look-back status fills aside), so a trace's dispatches can be labelled
+    by position."""
     import torch
+
+    manifest = []
+
+    def group(keys, calls, title, alg=None):
+        manifest.append({"keys": list(keys), "calls": calls, "title": title, "alg_bytes": alg or {}})
 
     src = torch.ones(1 << 28, device=dev)
     dst = torch.empty_like(src)
@@ -736,6 +754,10 @@ def profile_run(ctx, binding, inputs, dev, steps):
     a, u, s0 = d["a"].to(dev), d["u"].to(dev), d["s0"].to(dev)
     s = torch.empty_like(a)
     fin = torch.empty_like(s0)
+    cfg = inputs.GATED_LARGE
+    eb = elem_bytes(cfg["B"], cfg["T"], cfg["N"])
+    group(["scan_elem_gated_B16_T8192_N2048"], steps, "gated elementwise scan B=16 T=8192 N=2048 fp32",
+          {"scan_elem_gated_B16_T8192_N2048": eb})
     for _ in range(steps):
         binding.lrs_scan_gated(ctx, a, u, s0, s, fin)
     torch.cuda.synchronize()
@@ -744,8 +766,12 @@ def profile_run(ctx, binding, inputs, dev, steps):
     da = torch.empty_like(a)
     dx = torch.empty_like(a)
     ds0 = torch.empty_like(s0)
+    group(["scan_elem_gated_bwd_B16_T8192_N2048"], steps,
+          "gradient pass of the gated elementwise scan B=16 T=8192 N=2048 fp32")
     for _ in range(steps):
         binding.lrs_scan_gated_backward(ctx, a, u, s0, g["s"], g["ds"], g["dsf"], da, dx, ds0)
+    group(["scan_elem_fma_bwd_B16_T8192_N2048"], steps,
+          "gradient pass of the FMA elementwise scan B=16 T=8192 N=2048 fp32")
     for _ in range(steps):
         binding.lrs_scan_fma_backward(ctx, a, s0, g["s"], g["ds"], g["dsf"], da, dx, ds0)
     torch.cuda.synchronize()
@@ -754,6 +780,7 @@ def profile_run(ctx, binding, inputs, dev, steps):
     sa = torch.full(STEP_LARGE, 0.5, device=dev)
     sx = torch.ones(STEP_LARGE, device=dev)
     st = torch.zeros(STEP_LARGE, device=dev)
+    group(["step_elem_gated_B16_N4194304"], steps, "one gated step over B=16 x N=4194304 channels fp32")
     for _ in range(steps):
         binding.lrs_step_gated(ctx, sa, sx, st)
     torch.cuda.synchronize()
@@ -766,19 +793,23 @@ def profile_run(ctx, binding, inputs, dev, steps):
     ssa = torch.full(STEP_SMALL, 0.5, device=dev)
     ssx = torch.ones(STEP_SMALL, device=dev)
     sst = torch.zeros(STEP_SMALL, device=dev)
+    group(["scan_elem_fma_B2_T128_N128", "scan_elem_gated_B2_T128_N128", "step_elem_gated_B16_N2048"], steps,
+          "the launch-bound calls: FMA and gated scans B=2 T=128 N=128, one gated step B=16 N=2048")
     for _ in range(steps):
         binding.lrs_scan_fma(ctx, ea, eb, None, es, ef)
         binding.lrs_scan_gated(ctx, ea, eu, None, es, ef)
         binding.lrs_step_gated(ctx, ssa, ssx, sst)
     torch.cuda.synchronize()
     for name in MATRIX_ROWS:
-        label, kind, which, _, odt = MATRIX_ROWS[name]
+        label, kind, which, keys, odt = MATRIX_ROWS[name]
         m = gen_workload(inputs, which)
         q, k, v = (m[n].to(dev) for n in ("q", "k", "v"))
         B, T, H, V = v.shape
         K = q.shape[3]
         o = torch.empty((B, T, H, V), device=dev, dtype=torch.bfloat16 if odt == "bf16" else torch.float32)
         fin = torch.empty((B, H, K, V), device=dev)
+        call_bytes = (diag_bytes(m) if kind in ("diag", "keyscale") else delta_bytes(m, 2 if odt == "bf16" else 4))
+        group(keys, steps, label, {"call": call_bytes})
         for _ in range(steps):
             if kind == "diag":
                 binding.lrs_scan_diag_outer(ctx, q, k, v, m["g"].to(dev), m["decay_mode"],
@@ -794,13 +825,17 @@ def profile_run(ctx, binding, inputs, dev, steps):
                                            o, fin)
         torch.cuda.synchronize()
     for name in EPI_ROWS:
-        label, which, epi, _ = EPI_ROWS[name]
+        label, which, epi, keys = EPI_ROWS[name]
         m = with_epilogue(inputs, gen_workload(inputs, which), epi)
         fn, _ = epilogue_call(binding, ctx, m, dev)
+        group(keys, steps, label, {"call": epilogue_bytes(m)})
         for _ in range(steps):
             fn()
         torch.cuda.synchronize()
     assert binding.lrs_context_check(ctx) == binding.LRS_OK
+    if manifest_path:
+        with open(manifest_path, "w") as f:
+            json.dump(manifest, f, indent=1)
     log("[bench] profile run done")
 
 
@@ -812,6 +847,7 @@ def main():
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--row", help="run one row in this process and print it (used by the full run)")
+    ap.add_argument("--manifest", help="with --profile: write the launch order (JSON) here")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3 runs: launch each kernel a few times, plus a plain 1 GiB "
                          "device copy that calibrates the HBM byte counters; prints no JSON line")
@@ -833,7 +869,7 @@ def main():
     if args.profile:
         dev = torch.device("cuda:0")
         with binding.Context(0) as ctx:
-            profile_run(ctx, binding, inputs, dev, args.steps)
+            profile_run(ctx, binding, inputs, dev, args.steps, args.manifest)
         return
 
     # the rows first, each in a child process started before this process

@@ -215,13 +215,23 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     // plain form: sQ, sK as padded rows.  Decayed form: four unpadded tiles
     // whose 16-byte pieces are rotated by an XOR of the row (a hi/lo, later
     // overwritten by qt hi/lo, and b hi/lo), then the running log-decay G; the
-    // whole block is dead once A and M are formed, so sA and sT reuse it.  The
-    // decayed form thus fits three workgroups per compute unit at K = 64.
-    constexpr int TILE_D = L * KP * 2;
+    // whole block is dead once A and M are formed, so sA and sT reuse it.  At
+    // K = 128 the tiles hold half the keys and A and M are summed over the two
+    // halves in turn, so two workgroups fit a compute unit instead of one (prep
+    // ~171 -> ~120 us at B=4 T=4096 H=8); at K = 64 the registers, not the LDS,
+    // hold it to three workgroups, and the halves' extra barriers only cost.
+    constexpr int KH = KP > 64 ? KP / 2 : KP;      // keys per tile
+    constexpr int NHALF = KP / KH;
+    constexpr int TILE_D = L * KH * 2;
     constexpr int G_OFF = 4 * TILE_D;
     constexpr int QK_BYTES = DECAY ? G_OFF + L * LDG * 4 : 2 * L * LDK * 2;
     constexpr int AT_BYTES = 2 * L * LDA * 4;      // sA, sT (fp32) reuse the same space
-    constexpr int U_BYTES = QK_BYTES > AT_BYTES ? QK_BYTES : AT_BYTES;
+    // khat for W ([L][KP] bf16, hi and lo in the decayed form) goes into M's
+    // space, or past sA and sT where it does not fit there (decayed, K = 128)
+    constexpr int KHAT_BYTES = (DECAY ? 2 : 1) * L * KP * 2;
+    constexpr bool KH_PAST = KHAT_BYTES > L * LDA * 4;
+    constexpr int AK_BYTES = AT_BYTES + (KH_PAST ? KHAT_BYTES : 0);
+    constexpr int U_BYTES = QK_BYTES > AK_BYTES ? QK_BYTES : AK_BYTES;
     __shared__ __align__(16) unsigned char sU[U_BYTES];
     __shared__ __align__(16) float sBeta[L];
     __shared__ float sTot[DECAY ? 4 : 1][DECAY ? KP : 1];
@@ -352,10 +362,10 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             for (int r = 0; r < 16; ++r) dev = fmaxf(dev, fabsf(gl[kk][r] - ref));
         }
         const bool fast = !__syncthreads_or(dev > kHalfSpan);
-        u16* tAh = tile;                 // a hi, later qt hi
-        u16* tAl = tile + L * KP;        // a lo, later qt lo
-        u16* tBh = tile + 2 * L * KP;
-        u16* tBl = tile + 3 * L * KP;
+        u16* tAh = tile;                 // a hi, later qt hi (half the keys)
+        u16* tAl = tile + L * KH;        // a lo, later qt lo
+        u16* tBh = tile + 2 * L * KH;
+        u16* tBl = tile + 3 * L * KH;
         {
             // the scan's operands, relative to the chunk start: a = e^{G_{t-1}} k and
             // qt = e^{G_t} q as hi/lo planes, e^{G_L}, and khat = e^{G_L - G_t} k (kept
@@ -389,33 +399,13 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
             if (tid < KP) reinterpret_cast<float*>(blk + off_el<KP>())[tid] = __expf(sG[(L - 1) * LDG + tid]);
         }
         if (fast) {
-            // a = e^{G_{t-1} - ref} k and b = e^{ref - G_t} k as hi/lo, eight keys of
-            // one step per piece (the raw k in registers); A = a b^T; then
-            // qt = e^{G_t - ref} q into a's tiles and M = qt b^T
+            // per key range (all keys, or one half at K = 128): a = e^{G_{t-1} - ref} k
+            // and b = e^{ref - G_t} k as hi/lo (eight keys of one step per piece, the
+            // raw k in registers), A += a b^T; then qt = e^{G_t - ref} q into a's
+            // tiles, M += qt b^T
             constexpr int NPC = L * KP / 8 / NT;
 #pragma unroll
-            for (int j = 0; j < NPC; ++j) {
-                const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
-                const u32x4 kw = xk[j];
-                float av[8], bv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float r0 = sRef[i0 + e];
-                    const float gt = sG[t * LDG + i0 + e], gp = t > 0 ? sG[(t - 1) * LDG + i0 + e] : 0.0f;
-                    const float kv = bf2f(piece_elem(kw, e));
-                    av[e] = kv * __expf(gp - r0);
-                    bv[e] = kv * __expf(r0 - gt);
-                }
-                bf16x8 hi, lo;
-                const int o = tswz<KP>(t, i0);
-                split8(av, hi, lo);
-                *reinterpret_cast<bf16x8*>(tAh + o) = hi;
-                *reinterpret_cast<bf16x8*>(tAl + o) = lo;
-                split8(bv, hi, lo);
-                *reinterpret_cast<bf16x8*>(tBh + o) = hi;
-                *reinterpret_cast<bf16x8*>(tBl + o) = lo;
-            }
-            __syncthreads();
+            for (int m = 0; m < 5; ++m) acc[m] = zero4();
             auto blocks = [&](bool want_m) {
 #pragma unroll
                 for (int m = 0; m < 5; ++m) {
@@ -423,11 +413,11 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                     if ((n >= 10) != want_m) continue;
                     int bi, bj;
                     tri_block(n % 10, bi, bj);
-                    f32x4 a = zero4();
+                    f32x4 a = acc[m];
 #pragma unroll
-                    for (int k0 = 0; k0 < KP; k0 += 32) {
-                        const bf16x8 xh = tfrag<KP>(tAh, 16 * bi, k0, lane), xl = tfrag<KP>(tAl, 16 * bi, k0, lane);
-                        const bf16x8 yh = tfrag<KP>(tBh, 16 * bj, k0, lane), yl = tfrag<KP>(tBl, 16 * bj, k0, lane);
+                    for (int k0 = 0; k0 < KH; k0 += 32) {
+                        const bf16x8 xh = tfrag<KH>(tAh, 16 * bi, k0, lane), xl = tfrag<KH>(tAl, 16 * bi, k0, lane);
+                        const bf16x8 yh = tfrag<KH>(tBh, 16 * bj, k0, lane), yl = tfrag<KH>(tBl, 16 * bj, k0, lane);
                         a = mfma16(xl, yh, a);
                         a = mfma16(xh, yl, a);
                         a = mfma16(xh, yh, a);
@@ -435,32 +425,63 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                     acc[m] = a;
                 }
             };
-            blocks(false);
-            __syncthreads();   // a is read: its tiles take qt
 #pragma unroll
-            for (int j = 0; j < NPC; ++j) {
-                const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
-                const u32x4 qw = xq[j];
-                float qv[8];
+            for (int hh = 0; hh < NHALF; ++hh) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    qv[e] = bf2f(piece_elem(qw, e)) * __expf(sG[t * LDG + i0 + e] - sRef[i0 + e]);
-                bf16x8 hi, lo;
-                const int o = tswz<KP>(t, i0);
-                split8(qv, hi, lo);
-                *reinterpret_cast<bf16x8*>(tAh + o) = hi;
-                *reinterpret_cast<bf16x8*>(tAl + o) = lo;
+                for (int j = 0; j < NPC; ++j) {
+                    const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
+                    if (i0 / KH != hh) continue;
+                    const u32x4 kw = xk[j];
+                    float av[8], bv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float r0 = sRef[i0 + e];
+                        const float gt = sG[t * LDG + i0 + e], gp = t > 0 ? sG[(t - 1) * LDG + i0 + e] : 0.0f;
+                        const float kv = bf2f(piece_elem(kw, e));
+                        av[e] = kv * __expf(gp - r0);
+                        bv[e] = kv * __expf(r0 - gt);
+                    }
+                    bf16x8 hi, lo;
+                    const int o = tswz<KH>(t, i0 - hh * KH);
+                    split8(av, hi, lo);
+                    *reinterpret_cast<bf16x8*>(tAh + o) = hi;
+                    *reinterpret_cast<bf16x8*>(tAl + o) = lo;
+                    split8(bv, hi, lo);
+                    *reinterpret_cast<bf16x8*>(tBh + o) = hi;
+                    *reinterpret_cast<bf16x8*>(tBl + o) = lo;
+                }
+                __syncthreads();
+                blocks(false);
+                __syncthreads();   // a is read: its tiles take qt
+#pragma unroll
+                for (int j = 0; j < NPC; ++j) {
+                    const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
+                    if (i0 / KH != hh) continue;
+                    const u32x4 qw = xq[j];
+                    float qv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        qv[e] = bf2f(piece_elem(qw, e)) * __expf(sG[t * LDG + i0 + e] - sRef[i0 + e]);
+                    bf16x8 hi, lo;
+                    const int o = tswz<KH>(t, i0 - hh * KH);
+                    split8(qv, hi, lo);
+                    *reinterpret_cast<bf16x8*>(tAh + o) = hi;
+                    *reinterpret_cast<bf16x8*>(tAl + o) = lo;
+                }
+                __syncthreads();
+                blocks(true);
+                if (hh + 1 < NHALF) __syncthreads();   // the tiles take the second half
             }
-            __syncthreads();
-            blocks(true);
         } else {
             // strong decay: each needed entry from its pairs, exact exponentials
-            // (the raw k into tAh, the raw q into tBh)
+            // (the raw k and q as full-width tiles over the a and b half tiles)
+            u16* const tK = tAh;   // [L][KP], spans tAh and tAl
+            u16* const tQ = tBh;   // [L][KP], spans tBh and tBl
 #pragma unroll
             for (int j = 0; j < NPI; ++j) {
                 const int pc = tid + j * NT, t = pc / (KP / 8), i0 = (pc % (KP / 8)) * 8;
-                *reinterpret_cast<u32x4*>(tAh + tswz<KP>(t, i0)) = xk[j];
-                *reinterpret_cast<u32x4*>(tBh + tswz<KP>(t, i0)) = xq[j];
+                *reinterpret_cast<u32x4*>(tK + tswz<KP>(t, i0)) = xk[j];
+                *reinterpret_cast<u32x4*>(tQ + tswz<KP>(t, i0)) = xq[j];
             }
             __syncthreads();
 #pragma unroll
@@ -474,10 +495,10 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                     const int t = 16 * bi + 4 * g + r;
                     float sum = 0.0f;
                     if (n < 10 ? tau < t : tau <= t) {
-                        const u16* ltile = n < 10 ? tAh : tBh;
+                        const u16* ltile = n < 10 ? tK : tQ;
                         const float* gl_row = n < 10 ? sG + (t - 1) * LDG : sG + t * LDG;   // t >= 1 when n < 10
                         for (int i = 0; i < KP; ++i)
-                            sum += bf2f(ltile[tswz<KP>(t, i)]) * bf2f(tAh[tswz<KP>(tau, i)]) *
+                            sum += bf2f(ltile[tswz<KP>(t, i)]) * bf2f(tK[tswz<KP>(tau, i)]) *
                                    __expf(gl_row[i] - sG[tau * LDG + i]);
                     }
                     acc[m][r] = sum;
@@ -640,8 +661,7 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
     // bf16) or e^{G_L - G_t} k (decayed form, hi/lo), staged [step][key] in M's
     // space, or past sA and sT where it does not fit there (decayed, K = 128)
     {
-        constexpr bool KH_PAST = (DECAY ? 2 : 1) * L * KP * 2 > L * LDA * 4;
-        static_assert(!KH_PAST || U_BYTES - AT_BYTES >= 2 * L * KP * 2, "khat fits past sA and sT");
+        static_assert(!KH_PAST || U_BYTES - AT_BYTES >= KHAT_BYTES, "khat fits past sA and sT");
         u16* sKh = KH_PAST ? reinterpret_cast<u16*>(sU + AT_BYTES) : reinterpret_cast<u16*>(sM);
         u16* sKl = sKh + L * KP;
 #pragma unroll

@@ -723,12 +723,15 @@ __device__ __forceinline__ int swz(int r, int p) {
 
 // Wave w owns chunk rows 16w .. 16w+15 (Y, R, outputs) and state keys
 // 16 STW w .. (row tiles of S).  The chunk's operand tiles (q and k; decayed
-// form: a and qt as hi/lo), the MTb planes and the V tile are fetched one
-// chunk ahead straight into LDS (buffer loads with an LDS destination: whole
-// 1 KB runs per instruction, no registers held), double buffered by chunk
-// parity, into swizzled tiles read as matrix-core operands.  W (and e^{G_L})
-// of the next chunk are prefetched into registers: each wave reads only the
-// rows of its own state keys.  Per chunk, two barriers:
+// form: a and qt as hi/lo), the MTb planes and the V tile sit in one of two
+// LDS stages (by chunk parity) as swizzled tiles read as matrix-core
+// operands.  With vector loads the next chunk's are loaded into registers in
+// groups spread over a chunk (a q/k piece after each k-step of step 1, the
+// MTb planes after it, the V tile after the first barrier) and written to the
+// other stage at the end of the chunk; the first chunk's come through loads
+// with an LDS destination.  W (and e^{G_L}) of the next chunk are loaded into
+// registers too: each wave reads only the rows of its own state keys, as
+// contiguous 1 KB fragments.  Per chunk, two barriers:
 //   -- inputs of chunk c visible --
 //   1. Y = K S0, O1 = Q S0 (rows of this wave); R = V - Y -> LDS
 //   -- barrier --
@@ -736,8 +739,9 @@ __device__ __forceinline__ int swz(int r, int p) {
 //      -> LDS as the next chunk's operand
 // The decayed form at K = 128 has 64 KB of operand tiles per chunk, too much
 // to double buffer beside the rest: there they are single buffered, and each
-// wave loads the next chunk's rows of its own (the only rows it reads) as
-// soon as its step 1 is done with them, so they load during step 2.
+// wave loads the next chunk's rows of its own (the only rows it reads) with
+// LDS-destination loads as soon as its step 1 is done with them, so they
+// load during step 2.
 template <int KP, bool VEC, bool DECAY>
 __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     static_assert(!DECAY || KP == 64 || KP == KD, "decayed form: K <= 128");
@@ -795,12 +799,10 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     // takes slot s = 64 i + l, i.e. row s / PPR, stored piece s % PPR, which
     // holds the row's piece (s % PPR) ^ (row & (PPR - 1)).
     // Operand tiles into `so_`; all rows, or (SPLIT) this wave's 16.  With
-    // vector loads a wave issues its runs j0 .. j1 - 1 of NJ_OPS (a run: one
-    // load instruction per operand tile of the plain form, one in all of the
-    // decayed form), so that the loads can be spread over a chunk's work.
-    auto fetch_ops = [&](int c, unsigned char* so_, int j0 = 0, int j1 = -1) {
+    // vector loads a wave issues its NJ_OPS runs (a run: one load instruction
+    // per operand tile of the plain form, one in all of the decayed form).
+    auto fetch_ops = [&](int c, unsigned char* so_) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
-        if (j1 < 0) j1 = NJ_OPS;
         if constexpr (VEC) {
             if constexpr (DECAY) {
                 // a hi, a lo, qt hi, qt lo: four [L][KP] tiles, back to back in the workspace
@@ -808,7 +810,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 if constexpr (SPLIT) {
                     constexpr int RPR = 64 / PPR;   // rows per run
 #pragma unroll
-                    for (int j = j0; j < j1; ++j) {
+                    for (int j = 0; j < NJ_OPS; ++j) {
                         const int tl = j / (16 / RPR), row0 = 16 * wave + RPR * (j % (16 / RPR));
                         const int row = row0 + lane / PPR, pc = (lane % PPR) ^ (row & (PPR - 1));
                         const int off = off_aq<KP>() * 2 + tl * QB + row * KP * 2 + pc * 16;
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                     }
                 } else {
 #pragma unroll
-                    for (int j = j0; j < j1; ++j) {
+                    for (int j = 0; j < NJ_OPS; ++j) {
                         const int i = wave + 4 * j, tl = i / (QB / 1024), sl = 64 * (i % (QB / 1024)) + lane;
                         const int row = sl / PPR, pc = (sl % PPR) ^ (row & (PPR - 1));
                         const int off = off_aq<KP>() * 2 + tl * QB + row * KP * 2 + pc * 16;
@@ -830,7 +832,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 const BufRes wq = make_rsrc_window(qb, T * qk_row, t0 * qk_row);
                 const BufRes wk = make_rsrc_window(kb, T * qk_row, t0 * qk_row);
 #pragma unroll
-                for (int j = j0; j < j1; ++j) {
+                for (int j = 0; j < NJ_OPS; ++j) {
                     const int i = wave + 4 * j, sl = 64 * i + lane;
                     const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
                     const int off = col < K ? ((row * H + h) * K + col) * 2 : kBufOOB;
@@ -869,16 +871,14 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             }
         }
     };
-    // MTb planes (runs j0 .. j1 - 1 of NJ_P with vector loads) and, with
-    // `with_v`, the V tile into `sp_`
-    auto fetch_pv = [&](int c, unsigned char* sp_, int j0 = 0, int j1 = -1, bool with_v = true) {
+    // MTb planes and the V tile into `sp_`
+    auto fetch_pv = [&](int c, unsigned char* sp_) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
-        if (j1 < 0) j1 = NJ_P;
         if constexpr (VEC) {
             const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
             const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
 #pragma unroll
-            for (int j = j0; j < j1; ++j) {
+            for (int j = 0; j < NJ_P; ++j) {
                 const int i = wave + 4 * j;                 // run over the two MTb planes
                 const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
                 const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
@@ -886,7 +886,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     wp, (__attribute__((address_space(3))) void*)(sp_ + OFF_P + 1024 * i), 16, off, 0, 0, 0);
             }
-            if (with_v && wave < 2) {
+            if (wave < 2) {
                 const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
                 const int off = v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB;
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(

@@ -90,6 +90,23 @@ def test_graph_delta(ctx, decay):
     _replay_matches(run, x, fresh, [o, fin])
 
 
+def test_graph_delta_out_bf16_decay_k128(ctx):
+    # the decayed delta rule at K = 128 (half-key prep tiles, single-buffered
+    # scan operands, L2 touches) with a bf16 output
+    B, T, H, K, V = 1, 200, 2, 128, 64
+    d = inputs.rwkv7(B=B, T=T, H=H, K=K, V=V, seed=1601)
+    names = ("q", "k", "v", "g", "beta")
+    x = {n: d[n].to("cuda:0") for n in names}
+    o = torch.empty((B, T, H, V), device="cuda:0", dtype=torch.bfloat16)
+    fin = torch.empty((B, H, K, V), device="cuda:0")
+    say("graph: delta decay K=128, bf16 out")
+    run = lambda: binding.lrs_scan_delta_out(ctx, x["q"], x["k"], x["v"], x["g"], x["beta"], 1.0, None,  # noqa: E731
+                                             binding.LRS_DTYPE_BF16, o, fin)
+    fresh = lambda i: [inputs.rwkv7(B=B, T=T, H=H, K=K, V=V, seed=1700 + i)[n].to("cuda:0")  # noqa: E731
+                       for n in names]
+    _replay_matches(run, [x[n] for n in names], fresh, [o, fin])
+
+
 def test_graph_elementwise_stream_schedule(ctx):
     B, T, N = 2, 500, 256
     d = inputs.elementwise_small(B, T, N, seed=1601)

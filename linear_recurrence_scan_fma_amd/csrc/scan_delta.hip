@@ -57,7 +57,8 @@ constexpr int KD = 128;        // largest key width of the decayed form
 constexpr float kHalfSpan = 30.0f;   // decayed prep: factor exponents stay within +-30 nats
 
 // One chunk's workspace block, in u16 elements:
-//   MTb hi, MTb lo          2 x [L][L]
+//   MTb hi, MTb lo          4 x 2 x 2 blocks of 512: MTb in the scan's operand
+//                           order (as W; blocks above the diagonal unused)
 //   W hi, W lo              KP / 16 x 2 x 2 blocks of 512: W in the scan's
 //                           operand order (below)
 //   decayed form only:
@@ -70,6 +71,10 @@ constexpr int off_w() { return 2 * PLANE; }
 // lane l, keys 16 kt + l % 16 and steps 32 ks + 8 (l / 16) .. +7, so that each
 // of the scan's loads reads one contiguous kilobyte (whole cache lines).
 __device__ __forceinline__ int wfrag_off(int kt, int ks, int hl) { return ((kt * 2 + ks) * 2 + hl) * 512; }
+// MTb (64 steps t x 64 steps tau) in the same order: block (row tile rb, step
+// half ks, hi/lo) holds, for lane l, rows 16 rb + l % 16 and columns
+// 32 ks + 8 (l / 16) .. +7.  The scan reads blocks with ks <= rb / 2 only.
+__device__ __forceinline__ int mfrag_off(int rb, int ks, int hl) { return ((rb * 2 + ks) * 2 + hl) * 512; }
 template <int KP>
 constexpr int off_aq() { return 2 * PLANE + 2 * KP * L; }
 template <int KP>
@@ -638,22 +643,21 @@ __global__ __launch_bounds__(NT) void delta_prep_kernel(DeltaArgs p) {
                 const int to = (16 * bj + c16) * LDT + 16 * m + 4 * g;
                 X = mm16_la(*reinterpret_cast<const s16x4*>(tTh + to), *reinterpret_cast<const s16x4*>(tTl + to), a, X);
             }
-            // X[r]: row 16 bi + c16, column 16 bj + 4 g + r
+            // X[r]: row 16 bi + c16, column 16 bj + 4 g + r: fragment lane
+            // c16 + 16 (2 (bj % 2) + g / 2), elements 4 (g % 2) + r of block (bi, bj / 2)
             u16 hi[4], lo[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) split_bf16(X[r], hi[r], lo[r]);
-            const int idx = (16 * bi + c16) * L + 16 * bj + 4 * g;
+            const int idx = mfrag_off(bi, bj >> 1, 0) + (c16 + 16 * (2 * (bj & 1) + (g >> 1))) * 8 + 4 * (g & 1);
             store4(blk + idx, hi[0], hi[1], hi[2], hi[3]);
-            store4(blk + PLANE + idx, lo[0], lo[1], lo[2], lo[3]);
+            store4(blk + idx + 512, lo[0], lo[1], lo[2], lo[3]);
         }
-        // zeros for the blocks right of the diagonal
-        const int row = tid / 4, c0 = (tid % 4) * 16;
-        if (c0 >= 16 * (row / 16 + 1)) {
+        // zeros for the blocks right of the diagonal that the scan reads: (0, 1)
+        // and (2, 3), the upper halves (lanes 32 ..) of blocks (0, 0) and (2, 1)
+        if (tid < 128) {
+            const int rb = (tid >> 6) * 2, hl = (tid >> 5) & 1, lp = 32 + (tid & 31);
             const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(blk + row * L + c0) = z;
-            *reinterpret_cast<u32x4*>(blk + row * L + c0 + 8) = z;
-            *reinterpret_cast<u32x4*>(blk + PLANE + row * L + c0) = z;
-            *reinterpret_cast<u32x4*>(blk + PLANE + row * L + c0 + 8) = z;
+            *reinterpret_cast<u32x4*>(blk + mfrag_off(rb, rb >> 1, hl) + lp * 8) = z;
         }
     }
     __syncthreads();   // M is read: its space takes khat
@@ -754,11 +758,10 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     constexpr int OFF_AH = DECAY ? 0 : QB, OFF_AL = QB;        // k (a hi, a lo)
     constexpr int OFF_QH = DECAY ? 2 * QB : 0, OFF_QL = 3 * QB;   // q (qt hi, qt lo)
     constexpr int OPS = NOPS * QB;       // operand stage
-    constexpr int OFF_P = 0, OFF_V = 2 * PB;
-    constexpr int PVS = OFF_V + VB;      // MTb + V stage
+    constexpr int OFF_V = 0;
+    constexpr int PVS = OFF_V + VB;      // V stage
     // load runs per wave and chunk (vector loads): operand tiles, MTb planes
     constexpr int NJ_OPS = SPLIT ? 4 * 16 * PPR / 64 : (DECAY ? 4 : 1) * QB / 4096;
-    constexpr int NJ_P = 2 * PB / 4096;
     constexpr int CHUNK_BYTES = chunk_u16<KP, DECAY>() * 2;
     constexpr int LDK = KP + 8;
     constexpr int LDL = L + 8;
@@ -871,21 +874,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             }
         }
     };
-    // MTb planes and the V tile into `sp_`
+    // the V tile into `sp_`
     auto fetch_pv = [&](int c, unsigned char* sp_) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
         if constexpr (VEC) {
             const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
-            const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
-#pragma unroll
-            for (int j = 0; j < NJ_P; ++j) {
-                const int i = wave + 4 * j;                 // run over the two MTb planes
-                const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
-                const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
-                const int off = (pl * PLANE + row * L + col) * 2;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    wp, (__attribute__((address_space(3))) void*)(sp_ + OFF_P + 1024 * i), 16, off, 0, 0, 0);
-            }
             if (wave < 2) {
                 const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
                 const int off = v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB;
@@ -893,13 +886,6 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                     wv, (__attribute__((address_space(3))) void*)(sp_ + OFF_V + 1024 * wave), 16, off, 0, 0, 0);
             }
         } else {
-            const u16* pw = wsb + static_cast<int64_t>(c) * chunk_u16<KP, DECAY>();
-            for (int sl = tid; sl < 2 * L * 8; sl += NT) {
-                const int pl = sl / (L * 8), s2 = sl % (L * 8);
-                const int row = s2 / 8, col = ((s2 % 8) ^ (row & 7)) * 8;
-                *reinterpret_cast<u32x4*>(sp_ + OFF_P + 16 * sl) =
-                    *reinterpret_cast<const u32x4*>(pw + pl * PLANE + row * L + col);
-            }
             if (tid < L * 2) {
                 const int row = tid / 2, col = ((tid % 2) ^ (row & 1)) * 8;
                 const int64_t t = t0 + row;
@@ -916,9 +902,9 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     // (An LDS-direct load in flight makes the compiler wait for it before any
     // later LDS read it cannot tell apart, which would expose the prefetch.)
     // Plain form: q and k pieces of runs 0 .. QB/4096 - 1; decayed form (not
-    // SPLIT): the four operand tiles' runs; then the MTb planes and the V tile.
+    // SPLIT): the four operand tiles' runs; then the V tile.
     constexpr int NPO = SPLIT ? 1 : (DECAY ? 4 : 2) * QB / 4096;
-    u32x4 pre_o[NPO], pre_p[NJ_P], pre_v;
+    u32x4 pre_o[NPO], pre_v;
     auto preload_ops = [&](int c, int j0, int j1) {
         if constexpr (DECAY) {
             const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
@@ -942,16 +928,6 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             }
         }
     };
-    auto preload_p = [&](int c) {
-        const BufRes wp = make_rsrc_window(wsb, ws_bytes, static_cast<int64_t>(c) * CHUNK_BYTES);
-#pragma unroll
-        for (int j = 0; j < NJ_P; ++j) {
-            const int i = wave + 4 * j;
-            const int pl = i / (PB / 1024), sl = 64 * (i % (PB / 1024)) + lane;
-            const int row = sl / 8, col = ((sl % 8) ^ (row & 7)) * 8;
-            pre_p[j] = buf_load16(wp, (pl * PLANE + row * L + col) * 2);
-        }
-    };
     auto preload_v = [&](int c) {
         if (wave < 2) {
             const int64_t t0 = static_cast<int64_t>(c) * L;
@@ -973,9 +949,6 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 }
             }
         }
-#pragma unroll
-        for (int j = 0; j < NJ_P; ++j)
-            *reinterpret_cast<u32x4*>(sp_ + OFF_P + 1024 * (wave + 4 * j) + 16 * lane) = pre_p[j];
         if (wave < 2) *reinterpret_cast<u32x4*>(sp_ + OFF_V + 1024 * wave + 16 * lane) = pre_v;
     };
 
@@ -1023,12 +996,24 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
     };
 
-    // ---- W rows of this wave's state keys (and e^{G_L}), into registers ----
-    // W frag (st, ks): key 16 sr + c16, steps 32 ks + 8 g .. +7; hi then lo
-    u32x4 wcur[STW][2][2], wnxt[STW][2][2];
+    // ---- W rows of this wave's state keys (and e^{G_L}), and the MTb rows
+    // of its chunk rows, into registers ----
+    // W frag (st, ks): key 16 sr + c16, steps 32 ks + 8 g .. +7; hi then lo.
+    // MTb frag (ks): row 16 wave + c16, steps 32 ks + 8 g .. +7 (ks <= wave / 2)
+    u32x4 wcur[STW][2][2], wnxt[STW][2][2], mcur[2][2], mnxt[2][2];
     f32x4 ecur[DECAY ? STW : 1], enxt[DECAY ? STW : 1];
-    auto load_w = [&](int c, u32x4 (&w)[STW][2][2], f32x4 (&e)[DECAY ? STW : 1]) {
+    auto load_w = [&](int c, u32x4 (&w)[STW][2][2], f32x4 (&e)[DECAY ? STW : 1], u32x4 (&m)[2][2]) {
         const int64_t cb = static_cast<int64_t>(c) * CHUNK_BYTES;
+        {
+            // the workspace is the library's own (16-byte aligned): vector loads on both paths
+            const BufRes wp = make_rsrc_window(wsb, ws_bytes, cb);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    m[ks][hl] = ks <= wave / 2 ? buf_load16(wp, (mfrag_off(wave, ks, hl) + 8 * lane) * 2)
+                                               : u32x4{0u, 0u, 0u, 0u};
+        }
         if constexpr (VEC) {
             const BufRes wp = make_rsrc_window(wsb, ws_bytes, cb);
 #pragma unroll
@@ -1087,7 +1072,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     write_state_lds();
     fetch_ops(0, sOps);
     fetch_pv(0, sPV);
-    load_w(0, wcur, ecur);
+    load_w(0, wcur, ecur, mcur);
     if constexpr (VEC && DECAY)
         if (nchunks > 1) l2_touch(1);
 
@@ -1138,7 +1123,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             if (SPLIT || c == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if (more) {
-            load_w(c + 1, wnxt, enxt);
+            load_w(c + 1, wnxt, enxt, mnxt);
             if constexpr (VEC) {
                 preload_v(c + 1);
             } else {
@@ -1188,7 +1173,6 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             *reinterpret_cast<u32x2*>(sRTl + c16 * LDL + t) = u32x2{lo[0], lo[1]};
         }
         if constexpr (VEC) {
-            if (more) preload_p(c + 1);
             if constexpr (DECAY)   // (the plain form's shared lines already hit in L2)
                 if (c + 2 < nchunks) l2_touch(c + 2);
         }
@@ -1213,9 +1197,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks <= wave / 2) {   // MTb is lower triangular
-                const int po = swz<8>(arow, 4 * ks + g);
-                const bf16x8 mh = *reinterpret_cast<const bf16x8*>(sp + OFF_P + po);
-                const bf16x8 ml = *reinterpret_cast<const bf16x8*>(sp + OFF_P + PB + po);
+                const bf16x8 mh = as_bf16x8(mcur[ks][0]), ml = as_bf16x8(mcur[ks][1]);
                 o2 = mfma16(ml, rh[ks], o2);
                 o2 = mfma16(mh, rl[ks], o2);
                 o2 = mfma16(mh, rh[ks], o2);
@@ -1253,6 +1235,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                     wcur[s2][ks][1] = wnxt[s2][ks][1];
                 }
                 if constexpr (DECAY) ecur[s2] = enxt[s2];
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                mcur[ks][0] = mnxt[ks][0];
+                mcur[ks][1] = mnxt[ks][1];
             }
         }
     }

@@ -727,15 +727,16 @@ __device__ __forceinline__ int swz(int r, int p) {
 
 // Wave w owns chunk rows 16w .. 16w+15 (Y, R, outputs) and state keys
 // 16 STW w .. (row tiles of S).  The chunk's operand tiles (q and k; decayed
-// form: a and qt as hi/lo), the MTb planes and the V tile sit in one of two
-// LDS stages (by chunk parity) as swizzled tiles read as matrix-core
-// operands.  With vector loads the next chunk's are loaded into registers in
-// groups spread over a chunk (a q/k piece after each k-step of step 1, the
-// MTb planes after it, the V tile after the first barrier) and written to the
-// other stage at the end of the chunk; the first chunk's come through loads
-// with an LDS destination.  W (and e^{G_L}) of the next chunk are loaded into
-// registers too: each wave reads only the rows of its own state keys, as
-// contiguous 1 KB fragments.  Per chunk, two barriers:
+// form: a and qt as hi/lo) and the V tile sit in one of two LDS stages (by
+// chunk parity) as swizzled tiles read as matrix-core operands.  W, MTb (and
+// e^{G_L}) go straight to registers as operand fragments: each wave reads
+// only the W rows of its own state keys and the MTb rows of its own chunk
+// rows, as contiguous 1 KB fragments.  With vector loads all of the next
+// chunk's loads are issued at the top of a chunk: the operand and V tiles
+// into registers, written to the other stage at the chunk's end; W and MTb
+// into the other of two register sets (the chunk loop is unrolled twice, so
+// the sets alternate with no copies).  The first chunk's tiles come through
+// loads with an LDS destination.  Per chunk, two barriers:
 //   -- inputs of chunk c visible --
 //   1. Y = K S0, O1 = Q S0 (rows of this wave); R = V - Y -> LDS
 //   -- barrier --
@@ -904,6 +905,13 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     // Plain form: q and k pieces of runs 0 .. QB/4096 - 1; decayed form (not
     // SPLIT): the four operand tiles' runs; then the V tile.
     constexpr int NPO = SPLIT ? 1 : (DECAY ? 4 : 2) * QB / 4096;
+    constexpr int NJO = DECAY ? NPO : NPO / 2;   // runs of preload_ops
+    // DRAIN: the V piece is issued last, so its wait at the end of a chunk
+    // waits for all of the next chunk's loads.  At K = 128 (~84 KB per chunk)
+    // the loads take longer than the chunk's chain, and loads still in flight
+    // into the next chunk delay that chunk's own (measured slower); at K = 64
+    // the W / MTb loads may stay in flight until the next chunk's phase 2.
+    constexpr bool DRAIN = KP > 64;
     u32x4 pre_o[NPO], pre_v;
     auto preload_ops = [&](int c, int j0, int j1) {
         if constexpr (DECAY) {
@@ -929,12 +937,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
     };
     auto preload_v = [&](int c) {
-        if (wave < 2) {
-            const int64_t t0 = static_cast<int64_t>(c) * L;
-            const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
-            const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
-            pre_v = buf_load16(wv, v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB);
-        }
+        // issued by every wave (waves 2 and 3 read nothing), like every other load here
+        const int64_t t0 = static_cast<int64_t>(c) * L;
+        const BufRes wv = make_rsrc_window(vb, T * v_row, t0 * v_row);
+        const int sl = 64 * wave + lane, row = sl / 2, col = ((sl % 2) ^ (row & 1)) * 8;
+        pre_v = buf_load16(wv, wave < 2 && v0 + col < V ? ((row * H + h) * V + v0 + col) * 2 : kBufOOB);
     };
     auto prestore = [&](unsigned char* so_, unsigned char* sp_) {
         if constexpr (!SPLIT) {
@@ -1011,8 +1018,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
-                    m[ks][hl] = ks <= wave / 2 ? buf_load16(wp, (mfrag_off(wave, ks, hl) + 8 * lane) * 2)
-                                               : u32x4{0u, 0u, 0u, 0u};
+                    m[ks][hl] = buf_load16(wp, ks <= wave / 2 ? (mfrag_off(wave, ks, hl) + 8 * lane) * 2 : kBufOOB);
         }
         if constexpr (VEC) {
             const BufRes wp = make_rsrc_window(wsb, ws_bytes, cb);
@@ -1110,7 +1116,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             }
         }
     };
-    for (int c = 0; c < nchunks; ++c) {
+    // One chunk; the W / MTb / e^{G_L} registers alternate between two sets
+    // (this chunk's, the next chunk's) by unrolling the chunk loop twice, so no
+    // copy at the end of a chunk waits for the next chunk's loads.
+    auto step = [&](int c, u32x4 (&wc)[STW][2][2], f32x4 (&ec)[DECAY ? STW : 1], u32x4 (&mc)[2][2],
+                    u32x4 (&wn)[STW][2][2], f32x4 (&en)[DECAY ? STW : 1], u32x4 (&mn)[2][2]) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
         const unsigned char* st = sOps + (SPLIT ? 0 : (c & 1) * OPS);
         const unsigned char* sp = sPV + (c & 1) * PVS;
@@ -1122,14 +1132,18 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         if constexpr (VEC)
             if (SPLIT || c == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
-        if (more) {
-            load_w(c + 1, wnxt, enxt, mnxt);
-            if constexpr (VEC) {
-                preload_v(c + 1);
-            } else {
-                if constexpr (!SPLIT) fetch_ops(c + 1, so_n);
-                fetch_pv(c + 1, sp_n);
-            }
+        if constexpr (VEC) {
+            // All of the next chunk's loads, issued here (past the last chunk
+            // their windows are empty and read zero, so every chunk has the same
+            // loads in flight and the compiler's waits are exact).
+            if constexpr (!SPLIT) preload_ops(c + 1, 0, NJO);
+            if constexpr (!DRAIN) preload_v(c + 1);
+            load_w(c + 1, wn, en, mn);
+            if constexpr (DRAIN) preload_v(c + 1);
+        } else if (more) {
+            load_w(c + 1, wn, en, mn);
+            if constexpr (!SPLIT) fetch_ops(c + 1, so_n);
+            fetch_pv(c + 1, sp_n);
         }
         if (c > 0) store_outputs(t0 - L);
 
@@ -1152,10 +1166,6 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             y = mfma16(ah, sh, y);
             o1 = mfma16(qh, sl, o1);
             o1 = mfma16(qh, sh, o1);
-            // the next chunk's operand pieces, a share per k-step
-            constexpr int NJO = DECAY ? NPO : NPO / 2;
-            if constexpr (VEC && !SPLIT)
-                if (more) preload_ops(c + 1, ks * NJO / KS, (ks + 1) * NJO / KS);
         }
         {
             // V rows 16 wave + 4g .. +3 at column c16, by the transposing read
@@ -1197,7 +1207,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             if (ks <= wave / 2) {   // MTb is lower triangular
-                const bf16x8 mh = as_bf16x8(mcur[ks][0]), ml = as_bf16x8(mcur[ks][1]);
+                const bf16x8 mh = as_bf16x8(mc[ks][0]), ml = as_bf16x8(mc[ks][1]);
                 o2 = mfma16(ml, rh[ks], o2);
                 o2 = mfma16(mh, rl[ks], o2);
                 o2 = mfma16(mh, rh[ks], o2);
@@ -1210,40 +1220,26 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             f32x4 ds = zero4();
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8 wh = as_bf16x8(wcur[s2][ks][0]), wl = as_bf16x8(wcur[s2][ks][1]);
+                const bf16x8 wh = as_bf16x8(wc[s2][ks][0]), wl = as_bf16x8(wc[s2][ks][1]);
                 ds = mfma16(wl, rh[ks], ds);
                 ds = mfma16(wh, rl[ks], ds);
                 ds = mfma16(wh, rh[ks], ds);
             }
             if constexpr (DECAY) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) S[s2][r] = __builtin_fmaf(S[s2][r], ecur[s2][r], ds[r]);
+                for (int r = 0; r < 4; ++r) S[s2][r] = __builtin_fmaf(S[s2][r], ec[s2][r], ds[r]);
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[s2][r] += ds[r];
             }
         }
         write_state_lds();
-        if constexpr (VEC)
-            if (more) prestore(so_n, sp_n);   // the other stage (SPLIT: this wave's rows only)
-        if (more) {
-#pragma unroll
-            for (int s2 = 0; s2 < STW; ++s2) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    wcur[s2][ks][0] = wnxt[s2][ks][0];
-                    wcur[s2][ks][1] = wnxt[s2][ks][1];
-                }
-                if constexpr (DECAY) ecur[s2] = enxt[s2];
-            }
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                mcur[ks][0] = mnxt[ks][0];
-                mcur[ks][1] = mnxt[ks][1];
-            }
-        }
+        if constexpr (VEC) prestore(so_n, sp_n);   // the other stage (SPLIT: this wave's rows only)
+    };
+    for (int c = 0; c < nchunks; c += 2) {
+        step(c, wcur, ecur, mcur, wnxt, enxt, mnxt);
+        if (c + 1 < nchunks) step(c + 1, wnxt, enxt, mnxt, wcur, ecur, mcur);
     }
-
     store_outputs(static_cast<int64_t>(nchunks - 1) * L);
     if constexpr (VEC && DECAY) {
 #pragma unroll

@@ -909,9 +909,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     // DRAIN: the V piece is issued last, so its wait at the end of a chunk
     // waits for all of the next chunk's loads.  At K = 128 (~84 KB per chunk)
     // the loads take longer than the chunk's chain, and loads still in flight
-    // into the next chunk delay that chunk's own (measured slower); at K = 64
-    // the W / MTb loads may stay in flight until the next chunk's phase 2.
-    constexpr bool DRAIN = KP > 64;
+    // into the next chunk delay that chunk's own (measured slower), and the
+    // decayed form at K = 64 measured no better without it; in the plain form
+    // at K = 64 the W / MTb loads may stay in flight until the next chunk's
+    // phase 2.
+    constexpr bool DRAIN = KP > 64 || DECAY;
     u32x4 pre_o[NPO], pre_v;
     auto preload_ops = [&](int c, int j0, int j1) {
         if constexpr (DECAY) {

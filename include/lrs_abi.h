@@ -160,9 +160,14 @@ void lrs_context_destroy(LrsContext* ctx);
 
 /* Tuning knobs.  LRS_PARAM_ELEM_SCHEDULE picks how the elementwise scans
  * split the time axis:
- *   LRS_ELEM_SCHEDULE_AUTO      (default) look-back when the time axis spans
- *                               at least two chunks (128 steps) and its status
- *                               words fit in 256 MB, stream otherwise;
+ *   LRS_ELEM_SCHEDULE_AUTO      (default) stream when it walks a single
+ *                               128-step chunk, or when it has a workgroup for
+ *                               every compute unit (B * ceil(N / 64) of them
+ *                               with 16-byte aligned N % 4 == 0 channels, else
+ *                               B * ceil(N / 16)) and T <= 1024; otherwise
+ *                               look-back when the time axis spans at least two
+ *                               chunks and its status words fit in 256 MB,
+ *                               stream otherwise;
  *   LRS_ELEM_SCHEDULE_STREAM    each workgroup owns a set of channels and
  *                               walks the whole time axis, carrying the state
  *                               on chip (no inter-workgroup traffic);

@@ -6,6 +6,7 @@
 // handles, packed version, capability bits, int32 status codes and dims.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -139,6 +140,23 @@ lrs_status next_epoch(LrsContext* ctx, hipStream_t stream, unsigned int* out) {
     }
     *out = ++ctx->epoch;
     return LRS_OK;
+}
+
+// Compute units of `device` (an attribute query, no allocation), asked once per
+// device; threads may race on the first query, which only repeats it.
+int device_cus(int device) {
+    constexpr int kDevices = 64;
+    static std::atomic<int> cached[kDevices];
+    if (device < 0 || device >= kDevices) return 256;
+    int n = cached[device].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cached[device].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // Resolves the schedule and plan of an elementwise pass over [B,T,N] and, for
@@ -450,10 +468,11 @@ LRS_API lrs_status lrs_scan_gated_noalloc(const float* a, const float* u, const 
         (void)hipGetLastError();
         return LRS_E_DEVICE;
     }
-    // look-back whenever the time axis spans two chunks, as the automatic
-    // schedule does; under graph capture the stream schedule (no scratch, and
-    // no host-side epoch or counter base for a replay to reuse)
-    const int ksched = multi_chunk && !capturing(stream) ? lrs::kElemLookback : lrs::kElemStream;
+    // the automatic schedule's choice; under graph capture the stream schedule
+    // (no scratch, and no host-side epoch or counter base for a replay to reuse)
+    const int ksched = multi_chunk && !capturing(stream) &&
+                               lrs::elem_auto_schedule(B, T, N, al16, device_cus(device)) == lrs::kElemLookback
+                           ? lrs::kElemLookback : lrs::kElemStream;
     const lrs::ElemPlan plan = ksched == lrs::kElemLookback ? lb : lrs::elem_plan(B, T, N, al16, ksched);
     if (plan.grid > 0x7fffffff) return LRS_E_UNSUPPORTED;
     lrs::ElemParams p{};

@@ -713,12 +713,20 @@ ElemPlan elem_plan(int64_t B, int64_t T, int64_t N, bool aligned16, int schedule
 // running workgroups cover a compact band of rows of every tensor; measured on
 // the B=16 T=8192 N=2048 gated workload it streams at 5.8 TB/s against 4.9 TB/s
 // for the stream schedule (whose workgroups each sweep their own column strip
-// over the whole time axis).  It is used whenever there are at least two time
-// chunks and its status words stay within 256 MB.
+// over the whole time axis).  Where the look-back grid is larger than the
+// resident workgroup slots, its chunk-major tiles run in rounds, and each round
+// pays a load, publish and poll latency (~7 us per chunk row at B=16 N=2048);
+// so the stream schedule is taken when its own walk is a single chunk, or when
+// it has a workgroup for every compute unit and at most 8 chunks to walk
+// (T <= 1024: B=16 T=128 N=2048 6.8 against 31.6 us, T=1024 77 against 84 us;
+// at T=2048 the two tie, and from T=4096 on the look-back wins).  Otherwise
+// the look-back, while there are two or more chunks and its status words stay
+// within 256 MB.
 int elem_auto_schedule(int64_t B, int64_t T, int64_t N, bool aligned16, int num_cus) {
-    (void)num_cus;
     const ElemPlan lb = elem_plan(B, T, N, aligned16, kElemLookback);
     if (lb.chunks <= 1 || lb.words * sizeof(unsigned long long) > (size_t{256} << 20)) return kElemStream;
+    const ElemPlan st = elem_plan(B, T, N, aligned16, kElemStream);
+    if (st.chunks <= 1 || (st.grid >= num_cus && st.chunks <= 8)) return kElemStream;
     return kElemLookback;
 }
 

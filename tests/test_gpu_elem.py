@@ -85,6 +85,23 @@ def test_auto_schedule_small_workload(ctx, kind):
     assert rel(s, rs) <= TOL and rel(fin, rf) <= TOL
 
 
+@pytest.mark.parametrize("shape", [(16, 128, 2048), (8, 1000, 2048), (2, 1100, 8192)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_auto_schedule_short_wide(ctx, shape):
+    # short time axes over many channels, where the automatic choice takes the
+    # stream schedule (T <= 1024 with a workgroup per compute unit) or, just
+    # past that, the look-back; both entries, with an initial state
+    B, T, N = shape
+    a, x, s0 = _inputs("gated", B, T, N, seed=1200 + T, with_s0=True)
+    rs, rf = _oracle("gated", a, x, s0)
+    s, fin = _run(ctx, "gated", a, x, s0, binding.LRS_ELEM_SCHEDULE_AUTO)
+    assert rel(s, rs) <= TOL and rel(fin, rf) <= TOL
+    s2, f2 = torch.empty_like(s), torch.empty_like(fin)
+    binding.lrs_scan_gated_noalloc(dev(a), dev(x), dev(s0), s2, f2)
+    torch.cuda.synchronize()
+    assert rel(s2, rs) <= TOL and rel(f2, rf) <= TOL
+
+
 @pytest.mark.parametrize("schedule", SCHEDULES, ids=["stream", "lookback"])
 def test_continuation(ctx, schedule):
     # [SunnyNet log §4]: two segments with the state passed across equal one run.

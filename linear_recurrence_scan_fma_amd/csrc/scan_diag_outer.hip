@@ -990,11 +990,16 @@ DiagPlan diag_outer_plan(int B, int T, int H, int V, int K, int decay_mode, bool
         // holds two or more (the second round covers the tail of the first);
         // at least kMinChunksPerSegment chunks each, since every extra
         // segment adds a reduction pass over its chunks.  Measured on the
-        // Mamba-2, GLA, HGRN2 and associative-memory shapes.
+        // Mamba-2, GLA, HGRN2 and associative-memory shapes.  Where a compute
+        // unit holds one workgroup (8-wave per-key variants), filling the chip
+        // outweighs the extra reduction on short or narrow calls: segments
+        // down to 2 chunks (GLA B=4 T=1024 54.7 -> 38.6 us, B=1 T=4096
+        // 56.0 -> 41.1 us; the benchmark shapes keep their counts).
         const int res = resident_blocks(decay_mode, kscale_key, K, pl.waves, vec);
         const int64_t slots = static_cast<int64_t>(num_cus) * res;
         nseg = (res >= 2 ? 2 * slots : slots) / units;
-        if (nseg > pl.nchunks / kMinChunksPerSegment) nseg = pl.nchunks / kMinChunksPerSegment;
+        const int minc = res >= 2 ? kMinChunksPerSegment : 2;
+        if (nseg > pl.nchunks / minc) nseg = pl.nchunks / minc;
     }
     if (nseg > pl.nchunks) nseg = pl.nchunks;
     if (nseg < 1) nseg = 1;

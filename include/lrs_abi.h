@@ -99,7 +99,7 @@ extern "C" {
 
 /* ---- version and capabilities [SunnyNet log §6] ------------------------ */
 #define LRS_ABI_VERSION_MAJOR 1
-#define LRS_ABI_VERSION_MINOR 2
+#define LRS_ABI_VERSION_MINOR 3
 #define LRS_ABI_VERSION_PATCH 0
 #define LRS_ABI_VERSION \
     ((LRS_ABI_VERSION_MAJOR << 16) | (LRS_ABI_VERSION_MINOR << 8) | LRS_ABI_VERSION_PATCH)
@@ -182,9 +182,27 @@ void lrs_context_destroy(LrsContext* ctx);
  * product and a state contribution, kept in the context's workspace, and a
  * prefix over them gives each segment its starting state):
  *   0 (default)  one workgroup per resident workgroup slot of the device
- *                where a compute unit holds one of them, about two where it
- *                holds more, but at least 4 chunks (256 steps) per segment;
+ *                where a compute unit holds one of them (at least 2 chunks,
+ *                128 steps, per segment), about two where it holds more (at
+ *                least 4 chunks, 256 steps, per segment);
  *   n >= 1       n segments (capped at the number of chunks).
+ * Any value gives results within the documented tolerance.
+ *
+ * LRS_PARAM_DELTA_SEGMENTS (since 1.3) sets how many time segments the delta
+ * rule calls (lrs_scan_delta, lrs_scan_delta_decay, lrs_scan_delta_out) split
+ * the chunks into.  A segment pass gives each segment but the last its
+ * transition S_out = A_s S_in + B_s (A_s from identity columns run through
+ * the same update with zero values), a prefix over them gives each segment
+ * its starting state, and the output pass runs every segment at once; the
+ * context keeps the states and transitions (4 K (K + 2V) bytes per (batch,
+ * head) and segment) beside the per-chunk workspace:
+ *   0 (default)  one segment while the (batch, head, 16-column V-tile)
+ *                workgroups fill half the compute units or more; otherwise
+ *                the most segments (of at least 8 chunks, 512 steps) whose
+ *                output pass and segment pass each still fit the compute
+ *                units once;
+ *   1            one pass over all chunks;
+ *   n >= 2       n segments (capped at the number of chunks).
  * Any value gives results within the documented tolerance.
  *
  * LRS_PARAM_LOOKBACK_DELAY_SEED (since 1.2) is a verification knob for the
@@ -197,7 +215,12 @@ void lrs_context_destroy(LrsContext* ctx);
  *                words in an order unrelated to normal timing.  Results stay
  *                within the documented tolerance; calls are much slower.
  * Errors: LRS_E_INVAL for a NULL context, unknown parameter or value. */
-enum { LRS_PARAM_ELEM_SCHEDULE = 1, LRS_PARAM_DIAG_SEGMENTS = 2, LRS_PARAM_LOOKBACK_DELAY_SEED = 3 };
+enum {
+    LRS_PARAM_ELEM_SCHEDULE = 1,
+    LRS_PARAM_DIAG_SEGMENTS = 2,
+    LRS_PARAM_LOOKBACK_DELAY_SEED = 3,
+    LRS_PARAM_DELTA_SEGMENTS = 4
+};
 enum {
     LRS_ELEM_SCHEDULE_AUTO = 0,
     LRS_ELEM_SCHEDULE_STREAM = 1,
@@ -343,7 +366,9 @@ lrs_status lrs_scan_diag_outer(LrsContext* ctx, const lrs_bf16* q, const lrs_bf1
  * K > 64 (LRS_E_UNSUPPORTED beyond: one (batch, head) slice of the workspace
  * must stay under 2 GiB).  The context keeps a workspace per (batch, head,
  * 64-step chunk) of 32 KiB (K <= 64) or 48 KiB (K > 64), holding the chunk's
- * output and state-update factors, grown on demand (LRS_E_NOMEM if that
+ * output and state-update factors (plus, when the call runs in time
+ * segments, see LRS_PARAM_DELTA_SEGMENTS, their states and transitions),
+ * grown on demand (LRS_E_NOMEM if that
  * allocation fails); growing it first waits for the whole device, since an
  * earlier call on another stream may still use the old workspace.
  */

@@ -31,6 +31,7 @@ LRS_DTYPE_F32, LRS_DTYPE_BF16 = 0, 1
 LRS_PARAM_ELEM_SCHEDULE = 1
 LRS_PARAM_DIAG_SEGMENTS = 2
 LRS_PARAM_LOOKBACK_DELAY_SEED = 3
+LRS_PARAM_DELTA_SEGMENTS = 4
 LRS_ELEM_SCHEDULE_AUTO, LRS_ELEM_SCHEDULE_STREAM, LRS_ELEM_SCHEDULE_LOOKBACK = 0, 1, 2
 
 # Every symbol the header declares, with (restype, argtypes).

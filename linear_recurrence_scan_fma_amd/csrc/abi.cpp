@@ -34,6 +34,7 @@ struct LrsContext {
     size_t delta_ws_bytes = 0;
     // diag-outer segment pairs (decay products and state contributions), grown on demand
     int diag_segments = 0;   // 0: automatic
+    int delta_segments = 0;  // 0: automatic
     void* diag_ws = nullptr;
     size_t diag_ws_bytes = 0;
     hipStream_t last_stream = nullptr;
@@ -405,6 +406,11 @@ LRS_API lrs_status lrs_context_set_param(LrsContext* ctx, int32_t param, int32_t
         ctx->diag_segments = value;
         return LRS_OK;
     }
+    if (param == LRS_PARAM_DELTA_SEGMENTS) {
+        if (value < 0) return LRS_E_INVAL;
+        ctx->delta_segments = value;
+        return LRS_OK;
+    }
     if (param == LRS_PARAM_LOOKBACK_DELAY_SEED) {
         if (value < 0) return LRS_E_INVAL;
         ctx->lookback_delay_seed = static_cast<unsigned int>(value);
@@ -721,13 +727,14 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     if (static_cast<int64_t>(B) * H * nchunks > 0x7fffffff || static_cast<int64_t>(B) * H * vtiles > 0x7fffffff)
         return LRS_E_UNSUPPORTED;
     // the scan kernel addresses one (batch, head) slice of the workspace with 32-bit offsets
-    if (lrs::delta_workspace_bytes(1, T, 1, K, decay) >= (size_t{1} << 31)) return LRS_E_UNSUPPORTED;
+    if (lrs::delta_chunk_workspace_bytes(1, T, 1, K, decay) >= (size_t{1} << 31)) return LRS_E_UNSUPPORTED;
+    const int nseg = lrs::delta_plan_segments(B, T, H, K, V, ctx->num_cus, ctx->delta_segments);
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     DeviceGuard guard(ctx->device);
     if (!guard.ok()) return LRS_E_DEVICE;
     const lrs_status ws = grow_workspace(ctx, ctx->delta_ws, ctx->delta_ws_bytes,
-                                         lrs::delta_workspace_bytes(B, T, H, K, decay), st);
+                                         lrs::delta_workspace_bytes(B, T, H, K, V, decay, nseg), st);
     if (ws != LRS_OK) return ws;
     lrs::DeltaParams p{};
     p.q = q;
@@ -745,6 +752,7 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     p.K = K;
     p.V = V;
     p.out_bf16 = out_dtype == LRS_DTYPE_BF16 ? 1 : 0;
+    p.nseg = nseg;
     // the vector path addresses one batch row of each tensor with 32-bit buffer offsets
     const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&

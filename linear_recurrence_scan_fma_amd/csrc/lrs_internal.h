@@ -142,14 +142,20 @@ struct DeltaParams {
     int B, T, H, K, V;
     int vec;               // 16-byte vector loads allowed
     int out_bf16;          // o is bf16 (round to nearest even) instead of fp32
+    int nseg;              // time segments (<= 1: one pass over all chunks)
 };
 
 int delta_vtile();
 // Largest K of the decayed form.
 int delta_decay_max_k();
-// Device workspace the delta scan needs (per-chunk UT-transform planes, plus
-// the running log-decay with a decay).
-size_t delta_workspace_bytes(int B, int T, int H, int K, bool decay);
+// Device workspace the delta scan needs: per-chunk UT-transform planes (plus
+// the decayed operands with a decay), and with nseg > 1 the segment states and
+// transitions.
+size_t delta_chunk_workspace_bytes(int B, int T, int H, int K, bool decay);
+size_t delta_workspace_bytes(int B, int T, int H, int K, int V, bool decay, int nseg);
+// Time segments for a call: `requested` > 0 forces a count (capped at the
+// chunk count), else the automatic choice for `num_cus` compute units.
+int delta_plan_segments(int B, int T, int H, int K, int V, int num_cus, int requested);
 hipError_t launch_scan_delta(const DeltaParams& p, void* workspace, hipStream_t stream);
 
 // Fills `n` 64-bit words with zero (used to reset look-back status words).

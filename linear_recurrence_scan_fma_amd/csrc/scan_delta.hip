@@ -100,6 +100,14 @@ struct DeltaArgs {
     int vtiles;
     int nchunks;
     int out_bf16;     // o is bf16 (round to nearest even) instead of fp32
+    // time segments (nseg = 1: one pass over all chunks).  Segment s covers
+    // chunks [s cps, (s + 1) cps); across a segment the state obeys
+    // S_out = A_s S_in + B_s.  seg_state[s] ([B][H][K][V] fp32) is the state
+    // entering segment s (s >= 1); seg_ab[s] ([B][H][K][K + V] fp32) holds A_s
+    // in its first K columns and B_s after them (1 <= s <= nseg - 2).
+    int nseg, cps;
+    float* seg_state;
+    float* seg_ab;
 };
 
 __device__ __forceinline__ void tri_block(int n, int& i, int& j) {
@@ -747,7 +755,12 @@ __device__ __forceinline__ int swz(int r, int p) {
 // wave loads the next chunk's rows of its own (the only rows it reads) with
 // LDS-destination loads as soon as its step 1 is done with them, so they
 // load during step 2.
-template <int KP, bool VEC, bool DECAY>
+// SEGP = false: outputs of segment s from the state entering it (all
+// segments at once; the last writes s_final).  SEGP = true, the segment pass:
+// no readout; segment 0 runs its state columns from s0 and leaves the state
+// entering segment 1, and a segment s in 1 .. nseg - 2 runs K identity
+// columns with zero values (A_s) beside its state columns from zero (B_s).
+template <int KP, bool VEC, bool DECAY, bool SEGP = false>
 __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     static_assert(!DECAY || KP == 64 || KP == KD, "decayed form: K <= 128");
     constexpr bool SPLIT = DECAY && KP > 64;   // operand tiles single buffered
@@ -783,13 +796,39 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
-    const int vt = lid % p.vtiles;
-    const int bh = lid / p.vtiles;
+    // (batch, head, segment, tile): output pass V-tiles of every segment; the
+    // segment pass V-tiles of segment 0, then for each segment 1 .. nseg - 2
+    // its ceil(K / 16) A tiles and its V-tiles
+    int bh, seg, vt;
+    bool atile = false;   // segment pass: this tile runs identity columns (A_s)
+    if constexpr (SEGP) {
+        const int kt = (p.K + VT - 1) / VT;
+        const int per = p.vtiles + (p.nseg - 2) * (kt + p.vtiles);
+        bh = lid / per;
+        const int r = lid - bh * per;
+        if (r < p.vtiles) {
+            seg = 0;
+            vt = r;
+        } else {
+            seg = 1 + (r - p.vtiles) / (kt + p.vtiles);
+            const int t = (r - p.vtiles) % (kt + p.vtiles);
+            atile = t < kt;
+            vt = atile ? t : t - kt;
+        }
+    } else {
+        vt = lid % p.vtiles;
+        const int rest = lid / p.vtiles;
+        seg = rest % p.nseg;
+        bh = rest / p.nseg;
+    }
     const int b = bh / p.H, h = bh - b * p.H;
-    const int v0 = vt * VT;
     const int64_t T = p.T;
     const int K = p.K, V = p.V, H = p.H;
+    // identity columns read no values: their V-tile starts past V
+    const int v0 = atile ? V : vt * VT;
     const int nchunks = p.nchunks;
+    const int c_begin = seg * p.cps;
+    const int c_end = min(c_begin + p.cps, nchunks);
 
     const int64_t qk_row = static_cast<int64_t>(H) * K * 2, v_row = static_cast<int64_t>(H) * V * 2;   // bytes per step
     const u16* qb = p.q + b * T * H * static_cast<int64_t>(K);
@@ -933,7 +972,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 const int i = wave + 4 * j, sl = 64 * i + lane;
                 const int row = sl / PPR, col = ((sl % PPR) ^ (row & (PPR - 1))) * 8;
                 const int off = col < K ? ((row * H + h) * K + col) * 2 : kBufOOB;
-                pre_o[2 * j] = buf_load16(wq, off);
+                if constexpr (!SEGP) pre_o[2 * j] = buf_load16(wq, off);
                 pre_o[2 * j + 1] = buf_load16(wk, off);
             }
         }
@@ -953,7 +992,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
                 if constexpr (DECAY) {
                     *reinterpret_cast<u32x4*>(so_ + 1024 * i + 16 * lane) = pre_o[j];
                 } else {
-                    *reinterpret_cast<u32x4*>(so_ + OFF_QH + 1024 * i + 16 * lane) = pre_o[2 * j];
+                    if constexpr (!SEGP) *reinterpret_cast<u32x4*>(so_ + OFF_QH + 1024 * i + 16 * lane) = pre_o[2 * j];
                     *reinterpret_cast<u32x4*>(so_ + OFF_AH + 1024 * i + 16 * lane) = pre_o[2 * j + 1];
                 }
             }
@@ -1020,7 +1059,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
-                    m[ks][hl] = buf_load16(wp, ks <= wave / 2 ? (mfrag_off(wave, ks, hl) + 8 * lane) * 2 : kBufOOB);
+                    m[ks][hl] = SEGP ? u32x4{0u, 0u, 0u, 0u}
+                                     : buf_load16(wp, ks <= wave / 2 ? (mfrag_off(wave, ks, hl) + 8 * lane) * 2 : kBufOOB);
         }
         if constexpr (VEC) {
             const BufRes wp = make_rsrc_window(wsb, ws_bytes, cb);
@@ -1054,6 +1094,10 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
 
     // state: wave owns row tiles sr = STW * wave + st (keys 16 sr .. 16 sr + 15)
     f32x4 S[STW];
+    // the state entering the segment: s0 (segment 0), the one the prefix left
+    // (output pass, segment >= 1), zero (segment pass B_s), identity (A_s)
+    const float* sin = seg == 0 ? p.s0
+                     : (SEGP ? nullptr : p.seg_state + (static_cast<int64_t>(seg) * p.B * H + bh) * K * V);
 #pragma unroll
     for (int st = 0; st < STW; ++st) {
         const int sr = STW * wave + st;
@@ -1062,7 +1106,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         for (int r = 0; r < 4; ++r) {
             const int d = 16 * sr + 4 * g + r;
             float x = 0.0f;
-            if (p.s0 && d < K && j < V) x = p.s0[((static_cast<int64_t>(b) * H + h) * K + d) * V + j];
+            if (atile) x = d == 16 * vt + c16 ? 1.0f : 0.0f;
+            else if (sin && d < K && j < V) x = sin[(seg == 0 ? (static_cast<int64_t>(b) * H + h) * K : 0) * V + d * V + j];
             S[st][r] = x;
         }
     }
@@ -1078,11 +1123,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
     };
     write_state_lds();
-    fetch_ops(0, sOps);
-    fetch_pv(0, sPV);
-    load_w(0, wcur, ecur, mcur);
+    fetch_ops(c_begin, sOps + (SPLIT ? 0 : (c_begin & 1) * OPS));
+    fetch_pv(c_begin, sPV + (c_begin & 1) * PVS);
+    load_w(c_begin, wcur, ecur, mcur);
     if constexpr (VEC && DECAY)
-        if (nchunks > 1) l2_touch(1);
+        if (c_begin + 1 < c_end) l2_touch(c_begin + 1);
 
     const int arow = 16 * wave + c16;    // operand row of this wave
     // A chunk's outputs wait in this wave's LDS tile (rows 16 wave .., the 16
@@ -1126,13 +1171,13 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
         const unsigned char* st = sOps + (SPLIT ? 0 : (c & 1) * OPS);
         const unsigned char* sp = sPV + (c & 1) * PVS;
-        const bool more = c + 1 < nchunks;
+        const bool more = c + 1 < c_end;
         unsigned char* so_n = sOps + (SPLIT ? 0 : ((c + 1) & 1) * OPS);
         unsigned char* sp_n = sPV + ((c + 1) & 1) * PVS;
         // LDS-direct loads in flight (the first chunk's; SPLIT: every chunk's
         // operand rows) are waited for here; register-staged loads by their use
         if constexpr (VEC)
-            if (SPLIT || c == 0) __builtin_amdgcn_s_waitcnt(0x0F70);
+            if (SPLIT || c == c_begin) __builtin_amdgcn_s_waitcnt(0x0F70);
         __syncthreads();
         if constexpr (VEC) {
             // All of the next chunk's loads, issued here (past the last chunk
@@ -1147,7 +1192,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             if constexpr (!SPLIT) fetch_ops(c + 1, so_n);
             fetch_pv(c + 1, sp_n);
         }
-        if (c > 0) store_outputs(t0 - L);
+        if (!SEGP && c > c_begin) store_outputs(t0 - L);
 
         // ---- 1: Y = K S0, O1 = Q S0 (row block = wave), R = V - Y ----
         f32x4 y = zero4(), o1 = zero4();
@@ -1157,17 +1202,21 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             const bf16x8 sl = frag<LDK>(sSl, 0, 32 * ks, lane);
             const int po = swz<PPR>(arow, 4 * ks + g);
             const bf16x8 ah = *reinterpret_cast<const bf16x8*>(st + OFF_AH + po);
-            const bf16x8 qh = *reinterpret_cast<const bf16x8*>(st + OFF_QH + po);
             if constexpr (DECAY) {
                 const bf16x8 al = *reinterpret_cast<const bf16x8*>(st + OFF_AL + po);
-                const bf16x8 ql = *reinterpret_cast<const bf16x8*>(st + OFF_QL + po);
                 y = mfma16(al, sh, y);
-                o1 = mfma16(ql, sh, o1);
+                if constexpr (!SEGP) {
+                    const bf16x8 ql = *reinterpret_cast<const bf16x8*>(st + OFF_QL + po);
+                    o1 = mfma16(ql, sh, o1);
+                }
             }
             y = mfma16(ah, sl, y);
             y = mfma16(ah, sh, y);
-            o1 = mfma16(qh, sl, o1);
-            o1 = mfma16(qh, sh, o1);
+            if constexpr (!SEGP) {   // the segment pass has no readout
+                const bf16x8 qh = *reinterpret_cast<const bf16x8*>(st + OFF_QH + po);
+                o1 = mfma16(qh, sl, o1);
+                o1 = mfma16(qh, sh, o1);
+            }
         }
         {
             // V rows 16 wave + 4g .. +3 at column c16, by the transposing read
@@ -1186,7 +1235,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
         if constexpr (VEC) {
             if constexpr (DECAY)   // (the plain form's shared lines already hit in L2)
-                if (c + 2 < nchunks) l2_touch(c + 2);
+                if (c + 2 < c_end) l2_touch(c + 2);
         }
         if constexpr (SPLIT) {
             // this wave's operand rows are read (y and o1 hold them): the next
@@ -1205,18 +1254,20 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             rh[ks] = frag<LDL>(sRTh, 0, 32 * ks, lane);
             rl[ks] = frag<LDL>(sRTl, 0, 32 * ks, lane);
         }
-        f32x4 o2 = zero4();
+        if constexpr (!SEGP) {
+            f32x4 o2 = zero4();
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks <= wave / 2) {   // MTb is lower triangular
-                const bf16x8 mh = as_bf16x8(mc[ks][0]), ml = as_bf16x8(mc[ks][1]);
-                o2 = mfma16(ml, rh[ks], o2);
-                o2 = mfma16(mh, rl[ks], o2);
-                o2 = mfma16(mh, rh[ks], o2);
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks <= wave / 2) {   // MTb is lower triangular
+                    const bf16x8 mh = as_bf16x8(mc[ks][0]), ml = as_bf16x8(mc[ks][1]);
+                    o2 = mfma16(ml, rh[ks], o2);
+                    o2 = mfma16(mh, rl[ks], o2);
+                    o2 = mfma16(mh, rh[ks], o2);
+                }
             }
-        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) so[(4 * g + r) * LDO + c16] = p.scale * (o1[r] + o2[r]);
+            for (int r = 0; r < 4; ++r) so[(4 * g + r) * LDO + c16] = p.scale * (o1[r] + o2[r]);
+        }
 #pragma unroll
         for (int s2 = 0; s2 < STW; ++s2) {
             f32x4 ds = zero4();
@@ -1238,43 +1289,112 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         write_state_lds();
         if constexpr (VEC) prestore(so_n, sp_n);   // the other stage (SPLIT: this wave's rows only)
     };
-    for (int c = 0; c < nchunks; c += 2) {
+    for (int c = c_begin; c < c_end; c += 2) {
         step(c, wcur, ecur, mcur, wnxt, enxt, mnxt);
-        if (c + 1 < nchunks) step(c + 1, wnxt, enxt, mnxt, wcur, ecur, mcur);
+        if (c + 1 < c_end) step(c + 1, wnxt, enxt, mnxt, wcur, ecur, mcur);
     }
-    store_outputs(static_cast<int64_t>(nchunks - 1) * L);
+    if (!SEGP) store_outputs(static_cast<int64_t>(c_end - 1) * L);
     if constexpr (VEC && DECAY) {
 #pragma unroll
         for (int i = 0; i < NTOUCH; ++i) l2sink |= l2x[i];
         asm volatile("" ::"v"(l2sink));   // the touches stay
     }
+    // the state leaving the segment: s_final (last segment), the state entering
+    // segment 1 (segment pass, segment 0), or columns of A_s | B_s
+    float* sout = nullptr;
+    int64_t ld = V, col = v0 + c16;
+    bool colok = col < V;
+    if (!SEGP) {
+        if (seg == p.nseg - 1) sout = p.s_final + (static_cast<int64_t>(b) * H + h) * K * V;
+    } else if (seg == 0) {
+        sout = p.seg_state + (static_cast<int64_t>(p.B) * H + bh) * K * V;   // segment 1's entering state
+    } else {
+        sout = p.seg_ab + (static_cast<int64_t>(seg) * p.B * H + bh) * K * (K + V);
+        ld = K + V;
+        col = atile ? 16 * vt + c16 : K + v0 + c16;
+        colok = atile ? 16 * vt + c16 < K : v0 + c16 < V;
+    }
+    if (sout) {
 #pragma unroll
-    for (int s2 = 0; s2 < STW; ++s2) {
-        const int sr = STW * wave + s2;
-        const int j = v0 + c16;
+        for (int s2 = 0; s2 < STW; ++s2) {
+            const int sr = STW * wave + s2;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int d = 16 * sr + 4 * g + r;
-            if (d < K && j < V) p.s_final[((static_cast<int64_t>(b) * H + h) * K + d) * V + j] = S[s2][r];
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * sr + 4 * g + r;
+                if (d < K && colok) sout[d * ld + col] = S[s2][r];
+            }
         }
     }
 }
 
+// The states entering segments 2 .. nseg - 1, one after another:
+// S_{s+1} = A_s S_s + B_s, in fp32, summing over keys in order; a workgroup
+// owns a 16-column V-tile of one (batch, head) (its columns depend on no
+// other columns), S_s's tile staged in LDS.
+template <int KP>
+__global__ __launch_bounds__(NT) void delta_seg_prefix_kernel(DeltaArgs p) {
+    constexpr int CPT = 16 * KP / NT;   // columns per thread
+    __shared__ float sS[KP][16];
+    const int tid = threadIdx.x;
+    const int vt = blockIdx.x % p.vtiles, bh = blockIdx.x / p.vtiles;
+    const int K = p.K, V = p.V;
+    const int64_t bhs = static_cast<int64_t>(p.B) * p.H;
+    const int d = tid % KP, c0 = (tid / KP) * CPT;
+    for (int i = tid; i < KP * 16; i += NT) {
+        const int e = i / 16, col = VT * vt + i % 16;
+        sS[e][i % 16] = e < K && col < V ? p.seg_state[(bhs + bh) * K * V + static_cast<int64_t>(e) * V + col] : 0.0f;
+    }
+    __syncthreads();
+    for (int s = 1; s <= p.nseg - 2; ++s) {
+        const float* ab = p.seg_ab + (s * bhs + bh) * K * (K + V) + static_cast<int64_t>(d) * (K + V);
+        float acc[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int col = VT * vt + c0 + j;
+            acc[j] = d < K && col < V ? ab[K + col] : 0.0f;
+        }
+        if (d < K) {
+            for (int e = 0; e < K; ++e) {
+                const float a = ab[e];
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) acc[j] = __builtin_fmaf(a, sS[e][c0 + j], acc[j]);
+            }
+        }
+        __syncthreads();   // every read of S_s is done
+        float* out = p.seg_state + ((s + 1) * bhs + bh) * K * V;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            sS[d][c0 + j] = acc[j];
+            const int col = VT * vt + c0 + j;
+            if (d < K && col < V) out[static_cast<int64_t>(d) * V + col] = acc[j];
+        }
+        __syncthreads();
+    }
+}
+
+template <int KP, bool DECAY, bool VEC>
+void launch_passes(const DeltaArgs& a, hipStream_t stream) {
+    const int64_t gprep = static_cast<int64_t>(a.B) * a.H * a.nchunks;
+    const int64_t units = static_cast<int64_t>(a.B) * a.H * a.vtiles;
+    hipLaunchKernelGGL((delta_prep_kernel<KP, VEC, DECAY>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0, stream,
+                       a);
+    if (a.nseg > 1) {
+        const int kt = (a.K + VT - 1) / VT;
+        const int64_t gseg = static_cast<int64_t>(a.B) * a.H * (a.vtiles + (a.nseg - 2) * (kt + a.vtiles));
+        hipLaunchKernelGGL((delta_scan_kernel<KP, VEC, DECAY, true>), dim3(static_cast<unsigned>(gseg)), dim3(NT), 0,
+                           stream, a);
+        if (a.nseg > 2)
+            hipLaunchKernelGGL((delta_seg_prefix_kernel<KP>), dim3(static_cast<unsigned>(units)), dim3(NT), 0, stream,
+                               a);
+    }
+    hipLaunchKernelGGL((delta_scan_kernel<KP, VEC, DECAY>), dim3(static_cast<unsigned>(units * a.nseg)), dim3(NT), 0,
+                       stream, a);
+}
+
 template <int KP, bool DECAY>
 hipError_t launch_t(const DeltaArgs& a, bool vec, hipStream_t stream) {
-    const int64_t gprep = static_cast<int64_t>(a.B) * a.H * a.nchunks;
-    const int64_t gscan = static_cast<int64_t>(a.B) * a.H * a.vtiles;
-    if (vec) {
-        hipLaunchKernelGGL((delta_prep_kernel<KP, true, DECAY>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
-                           stream, a);
-        hipLaunchKernelGGL((delta_scan_kernel<KP, true, DECAY>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
-                           stream, a);
-    } else {
-        hipLaunchKernelGGL((delta_prep_kernel<KP, false, DECAY>), dim3(static_cast<unsigned>(gprep)), dim3(NT), 0,
-                           stream, a);
-        hipLaunchKernelGGL((delta_scan_kernel<KP, false, DECAY>), dim3(static_cast<unsigned>(gscan)), dim3(NT), 0,
-                           stream, a);
-    }
+    if (vec) launch_passes<KP, DECAY, true>(a, stream);
+    else launch_passes<KP, DECAY, false>(a, stream);
     return hipGetLastError();
 }
 
@@ -1282,11 +1402,41 @@ hipError_t launch_t(const DeltaArgs& a, bool vec, hipStream_t stream) {
 
 int delta_vtile() { return VT; }
 
-size_t delta_workspace_bytes(int B, int T, int H, int K, bool decay) {
+size_t delta_chunk_workspace_bytes(int B, int T, int H, int K, bool decay) {
     const int64_t nchunks = (static_cast<int64_t>(T) + L - 1) / L;
     const size_t per_chunk = decay ? (K <= 64 ? chunk_u16<64, true>() : chunk_u16<128, true>())
                                    : (K <= 64 ? chunk_u16<64, false>() : chunk_u16<128, false>());
     return static_cast<size_t>(B) * H * nchunks * per_chunk * sizeof(u16);
+}
+
+size_t delta_workspace_bytes(int B, int T, int H, int K, int V, bool decay, int nseg) {
+    size_t n = delta_chunk_workspace_bytes(B, T, H, K, decay);
+    if (nseg > 1) {
+        const size_t bh = static_cast<size_t>(B) * H;
+        n += static_cast<size_t>(nseg) * bh * K * V * sizeof(float);          // seg_state
+        n += static_cast<size_t>(nseg) * bh * K * (K + V) * sizeof(float);    // seg_ab
+    }
+    return n;
+}
+
+// Time segments: where the (batch, head, V-tile) workgroups leave most compute
+// units idle, split the chunks into the most segments whose output pass and
+// segment pass (which also runs ceil(K / 16) identity tiles per inner
+// segment) each fit the compute units once, with at least 8 chunks a segment.
+int delta_plan_segments(int B, int T, int H, int K, int V, int num_cus, int requested) {
+    const int64_t nchunks = (static_cast<int64_t>(T) + L - 1) / L;
+    if (requested > 0) return static_cast<int>(requested < nchunks ? requested : nchunks);
+    const int64_t vtiles = (V + VT - 1) / VT, kt = (K + VT - 1) / VT;
+    const int64_t units = static_cast<int64_t>(B) * H * vtiles;
+    int best = 1;
+    for (int ns = 2; ns <= 64; ++ns) {
+        const int64_t cps = (nchunks + ns - 1) / ns;
+        if (cps < 8 || (nchunks + cps - 1) / cps != ns) continue;
+        if (units * ns > num_cus) break;
+        if (static_cast<int64_t>(B) * H * (vtiles + (ns - 2) * (kt + vtiles)) > num_cus) break;
+        best = ns;
+    }
+    return best;
 }
 
 int delta_decay_max_k() { return KD; }
@@ -1311,6 +1461,15 @@ hipError_t launch_scan_delta(const DeltaParams& prm, void* workspace, hipStream_
     a.vtiles = (prm.V + VT - 1) / VT;
     a.nchunks = (prm.T + L - 1) / L;
     a.out_bf16 = prm.out_bf16;
+    a.nseg = prm.nseg > 1 ? prm.nseg : 1;
+    a.cps = (a.nchunks + a.nseg - 1) / a.nseg;
+    a.nseg = (a.nchunks + a.cps - 1) / a.cps;   // no empty segment
+    if (a.nseg > 1) {
+        const bool decay = prm.g != nullptr;
+        char* base = static_cast<char*>(workspace) + delta_chunk_workspace_bytes(prm.B, prm.T, prm.H, prm.K, decay);
+        a.seg_state = reinterpret_cast<float*>(base);
+        a.seg_ab = a.seg_state + static_cast<size_t>(a.nseg) * prm.B * prm.H * prm.K * prm.V;
+    }
     if (prm.g) {
         if (prm.K > KD) return hipErrorInvalidValue;
         return prm.K <= 64 ? launch_t<64, true>(a, prm.vec != 0, stream) : launch_t<128, true>(a, prm.vec != 0, stream);

@@ -46,7 +46,8 @@ def test_exports_every_declared_symbol(lib):
 def test_python_mirrors_header_constants():
     for name in ("LRS_OK", "LRS_E_INVAL", "LRS_E_NOMEM", "LRS_E_UNSUPPORTED", "LRS_E_DEVICE",
                  "LRS_PARAM_ELEM_SCHEDULE", "LRS_ELEM_SCHEDULE_STREAM", "LRS_PARAM_LOOKBACK_DELAY_SEED",
-                 "LRS_ELEM_SCHEDULE_LOOKBACK", "LRS_PARAM_DIAG_SEGMENTS", "LRS_CAP_SCAN_FMA",
+                 "LRS_ELEM_SCHEDULE_LOOKBACK", "LRS_PARAM_DIAG_SEGMENTS", "LRS_PARAM_DELTA_SEGMENTS",
+                 "LRS_CAP_SCAN_FMA",
                  "LRS_CAP_SCAN_GATED", "LRS_CAP_SCAN_DIAG_OUTER", "LRS_CAP_SCAN_DELTA",
                  "LRS_CAP_ELEM_BACKWARD", "LRS_CAP_ELEM_STEP", "LRS_CAP_SCAN_DELTA_DECAY",
                  "LRS_CAP_SCAN_DIAG_KEYSCALE", "LRS_CAP_SCAN_DIAG_EPILOGUE", "LRS_CAP_SCAN_DELTA_OUT",
@@ -58,7 +59,7 @@ def test_python_mirrors_header_constants():
 
 def test_version_and_check(lib):
     v = binding.lrs_abi_version()
-    assert v == (1 << 16) | (2 << 8) | 0
+    assert v == (1 << 16) | (3 << 8) | 0
     assert binding.LRS_ABI_VERSION_MAJOR == 1
     assert binding.lrs_abi_check(1) == binding.LRS_OK
     assert binding.lrs_abi_check(2) == binding.LRS_E_UNSUPPORTED

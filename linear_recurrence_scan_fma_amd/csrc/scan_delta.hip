@@ -43,6 +43,16 @@
 //    phases and two barriers: Y = K S0 (a S0) and Q S0 (qt S0), R = V - Y;
 //    then MTb R for the outputs and S = S0 + W R (diag(e^{G_L}) S0 + W R).
 //    fp32 operands are split into hi + lo bf16 terms.  K <= 128 in both forms.
+//
+// Time segments, where the (batch, head, V-tile) workgroups would leave most
+// of the device idle: a chunk maps its entering state affinely,
+// S_L = (I - W K) S0 + W V (decayed: (diag(e^{G_L}) - W a) S0 + W V), so a
+// run of chunks does too, S_out = A_s S_in + B_s.  A segment pass (the scan
+// without its readout) runs segment 0 from s0 and, for every later segment
+// but the last, K identity columns with zero values (their state at the end
+// is A_s) beside state columns from zero (B_s); delta_seg_prefix chains the
+// entering states in fp32; then the scan runs every segment at once from its
+// entering state.
 #include "lrs_internal.h"
 #include "mfma_util.h"
 

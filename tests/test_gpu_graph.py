@@ -107,6 +107,25 @@ def test_graph_delta_out_bf16_decay_k128(ctx):
     _replay_matches(run, [x[n] for n in names], fresh, [o, fin])
 
 
+def test_graph_delta_time_segments(ctx):
+    # the delta rule in time segments (segment pass, prefix, output pass)
+    B, T, H, K, V = 1, 1300, 2, 128, 128
+    d = inputs.deltanet(B=B, T=T, H=H, K=K, V=V, seed=1611)
+    names = ("q", "k", "v", "beta")
+    x = {n: d[n].to("cuda:0") for n in names}
+    o = torch.empty((B, T, H, V), device="cuda:0")
+    fin = torch.empty((B, H, K, V), device="cuda:0")
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_DELTA_SEGMENTS, 3)
+    try:
+        say("graph: delta rule, 3 time segments")
+        run = lambda: binding.lrs_scan_delta(ctx, x["q"], x["k"], x["v"], x["beta"], 1.0, None, o, fin)  # noqa: E731
+        fresh = lambda i: [inputs.deltanet(B=B, T=T, H=H, K=K, V=V, seed=1710 + i)[n].to("cuda:0")  # noqa: E731
+                           for n in names]
+        _replay_matches(run, [x[n] for n in names], fresh, [o, fin])
+    finally:
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_DELTA_SEGMENTS, 0)
+
+
 def test_graph_elementwise_stream_schedule(ctx):
     B, T, N = 2, 500, 256
     d = inputs.elementwise_small(B, T, N, seed=1601)

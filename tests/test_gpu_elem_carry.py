@@ -1,0 +1,120 @@
+"""GPU parity of the elementwise scans on inputs whose carries persist, against
+the sequential fp64 oracle, through the C ABI.
+
+With the workloads' own coefficients (a in (0.5, 1)) the product of a over a
+128-step tile is below 1e-15, so a carry reaches only the first steps of the
+next tile and a tile's aggregate product never matters: a look-back that
+composed aggregates wrongly would pass.  Here the carry spans the whole
+sequence: the FMA form with a = 1 exactly (running sums: every aggregate
+product is 1 and every earlier step shifts every later output), and the gated
+form with a = 1 - U(0, 1e-3) (a tile keeps >= 88% of its carry).  Both
+schedules, the look-back under scrambled arrival, the gradient passes (whose
+reverse carries are the same products) and the allocation-free entry.
+
+Tolerance: normwise 1e-5 per tensor, as for the other elementwise tests.
+A sequential fp32 running sum over 16,384 steps is itself ~4e-6 off the fp64
+sums (numpy, measured); the blocked order of the kernels is no worse.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrence_scan_fma_amd import binding, inputs
+from _helpers import dev, rel, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    c = binding.Context(0)
+    yield c
+    binding.lrs_context_set_param(c, binding.LRS_PARAM_ELEM_SCHEDULE, 0)
+    binding.lrs_context_set_param(c, binding.LRS_PARAM_LOOKBACK_DELAY_SEED, 0)
+    c.close()
+
+
+def _slow_gated(B, T, N, seed):
+    rng = np.random.default_rng(seed)
+    a = torch.from_numpy((1.0 - rng.uniform(0.0, 1e-3, (B, T, N))).astype(np.float32))
+    u = torch.from_numpy(rng.standard_normal((B, T, N)).astype(np.float32))
+    return a, u, inputs.random_state((B, N), seed + 1)
+
+
+def _running_sum(B, T, N, seed):
+    rng = np.random.default_rng(seed)
+    a = torch.ones((B, T, N), dtype=torch.float32)
+    b = torch.from_numpy(rng.standard_normal((B, T, N)).astype(np.float32))
+    return a, b, inputs.random_state((B, N), seed + 1)
+
+
+# (schedule, look-back delay seed): both schedules, and the look-back with
+# tiles publishing and reading in scrambled orders
+MODES = [(binding.LRS_ELEM_SCHEDULE_STREAM, 0), (binding.LRS_ELEM_SCHEDULE_LOOKBACK, 0),
+         (binding.LRS_ELEM_SCHEDULE_LOOKBACK, 7), (binding.LRS_ELEM_SCHEDULE_LOOKBACK, 4242)]
+MODE_IDS = ["stream", "lookback", "scrambled7", "scrambled4242"]
+
+CASES = [
+    ("gated", (2, 65613, 130)),   # 513 tiles with a ragged tail; N % 4 != 0 (one channel per lane)
+    ("gated", (1, 65536, 256)),   # float4 lanes, 4 channel tiles
+    ("fma", (2, 16387, 68)),      # running sums, ragged in T and N
+]
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-" + "x".join(map(str, c[1])))
+def test_persistent_carry(ctx, case, mode):
+    kind, (B, T, N) = case
+    schedule, delay_seed = mode
+    say(f"elem carry {kind} B={B} T={T} N={N} schedule={schedule} delay_seed={delay_seed}")
+    a, x, s0 = (_slow_gated if kind == "gated" else _running_sum)(B, T, N, 3100 + T + N)
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, schedule)
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_LOOKBACK_DELAY_SEED, delay_seed)
+    try:
+        s, fin = binding.scan_elementwise(ctx, kind, dev(a), dev(x), dev(s0))
+        torch.cuda.synchronize()
+        assert binding.lrs_context_check(ctx) == binding.LRS_OK
+        rs, rf = (oracle.scan_gated if kind == "gated" else oracle.scan_fma)(a, x, s0)
+        err = max(rel(s, rs), rel(fin, rf))
+        say(f"   forward rel err {err:.2e}")
+        assert err <= TOL, err
+        assert torch.equal(fin, s[:, -1])
+
+        # gradient pass from the oracle's forward states
+        rng = np.random.default_rng(T + N)
+        ds = torch.from_numpy(rng.standard_normal((B, T, N)).astype(np.float32))
+        dsf = torch.from_numpy(rng.standard_normal((B, N)).astype(np.float32))
+        sref = torch.from_numpy(rs.astype(np.float32))
+        da, dx, ds0 = binding.scan_elementwise_backward(ctx, kind, dev(a), dev(x), dev(sref), dev(ds), dev(s0),
+                                                        dev(dsf))
+        torch.cuda.synchronize()
+        assert binding.lrs_context_check(ctx) == binding.LRS_OK
+        if kind == "gated":
+            r = oracle.scan_gated_backward(a, x, sref, ds, s0, dsf)
+        else:
+            r = oracle.scan_fma_backward(a, sref, ds, s0, dsf)
+        err = max(rel(da, r[0]), rel(dx, r[1]), rel(ds0, r[2]))
+        say(f"   gradient rel err {err:.2e}")
+        assert err <= TOL, err
+    finally:
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, 0)
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_LOOKBACK_DELAY_SEED, 0)
+
+
+def test_persistent_carry_noalloc(ctx):
+    B, T, N = 2, 65613, 130
+    say(f"elem carry noalloc gated B={B} T={T} N={N}")
+    a, u, s0 = _slow_gated(B, T, N, 3200)
+    s = torch.empty((B, T, N), dtype=torch.float32, device="cuda:0")
+    fin = torch.empty((B, N), dtype=torch.float32, device="cuda:0")
+    binding.lrs_scan_gated_noalloc(dev(a), dev(u), dev(s0), s, fin)
+    torch.cuda.synchronize()
+    rs, rf = oracle.scan_gated(a, u, s0)
+    err = max(rel(s, rs), rel(fin, rf))
+    say(f"   rel err {err:.2e}")
+    assert err <= TOL, err

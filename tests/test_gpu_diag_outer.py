@@ -152,6 +152,19 @@ def test_time_segments(ctx, mode, V, segments):
         _check(ctx, d, inputs.random_state((B, H, K, V), 8))
 
 
+@pytest.mark.parametrize("segments", [1, 5])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_no_decay(ctx, mode, segments):
+    # g = 0: plain linear attention, the state a running sum of k v^T that
+    # grows over the whole sequence (every segment's carry matters in full)
+    B, T, H, K, V = 1, 2000, 2, 128, 64
+    d = _mamba(B, T, H, K, V, seed=71) if mode == 0 else inputs.gla(B=B, T=T, H=H, K=K, V=V, seed=72)
+    d["g"] = torch.zeros_like(d["g"])
+    say(f"diag mode{mode} no decay segments={segments}")
+    with _Segments(ctx, segments):
+        _check(ctx, d, inputs.random_state((B, H, K, V), 9))
+
+
 def test_scalar_decay_strong_gates(ctx):
     B, T, H, K, V = 1, 192, 2, 128, 64
     d = _mamba(B, T, H, K, V, seed=41)

@@ -6,10 +6,15 @@ With the workloads' own coefficients (a in (0.5, 1)) the product of a over a
 next tile and a tile's aggregate product never matters: a look-back that
 composed aggregates wrongly would pass.  Here the carry spans the whole
 sequence: the FMA form with a = 1 exactly (running sums: every aggregate
-product is 1 and every earlier step shifts every later output), and the gated
-form with a = 1 - U(0, 1e-3) (a tile keeps >= 88% of its carry).  Both
+product is 1 and every earlier step shifts every later output) or a = +-1
+with random signs (aggregate products of either sign), and the gated form
+with a = 1 - U(0, 1e-3) (a tile keeps >= 88% of its carry).  Both
 schedules, the look-back under scrambled arrival, the gradient passes (whose
 reverse carries are the same products) and the allocation-free entry.
+
+Gates of exactly 0 and 1 (reset to u, hold the state) make every result a
+copy of one input value, which fp32 represents exactly whatever the order of
+composition: there the scan must reproduce the oracle bit for bit.
 
 Tolerance: normwise 1e-5 per tensor, as for the other elementwise tests.
 A sequential fp32 running sum over 16,384 steps is itself ~4e-6 off the fp64
@@ -46,9 +51,11 @@ def _slow_gated(B, T, N, seed):
     return a, u, inputs.random_state((B, N), seed + 1)
 
 
-def _running_sum(B, T, N, seed):
+def _running_sum(B, T, N, seed, signs=False):
     rng = np.random.default_rng(seed)
     a = torch.ones((B, T, N), dtype=torch.float32)
+    if signs:
+        a = torch.from_numpy(rng.choice(np.array([-1.0, 1.0], np.float32), (B, T, N)))
     b = torch.from_numpy(rng.standard_normal((B, T, N)).astype(np.float32))
     return a, b, inputs.random_state((B, N), seed + 1)
 
@@ -63,6 +70,7 @@ CASES = [
     ("gated", (2, 65613, 130)),   # 513 tiles with a ragged tail; N % 4 != 0 (one channel per lane)
     ("gated", (1, 65536, 256)),   # float4 lanes, 4 channel tiles
     ("fma", (2, 16387, 68)),      # running sums, ragged in T and N
+    ("fma_signs", (1, 16384, 256)),   # a = +-1
 ]
 
 
@@ -72,7 +80,11 @@ def test_persistent_carry(ctx, case, mode):
     kind, (B, T, N) = case
     schedule, delay_seed = mode
     say(f"elem carry {kind} B={B} T={T} N={N} schedule={schedule} delay_seed={delay_seed}")
-    a, x, s0 = (_slow_gated if kind == "gated" else _running_sum)(B, T, N, 3100 + T + N)
+    if kind == "gated":
+        a, x, s0 = _slow_gated(B, T, N, 3100 + T + N)
+    else:
+        a, x, s0 = _running_sum(B, T, N, 3100 + T + N, signs=kind == "fma_signs")
+        kind = "fma"
     binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, schedule)
     binding.lrs_context_set_param(ctx, binding.LRS_PARAM_LOOKBACK_DELAY_SEED, delay_seed)
     try:
@@ -118,3 +130,29 @@ def test_persistent_carry_noalloc(ctx):
     err = max(rel(s, rs), rel(fin, rf))
     say(f"   rel err {err:.2e}")
     assert err <= TOL, err
+
+
+@pytest.mark.parametrize("mode", MODES, ids=MODE_IDS)
+def test_hold_and_reset_exact(ctx, mode):
+    # a in {0, 1}: s_t is u at the last reset, or s0 before any; exact in fp32
+    # for any composition order, so the scan must match the oracle bit for bit
+    B, T, N = 2, 20000, 132
+    schedule, delay_seed = mode
+    say(f"elem gated hold/reset B={B} T={T} N={N} schedule={schedule} delay_seed={delay_seed}")
+    rng = np.random.default_rng(3300)
+    # resets are rare (1 in 300 steps), so states are held across many tiles
+    a = torch.from_numpy((rng.uniform(0.0, 1.0, (B, T, N)) >= 1.0 / 300).astype(np.float32))
+    u = torch.from_numpy(rng.standard_normal((B, T, N)).astype(np.float32))
+    s0 = inputs.random_state((B, N), 3301)
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, schedule)
+    binding.lrs_context_set_param(ctx, binding.LRS_PARAM_LOOKBACK_DELAY_SEED, delay_seed)
+    try:
+        s, fin = binding.scan_elementwise(ctx, "gated", dev(a), dev(u), dev(s0))
+        torch.cuda.synchronize()
+        assert binding.lrs_context_check(ctx) == binding.LRS_OK
+    finally:
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_ELEM_SCHEDULE, 0)
+        binding.lrs_context_set_param(ctx, binding.LRS_PARAM_LOOKBACK_DELAY_SEED, 0)
+    rs, rf = oracle.scan_gated(a, u, s0)
+    assert torch.equal(s.cpu(), torch.from_numpy(rs.astype(np.float32)))
+    assert torch.equal(fin.cpu(), torch.from_numpy(rf.astype(np.float32)))

@@ -243,8 +243,9 @@ lrs_status lrs_context_check(LrsContext* ctx);
  *   s             fp32 [B,T,N]   output: s[:,t-1,:] = s_t, t = 1..T
  *   s_final       fp32 [B,N]     output: s_T (bit-equal to s[:,T-1,:])
  *
- * The gated form is evaluated as fma(a, s - u, u), algebraically equal to
- * a s + (1 - a) u.  Any int32 sizes are accepted (offsets are 64-bit).  The
+ * The gated form is evaluated as written, fma(a, s, (1 - a) u) in fp32 (so a
+ * gate of exactly 1 holds the state bit for bit and one of 0 copies u).  Any
+ * int32 sizes are accepted (offsets are 64-bit).  The
  * look-back schedule keeps 24 bytes of status words per channel and 128 time
  * steps in the context workspace (about 50 MB for B=16, T=8192, N=2048).
  */
@@ -299,7 +300,7 @@ lrs_status lrs_scan_gated_backward(LrsContext* ctx, const float* a, const float*
  *
  *   a, b (or u)   fp32 [B,N]   this step's inputs
  *   s             fp32 [B,N]   state, read and overwritten:
- *                              s = a s + b   or   s = fma(a, s - u, u)
+ *                              s = a s + b   or   s = a s + (1 - a) u
  *
  * Bit-identical to lrs_scan_fma / lrs_scan_gated with T = 1.  s must not
  * overlap a or b (u).  Errors as lrs_scan_fma.

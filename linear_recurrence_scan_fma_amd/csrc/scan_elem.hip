@@ -1,6 +1,6 @@
 // Elementwise first-order scans on gfx950:
 //   FMA form    s_t = a_t s_{t-1} + b_t
-//   gated form  s_t = a_t s_{t-1} + (1 - a_t) u_t   (evaluated as fma(a, s - u, u))
+//   gated form  s_t = a_t s_{t-1} + (1 - a_t) u_t   (evaluated as fma(a, s, (1 - a) u))
 // [SunnyNet log §2.1: "SunnyNet 工程化实录：一个 O(N) 架构如何长出自己的 C 推理运行时",
 //  developer.aliyun.com/article/1773847 -- the unified kernel's two forms].
 //

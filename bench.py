@@ -500,6 +500,13 @@ MATRIX_ROWS = {
     "decay_k128_bf16": ("scan_delta_out B=4 T=4096 H=8 K=128 V=128 (per-key decay), bf16 out", "decay",
                         "decay_k128", ["delta_prep_decay_B4_T4096_H8_K128",
                                        "delta_scan_decay_B4_T4096_H8_K128_V128_bf16"], "bf16"),
+    # one long sequence: the automatic plan runs it in time segments (segment
+    # pass, prefix over segments, output pass)
+    "deltanet_b1_long": ("scan_delta DeltaNet B=1 T=16384 H=8 K=128 V=128 (time segments)", "delta",
+                         "deltanet_b1_long",
+                         ["delta_prep_deltanet_B1_T16384_H8_K128", "delta_segscan_deltanet_B1_T16384_H8_K128_V128",
+                          "delta_segprefix_deltanet_B1_T16384_H8_K128_V128",
+                          "delta_scan_deltanet_B1_T16384_H8_K128_V128"], "f32"),
 }
 
 
@@ -511,7 +518,8 @@ def gen_workload(inputs, which):
             "deltanet": lambda: inputs.deltanet(**inputs.DELTANET),
             "deltanet_k64": lambda: inputs.deltanet(**inputs.DELTANET_K64),
             "rwkv7": lambda: inputs.rwkv7(**inputs.RWKV7),
-            "decay_k128": lambda: inputs.rwkv7(**inputs.DELTA_DECAY_K128)}[which]()
+            "decay_k128": lambda: inputs.rwkv7(**inputs.DELTA_DECAY_K128),
+            "deltanet_b1_long": lambda: inputs.deltanet(**inputs.DELTANET_B1_LONG)}[which]()
 
 
 def oracle_matrix(kind, d, nthreads, heads=None):

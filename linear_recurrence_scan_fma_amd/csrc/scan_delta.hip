@@ -1338,47 +1338,104 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
 }
 
 // The states entering segments 2 .. nseg - 1, one after another:
-// S_{s+1} = A_s S_s + B_s, in fp32, summing over keys in order; a workgroup
-// owns a 16-column V-tile of one (batch, head) (its columns depend on no
-// other columns), S_s's tile staged in LDS.
+// S_{s+1} = A_s S_s + B_s, in fp32; a workgroup owns a 16-column V-tile of
+// one (batch, head) (its columns depend on no other columns).  The chain over
+// segments is sequential, so each step is kept short: A_s comes into LDS from
+// 16-byte pieces loaded one step ahead (the loads do not depend on the chain),
+// and the product runs on the fp32 matrix cores (16x16x4: lane l holds
+// A[l % 16][l / 16], B[l / 16][l % 16] and C[4 (l / 16) + r][l % 16]), wave w
+// owning the 16-row tiles w, w + 4 of the KP rows.  Four consecutive keys of a
+// lane's row feed four products in turn (the contraction index permuted the
+// same way in A and B), so one 16-byte LDS read serves four products.  Rows
+// and keys past K are zero.
 template <int KP>
 __global__ __launch_bounds__(NT) void delta_seg_prefix_kernel(DeltaArgs p) {
-    constexpr int CPT = 16 * KP / NT;   // columns per thread
-    __shared__ float sS[KP][16];
-    const int tid = threadIdx.x;
+    constexpr int LDA = KP + 4;            // 16-byte aligned rows, 4 banks apart
+    constexpr int NP = KP * KP / 4 / NT;   // 16-byte pieces of A_s per thread
+    constexpr int RT = KP / 64;            // 16-row tiles per wave
+    static_assert(NT == 256 && VT == 16, "four waves, 16-column tiles");
+    __shared__ __align__(16) float sST[VT * LDA];   // S_s^T: [column][key]
+    __shared__ __align__(16) float sA[KP * LDA];    // A_s: [row][key]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
     const int vt = blockIdx.x % p.vtiles, bh = blockIdx.x / p.vtiles;
     const int K = p.K, V = p.V;
     const int64_t bhs = static_cast<int64_t>(p.B) * p.H;
-    const int d = tid % KP, c0 = (tid / KP) * CPT;
-    for (int i = tid; i < KP * 16; i += NT) {
-        const int e = i / 16, col = VT * vt + i % 16;
-        sS[e][i % 16] = e < K && col < V ? p.seg_state[(bhs + bh) * K * V + static_cast<int64_t>(e) * V + col] : 0.0f;
-    }
-    __syncthreads();
-    for (int s = 1; s <= p.nseg - 2; ++s) {
-        const float* ab = p.seg_ab + (s * bhs + bh) * K * (K + V) + static_cast<int64_t>(d) * (K + V);
-        float acc[CPT];
+    const int col = VT * vt + c16;
+    // 16-byte loads when every row of A_s | B_s starts 16-byte aligned
+    const bool v4 = (K + V) % 4 == 0 && reinterpret_cast<uintptr_t>(p.seg_ab) % 16 == 0;
+    f32x4 pa[NP];
+    auto load_a = [&](int s) {
+        const float* ab = p.seg_ab + (s * bhs + bh) * K * (K + V);
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            const int col = VT * vt + c0 + j;
-            acc[j] = d < K && col < V ? ab[K + col] : 0.0f;
+        for (int j = 0; j < NP; ++j) {
+            const int pc = tid + j * NT, r = pc / (KP / 4), e0 = (pc % (KP / 4)) * 4;
+            const float* src = ab + static_cast<int64_t>(r) * (K + V) + e0;
+            // (no use of the loaded values here: a use would wait for each load
+            // in turn; keys past K - 1 are zeroed where the pieces are stored)
+            f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (r < K && e0 < K) {
+                if (v4) {
+                    x = *reinterpret_cast<const f32x4*>(src);   // may run past key K - 1 into B_s
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (e0 + q < K) x[q] = src[q];
+                }
+            }
+            pa[j] = x;
         }
-        if (d < K) {
-            for (int e = 0; e < K; ++e) {
-                const float a = ab[e];
+    };
+    for (int i = tid; i < KP * VT; i += NT) {
+        const int e = i / VT, c = i % VT;
+        sST[c * LDA + e] = e < K && VT * vt + c < V
+                               ? p.seg_state[(bhs + bh) * K * V + static_cast<int64_t>(e) * V + VT * vt + c]
+                               : 0.0f;
+    }
+    if (p.nseg > 2) load_a(1);
+    for (int s = 1; s <= p.nseg - 2; ++s) {
+        const float* ab = p.seg_ab + (s * bhs + bh) * K * (K + V);
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) acc[j] = __builtin_fmaf(a, sS[e][c0 + j], acc[j]);
+        for (int j = 0; j < NP; ++j) {
+            const int pc = tid + j * NT, r = pc / (KP / 4), e0 = (pc % (KP / 4)) * 4;
+            f32x4 x = pa[j];
+            if (e0 + 4 > K) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[q] = e0 + q < K ? x[q] : 0.0f;
+            }
+            *reinterpret_cast<f32x4*>(sA + r * LDA + e0) = x;
+        }
+        // B_s into the accumulators: rows 16 (wave + 4 t) + 4 g + r, column col
+        f32x4 acc[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int d = 16 * (wave + 4 * t) + 4 * g + r;
+                acc[t][r] = d < K && col < V ? ab[static_cast<int64_t>(d) * (K + V) + K + col] : 0.0f;
+            }
+        __syncthreads();   // A_s staged, S_s written
+        if (s + 1 <= p.nseg - 2) load_a(s + 1);   // in flight during the product
+#pragma unroll
+        for (int kb = 0; kb < KP / 16; ++kb) {
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(sST + c16 * LDA + 16 * kb + 4 * g);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(sA + (16 * (wave + 4 * t) + c16) * LDA + 16 * kb + 4 * g);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[j], b4[j], acc[t], 0, 0, 0);
             }
         }
-        __syncthreads();   // every read of S_s is done
+        __syncthreads();   // every read of S_s and A_s is done
         float* out = p.seg_state + ((s + 1) * bhs + bh) * K * V;
 #pragma unroll
-        for (int j = 0; j < CPT; ++j) {
-            sS[d][c0 + j] = acc[j];
-            const int col = VT * vt + c0 + j;
-            if (d < K && col < V) out[static_cast<int64_t>(d) * V + col] = acc[j];
+        for (int t = 0; t < RT; ++t) {
+            const int d0 = 16 * (wave + 4 * t) + 4 * g;
+            *reinterpret_cast<f32x4*>(sST + c16 * LDA + d0) = acc[t];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (d0 + r < K && col < V) out[static_cast<int64_t>(d0 + r) * V + col] = acc[t][r];
         }
-        __syncthreads();
     }
 }
 

@@ -59,6 +59,9 @@ RWKV7 = dict(B=4, T=4096, H=12, K=64, V=64)
 DELTA_DECAY_K128 = dict(B=4, T=4096, H=8, K=128, V=128)   # RWKV-7's decay law at DeltaNet's head shape
 HGRN2 = dict(B=4, T=4096, H=16, K=128, V=128)
 ASSOC = dict(B=4, T=4096, H=8, K=64, V=64)
+# one long DeltaNet sequence: too few (head, V-tile) workgroups to fill the
+# chip, so the call splits the time axis into segments
+DELTANET_B1_LONG = dict(B=1, T=16384, H=8, K=128, V=128)
 
 
 def _f32(x64: np.ndarray) -> torch.Tensor:

@@ -745,13 +745,15 @@ __device__ __forceinline__ int swz(int r, int p) {
 
 // Wave w owns chunk rows 16w .. 16w+15 (Y, R, outputs) and state keys
 // 16 STW w .. (row tiles of S).  The chunk's operand tiles (q and k; decayed
-// form: a and qt as hi/lo) and the V tile sit in one of two LDS stages (by
-// chunk parity) as swizzled tiles read as matrix-core operands.  W, MTb (and
+// form: a and qt as hi/lo) and the V tile sit in LDS as swizzled tiles read
+// as matrix-core operands (one stage each with vector loads, two by chunk
+// parity on the scalar path).  W, MTb (and
 // e^{G_L}) go straight to registers as operand fragments: each wave reads
 // only the W rows of its own state keys and the MTb rows of its own chunk
 // rows, as contiguous 1 KB fragments.  With vector loads all of the next
 // chunk's loads are issued at the top of a chunk: the operand and V tiles
-// into registers, written to the other stage at the chunk's end; W and MTb
+// into registers, written to LDS at the chunk's end (after the middle
+// barrier, no wave reads the chunk's own tiles any more); W and MTb
 // into the other of two register sets (the chunk loop is unrolled twice, so
 // the sets alternate with no copies).  The first chunk's tiles come through
 // loads with an LDS destination.  Per chunk, two barriers:
@@ -761,8 +763,8 @@ __device__ __forceinline__ int swz(int r, int p) {
 //   2. O = scale (O1 + MTb R) -> outputs; S = D S0 + W R (tiles of this wave)
 //      -> LDS as the next chunk's operand
 // The decayed form at K = 128 has 64 KB of operand tiles per chunk, too much
-// to double buffer beside the rest: there they are single buffered, and each
-// wave loads the next chunk's rows of its own (the only rows it reads) with
+// to stage through registers beside the rest: each wave loads the next
+// chunk's rows of its own (the only rows it reads) with
 // LDS-destination loads as soon as its step 1 is done with them, so they
 // load during step 2.
 // SEGP = false: outputs of segment s from the state entering it (all
@@ -794,8 +796,13 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     static_assert(STW >= 1, "state tiles");
     static_assert(QB % 1024 == 0 && PB % 1024 == 0 && VB == 2048, "1 KB load runs");
 
-    __shared__ __align__(16) unsigned char sOps[(SPLIT ? 1 : 2) * OPS];
-    __shared__ __align__(16) unsigned char sPV[2 * PVS];
+    // Stages: with vector loads the next chunk's tiles are written at the end of
+    // a chunk, after its middle barrier, when no wave reads the chunk's own
+    // tiles any more: one stage of each.  The scalar path loads the next
+    // chunk's tiles into LDS during the chunk: two stages, by chunk parity.
+    constexpr int NSO = (SPLIT || VEC) ? 1 : 2, NSV = VEC ? 1 : 2;
+    __shared__ __align__(16) unsigned char sOps[NSO * OPS];
+    __shared__ __align__(16) unsigned char sPV[NSV * PVS];
     __shared__ __align__(16) u16 sRTh[VT * LDL];     // R^T hi/lo
     __shared__ __align__(16) u16 sRTl[VT * LDL];
     __shared__ __align__(16) u16 sSh[VT * LDK];      // S^T hi/lo entering the chunk
@@ -948,7 +955,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
 
     // ---- register-staged prefetch of the next chunk (vector loads) ----
     // The same 16-byte slots as the LDS-direct loads above, loaded into
-    // registers during a chunk and written to the other stage at its end.
+    // registers during a chunk and written to LDS at its end.
     // (An LDS-direct load in flight makes the compiler wait for it before any
     // later LDS read it cannot tell apart, which would expose the prefetch.)
     // Plain form: q and k pieces of runs 0 .. QB/4096 - 1; decayed form (not
@@ -1133,8 +1140,8 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
         }
     };
     write_state_lds();
-    fetch_ops(c_begin, sOps + (SPLIT ? 0 : (c_begin & 1) * OPS));
-    fetch_pv(c_begin, sPV + (c_begin & 1) * PVS);
+    fetch_ops(c_begin, sOps + (NSO == 2 ? (c_begin & 1) * OPS : 0));
+    fetch_pv(c_begin, sPV + (NSV == 2 ? (c_begin & 1) * PVS : 0));
     load_w(c_begin, wcur, ecur, mcur);
     if constexpr (VEC && DECAY)
         if (c_begin + 1 < c_end) l2_touch(c_begin + 1);
@@ -1179,11 +1186,11 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
     auto step = [&](int c, u32x4 (&wc)[STW][2][2], f32x4 (&ec)[DECAY ? STW : 1], u32x4 (&mc)[2][2],
                     u32x4 (&wn)[STW][2][2], f32x4 (&en)[DECAY ? STW : 1], u32x4 (&mn)[2][2]) {
         const int64_t t0 = static_cast<int64_t>(c) * L;
-        const unsigned char* st = sOps + (SPLIT ? 0 : (c & 1) * OPS);
-        const unsigned char* sp = sPV + (c & 1) * PVS;
+        const unsigned char* st = sOps + (NSO == 2 ? (c & 1) * OPS : 0);
+        const unsigned char* sp = sPV + (NSV == 2 ? (c & 1) * PVS : 0);
         const bool more = c + 1 < c_end;
-        unsigned char* so_n = sOps + (SPLIT ? 0 : ((c + 1) & 1) * OPS);
-        unsigned char* sp_n = sPV + ((c + 1) & 1) * PVS;
+        unsigned char* so_n = sOps + (NSO == 2 ? ((c + 1) & 1) * OPS : 0);
+        unsigned char* sp_n = sPV + (NSV == 2 ? ((c + 1) & 1) * PVS : 0);
         // LDS-direct loads in flight (the first chunk's; SPLIT: every chunk's
         // operand rows) are waited for here; register-staged loads by their use
         if constexpr (VEC)
@@ -1297,7 +1304,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             }
         }
         write_state_lds();
-        if constexpr (VEC) prestore(so_n, sp_n);   // the other stage (SPLIT: this wave's rows only)
+        if constexpr (VEC) prestore(so_n, sp_n);   // the next chunk's tiles (SPLIT: the V tile only)
     };
     for (int c = c_begin; c < c_end; c += 2) {
         step(c, wcur, ecur, mcur, wnxt, enxt, mnxt);

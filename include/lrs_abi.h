@@ -197,10 +197,9 @@ void lrs_context_destroy(LrsContext* ctx);
  * context keeps the states and transitions (4 K (K + 2V) bytes per (batch,
  * head) and segment) beside the per-chunk workspace:
  *   0 (default)  one segment while the (batch, head, 16-column V-tile)
- *                workgroups fill half the compute units or more; otherwise
- *                the most segments (of at least 8 chunks, 512 steps) whose
- *                output pass and segment pass each still fit the compute
- *                units once;
+ *                workgroups outnumber half the compute units; otherwise the
+ *                most segments (of at least 8 chunks, 512 steps) whose output
+ *                pass and segment pass each still fit the compute units once;
  *   1            one pass over all chunks;
  *   n >= 2       n segments (capped at the number of chunks).
  * Any value gives results within the documented tolerance.

@@ -1254,15 +1254,15 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
             if constexpr (DECAY)   // (the plain form's shared lines already hit in L2)
                 if (c + 2 < c_end) l2_touch(c + 2);
         }
-        if constexpr (SPLIT) {
-            // this wave's operand rows are read (y and o1 hold them): the next
-            // chunk's may overwrite them
-            if (more) {
-                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS reads are done
-                fetch_ops(c + 1, sOps);
-            }
-        }
         __syncthreads();
+        if constexpr (SPLIT) {
+            // this wave's operand rows are read (y and o1 hold them; the
+            // barrier waited for its LDS reads): the next chunk's may overwrite
+            // them.  Issued after the barrier, which would otherwise wait for
+            // these LDS-destination loads; the wait at the top of the next
+            // chunk takes them instead, after step 2.
+            if (more) fetch_ops(c + 1, sOps);
+        }
 
         // ---- 2: O = scale (O1 + MTb R); S = D S0 + W R ----
         bf16x8 rh[2], rl[2];

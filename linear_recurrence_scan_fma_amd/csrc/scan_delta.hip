@@ -1351,7 +1351,7 @@ __global__ __launch_bounds__(NT) void delta_scan_kernel(DeltaArgs p) {
 // 16-byte pieces loaded one step ahead (the loads do not depend on the chain),
 // and the product runs on the fp32 matrix cores (16x16x4: lane l holds
 // A[l % 16][l / 16], B[l / 16][l % 16] and C[4 (l / 16) + r][l % 16]), wave w
-// owning the 16-row tiles w, w + 4 of the KP rows.  Four consecutive keys of a
+// owning the 16-row tiles w, w + 4, ... (KP / 64 of them).  Four consecutive keys of a
 // lane's row feed four products in turn (the contraction index permuted the
 // same way in A and B), so one 16-byte LDS read serves four products.  Rows
 // and keys past K are zero.

@@ -2,7 +2,11 @@
 
 This module holds no recurrence arithmetic.  It draws the inputs that both the
 GPU library and the CPU reference consume, so the two sides always see exactly
-the same values.  Every generator returns host (CPU) torch tensors.
+the same values.  Every generator returns host (CPU) torch tensors, except the
+``*_device`` ones at the end: for tensors of several GiB (the cases past
+32-bit offsets) host draws would take minutes, so those follow the same
+recipes with torch's seeded device generator, in float32, and return device
+tensors (their values depend on the seed and on torch's generator).
 
 Recipe (all draws from ``numpy.random.default_rng(seed)``; transcendentals in
 float64; rounding to float32 by round-to-nearest-even; bfloat16 values are
@@ -221,3 +225,89 @@ def random_normal(shape, seed):
     for i in range(shape[0]):
         out[i] = _f32(rng.standard_normal(tuple(shape[1:])))
     return out
+
+
+# ---- device-side draws, for tensors past 32-bit offsets ----
+
+def _device_gen(seed, device):
+    return torch.Generator(device=device).manual_seed(int(seed))
+
+
+def _normal_bf16_device(shape, gen, device, unit_rows=False):
+    """N(0,1) draws rounded to bf16, one leading-axis slice at a time (so the
+    float32 temporaries stay one slice); unit_rows: each last-axis row divided
+    by its L2 norm before the rounding."""
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    for i in range(shape[0]):
+        x = torch.randn(shape[1:], generator=gen, device=device)
+        if unit_rows:
+            x /= x.norm(dim=-1, keepdim=True)
+        out[i] = x.to(torch.bfloat16)
+    return out
+
+
+def gated_device(B, T, N, seed=SEED_BASE + 11, device="cuda:0"):
+    """The gated recipe on the device: a = sigmoid(z), z ~ N(2,1); u ~ N(0,1);
+    s0 ~ N(0,1); fp32 [B,T,N]."""
+    gen = _device_gen(seed, device)
+    a = torch.randn((B, T, N), generator=gen, device=device).add_(2.0).sigmoid_()
+    u = torch.randn((B, T, N), generator=gen, device=device)
+    s0 = torch.randn((B, N), generator=gen, device=device)
+    return dict(a=a, u=u, s0=s0)
+
+
+def deltanet_device(B, T, H, K, V, seed=SEED_BASE + 12, device="cuda:0"):
+    """The DeltaNet recipe on the device: L2-normalised q, k and v ~ N(0,1) in
+    bf16, beta = sigmoid(N(0,1)) fp32."""
+    gen = _device_gen(seed, device)
+    q = _normal_bf16_device((B, T, H, K), gen, device, unit_rows=True)
+    k = _normal_bf16_device((B, T, H, K), gen, device, unit_rows=True)
+    v = _normal_bf16_device((B, T, H, V), gen, device)
+    beta = torch.randn((B, T, H), generator=gen, device=device).sigmoid_()
+    return dict(q=q, k=k, v=v, beta=beta, scale=1.0, s0=None)
+
+
+def mamba2_device(B, T, H, K, V, seed=SEED_BASE + 13, device="cuda:0"):
+    """The Mamba-2 recipe on the device (one B/C group): dt = softplus(N(0,1)),
+    A_h = -exp(U(0,2)), g = dt A_h, B, C, x ~ N(0,1) bf16."""
+    gen = _device_gen(seed, device)
+    dt = torch.nn.functional.softplus(torch.randn((B, T, H), generator=gen, device=device))
+    A = -torch.exp(2.0 * torch.rand((H,), generator=gen, device=device))
+    g = dt * A
+    Bm = _normal_bf16_device((B, T, 1, K), gen, device)
+    Cm = _normal_bf16_device((B, T, 1, K), gen, device)
+    x = _normal_bf16_device((B, T, H, V), gen, device)
+    return dict(q=Cm, k=Bm, v=x, g=g, decay_mode=0, k_scale=dt, scale=1.0, s0=None)
+
+
+def gla_device(B, T, H, K, V, seed=SEED_BASE + 14, device="cuda:0"):
+    """The GLA recipe on the device: q, k, v ~ N(0,1) bf16, per-key
+    gk = logsigmoid(N(0,1))/16 fp32, readout scale K**-0.5."""
+    gen = _device_gen(seed, device)
+    q = _normal_bf16_device((B, T, H, K), gen, device)
+    k = _normal_bf16_device((B, T, H, K), gen, device)
+    v = _normal_bf16_device((B, T, H, V), gen, device)
+    g = torch.empty((B, T, H, K), dtype=torch.float32, device=device)
+    for i in range(B):
+        g[i] = torch.nn.functional.logsigmoid(torch.randn((T, H, K), generator=gen, device=device)) / 16.0
+    return dict(q=q, k=k, v=v, g=g, decay_mode=1, k_scale=None, scale=float(K) ** -0.5, s0=None)
+
+
+def rwkv7_device(B, T, H, K, V, seed=SEED_BASE + 15, device="cuda:0"):
+    """The RWKV-7 recipe on the device: DeltaNet's q, k, v, beta plus the
+    per-key log-decay g = -exp(-softplus(-z) - 0.5), z ~ N(0,1), fp32."""
+    d = deltanet_device(B, T, H, K, V, seed=seed, device=device)
+    gen = _device_gen(seed + 1000, device)
+    g = torch.empty((B, T, H, K), dtype=torch.float32, device=device)
+    for i in range(B):
+        z = torch.randn((T, H, K), generator=gen, device=device)
+        g[i] = -torch.exp(-torch.nn.functional.softplus(-z) - 0.5)
+    d["g"] = g
+    return d
+
+
+def random_normal_device(shape, seed, device="cuda:0"):
+    """An fp32 N(0, 1) tensor drawn on the device (incoming gradients and
+    stand-in forward states of the gradient pass at sizes past 32-bit offsets)."""
+    return torch.randn(tuple(shape), generator=_device_gen(seed, device), device=device)
+

@@ -72,7 +72,9 @@
  *   the stream schedule when the schedule is automatic, and returns
  *   LRS_E_UNSUPPORTED (nothing captured) when the look-back is forced.
  * Errors.  Arguments are validated on the host before anything is enqueued.
- *   On a non-zero status nothing was enqueued and the outputs are untouched.
+ *   On LRS_E_INVAL, LRS_E_UNSUPPORTED or LRS_E_NOMEM nothing was enqueued and
+ *   the outputs are untouched.  LRS_E_DEVICE means a launch failed; work the
+ *   call enqueued before it (clearing a freshly grown workspace) may still run.
  *   LRS_E_INVAL       NULL context or required pointer, a dimension < 1,
  *                     misalignment, an output that overlaps another buffer,
  *                     an unknown mode value.

@@ -753,10 +753,11 @@ lrs_status scan_delta_impl(LrsContext* ctx, const lrs_bf16* q, const lrs_bf16* k
     p.V = V;
     p.out_bf16 = out_dtype == LRS_DTYPE_BF16 ? 1 : 0;
     p.nseg = nseg;
-    // the vector path addresses one batch row of each tensor with 32-bit buffer offsets
+    // the vector path addresses one batch row of each tensor with 32-bit buffer
+    // offsets, and stores each lane's four outputs at once (16 or 8 bytes)
     const int64_t row_bytes = (static_cast<int64_t>(T) + 64) * H * (K > V ? K : V) * 4;
     p.vec = (K % 8 == 0 && V % 8 == 0 && aligned(q, 16) && aligned(k, 16) && aligned(v, 16) &&
-             aligned(g, 16) && row_bytes < (int64_t{1} << 31)) ? 1 : 0;
+             aligned(g, 16) && aligned(o, 16) && row_bytes < (int64_t{1} << 31)) ? 1 : 0;
     if (lrs::launch_scan_delta(p, ctx->delta_ws, st) != hipSuccess) return LRS_E_DEVICE;
     if (capturing(st)) ctx->captured = true;
     ctx->last_stream = st;

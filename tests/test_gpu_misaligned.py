@@ -68,6 +68,23 @@ def test_elementwise_misaligned(ctx, kind):
     assert err <= 1e-5, err
 
 
+@pytest.mark.parametrize("kind", ["fma", "gated"])
+def test_step_misaligned(ctx, kind):
+    B, N = 16, 2048
+    say(f"step {kind} misaligned B={B} N={N}")
+    d = inputs.elementwise_small(B, 1, N, seed=4208)
+    x = d["b"] if kind == "fma" else d["u"]
+    s0 = inputs.random_state((B, N), 4209)
+    s = _off(s0)
+    (binding.lrs_step_fma if kind == "fma" else binding.lrs_step_gated)(ctx, _off(d["a"][:, 0]), _off(x[:, 0]), s)
+    torch.cuda.synchronize()
+    # one step is the one-step scan
+    rs, _ = (oracle.scan_fma if kind == "fma" else oracle.scan_gated)(d["a"], x, s0)
+    err = rel(s, rs[:, 0])
+    say(f"   rel err {err:.2e}")
+    assert err <= 1e-5, err
+
+
 @pytest.mark.parametrize("decay", [False, True], ids=["plain", "decayed"])
 def test_delta_misaligned(ctx, decay):
     B, T, H, K, V = 1, 200, 2, 128 if not decay else 64, 128 if not decay else 64
